@@ -1,0 +1,336 @@
+// extern "C" entry points of libskinny_gemm (declared in include/skinny_gemm.h).
+//
+// Every entry point validates all of its arguments on the host before it
+// enqueues anything, then launches the kernels the configuration table names.
+// Argument checks are explicit branches that return a status (never assert),
+// so they hold in every build mode.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "sg_launch.h"
+#include "skinny_gemm.h"
+
+namespace {
+
+using sg::DotProblem;
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool al2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SG_OK : SG_ERR_HIP; }
+
+// Checks shared by every dot-product call once sizes are known non-negative
+// and the problem is non-empty.
+int check_operand16(const void* p, int64_t ld, int64_t min_ld) {
+  if (p == nullptr) return SG_ERR_INVALID_ARG;
+  if (ld < min_ld) return SG_ERR_INVALID_ARG;
+  if (!al16(p) || (ld % 8) != 0) return SG_ERR_MISALIGNED;
+  return SG_OK;
+}
+
+int check_output2(const void* p, int64_t ld, int64_t min_ld) {
+  if (p == nullptr) return SG_ERR_INVALID_ARG;
+  if (ld < min_ld) return SG_ERR_INVALID_ARG;
+  if (!al2(p)) return SG_ERR_MISALIGNED;
+  return SG_OK;
+}
+
+int check_workspace(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return SG_OK;
+  if (ws == nullptr || ws_bytes < need) return SG_ERR_WORKSPACE;
+  if (!al16(ws)) return SG_ERR_MISALIGNED;
+  return SG_OK;
+}
+
+bool same_config(const sg_config_t& a, const sg_config_t& b) {
+  return a.kind == b.kind && a.m_tile == b.m_tile && a.rows == b.rows && a.waves == b.waves &&
+         a.k_split == b.k_split && a.grid == b.grid;
+}
+
+// Enqueue out = a @ w^T (+res) with configuration c.  ws holds the split-K
+// partials when c.k_split > 1 (size checked by the caller).
+int enqueue_dot(DotProblem p, const sg_config_t& c, void* ws, hipStream_t s) {
+  switch (c.kind) {
+    case SG_KIND_NONE:
+      return SG_OK;
+    case SG_KIND_GEMV_SMALLK:
+      return hip_status(sg::launch_smallk(p, c, s));
+    case SG_KIND_GEMV_ROW:
+    case SG_KIND_GEMV_SPLITK:
+    case SG_KIND_MFMA_TILE: {
+      const bool split = c.k_split > 1;
+      if (split) p.partial = static_cast<float*>(ws);
+      hipError_t e = (c.kind == SG_KIND_MFMA_TILE) ? sg::launch_mfma(p, c, s) : sg::launch_gemv(p, c, s);
+      if (e != hipSuccess) return SG_ERR_HIP;
+      if (!split) return SG_OK;
+      sg::ReduceProblem r{};
+      r.partial = p.partial;
+      r.S = c.k_split;
+      r.M = p.M;
+      r.N = p.N;
+      r.res = p.res;
+      r.ldr = p.ldr;
+      r.out = p.out;
+      r.ldc = p.ldc;
+      return hip_status(sg::launch_reduce(r, s));
+    }
+    default:
+      return SG_ERR_UNSUPPORTED;
+  }
+}
+
+// Validation of skinny_gemm arguments; fills *cfg on success.
+int validate_gemm(const sg_bf16* A, int64_t lda, const sg_bf16* W, int64_t ldw, const sg_bf16* R,
+                  int64_t ldr, sg_bf16* C, int64_t ldc, int M, int N, int K,
+                  const sg_config_t* user_cfg, void* ws, size_t ws_bytes, sg_config_t* cfg,
+                  bool* empty) {
+  *empty = false;
+  if (M < 0 || N < 0 || K < 0) return SG_ERR_INVALID_ARG;
+  int st = sg_select(M, N, K, R != nullptr, cfg);
+  if (st != SG_OK) return st;
+  if (cfg->kind == SG_KIND_NONE) {
+    *empty = true;
+    return SG_OK;
+  }
+  if (K > 0) {  // with K == 0 the operands are never read
+    if ((st = check_operand16(A, lda, K)) != SG_OK) return st;
+    if ((st = check_operand16(W, ldw, K)) != SG_OK) return st;
+  }
+  if ((st = check_output2(C, ldc, N)) != SG_OK) return st;
+  if (R != nullptr && (st = check_output2(R, ldr, N)) != SG_OK) return st;
+  if (user_cfg != nullptr && !same_config(*user_cfg, *cfg)) return SG_ERR_UNSUPPORTED;
+  return check_workspace(ws, ws_bytes, sg_workspace_bytes(SG_OP_GEMM, M, N, K));
+}
+
+// The F_A/beta stage configuration: the table's choice, run in partial mode.
+// The small-K kernel has no partial mode, so that case uses the GEMV kernel
+// with one split.
+sg_config_t fab_config(int M, int n_ab, int K) {
+  sg_config_t c;
+  sg_select(M, n_ab, K, 0, &c);
+  if (c.kind == SG_KIND_GEMV_SMALLK) {
+    c.kind = SG_KIND_GEMV_SPLITK;
+    c.rows = 1;
+    c.k_split = 1;
+  }
+  if (c.k_split < 1) c.k_split = 1;
+  return c;
+}
+
+int validate_fab_fb(const sg_bf16* x, const sg_bf16* w_ab, const sg_bf16* w_b, sg_bf16* beta,
+                    sg_bf16* g1, sg_bf16* f_a, int M, int K, int n_ab, int rank, int n_b,
+                    void* ws, size_t ws_bytes, bool* empty) {
+  *empty = false;
+  if (M < 0 || K < 0 || n_b < 0 || rank <= 0 || n_ab <= rank) return SG_ERR_INVALID_ARG;
+  if (rank % 8 != 0 || rank > 512) return SG_ERR_UNSUPPORTED;
+  if (K % 8 != 0 || M > 256) return SG_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(M) * rank > sg::kFbMaxMRank) return SG_ERR_UNSUPPORTED;
+  if (M == 0) {
+    *empty = true;
+    return SG_OK;
+  }
+  int st;
+  if ((st = check_operand16(x, K, K)) != SG_OK) return st;
+  if ((st = check_operand16(w_ab, K, K)) != SG_OK) return st;
+  if ((st = check_operand16(w_b, rank, rank)) != SG_OK) return st;
+  if ((st = check_output2(beta, n_ab - rank, n_ab - rank)) != SG_OK) return st;
+  if (n_b > 0 && (st = check_output2(g1, n_b, n_b)) != SG_OK) return st;
+  if (n_b == 0 && g1 != nullptr && !al2(g1)) return SG_ERR_MISALIGNED;
+  if (f_a != nullptr && !al2(f_a)) return SG_ERR_MISALIGNED;
+  return check_workspace(ws, ws_bytes, sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K));
+}
+
+int enqueue_fab_fb(const sg_bf16* x, const sg_bf16* w_ab, const sg_bf16* w_b, sg_bf16* f_a,
+                   sg_bf16* beta, sg_bf16* g1, int M, int K, int n_ab, int rank, int n_b, void* ws,
+                   hipStream_t s) {
+  const sg_config_t c = fab_config(M, n_ab, K);
+  DotProblem p{};
+  p.a = x;
+  p.lda = K;
+  p.w = w_ab;
+  p.ldw = K;
+  p.M = M;
+  p.N = n_ab;
+  p.K = K;
+  p.partial = static_cast<float*>(ws);
+  hipError_t e = (c.kind == SG_KIND_MFMA_TILE) ? sg::launch_mfma(p, c, s) : sg::launch_gemv(p, c, s);
+  if (e != hipSuccess) return SG_ERR_HIP;
+  sg::FbProblem fb{};
+  fb.partial = p.partial;
+  fb.S = c.k_split;
+  fb.M = M;
+  fb.n_ab = n_ab;
+  fb.rank = rank;
+  fb.n_b = n_b;
+  fb.w_b = w_b;
+  fb.f_a = f_a;
+  fb.beta = beta;
+  fb.g1 = g1;
+  return hip_status(sg::launch_fab_fb_tail(fb, s));
+}
+
+}  // namespace
+
+extern "C" int skinny_gemm(const sg_bf16* A, int64_t lda, const sg_bf16* W, int64_t ldw,
+                           const sg_bf16* R, int64_t ldr, sg_bf16* C, int64_t ldc, int M, int N,
+                           int K, const sg_config_t* cfg, void* ws, size_t ws_bytes,
+                           sg_stream_t stream) {
+  sg_config_t c;
+  bool empty = false;
+  int st = validate_gemm(A, lda, W, ldw, R, ldr, C, ldc, M, N, K, cfg, ws, ws_bytes, &c, &empty);
+  if (st != SG_OK || empty) return st;
+  DotProblem p{};
+  p.a = A;
+  p.lda = lda;
+  p.w = W;
+  p.ldw = ldw;
+  p.res = R;
+  p.ldr = ldr;
+  p.out = C;
+  p.ldc = ldc;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  return enqueue_dot(p, c, ws, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int kda_qkvg_proj(const sg_bf16* x, const sg_bf16* w_qkvg, sg_bf16* qkvg, int M, int N,
+                             int K, void* ws, size_t ws_bytes, sg_stream_t stream) {
+  return skinny_gemm(x, K, w_qkvg, K, nullptr, N, qkvg, N, M, N, K, nullptr, ws, ws_bytes, stream);
+}
+
+extern "C" int kda_fab_fb_proj(const sg_bf16* x, const sg_bf16* w_ab, const sg_bf16* w_b,
+                               sg_bf16* f_a, sg_bf16* beta, sg_bf16* g1, int M, int K, int n_ab,
+                               int rank, int n_b, void* ws, size_t ws_bytes, sg_stream_t stream) {
+  bool empty = false;
+  int st = validate_fab_fb(x, w_ab, w_b, beta, g1, f_a, M, K, n_ab, rank, n_b, ws, ws_bytes, &empty);
+  if (st != SG_OK || empty) return st;
+  return enqueue_fab_fb(x, w_ab, w_b, f_a, beta, g1, M, K, n_ab, rank, n_b, ws,
+                        static_cast<hipStream_t>(stream));
+}
+
+extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
+                                      const sg_bf16* w_b, sg_bf16* qkvg, sg_bf16* beta,
+                                      sg_bf16* g1, int M, int K, int n_qkvg, int n_ab, int rank,
+                                      int n_b, void* ws_main, size_t ws_main_bytes, void* ws_aux,
+                                      size_t ws_aux_bytes, sg_stream_t main_stream,
+                                      sg_stream_t aux_stream, sg_event_t fork, sg_event_t join) {
+  if (M < 0 || K < 0 || n_qkvg < 0) return SG_ERR_INVALID_ARG;
+  // Validate both branches completely before anything is enqueued.
+  sg_config_t c;
+  bool empty_q = false, empty_f = false;
+  const sg_bf16* w_qkvg = packed_w;
+  const sg_bf16* w_ab = packed_w ? packed_w + static_cast<int64_t>(n_qkvg) * K : nullptr;
+  int st = validate_gemm(x, K, w_qkvg, K, nullptr, n_qkvg, qkvg, n_qkvg, M, n_qkvg, K, nullptr,
+                         ws_main, ws_main_bytes, &c, &empty_q);
+  if (st != SG_OK) return st;
+  st = validate_fab_fb(x, w_ab, w_b, beta, g1, nullptr, M, K, n_ab, rank, n_b, ws_aux, ws_aux_bytes,
+                       &empty_f);
+  if (st != SG_OK) return st;
+  if (M == 0) return SG_OK;
+  // The two workspaces are used concurrently: they must not overlap.
+  const size_t need_main = sg_workspace_bytes(SG_OP_GEMM, M, n_qkvg, K);
+  const size_t need_aux = sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K);
+  if (need_main > 0 && need_aux > 0) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(ws_main), a1 = a0 + need_main;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(ws_aux), b1 = b0 + need_aux;
+    if (a0 < b1 && b0 < a1) return SG_ERR_INVALID_ARG;
+  }
+
+  hipStream_t sm = static_cast<hipStream_t>(main_stream);
+  hipStream_t sa = static_cast<hipStream_t>(aux_stream);
+  hipEvent_t ef = static_cast<hipEvent_t>(fork);
+  hipEvent_t ej = static_cast<hipEvent_t>(join);
+  const bool concurrent = sa != nullptr && ef != nullptr && ej != nullptr;
+
+  DotProblem p{};
+  p.a = x;
+  p.lda = K;
+  p.w = w_qkvg;
+  p.ldw = K;
+  p.out = qkvg;
+  p.ldc = n_qkvg;
+  p.ldr = n_qkvg;
+  p.M = M;
+  p.N = n_qkvg;
+  p.K = K;
+
+  if (!concurrent) {
+    if (!empty_q && (st = enqueue_dot(p, c, ws_main, sm)) != SG_OK) return st;
+    return enqueue_fab_fb(x, w_ab, w_b, nullptr, beta, g1, M, K, n_ab, rank, n_b, ws_aux, sm);
+  }
+  if (hipEventRecord(ef, sm) != hipSuccess) return SG_ERR_HIP;
+  if (hipStreamWaitEvent(sa, ef, 0) != hipSuccess) return SG_ERR_HIP;
+  if (!empty_q && (st = enqueue_dot(p, c, ws_main, sm)) != SG_OK) return st;
+  if ((st = enqueue_fab_fb(x, w_ab, w_b, nullptr, beta, g1, M, K, n_ab, rank, n_b, ws_aux, sa)) !=
+      SG_OK)
+    return st;
+  if (hipEventRecord(ej, sa) != hipSuccess) return SG_ERR_HIP;
+  if (hipStreamWaitEvent(sm, ej, 0) != hipSuccess) return SG_ERR_HIP;
+  return SG_OK;
+}
+
+extern "C" int latent_moe_tail(const sg_bf16* latent, const sg_bf16* gamma, float eps,
+                               const sg_bf16* w_up, const sg_bf16* shared, sg_bf16* out, int M,
+                               int d_latent, int d_hidden, void* ws, size_t ws_bytes,
+                               sg_stream_t stream) {
+  if (M < 0 || d_latent < 0 || d_hidden < 0) return SG_ERR_INVALID_ARG;
+  if (!isfinite(eps) || !(eps > 0.f)) return SG_ERR_INVALID_ARG;
+  sg_config_t c;
+  int st = sg_select(M, d_hidden, d_latent, shared != nullptr, &c);
+  if (st != SG_OK) return st;
+  if (c.kind == SG_KIND_NONE) return SG_OK;
+  if (d_latent == 0) return SG_ERR_INVALID_ARG;  // RMS of an empty row is undefined
+  if ((st = check_operand16(latent, d_latent, d_latent)) != SG_OK) return st;
+  if ((st = check_operand16(gamma, d_latent, d_latent)) != SG_OK) return st;
+  if ((st = check_operand16(w_up, d_latent, d_latent)) != SG_OK) return st;
+  if ((st = check_output2(out, d_hidden, d_hidden)) != SG_OK) return st;
+  if (shared != nullptr && (st = check_output2(shared, d_hidden, d_hidden)) != SG_OK) return st;
+  const size_t need = sg_workspace_bytes(SG_OP_LATENT_TAIL, M, d_hidden, d_latent);
+  if ((st = check_workspace(ws, ws_bytes, need)) != SG_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (c.kind == SG_KIND_MFMA_TILE) {
+    // RMSNorm into a bf16 buffer at the start of the workspace, then the MFMA
+    // GEMM with the shared-expert add in its epilogue.
+    const size_t norm_bytes = (static_cast<size_t>(M) * d_latent * sizeof(uint16_t) + 255) & ~size_t(255);
+    sg::NormProblem np{latent, gamma, static_cast<uint16_t*>(ws), M, d_latent, eps};
+    if (sg::launch_rmsnorm(np, s) != hipSuccess) return SG_ERR_HIP;
+    DotProblem p{};
+    p.a = static_cast<const uint16_t*>(ws);
+    p.lda = d_latent;
+    p.w = w_up;
+    p.ldw = d_latent;
+    p.res = shared;
+    p.ldr = d_hidden;
+    p.out = out;
+    p.ldc = d_hidden;
+    p.M = M;
+    p.N = d_hidden;
+    p.K = d_latent;
+    return enqueue_dot(p, c, static_cast<char*>(ws) + norm_bytes, s);
+  }
+  // M <= 16: one GEMV launch that normalises the latent on the fly.  The
+  // small-K GEMV has no fold, so small latents use the GEMV kernel too.
+  if (c.kind == SG_KIND_GEMV_SMALLK) {
+    c.kind = SG_KIND_GEMV_SPLITK;
+    c.rows = 1;
+    c.k_split = 1;
+  }
+  DotProblem p{};
+  p.a = latent;
+  p.lda = d_latent;
+  p.w = w_up;
+  p.ldw = d_latent;
+  p.res = shared;
+  p.ldr = d_hidden;
+  p.out = out;
+  p.ldc = d_hidden;
+  p.M = M;
+  p.N = d_hidden;
+  p.K = d_latent;
+  p.gamma = gamma;
+  p.eps = eps;
+  return enqueue_dot(p, c, ws, s);
+}

@@ -1,0 +1,169 @@
+// Configuration table, overlap gate and workspace sizing (host-only, pure).
+//
+// The analogue of ShapeDynamicSkinnyGemm._config(m, n, k) ("Kimi K3 support,
+// phase 1", skinny_gemm.py), which picks a launch configuration from the
+// problem shape, and of the KDA_QKVG_CONFIGS / KDA_PROJECTION_OVERLAP_MAX_TOKENS
+// constants ("Overlap low-M TP8 KDA projections", low_latency_gemm.py).  The
+// rule and its values are this library's own, written for MI355X: 256 compute
+// units, 64-lane waves, 16-byte loads.  Nothing here touches the GPU, so the
+// table can be tested on any host.
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "skinny_gemm.h"
+
+namespace {
+
+constexpr int kWaves = 4;            // waves per workgroup for every kind
+constexpr int kGemvRowMinN = 1024;   // below this N the GEMV splits K
+constexpr int kGemvWaveTarget = 2048;  // waves the split-K GEMV aims for
+constexpr int kSmallK = 256;         // K at or below this: small-K GEMV
+constexpr int kMfmaNoSplitTiles = 192;  // weight tiles that fill the chip alone
+constexpr int kMfmaTileTarget = 256; // workgroups the MFMA split aims for
+constexpr int kMfmaMinStepsPerSplit = 8;
+constexpr int kOverlapMaxTokens = 32;
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+int pow2_ceil(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+
+// Split `steps` units of work into at most `want` contiguous ranges of equal
+// length; returns the number of non-empty ranges.
+int effective_split(int steps, int want) {
+  if (steps <= 0 || want <= 1) return 1;
+  if (want > steps) want = steps;
+  const int per = ceil_div(steps, want);
+  return ceil_div(steps, per);
+}
+
+int gemv_rows_for(int M) {
+  if (M <= 2) return 1;
+  if (M <= 8) return 2;
+  return 4;
+}
+
+}  // namespace
+
+extern "C" int sg_select(int M, int N, int K, int has_residual, sg_config_t* out) {
+  (void)has_residual;
+  if (out == nullptr) return SG_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K < 0) return SG_ERR_INVALID_ARG;
+  if (K % 8 != 0) return SG_ERR_UNSUPPORTED;
+  if (M > 256) return SG_ERR_UNSUPPORTED;
+  sg_config_t c;
+  memset(&c, 0, sizeof c);
+  if (M == 0 || N == 0) {
+    c.kind = SG_KIND_NONE;
+    *out = c;
+    return SG_OK;
+  }
+  const int K8 = K / 8;
+  c.waves = kWaves;
+  c.nt_weights = 1;
+  if (M <= 16) {
+    c.m_tile = M;
+    if (K <= kSmallK) {
+      c.kind = SG_KIND_GEMV_SMALLK;
+      const int G = pow2_ceil(K8 > 0 ? K8 : 1);
+      c.rows = 64 / G;
+      c.k_split = 1;
+      c.k_unroll = 1;
+      c.grid = ceil_div(N, kWaves * c.rows);
+    } else {
+      const int steps = ceil_div(K8, 64);
+      if (N >= kGemvRowMinN) {
+        c.kind = SG_KIND_GEMV_ROW;
+        c.rows = gemv_rows_for(M);
+        c.k_split = 1;
+      } else {
+        c.kind = SG_KIND_GEMV_SPLITK;
+        c.rows = 1;
+        c.k_split = effective_split(steps, ceil_div(kGemvWaveTarget, N));
+      }
+      c.k_unroll = 16 / c.rows;
+      c.grid = ceil_div(N, kWaves * c.rows) * c.k_split;
+    }
+  } else {
+    c.kind = SG_KIND_MFMA_TILE;
+    c.m_tile = 16 * ceil_div(M, 16);
+    c.rows = 1;
+    c.k_unroll = 8;
+    const int tiles = ceil_div(N, 16 * c.rows);
+    const int ksteps = ceil_div(K, 32);
+    if (tiles >= kMfmaNoSplitTiles) {
+      c.k_split = 1;
+    } else {
+      int want = ceil_div(kMfmaTileTarget, tiles);
+      int cap = ksteps / kMfmaMinStepsPerSplit;
+      if (cap < 1) cap = 1;
+      if (want > cap) want = cap;
+      c.k_split = effective_split(ksteps, want);
+    }
+    c.grid = tiles * c.k_split;
+  }
+  *out = c;
+  return SG_OK;
+}
+
+extern "C" int sg_overlap_max_tokens(void) { return kOverlapMaxTokens; }
+
+extern "C" int sg_overlap_gate(int M, int x_contiguous, int have_aux_stream, int have_events,
+                               int enabled) {
+  return (enabled && M > 0 && M <= kOverlapMaxTokens && x_contiguous && have_aux_stream &&
+          have_events)
+             ? 1
+             : 0;
+}
+
+namespace sg {
+
+// Workspace regions start on 256-byte boundaries.
+size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace sg
+
+extern "C" size_t sg_workspace_bytes(int op, int M, int N, int K) {
+  sg_config_t c;
+  if (sg_select(M, N, K, 0, &c) != SG_OK) return 0;
+  if (c.kind == SG_KIND_NONE) return 0;
+  const size_t S = static_cast<size_t>(c.k_split > 0 ? c.k_split : 1);
+  const size_t plane = static_cast<size_t>(M) * static_cast<size_t>(N) * sizeof(float);
+  switch (op) {
+    case SG_OP_GEMM:
+      return c.k_split > 1 ? sg::round256(S * plane) : 0;
+    case SG_OP_FAB_FB: {
+      // The F_A/beta stage always leaves partials for the F_B stage to sum.
+      const size_t s = (c.kind == SG_KIND_GEMV_SMALLK) ? 1 : S;
+      return sg::round256(s * plane);
+    }
+    case SG_OP_LATENT_TAIL: {
+      // M > 16: the bf16 normalised latent [M,K], then any split partials.
+      // M <= 16: the GEMV normalises on the fly; only split partials.
+      const size_t part = (c.k_split > 1 && c.kind != SG_KIND_GEMV_SMALLK) ? sg::round256(S * plane) : 0;
+      if (c.kind == SG_KIND_MFMA_TILE)
+        return sg::round256(static_cast<size_t>(M) * static_cast<size_t>(K) * 2) + part;
+      return part;
+    }
+    default:
+      return 0;
+  }
+}
+
+extern "C" const char* sg_strerror(int status) {
+  switch (status) {
+    case SG_OK: return "ok";
+    case SG_ERR_INVALID_ARG: return "invalid argument";
+    case SG_ERR_UNSUPPORTED: return "unsupported shape or configuration";
+    case SG_ERR_MISALIGNED: return "misaligned pointer or row stride";
+    case SG_ERR_WORKSPACE: return "workspace missing or too small";
+    case SG_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" const char* sg_version(void) { return "0.1.0"; }

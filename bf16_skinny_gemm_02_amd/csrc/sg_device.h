@@ -1,0 +1,122 @@
+// Device helpers shared by the gfx950 kernels of libskinny_gemm.
+//
+// Data movement is in 16-byte chunks (8 bf16), the widest per-lane global load
+// (global_load_dwordx4).  Weights are streamed with non-temporal loads, the
+// analogue of the reference's STREAMING cache mode for B (CuteSkinnyGemm copy
+// atoms, "Kimi K3 support, phase 1"): each weight byte is used once, so it
+// should not displace the activations from the caches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sg {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---- loads -----------------------------------------------------------------
+
+__device__ __forceinline__ u32x4 load_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ u32x4 load_cached(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// ---- bf16 <-> fp32 ---------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(v) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---- 8-element dot product, fp32 accumulate ---------------------------------
+
+// acc + sum_{i<8} a[i]*b[i] for two 16-byte chunks of bf16, four
+// v_dot2c_f32_bf16 (two bf16 products per instruction, fp32 accumulate).
+// The pairs are taken with whole-vector casts and shuffles: this compiler
+// mis-lowers __builtin_bit_cast applied directly to a vector element
+// expression (it reads element 0), so element-wise casts are avoided
+// throughout these kernels.
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc) {
+  const bf16x8 av = __builtin_bit_cast(bf16x8, a);
+  const bf16x8 bv = __builtin_bit_cast(bf16x8, b);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(av, av, 0, 1),
+                                        __builtin_shufflevector(bv, bv, 0, 1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(av, av, 2, 3),
+                                        __builtin_shufflevector(bv, bv, 2, 3), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(av, av, 4, 5),
+                                        __builtin_shufflevector(bv, bv, 4, 5), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(av, av, 6, 7),
+                                        __builtin_shufflevector(bv, bv, 6, 7), acc, false);
+  return acc;
+}
+
+// Sum of the two halves returned by v_permlane{16,32}_swap (a 2-vector),
+// read through a scalar copy of each element (see dot8).
+template <typename V>
+__device__ __forceinline__ float swap_pair_sum(V s) {
+  const uint32_t s0 = s[0];
+  const uint32_t s1 = s[1];
+  return __builtin_bit_cast(float, s0) + __builtin_bit_cast(float, s1);
+}
+
+__device__ __forceinline__ float xor16_sum(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  return swap_pair_sum(__builtin_amdgcn_permlane16_swap(u, u, false, false));
+}
+
+__device__ __forceinline__ float xor32_sum(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  return swap_pair_sum(__builtin_amdgcn_permlane32_swap(u, u, false, false));
+}
+
+// ---- wave-level reductions ---------------------------------------------------
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of 16 lanes; every lane of the group gets it.
+// DPP quad_perm [1,0,3,2] and [2,3,0,1] sum a quad, row_half_mirror pairs the
+// two quads of an 8-lane half, row_mirror pairs the two halves of a 16-lane row.
+__device__ __forceinline__ float row16_allreduce(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  return v;
+}
+
+// Sum over all 64 lanes; every lane gets it.  After the 16-lane sums,
+// v_permlane16_swap exchanges odd and even rows and v_permlane32_swap the two
+// 32-lane halves.
+__device__ __forceinline__ float wave_allreduce(float v) {
+  return xor32_sum(xor16_sum(row16_allreduce(v)));
+}
+
+__device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return static_cast<int>(threadIdx.x) >> 6; }
+
+}  // namespace sg

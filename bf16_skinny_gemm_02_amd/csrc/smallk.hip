@@ -1,0 +1,254 @@
+// Small-K GEMV, the F_B stage of the KDA F_A/beta -> F_B branch, the
+// fixed-order split-K reduction and the latent RMSNorm (gfx950).
+//
+// Small K (K <= 256 for skinny_gemm, K = rank = 128 for F_B): a weight row is
+// at most 32 chunks of 16 bytes, so a group of G lanes (G = next power of two
+// >= K/8) covers one row and a wave covers 64/G rows at once.  Each lane loads
+// its weight chunk once and reuses it for every activation row; the G-lane sum
+// uses DPP within a 16-lane row (plus a permlane swap for G = 32, 64).
+//
+// The F_B stage follows "Overlap low-M TP8 KDA projections"
+// (run_kda_projection_overlap / run_fab_fb): P = bf16(x @ W_ab^T) is split into
+// f_a = P[:, :rank] and beta = P[:, rank:], and the bf16 f_a feeds F_B.  Here
+// the F_A/beta kernel leaves fp32 split-K partials; every F_B workgroup sums
+// them in the same fixed order (so all agree bit for bit), rounds f_a to bf16
+// into LDS and workgroup 0 also stores beta (and f_a if asked).  This replaces
+// a separate reduction launch: the F_B kernel is launched anyway.
+#include "sg_device.h"
+#include "sg_launch.h"
+
+namespace sg {
+namespace {
+
+constexpr int kSmallkWaves = 4;
+
+// Sum over aligned groups of G lanes (G a power of two, 1..64).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dpp<0xB1>(v);
+  if constexpr (G >= 4) v += dpp<0x4E>(v);
+  if constexpr (G >= 8) v += dpp<0x141>(v);
+  if constexpr (G >= 16) v += dpp<0x140>(v);
+  if constexpr (G >= 32) v = xor16_sum(v);
+  if constexpr (G >= 64) v = xor32_sum(v);
+  return v;
+}
+
+struct SmallkArgs {
+  const uint16_t* a;
+  int64_t lda;
+  const uint16_t* w;
+  int64_t ldw;
+  const uint16_t* res;
+  int64_t ldr;
+  uint16_t* out;
+  int64_t ldc;
+  int M, N, K;
+};
+
+// One row per group of G lanes; lane j of the group holds chunk j of the row.
+template <int G>
+__global__ __launch_bounds__(kSmallkWaves * kWave) void smallk_kernel(SmallkArgs g) {
+  const int lane = lane_id();
+  const int j = lane & (G - 1);
+  const int rows_per_wave = kWave / G;
+  const int n = (static_cast<int>(blockIdx.x) * kSmallkWaves + wave_id()) * rows_per_wave + lane / G;
+  const int K8 = g.K >> 3;
+  const bool nvalid = n < g.N;
+  const bool cvalid = j < K8;
+  const u32x4 wv = (nvalid && cvalid) ? load_nt(g.w + static_cast<int64_t>(n) * g.ldw + j * 8) : zero4();
+  for (int m = 0; m < g.M; ++m) {
+    const u32x4 xv = cvalid ? load_cached(g.a + m * g.lda + j * 8) : zero4();
+    float v = group_sum<G>(dot8(xv, wv, 0.f));
+    if (nvalid && j == 0) {
+      if (g.res != nullptr) v += bf16_to_f32(g.res[m * g.ldr + n]);
+      g.out[m * g.ldc + n] = f32_to_bf16(v);
+    }
+  }
+}
+
+struct FbArgs {
+  const float* partial;
+  int S, M, n_ab, rank, n_b;
+  const uint16_t* w_b;
+  uint16_t* f_a;
+  uint16_t* beta;
+  uint16_t* g1;
+};
+
+template <int G>
+__global__ __launch_bounds__(kSmallkWaves * kWave) void fab_fb_tail_kernel(FbArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t fa_lds[kFbMaxMRank];
+  const int tid = static_cast<int>(threadIdx.x);
+  const int nthreads = kSmallkWaves * kWave;
+  const int64_t plane = static_cast<int64_t>(g.M) * g.n_ab;
+
+  // 1. f_a = bf16(sum_s partial[s][m][r]) for r < rank, fixed order s = 0..S-1.
+  const int mr = g.M * g.rank;
+  for (int idx = tid; idx < mr; idx += nthreads) {
+    const int m = idx / g.rank, r = idx - m * g.rank;
+    const float* p = g.partial + static_cast<int64_t>(m) * g.n_ab + r;
+    float acc = 0.f;
+    for (int s = 0; s < g.S; ++s) acc += p[s * plane];
+    const uint16_t b = f32_to_bf16(acc);
+    fa_lds[idx] = b;
+    if (blockIdx.x == 0 && g.f_a != nullptr) g.f_a[idx] = b;
+  }
+  // 2. beta = bf16(sum_s partial[s][m][rank + h]) (workgroup 0 only).
+  if (blockIdx.x == 0) {
+    const int nbeta = g.n_ab - g.rank;
+    const int mb = g.M * nbeta;
+    for (int idx = tid; idx < mb; idx += nthreads) {
+      const int m = idx / nbeta, h = idx - m * nbeta;
+      const float* p = g.partial + static_cast<int64_t>(m) * g.n_ab + g.rank + h;
+      float acc = 0.f;
+      for (int s = 0; s < g.S; ++s) acc += p[s * plane];
+      g.beta[idx] = f32_to_bf16(acc);
+    }
+  }
+  __syncthreads();
+
+  // 3. g1[m, i] = bf16(sum_r f_a[m, r] * w_b[i, r]).
+  const int lane = lane_id();
+  const int j = lane & (G - 1);
+  const int rows_per_wave = kWave / G;
+  const int i = (static_cast<int>(blockIdx.x) * kSmallkWaves + wave_id()) * rows_per_wave + lane / G;
+  const int K8 = g.rank >> 3;
+  const bool ivalid = i < g.n_b;
+  const bool cvalid = j < K8;
+  const u32x4 wv =
+      (ivalid && cvalid) ? load_nt(g.w_b + static_cast<int64_t>(i) * g.rank + j * 8) : zero4();
+  for (int m = 0; m < g.M; ++m) {
+    const u32x4 xv = cvalid ? *reinterpret_cast<const u32x4*>(fa_lds + m * g.rank + j * 8) : zero4();
+    const float v = group_sum<G>(dot8(xv, wv, 0.f));
+    if (ivalid && j == 0) g.g1[static_cast<int64_t>(m) * g.n_b + i] = f32_to_bf16(v);
+  }
+}
+
+struct ReduceArgs {
+  const float* partial;
+  int S, M, N;
+  const uint16_t* res;
+  int64_t ldr;
+  uint16_t* out;
+  int64_t ldc;
+};
+
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs g) {
+  const int64_t total = static_cast<int64_t>(g.M) * g.N;
+  const int64_t plane = total;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * 256) {
+    const int m = static_cast<int>(idx / g.N);
+    const int n = static_cast<int>(idx - static_cast<int64_t>(m) * g.N);
+    float acc = 0.f;
+    for (int s = 0; s < g.S; ++s) acc += g.partial[s * plane + idx];
+    if (g.res != nullptr) acc += bf16_to_f32(g.res[m * g.ldr + n]);
+    g.out[m * g.ldc + n] = f32_to_bf16(acc);
+  }
+}
+
+// One workgroup per latent row: sum of squares with a fixed-order tree
+// (wave butterfly, then the four wave sums in order), then the bf16 output.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(NormProblem p) {
+  __shared__ float wsum[4];
+  const int m = static_cast<int>(blockIdx.x);
+  const uint16_t* row = p.latent + static_cast<int64_t>(m) * p.d;
+  const int d8 = p.d >> 3;
+  float ss = 0.f;
+  for (int c = static_cast<int>(threadIdx.x); c < d8; c += 256) {
+    const u32x4 v = load_cached(row + c * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float l0 = bf16_lo(v[i]), l1 = bf16_hi(v[i]);
+      ss = fmaf(l0, l0, ss);
+      ss = fmaf(l1, l1, ss);
+    }
+  }
+  ss = wave_allreduce(ss);
+  if (lane_id() == 0) wsum[wave_id()] = ss;
+  __syncthreads();
+  const float total = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  const float r = __frsqrt_rn(total / static_cast<float>(p.d) + p.eps);
+  uint16_t* orow = p.out + static_cast<int64_t>(m) * p.d;
+  for (int c = static_cast<int>(threadIdx.x); c < d8; c += 256) {
+    const u32x4 v = load_cached(row + c * 8);
+    const u32x4 gv = load_cached(p.gamma + c * 8);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = pack_bf16x2(bf16_lo(v[i]) * r * bf16_lo(gv[i]), bf16_hi(v[i]) * r * bf16_hi(gv[i]));
+    *reinterpret_cast<u32x4*>(orow + c * 8) = o;
+  }
+}
+
+int lanes_for(int K8) {
+  int G = 1;
+  while (G < K8) G <<= 1;
+  return G;
+}
+
+template <int G>
+hipError_t launch_smallk_g(const SmallkArgs& g, hipStream_t s) {
+  const int rows_per_wg = kSmallkWaves * (kWave / G);
+  const dim3 grid((g.N + rows_per_wg - 1) / rows_per_wg);
+  hipLaunchKernelGGL((smallk_kernel<G>), grid, dim3(kSmallkWaves * kWave), 0, s, g);
+  return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_fb_g(const FbArgs& g, hipStream_t s) {
+  const int rows_per_wg = kSmallkWaves * (kWave / G);
+  // At least one workgroup: workgroup 0 also stores beta and f_a.
+  const int blocks = (g.n_b + rows_per_wg - 1) / rows_per_wg;
+  const dim3 grid(blocks > 0 ? blocks : 1);
+  hipLaunchKernelGGL((fab_fb_tail_kernel<G>), grid, dim3(kSmallkWaves * kWave), 0, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_smallk(const DotProblem& p, const sg_config_t& cfg, hipStream_t s) {
+  (void)cfg;
+  SmallkArgs g{p.a, p.lda, p.w, p.ldw, p.res, p.ldr, p.out, p.ldc, p.M, p.N, p.K};
+  switch (lanes_for(p.K >> 3)) {
+    case 1: return launch_smallk_g<1>(g, s);
+    case 2: return launch_smallk_g<2>(g, s);
+    case 4: return launch_smallk_g<4>(g, s);
+    case 8: return launch_smallk_g<8>(g, s);
+    case 16: return launch_smallk_g<16>(g, s);
+    case 32: return launch_smallk_g<32>(g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_fab_fb_tail(const FbProblem& p, hipStream_t s) {
+  FbArgs g{p.partial, p.S, p.M, p.n_ab, p.rank, p.n_b, p.w_b, p.f_a, p.beta, p.g1};
+  switch (lanes_for(p.rank >> 3)) {
+    case 1: return launch_fb_g<1>(g, s);
+    case 2: return launch_fb_g<2>(g, s);
+    case 4: return launch_fb_g<4>(g, s);
+    case 8: return launch_fb_g<8>(g, s);
+    case 16: return launch_fb_g<16>(g, s);
+    case 32: return launch_fb_g<32>(g, s);
+    case 64: return launch_fb_g<64>(g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_reduce(const ReduceProblem& p, hipStream_t s) {
+  ReduceArgs g{p.partial, p.S, p.M, p.N, p.res, p.ldr, p.out, p.ldc};
+  const int64_t total = static_cast<int64_t>(p.M) * p.N;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const NormProblem& p, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(static_cast<unsigned>(p.M)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace sg

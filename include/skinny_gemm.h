@@ -1,0 +1,220 @@
+/*
+ * skinny_gemm.h -- C ABI of libskinny_gemm.so, low-M bf16 GEMMs for gfx950
+ * (AMD Instinct MI355X): the Kimi-K3 KDA decode projections and the
+ * latent-MoE tail.
+ *
+ * Sources for what each call computes (vLLM pull-request summaries on
+ * prhub.com.cn):
+ *   [P1] "Kimi K3 support, phase 1" (vLLM #50089), key source snippets:
+ *        _skinny_gemm.py (CuteSkinnyGemm), skinny_gemm.py
+ *        (SkinnyGemmConfig, ShapeDynamicSkinnyGemm._config) and
+ *        latent_moe_runner.py (LatentMoERunner).
+ *   [P3] "Overlap low-M TP8 KDA projections" (vLLM #54697), key source
+ *        snippets: low_latency_gemm.py (run_kda_projection_overlap, run_qkvg,
+ *        run_fab_fb), kda_skinny_gemm.py (_KdaSkinnyNGemm) and kda.py
+ *        (KimiK3DeltaAttention.forward gate).
+ *
+ * Conventions that hold for every call below:
+ *  - Element type: bf16, passed as its 16-bit pattern (sg_bf16).  Arithmetic:
+ *    products and sums in fp32, one round-to-nearest-even to bf16 per output.
+ *  - Layout: every matrix is row-major with unit column stride.  Activations
+ *    are [M, K]; weights are [N, K] (the nn.Linear layout), so y = x * W^T and
+ *    each output is the dot product of two contiguous K-vectors.  lda/ldw/ldr/
+ *    ldc are row strides in elements.
+ *  - Pointers: every matrix pointer is a DEVICE pointer (hipMalloc'd or a
+ *    torch CUDA tensor) owned by the caller.  Base pointers and row strides
+ *    must keep every row 16-byte aligned (pointer % 16 == 0 and ld % 8 == 0)
+ *    for inputs and weights; outputs and residuals need 2-byte alignment and
+ *    ld % 8 == 0 is not required for them.
+ *  - Workspace: some paths keep fp32 split-K partial sums in a caller-owned
+ *    device workspace; query its size with sg_workspace_bytes().  Its contents
+ *    need no initialisation and are dead after the call.  Two calls that may
+ *    run concurrently must not share one workspace.
+ *  - Streams/events: sg_stream_t is a hipStream_t (NULL = the legacy default
+ *    stream); sg_event_t is a hipEvent_t.  Both are owned by the caller.
+ *  - Asynchrony: calls validate every argument on the host, then enqueue
+ *    kernels and return without synchronising.  All calls are capturable
+ *    into a hipGraph (no allocation, no memset, no host synchronisation).
+ *  - Errors: every argument is validated before anything is enqueued, so an
+ *    error return means no work was enqueued.  Launch failures reported by
+ *    the runtime are returned as SG_ERR_HIP.  M == 0 (or an empty N) is a
+ *    valid no-op that returns SG_OK.
+ *  - Every output element is written on every successful path.
+ *  - State: the library allocates nothing and keeps no mutable global state;
+ *    the entry points are thread-safe.
+ */
+#ifndef SKINNY_GEMM_H
+#define SKINNY_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t sg_bf16;   /* bf16 bit pattern */
+typedef void *sg_stream_t;  /* hipStream_t */
+typedef void *sg_event_t;   /* hipEvent_t */
+
+/* Status codes. */
+enum {
+    SG_OK = 0,
+    SG_ERR_INVALID_ARG = -1,  /* NULL pointer, negative size, bad eps, ... */
+    SG_ERR_UNSUPPORTED = -2,  /* shape outside what the kernels cover */
+    SG_ERR_MISALIGNED = -3,   /* pointer / row stride alignment violated */
+    SG_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than required */
+    SG_ERR_HIP = -5           /* the HIP runtime reported a launch error */
+};
+
+/* Kernel families a configuration can name. */
+enum {
+    SG_KIND_NONE = 0,         /* empty problem: nothing to launch */
+    SG_KIND_GEMV_ROW = 1,     /* M <= 16: one wave streams whole weight rows */
+    SG_KIND_GEMV_SPLITK = 2,  /* M <= 16, small N: K split across waves */
+    SG_KIND_GEMV_SMALLK = 3,  /* M <= 16, K <= 256: several rows per wave */
+    SG_KIND_MFMA_TILE = 4     /* 16 < M <= 256: bf16 MFMA tiles */
+};
+
+/* Launch configuration chosen per (M, N, K): the analogue of the reference's
+ * SkinnyGemmConfig [P1 skinny_gemm.py].  Fields not used by a kind are 0.
+ *   kind     SG_KIND_*
+ *   m_tile   rows of the activation the kernel instance is built for
+ *            (GEMV: M; MFMA: M rounded up to a multiple of 16)
+ *   rows     GEMV: weight rows per wave; MFMA: 16-row weight blocks per wave
+ *   waves    waves (64 lanes) per workgroup
+ *   k_split  workgroups that split K; > 1 means fp32 partials in workspace
+ *   k_unroll 16-byte weight chunks (GEMV) or 32-deep k-steps (MFMA) each
+ *            lane keeps in flight
+ *   grid     workgroups launched by the main kernel
+ *   nt_weights 1 = weights are read with non-temporal (streaming) loads */
+typedef struct {
+    int32_t kind;
+    int32_t m_tile;
+    int32_t rows;
+    int32_t waves;
+    int32_t k_split;
+    int32_t k_unroll;
+    int32_t grid;
+    int32_t nt_weights;
+} sg_config_t;
+
+/* Operation identifiers for sg_workspace_bytes(). */
+enum {
+    SG_OP_GEMM = 0,         /* skinny_gemm / kda_qkvg_proj:  N = N            */
+    SG_OP_FAB_FB = 1,       /* kda_fab_fb_proj:              N = n_ab         */
+    SG_OP_LATENT_TAIL = 2   /* latent_moe_tail:   N = d_hidden, K = d_latent  */
+};
+
+/* Host-only, pure: the configuration the library uses for C[M,N] = A[M,K] *
+ * W[N,K]^T.  Plays the role of ShapeDynamicSkinnyGemm._config(m, n, k)
+ * [P1 skinny_gemm.py] with a table of this library's own (the reference's
+ * values were tuned for other hardware).  has_residual does not change the
+ * choice today; it is part of the key so that it may.
+ * Returns SG_OK and fills *out, SG_ERR_INVALID_ARG for negative sizes or a
+ * NULL out, SG_ERR_UNSUPPORTED for K % 8 != 0 or M > 256.  An empty problem
+ * (M == 0 or N == 0) returns SG_OK with kind SG_KIND_NONE. */
+int sg_select(int M, int N, int K, int has_residual, sg_config_t *out);
+
+/* Host-only, pure: whether the two-stream KDA projection should be used, the
+ * analogue of the gate in KimiK3DeltaAttention.forward [P3 kda.py]:
+ *   enabled && 0 < M <= sg_overlap_max_tokens() && x_contiguous &&
+ *   have_aux_stream && have_events.
+ * (The reference also requires CUDA-graph capture; capture state is the
+ * caller's to test.)  Returns 1 or 0. */
+int sg_overlap_gate(int M, int x_contiguous, int have_aux_stream, int have_events, int enabled);
+
+/* The largest M for which sg_overlap_gate() opens (the analogue of
+ * KDA_PROJECTION_OVERLAP_MAX_TOKENS [P3 low_latency_gemm.py]). */
+int sg_overlap_max_tokens(void);
+
+/* Bytes of device workspace the operation needs at this shape (0 if none).
+ * Returns 0 for invalid arguments as well; the entry point then reports the
+ * error. */
+size_t sg_workspace_bytes(int op, int M, int N, int K);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *sg_strerror(int status);
+
+/* Library version, "MAJOR.MINOR.PATCH" (static string). */
+const char *sg_version(void);
+
+/* ---- Entry points ------------------------------------------------------- */
+
+/* Generic skinny GEMM [P1 _skinny_gemm.py CuteSkinnyGemm]:
+ *   C[m,n] = bf16( sum_k A[m,k] * W[n,k] + R[m,n] )   (R omitted when NULL)
+ * A [M,K] lda, W [N,K] ldw, R [M,N] ldr (nullable), C [M,N] ldc.
+ * cfg: NULL = sg_select(M, N, K, R != NULL); a caller-supplied config must
+ * equal the one sg_select returns for that shape in every field except
+ * k_unroll / nt_weights, which are ignored (kernels are compiled per table
+ * entry), else SG_ERR_UNSUPPORTED.  C may alias R exactly (in-place add);
+ * any other overlap of C with an input is undefined. */
+int skinny_gemm(const sg_bf16 *A, int64_t lda, const sg_bf16 *W, int64_t ldw,
+                const sg_bf16 *R, int64_t ldr, sg_bf16 *C, int64_t ldc,
+                int M, int N, int K, const sg_config_t *cfg,
+                void *ws, size_t ws_bytes, sg_stream_t stream);
+
+/* KDA packed Q/K/V/G projection [P3 low_latency_gemm.py run_qkvg]:
+ *   qkvg[m,n] = bf16( sum_k x[m,k] * w_qkvg[n,k] )
+ * x [M,K] contiguous, w_qkvg [N,K] contiguous (N = 4096 for one TP8 rank:
+ * q, k, v, g, 1024 columns each), qkvg [M,N] contiguous. */
+int kda_qkvg_proj(const sg_bf16 *x, const sg_bf16 *w_qkvg, sg_bf16 *qkvg,
+                  int M, int N, int K, void *ws, size_t ws_bytes, sg_stream_t stream);
+
+/* KDA F_A/beta -> F_B branch [P3 low_latency_gemm.py run_fab_fb,
+ * kda_skinny_gemm.py]:
+ *   P[m,j]    = bf16( sum_k x[m,k] * w_ab[j,k] ),   j < n_ab
+ *   f_a       = P[:, 0:rank]        (low-rank gate input, bf16)
+ *   beta      = P[:, rank:n_ab]     (raw beta heads, no activation)
+ *   g1[m,i]   = bf16( sum_r f_a[m,r] * w_b[i,r] ),  i < n_b
+ * x [M,K], w_ab [n_ab,K], w_b [n_b,rank], f_a [M,rank] (nullable: not
+ * stored), beta [M,n_ab-rank], g1 [M,n_b]; all contiguous.  Requires
+ * 0 < rank < n_ab, rank % 8 == 0, rank <= 512.  Needs workspace
+ * sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K). */
+int kda_fab_fb_proj(const sg_bf16 *x, const sg_bf16 *w_ab, const sg_bf16 *w_b,
+                    sg_bf16 *f_a, sg_bf16 *beta, sg_bf16 *g1,
+                    int M, int K, int n_ab, int rank, int n_b,
+                    void *ws, size_t ws_bytes, sg_stream_t stream);
+
+/* Concurrent KDA projection [P3 low_latency_gemm.py
+ * run_kda_projection_overlap]: kda_qkvg_proj on packed_w rows [0, n_qkvg) on
+ * `main`, and kda_fab_fb_proj on packed_w rows [n_qkvg, n_qkvg + n_ab) with
+ * w_b on `aux`.  Fork: `fork` is recorded on main and waited on by aux; join:
+ * `join` is recorded on aux and waited on by main, so that every output is
+ * complete in main's order when the call's work retires.  If aux, fork or
+ * join is NULL the two branches run one after the other on main (the
+ * reference's fallback).  Outputs are bitwise identical either way.
+ * packed_w [n_qkvg + n_ab, K] contiguous; qkvg [M,n_qkvg]; beta, g1 as in
+ * kda_fab_fb_proj (f_a is not returned, as in the reference).  ws_main needs
+ * sg_workspace_bytes(SG_OP_GEMM, M, n_qkvg, K) and ws_aux
+ * sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K); they must not overlap. */
+int kda_projection_overlap(const sg_bf16 *x, const sg_bf16 *packed_w, const sg_bf16 *w_b,
+                           sg_bf16 *qkvg, sg_bf16 *beta, sg_bf16 *g1,
+                           int M, int K, int n_qkvg, int n_ab, int rank, int n_b,
+                           void *ws_main, size_t ws_main_bytes,
+                           void *ws_aux, size_t ws_aux_bytes,
+                           sg_stream_t main_stream, sg_stream_t aux_stream,
+                           sg_event_t fork, sg_event_t join);
+
+/* Latent-MoE tail [P1 latent_moe_runner.py LatentMoERunner: RMS-norm of the
+ * latent partial, replicated up-projection, shared-expert add folded into
+ * the GEMM epilogue]:
+ *   r[m]     = 1 / sqrt( (1/d_latent) * sum_k L[m,k]^2 + eps )
+ *   n[m,k]   = bf16( L[m,k] * r[m] * gamma[k] )      (the bf16 RMSNorm output)
+ *   out[m,j] = bf16( S[m,j] + sum_k n[m,k] * w_up[j,k] )
+ * latent [M,d_latent], gamma [d_latent], w_up [d_hidden,d_latent], shared
+ * [M,d_hidden] (nullable: no add), out [M,d_hidden]; all contiguous.  eps
+ * must be finite and > 0, d_latent > 0.  out may alias shared exactly.
+ * For M <= 16 one kernel normalises on the fly; for M > 16 the normalised
+ * latent is written to the workspace (sg_workspace_bytes(SG_OP_LATENT_TAIL,
+ * M, d_hidden, d_latent)) and consumed by the MFMA GEMM. */
+int latent_moe_tail(const sg_bf16 *latent, const sg_bf16 *gamma, float eps,
+                    const sg_bf16 *w_up, const sg_bf16 *shared, sg_bf16 *out,
+                    int M, int d_latent, int d_hidden,
+                    void *ws, size_t ws_bytes, sg_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKINNY_GEMM_H */

@@ -136,10 +136,13 @@ void oracle_rms_scale(int M, int d, const uint16_t *L, long ldl, double eps, dou
 /* Latent-MoE tail (LatentMoERunner docstring, #50089):
  *   out[m,j] = round_bf16( S[m,j] + sum_k n[m,k] * Wup[j,k] ),
  *   n[m,k]   = L[m,k] * r[m] * gamma[k].
- * variant 0 keeps n in double (primary reading); variant 1 rounds n to bf16
- * before the up-projection (the reading in which the normalised latent is a
- * bf16 tensor).  S may be NULL (no shared-expert add).  L is [M,d], Wup is
- * [D,d], S and out are [M,D]; all row-major and contiguous. */
+ * variant 1 rounds n to bf16 before the up-projection: the RMSNorm output is
+ * a bf16 tensor that the up-projection GEMM consumes, as in the runner's
+ * unfused path (norm, then a bf16 addmm).  This is the reading the library is
+ * held to.  variant 0 keeps n in double (the exact-arithmetic value, used to
+ * bound how far the two readings can drift apart).  S may be NULL (no
+ * shared-expert add).  L is [M,d], Wup is [D,d], S and out are [M,D]; all
+ * row-major and contiguous. */
 void oracle_latent_tail(int M, int d, int D,
                         const uint16_t *L, const uint16_t *gamma, double eps,
                         const uint16_t *Wup, const uint16_t *S,

@@ -19,10 +19,13 @@ O3 ``fab_fb``        P = bf16(x @ W_ab^T); f_a = P[:, :rank]; beta = P[:, rank:]
 O4 ``projection_overlap``  (O2 on packed rows [0, n_qkvg), O3 on the next n_ab
                      rows): #54697 run_kda_projection_overlap, and the packed
                      sequential fallback in kda.py forward.
-O5 ``latent_tail``   r = 1/sqrt(mean(L^2) + eps); out = bf16(S + (L*r*gamma) @ W_up^T).
+O5 ``latent_tail``   r = 1/sqrt(mean(L^2) + eps); n = bf16(L*r*gamma);
+                     out = bf16(S + n @ W_up^T).
                      #50089, latent_moe_runner.py LatentMoERunner docstring.
-                     variant 0 keeps the normalised latent in fp64, variant 1
-                     rounds it to bf16 first.
+                     variant 1 (default): the RMSNorm output n is a bf16 tensor
+                     fed to the up-projection, as in the runner's unfused path.
+                     variant 0 keeps n in fp64 (used to bound the drift
+                     between the two readings).
 """
 from __future__ import annotations
 
@@ -168,7 +171,7 @@ def rms_scale(L: np.ndarray, eps: float) -> np.ndarray:
     return r
 
 
-def latent_tail(L, gamma, eps, w_up, S=None, variant: int = 0):
+def latent_tail(L, gamma, eps, w_up, S=None, variant: int = 1):
     """O5: returns (exact float64 [M,D], bf16 bits [M,D])."""
     L = _u16(L)
     gamma = _u16(gamma)

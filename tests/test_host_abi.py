@@ -1,0 +1,251 @@
+"""Host-side tests of libskinny_gemm (no GPU needed).
+
+* the shared library loads and exports every function include/skinny_gemm.h
+  declares;
+* the configuration table and the overlap gate agree field by field with the
+  independent selection oracle, over an exhaustive grid of shapes;
+* every entry point rejects invalid arguments with the documented status, and
+  returns before touching the GPU (validation happens before any HIP call).
+"""
+from __future__ import annotations
+
+import ctypes
+import itertools
+import re
+from pathlib import Path
+
+import pytest
+
+from bf16_skinny_gemm_02_amd import _lib
+from oracle import selection
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "skinny_gemm.h"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not _lib.LIB_PATH.exists():
+        pytest.fail(f"{_lib.LIB_PATH} not built: run `python -m bf16_skinny_gemm_02_amd.build`")
+    return _lib.load()
+
+
+def _declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = _declared_functions()
+    assert set(names) == set(_lib.EXPORTED_SYMBOLS), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_and_version(lib):
+    for st in (0, -1, -2, -3, -4, -5, 7):
+        assert lib.sg_strerror(st)
+    assert re.fullmatch(rb"\d+\.\d+\.\d+", lib.sg_version())
+
+
+# ---- configuration table ------------------------------------------------------------
+
+SHAPES = [(4096, 7168), (136, 7168), (140, 7168), (144, 7168), (1024, 128), (7168, 2048),
+          (4232, 7168), (1, 8), (3, 16), (1000, 1000), (300, 264), (17, 0), (0, 64), (5, 256),
+          (5, 264), (1023, 4096), (1024, 4096), (2048, 520), (3072, 6144), (100, 2)]
+
+
+def _c_select(lib, M, N, K, res):
+    cfg = _lib.SgConfig()
+    st = lib.sg_select(M, N, K, res, ctypes.byref(cfg))
+    return st, cfg.as_dict()
+
+
+def test_select_matches_oracle_exhaustive(lib):
+    checked = 0
+    for (N, K), M, res in itertools.product(SHAPES, range(-1, 301), (0, 1)):
+        st_c, cfg_c = _c_select(lib, M, N, K, res)
+        st_o, cfg_o = selection.select(M, N, K, bool(res))
+        assert st_c == st_o, (M, N, K)
+        if st_o == selection.OK:
+            assert cfg_c == cfg_o, (M, N, K, cfg_c, cfg_o)
+        checked += 1
+    assert checked > 10000
+
+
+def test_select_matches_oracle_random(lib):
+    import random
+    rnd = random.Random(1234)
+    for _ in range(20000):
+        M = rnd.randint(-2, 300)
+        N = rnd.choice([rnd.randint(-2, 40), rnd.randint(0, 20000)])
+        K = rnd.choice([rnd.randint(-2, 600), 8 * rnd.randint(0, 2000)])
+        res = rnd.randint(0, 1)
+        st_c, cfg_c = _c_select(lib, M, N, K, res)
+        st_o, cfg_o = selection.select(M, N, K, bool(res))
+        assert st_c == st_o, (M, N, K)
+        if st_o == selection.OK:
+            assert cfg_c == cfg_o, (M, N, K)
+
+
+def test_select_null_out(lib):
+    assert lib.sg_select(1, 1, 8, 0, None) == _lib.SG_ERR_INVALID_ARG
+
+
+def test_kind_follows_m_boundaries():
+    for M in range(1, 257):
+        st, cfg = selection.select(M, 4096, 7168)
+        assert st == selection.OK
+        assert cfg["kind"] == (selection.GEMV_ROW if M <= 16 else selection.MFMA_TILE)
+    assert selection.select(257, 4096, 7168)[0] == selection.UNSUPPORTED
+    assert selection.select(0, 4096, 7168)[1]["kind"] == selection.NONE
+
+
+def test_overlap_gate_matches_oracle(lib):
+    assert lib.sg_overlap_max_tokens() == selection.OVERLAP_MAX_TOKENS
+    for M, c, a, e, en in itertools.product(range(-1, 70), (0, 1), (0, 1), (0, 1), (0, 1)):
+        assert bool(lib.sg_overlap_gate(M, c, a, e, en)) == selection.overlap_gate(M, c, a, e, en)
+
+
+def test_workspace_bytes(lib):
+    # QKVG at decode sizes needs no workspace; F_A/beta always keeps partials.
+    assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, 1, 4096, 7168) == 0
+    assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, 64, 4096, 7168) == 0
+    for M in (1, 2, 4, 8, 16, 32):
+        st, cfg = selection.select(M, 136, 7168)
+        need = lib.sg_workspace_bytes(_lib.SG_OP_FAB_FB, M, 136, 7168)
+        assert need >= cfg["k_split"] * M * 136 * 4
+        assert need % 256 == 0
+    assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, -1, 4, 8) == 0
+    assert lib.sg_workspace_bytes(99, 4, 4, 8) == 0
+
+
+# ---- argument validation (host only: every call returns before any HIP call) ----------
+
+A16 = ctypes.c_void_p(0x10000)    # 16-byte aligned fake device addresses: never dereferenced
+B16 = ctypes.c_void_p(0x20000)
+C16 = ctypes.c_void_p(0x30000)
+ODD = ctypes.c_void_p(0x10008)    # 8-byte aligned only
+NUL = None
+
+
+def _gemm(lib, A=A16, lda=64, W=B16, ldw=64, R=NUL, ldr=32, C=C16, ldc=32, M=4, N=32, K=64,
+          cfg=None, ws=NUL, ws_bytes=0):
+    return lib.skinny_gemm(A, lda, W, ldw, R, ldr, C, ldc, M, N, K, cfg, ws, ws_bytes, None)
+
+
+def test_skinny_gemm_validation(lib):
+    E = _lib
+    assert _gemm(lib, M=-1) == E.SG_ERR_INVALID_ARG
+    assert _gemm(lib, K=-8) == E.SG_ERR_INVALID_ARG
+    assert _gemm(lib, K=60) == E.SG_ERR_UNSUPPORTED
+    assert _gemm(lib, M=257) == E.SG_ERR_UNSUPPORTED
+    assert _gemm(lib, A=NUL) == E.SG_ERR_INVALID_ARG
+    assert _gemm(lib, W=NUL) == E.SG_ERR_INVALID_ARG
+    assert _gemm(lib, C=NUL) == E.SG_ERR_INVALID_ARG
+    assert _gemm(lib, lda=32) == E.SG_ERR_INVALID_ARG
+    assert _gemm(lib, ldc=16) == E.SG_ERR_INVALID_ARG
+    assert _gemm(lib, A=ODD) == E.SG_ERR_MISALIGNED
+    assert _gemm(lib, W=ODD) == E.SG_ERR_MISALIGNED
+    assert _gemm(lib, lda=68) == E.SG_ERR_MISALIGNED
+    assert _gemm(lib, C=ctypes.c_void_p(0x30001)) == E.SG_ERR_MISALIGNED
+    assert _gemm(lib, R=ctypes.c_void_p(0x40001)) == E.SG_ERR_MISALIGNED
+    # a config that is not the table's choice
+    bad = _lib.SgConfig(kind=4, m_tile=16, rows=1, waves=4, k_split=1, k_unroll=8, grid=2)
+    assert _gemm(lib, cfg=ctypes.byref(bad)) == E.SG_ERR_UNSUPPORTED
+    # a split-K shape without workspace
+    st, cfg = selection.select(4, 32, 4096)
+    assert cfg["k_split"] > 1
+    assert _gemm(lib, lda=4096, ldw=4096, K=4096) == E.SG_ERR_WORKSPACE
+    need = lib.sg_workspace_bytes(_lib.SG_OP_GEMM, 4, 32, 4096)
+    assert _gemm(lib, lda=4096, ldw=4096, K=4096, ws=ctypes.c_void_p(0x50000),
+                 ws_bytes=need - 1) == E.SG_ERR_WORKSPACE
+    assert _gemm(lib, lda=4096, ldw=4096, K=4096, ws=ctypes.c_void_p(0x50004),
+                 ws_bytes=need) == E.SG_ERR_MISALIGNED
+    # empty problems are no-ops
+    assert _gemm(lib, M=0) == E.SG_OK
+    assert _gemm(lib, N=0) == E.SG_OK
+    assert _gemm(lib, M=0, A=NUL, W=NUL, C=NUL) == E.SG_OK
+
+
+def test_qkvg_validation(lib):
+    E = _lib
+    assert lib.kda_qkvg_proj(A16, B16, C16, -1, 4096, 7168, NUL, 0, None) == E.SG_ERR_INVALID_ARG
+    assert lib.kda_qkvg_proj(A16, B16, C16, 1, 4096, 7164, NUL, 0, None) == E.SG_ERR_UNSUPPORTED
+    assert lib.kda_qkvg_proj(NUL, B16, C16, 1, 4096, 7168, NUL, 0, None) == E.SG_ERR_INVALID_ARG
+    assert lib.kda_qkvg_proj(A16, B16, C16, 0, 4096, 7168, NUL, 0, None) == E.SG_OK
+
+
+def _fab(lib, x=A16, w_ab=B16, w_b=C16, f_a=NUL, beta=ctypes.c_void_p(0x60000),
+         g1=ctypes.c_void_p(0x70000), M=2, K=7168, n_ab=136, rank=128, n_b=1024, ws=NUL,
+         ws_bytes=0):
+    return lib.kda_fab_fb_proj(x, w_ab, w_b, f_a, beta, g1, M, K, n_ab, rank, n_b, ws, ws_bytes,
+                               None)
+
+
+def test_fab_fb_validation(lib):
+    E = _lib
+    assert _fab(lib, rank=0) == E.SG_ERR_INVALID_ARG
+    assert _fab(lib, n_ab=128) == E.SG_ERR_INVALID_ARG
+    assert _fab(lib, rank=124) == E.SG_ERR_UNSUPPORTED
+    assert _fab(lib, rank=520, n_ab=600) == E.SG_ERR_UNSUPPORTED
+    assert _fab(lib, M=300) == E.SG_ERR_UNSUPPORTED
+    assert _fab(lib, M=256, rank=256, n_ab=300) == E.SG_ERR_UNSUPPORTED  # f_a too big for LDS
+    assert _fab(lib, x=NUL) == E.SG_ERR_INVALID_ARG
+    assert _fab(lib, beta=NUL) == E.SG_ERR_INVALID_ARG
+    assert _fab(lib, g1=NUL) == E.SG_ERR_INVALID_ARG
+    assert _fab(lib, w_b=ODD) == E.SG_ERR_MISALIGNED
+    assert _fab(lib) == E.SG_ERR_WORKSPACE  # F_A/beta always needs its partials
+    assert _fab(lib, M=0) == E.SG_OK
+
+
+def test_overlap_validation(lib):
+    E = _lib
+    need_aux = lib.sg_workspace_bytes(_lib.SG_OP_FAB_FB, 2, 136, 7168)
+
+    def ov(**kw):
+        args = dict(x=A16, packed=B16, w_b=C16, qkvg=ctypes.c_void_p(0x80000),
+                    beta=ctypes.c_void_p(0x60000), g1=ctypes.c_void_p(0x70000), M=2, K=7168,
+                    n_qkvg=4096, n_ab=136, rank=128, n_b=1024, wsm=NUL, wsm_b=0,
+                    wsa=ctypes.c_void_p(0x90000), wsa_b=need_aux)
+        args.update(kw)
+        return lib.kda_projection_overlap(
+            args["x"], args["packed"], args["w_b"], args["qkvg"], args["beta"], args["g1"],
+            args["M"], args["K"], args["n_qkvg"], args["n_ab"], args["rank"], args["n_b"],
+            args["wsm"], args["wsm_b"], args["wsa"], args["wsa_b"], None, None, None, None)
+
+    assert ov(M=-1) == E.SG_ERR_INVALID_ARG
+    assert ov(packed=NUL) == E.SG_ERR_INVALID_ARG
+    assert ov(qkvg=NUL) == E.SG_ERR_INVALID_ARG
+    assert ov(wsa=NUL) == E.SG_ERR_WORKSPACE
+    assert ov(rank=100) == E.SG_ERR_UNSUPPORTED
+    assert ov(M=0) == E.SG_OK
+
+
+def test_latent_tail_validation(lib):
+    E = _lib
+    out = ctypes.c_void_p(0x80000)
+
+    def tail(L=A16, g=B16, eps=1e-6, w=C16, S=NUL, o=out, M=8, d=2048, D=7168):
+        return lib.latent_moe_tail(L, g, eps, w, S, o, M, d, D, NUL, 0, None)
+
+    assert tail(eps=0.0) == E.SG_ERR_INVALID_ARG
+    assert tail(eps=-1.0) == E.SG_ERR_INVALID_ARG
+    assert tail(eps=float("nan")) == E.SG_ERR_INVALID_ARG
+    assert tail(eps=float("inf")) == E.SG_ERR_INVALID_ARG
+    assert tail(M=-1) == E.SG_ERR_INVALID_ARG
+    assert tail(M=257) == E.SG_ERR_UNSUPPORTED
+    assert tail(d=2044) == E.SG_ERR_UNSUPPORTED
+    assert tail(d=0) == E.SG_ERR_INVALID_ARG
+    assert tail(L=NUL) == E.SG_ERR_INVALID_ARG
+    assert tail(g=ODD) == E.SG_ERR_MISALIGNED
+    assert tail(o=NUL) == E.SG_ERR_INVALID_ARG
+    assert tail(S=ctypes.c_void_p(0x90001)) == E.SG_ERR_MISALIGNED
+    assert tail(M=0) == E.SG_OK
+    assert tail(D=0) == E.SG_OK

@@ -258,14 +258,19 @@ def test_latent_tail_constant_and_one_hot_rows():
     w_up = _one_hot_rows(D, d, cols)
     c = -0.75
     L = synth.to_bf16_bits(np.full((1, d), c))
-    ex, _ = oracle.latent_tail(L, gamma, eps, w_up)
+    ex, _ = oracle.latent_tail(L, gamma, eps, w_up, variant=0)
     want = c / math.sqrt(c * c + eps) * g[cols]
     assert np.allclose(ex[0], want, rtol=1e-14, atol=0)
+    # variant 1: each output is the bf16 rounding of c * r * gamma_k itself
+    _, bits = oracle.latent_tail(L, gamma, eps, w_up)
+    r = 1.0 / math.sqrt(c * c + eps)
+    for j, k in enumerate(cols):
+        assert int(bits[0, j]) == exact.nearest_bf16(exact.Fraction(c * r * float(g[k])))[0]
     # one-hot latent row: n_j = gamma_j * c / sqrt(c^2/d + eps), about +-45.25 gamma_j
     j = int(cols[3])
     L = np.zeros((1, d), np.uint16)
     L[0, j] = synth.to_bf16_bits(np.array([c]))[0]
-    ex, _ = oracle.latent_tail(L, gamma, eps, w_up)
+    ex, _ = oracle.latent_tail(L, gamma, eps, w_up, variant=0)
     expect = np.where(cols == j, g[j] * c / math.sqrt(c * c / d + eps), 0.0)
     assert np.allclose(ex[0], expect, rtol=1e-14, atol=0)
     assert abs(abs(expect[3]) / g[j] - math.sqrt(d)) < 0.1  # ~45.25 for |c| >> sqrt(eps*d)
@@ -288,15 +293,16 @@ def test_latent_tail_zero_weights_and_unit_rows():
 def test_latent_tail_scale_invariance_and_variants():
     M, d, D = 4, 2048, 64
     L, gamma, w_up, S = synth.tail_inputs(M, seed=78, D=D)
-    ex, _ = oracle.latent_tail(L, gamma, 1e-6, w_up, S)
+    ex, _ = oracle.latent_tail(L, gamma, 1e-6, w_up, S, variant=0)
     L4 = synth.to_bf16_bits(oracle.to_f64(L) * 4.0)  # exact power-of-two scaling
-    ex4, _ = oracle.latent_tail(L4, gamma, 1e-6, w_up, S)
+    ex4, _ = oracle.latent_tail(L4, gamma, 1e-6, w_up, S, variant=0)
     assert np.allclose(ex4, ex, rtol=0, atol=1e-5 * np.abs(ex).max())
     # Rounding the normalised latent to bf16 perturbs each product by <= 2^-9
     # relative; over 2048 terms of unit-variance products the output moves by
-    # ~1.1e-3 (one sigma).  Both readings sit well inside the 1e-2 tolerance.
+    # ~1.2e-3 (one sigma), up to ~9e-3 over a 256 x 7168 output.
     ex1, _ = oracle.latent_tail(L, gamma, 1e-6, w_up, S, variant=1)
     assert np.all(np.abs(ex1 - ex) <= 5e-3 * np.maximum(1.0, np.abs(ex)))
+    assert np.abs(ex1 - ex).max() > 1e-4  # the two readings do differ
 
 
 # ---- planted mistakes: the pins above must reject each ------------------------------------
