@@ -1,0 +1,360 @@
+"""Benchmark of the KDA decode projections and the latent-MoE tail on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+One step is one pass of the whole hot path over the decode batch sizes
+M in {1, 2, 3, 4, 8, 16, 17, 32, 64}: for every M, the concurrent KDA projection
+(packed Q/K/V/G on the main stream || F_A/beta -> F_B on an aux stream, event
+fork/join) and the latent-MoE tail (RMSNorm -> up-projection -> shared add).
+Each (op, M) is a hipGraph of R back-to-back calls that cycle through R copies
+of the weights, with R chosen so that the copies span >= 512 MiB: the 256 MiB
+Infinity Cache cannot hold them, so the weights stream from HBM on every call.
+Inputs are resident in HBM before timing starts.
+
+Reported ``value``: mean microseconds per KDA projection call over the M sweep
+(the metric's unit).  The same line carries the per-M breakdown (projection,
+tail, GB/s, fraction of HBM peak), the roofline of the dominant kernel (the
+Q/K/V/G GEMV at M = 1, timed with HIP events on its own stream) and the CPU
+oracle timed on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+import torch
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+import bf16_skinny_gemm_02_amd as sg  # noqa: E402
+import synth  # noqa: E402
+
+METRIC = "µs/call and % of HBM roofline (GB/s) for KDA decode projections, M=1..64"
+M_SWEEP = [1, 2, 3, 4, 8, 16, 17, 32, 64]
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+COLD_BYTES = 512 << 20          # weights rotated across at least this many bytes
+
+K = synth.HIDDEN
+N_QKVG, N_AB, RANK, N_B = synth.N_QKVG, synth.N_AB, synth.RANK, synth.N_B
+D_LAT, D_HID = synth.D_LATENT, synth.D_HIDDEN
+
+
+def bf16_dev(bits, device):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy()).to(device).view(
+        torch.bfloat16)
+
+
+# ---- algorithmic bytes / flops (each weight, input and output touched once) --------
+
+def proj_bytes(M):
+    return 2 * ((N_QKVG + N_AB) * K + N_B * RANK + M * K + M * (N_QKVG + (N_AB - RANK) + N_B))
+
+
+def proj_flops(M):
+    return 2 * M * ((N_QKVG + N_AB) * K + N_B * RANK)
+
+
+def qkvg_bytes(M):
+    return 2 * (N_QKVG * K + M * K + M * N_QKVG)
+
+
+def tail_bytes(M):
+    return 2 * (D_HID * D_LAT + M * D_LAT + D_LAT + 2 * M * D_HID)
+
+
+def tail_flops(M):
+    return 2 * M * D_HID * D_LAT
+
+
+# ---- graph construction -------------------------------------------------------------
+
+def copies_for(weight_bytes):
+    return max(2, math.ceil(COLD_BYTES / weight_bytes))
+
+
+class ProjectionCase:
+    """R concurrent KDA projection calls at batch M, one weight copy each."""
+
+    def __init__(self, M, device, aux, fork, join):
+        x, packed, w_b = synth.overlap_inputs(M)
+        self.M = M
+        self.R = copies_for(2 * ((N_QKVG + N_AB) * K + N_B * RANK))
+        self.x = bf16_dev(x, device)
+        p0 = bf16_dev(packed, device)
+        b0 = bf16_dev(w_b, device)
+        self.packed = [p0] + [p0.clone() for _ in range(self.R - 1)]
+        self.w_b = [b0] + [b0.clone() for _ in range(self.R - 1)]
+        self.qkvg = torch.empty((M, N_QKVG), dtype=torch.bfloat16, device=device)
+        self.g1 = torch.empty((M, N_B), dtype=torch.bfloat16, device=device)
+        self.beta = torch.empty((M, N_AB - RANK), dtype=torch.bfloat16, device=device)
+        self.ws_aux = torch.empty(max(sg.sg_kda_workspace_bytes(1, M, K, N_QKVG, N_AB), 256),
+                                  dtype=torch.uint8, device=device)
+        self.ws_main = torch.empty(max(sg.sg_kda_workspace_bytes(0, M, K, N_QKVG, N_AB), 256),
+                                   dtype=torch.uint8, device=device)
+        self.aux, self.fork, self.join = aux, fork, join
+
+    def call(self, r, concurrent=True):
+        sg.kda_projection_overlap(self.x, self.packed[r], self.w_b[r], qkvg=self.qkvg, g1=self.g1,
+                                  beta=self.beta, ws_main=self.ws_main, ws_aux=self.ws_aux,
+                                  aux_stream=self.aux if concurrent else None,
+                                  fork=self.fork, join=self.join)
+
+
+class TailCase:
+    def __init__(self, M, device):
+        L, gamma, w_up, S = synth.tail_inputs(M)
+        self.M = M
+        self.R = copies_for(2 * D_HID * D_LAT)
+        self.L = bf16_dev(L, device)
+        self.gamma = bf16_dev(gamma, device)
+        w0 = bf16_dev(w_up, device)
+        self.w_up = [w0] + [w0.clone() for _ in range(self.R - 1)]
+        self.S = bf16_dev(S, device)
+        self.out = torch.empty((M, D_HID), dtype=torch.bfloat16, device=device)
+        self.ws = torch.empty(max(sg.sg_workspace_bytes(sg.SG_OP_LATENT_TAIL, M, D_HID, D_LAT), 256),
+                              dtype=torch.uint8, device=device)
+
+    def call(self, r):
+        sg.latent_moe_tail(self.L, self.gamma, self.w_up[r], self.S, eps=1e-6, out=self.out,
+                           workspace=self.ws)
+
+
+def capture(fn, R, stream):
+    """hipGraph of fn(0), ..., fn(R-1) captured on `stream`."""
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for r in range(R):       # warm the code paths once outside capture
+            fn(r)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(R):
+                fn(r)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, stream, reps):
+    """Mean ms per replay, timed with events on the replay stream."""
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(reps):
+            g.replay()
+        stop.record(stream)
+    stop.synchronize()
+    return start.elapsed_time(stop) / reps
+
+
+# ---- dominant-kernel roofline leg ---------------------------------------------------
+
+def qkvg_kernel_leg(device, reps=200):
+    """Average duration of the Q/K/V/G GEMV at M = 1 (config: x[1,7168] x W[4096,7168]^T),
+    back-to-back launches on one stream cycling cold weight copies, timed with
+    HIP events recorded on that stream."""
+    x, w = synth.qkvg_inputs(1, seed=1000 * synth.WL_QKVG_GEMV + 1)
+    R = copies_for(2 * N_QKVG * K)
+    xd = bf16_dev(x, device)
+    w0 = bf16_dev(w, device)
+    ws = [w0] + [w0.clone() for _ in range(R - 1)]
+    out = torch.empty((1, N_QKVG), dtype=torch.bfloat16, device=device)
+    stream = torch.cuda.Stream(device)
+    g = capture(lambda r: sg.kda_qkvg_proj(xd, ws[r], out=out), R, stream)
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = time_graph(g, stream, reps)
+    us = ms * 1000.0 / R
+    gbs = qkvg_bytes(1) / (us * 1e-6) / 1e9
+    return {"kernel": "gemv_kernel<M=1,R=1> (kda_qkvg_proj M=1)", "us_per_launch": us,
+            "launches_timed": reps * R, "gbs": gbs}
+
+
+# ---- CPU baseline -------------------------------------------------------------------
+
+def cpu_baseline(budget_s=15.0):
+    """The oracle (fp64, OpenMP over outputs) on this host's cores, on a bounded
+    sample: whole passes over the M sweep of the KDA projection, as many as fit
+    in the budget (at least one)."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+    oracle.set_threads(cores)
+    inputs = {M: synth.overlap_inputs(M) for M in M_SWEEP}
+    calls = 0
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        for M in M_SWEEP:
+            x, packed, w_b = inputs[M]
+            oracle.projection_overlap(x, packed, w_b)
+            calls += 1
+        passes += 1
+        if time.perf_counter() - t0 >= budget_s or passes >= 50:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": dt / calls * 1e6, "unit": "us/call", "cores": cores, "kind": "oracle",
+            "sample": f"{passes} pass(es) over the KDA projection M sweep {M_SWEEP} "
+                      f"({calls} calls, {dt:.1f} s, fp64 oracle, OpenMP {cores} threads)"}
+
+
+# ---- main -----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--comparators", action="store_true",
+                    help="also time the sequential paths (S1: same kernels on one stream; "
+                         "S2: packed N=4232 GEMM then F_B)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the hot path has no cross-GPU step (each TP8 rank's "
+              "projection slice is independent), so only --gpus 1 is supported.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    print(f"[bench] building cases for M in {M_SWEEP}", file=sys.stderr, flush=True)
+
+    main_stream = torch.cuda.Stream(device)
+    aux = torch.cuda.Stream(device)
+    fork, join = sg.HipEvent(), sg.HipEvent()
+    proj = {M: ProjectionCase(M, device, aux, fork, join) for M in M_SWEEP}
+    tail = {M: TailCase(M, device) for M in M_SWEEP}
+    g_proj = {M: capture(lambda r, c=proj[M]: c.call(r), proj[M].R, main_stream) for M in M_SWEEP}
+    g_tail = {M: capture(lambda r, c=tail[M]: c.call(r), tail[M].R, main_stream) for M in M_SWEEP}
+    print("[bench] graphs captured", file=sys.stderr, flush=True)
+
+    def step():
+        for M in M_SWEEP:
+            g_proj[M].replay()
+            g_tail[M].replay()
+
+    with torch.cuda.stream(main_stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` steps, synchronised on both sides.  Events
+    # on the replay stream bracket each graph; they are read after the region.
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in M_SWEEP]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    with torch.cuda.stream(main_stream):
+        for st in range(args.steps):
+            for i, M in enumerate(M_SWEEP):
+                e = evs[st][i]
+                e[0].record(main_stream)
+                g_proj[M].replay()
+                e[1].record(main_stream)
+                g_tail[M].replay()
+                e[2].record(main_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    t_proj = {M: 0.0 for M in M_SWEEP}
+    t_tail = {M: 0.0 for M in M_SWEEP}
+    for st in range(args.steps):
+        for i, M in enumerate(M_SWEEP):
+            e = evs[st][i]
+            t_proj[M] += e[0].elapsed_time(e[1])
+            t_tail[M] += e[1].elapsed_time(e[2])
+    print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    breakdown = {}
+    for M in M_SWEEP:
+        pu = t_proj[M] * 1000.0 / (args.steps * proj[M].R)
+        tu = t_tail[M] * 1000.0 / (args.steps * tail[M].R)
+        breakdown[str(M)] = {
+            "proj_us": round(pu, 3),
+            "proj_gbs": round(proj_bytes(M) / (pu * 1e-6) / 1e9, 1),
+            "proj_hbm_frac": round(proj_bytes(M) / (pu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "proj_tflops": round(proj_flops(M) / (pu * 1e-6) / 1e12, 2),
+            "tail_us": round(tu, 3),
+            "tail_gbs": round(tail_bytes(M) / (tu * 1e-6) / 1e9, 1),
+            "tail_hbm_frac": round(tail_bytes(M) / (tu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "tail_tflops": round(tail_flops(M) / (tu * 1e-6) / 1e12, 2),
+            "weight_copies": [proj[M].R, tail[M].R],
+        }
+    value = sum(b["proj_us"] for b in breakdown.values()) / len(M_SWEEP)
+    ms_per_step = wall * 1000.0 / args.steps
+
+    if args.comparators:
+        for M in M_SWEEP:
+            c = proj[M]
+            g_s1 = capture(lambda r, c=c: c.call(r, concurrent=False), c.R, main_stream)
+            s1 = time_graph(g_s1, main_stream, 10) * 1000.0 / c.R
+            pw = c.packed
+            out_packed = torch.empty((M, N_QKVG + N_AB), dtype=torch.bfloat16, device=device)
+            g1_s2 = torch.empty((M, N_B), dtype=torch.bfloat16, device=device)
+            ws2 = torch.empty(max(sg.sg_workspace_bytes(sg.SG_OP_GEMM, M, N_QKVG + N_AB, K), 256),
+                              dtype=torch.uint8, device=device)
+
+            def s2_call(r, c=c, out_packed=out_packed, g1_s2=g1_s2, ws2=ws2, pw=pw):
+                sg.skinny_gemm(c.x, pw[r], out=out_packed, workspace=ws2)
+                sg.skinny_gemm(out_packed[:, N_QKVG:N_QKVG + RANK], c.w_b[r], out=g1_s2)
+
+            g_s2 = capture(s2_call, c.R, main_stream)
+            s2 = time_graph(g_s2, main_stream, 10) * 1000.0 / c.R
+            b = breakdown[str(M)]
+            b["s1_us"] = round(s1, 3)
+            b["s2_us"] = round(s2, 3)
+            b["speedup_vs_s1"] = round(s1 / b["proj_us"], 3)
+            b["speedup_vs_s2"] = round(s2 / b["proj_us"], 3)
+
+    leg = qkvg_kernel_leg(device)
+    roofline = {"bound": "hbm", "achieved": round(leg["gbs"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(leg["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": leg["kernel"], "us_per_launch": round(leg["us_per_launch"], 3),
+                "algorithmic_bytes_per_launch": qkvg_bytes(1)}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "kda_decode_projection_sweep",
+            "description": "concurrent KDA projection (packed QKVG [4096,7168] on main || "
+                           "F_A/beta [136,7168] -> F_B [1024,128] on aux, hipGraph) per M, plus "
+                           "the latent-MoE tail (RMSNorm 2048 -> up-proj [7168,2048] + shared "
+                           "add) per M; value = mean us per projection call over the sweep; "
+                           "weights cold (rotated over >= 512 MiB)",
+            "m_sweep": M_SWEEP, "hidden": K, "n_qkvg": N_QKVG, "n_ab": N_AB, "rank": RANK,
+            "n_b": N_B, "d_latent": D_LAT, "d_hidden": D_HID, "parallelism": "single_gpu",
+        },
+        "roofline": roofline,
+        "breakdown": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,7 +25,8 @@ from ._lib import (SG_KIND_GEMV_ROW, SG_KIND_GEMV_SMALLK, SG_KIND_GEMV_SPLITK,  
                    SG_OP_LATENT_TAIL, SgConfig)
 
 __all__ = [
-    "sg_select", "sg_overlap_gate", "sg_overlap_max_tokens", "sg_workspace_bytes", "sg_version",
+    "sg_select", "sg_overlap_gate", "sg_overlap_max_tokens", "sg_workspace_bytes",
+    "sg_kda_workspace_bytes", "sg_version",
     "skinny_gemm", "kda_qkvg_proj", "kda_fab_fb_proj", "kda_projection_overlap",
     "latent_moe_tail", "HipEvent", "library_path",
 ]
@@ -60,6 +61,11 @@ def sg_overlap_max_tokens() -> int:
 
 def sg_workspace_bytes(op: int, M: int, N: int, K: int) -> int:
     return int(_lib.load().sg_workspace_bytes(int(op), int(M), int(N), int(K)))
+
+
+def sg_kda_workspace_bytes(which: int, M: int, K: int, n_qkvg: int, n_ab: int) -> int:
+    return int(_lib.load().sg_kda_workspace_bytes(int(which), int(M), int(K), int(n_qkvg),
+                                                  int(n_ab)))
 
 
 def sg_version() -> str:
@@ -226,8 +232,8 @@ def kda_projection_overlap(x: torch.Tensor, packed_w: torch.Tensor, w_b: torch.T
     qkvg = _out(qkvg, (M, n_qkvg), x, "qkvg")
     beta = _out(beta, (M, n_ab - rank), x, "beta")
     g1 = _out(g1, (M, n_b), x, "g1")
-    wsm, wsm_bytes = _workspace(ws_main, sg_workspace_bytes(SG_OP_GEMM, M, n_qkvg, K), x.device)
-    wsa, wsa_bytes = _workspace(ws_aux, sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K), x.device)
+    wsm, wsm_bytes = _workspace(ws_main, sg_kda_workspace_bytes(0, M, K, n_qkvg, n_ab), x.device)
+    wsa, wsa_bytes = _workspace(ws_aux, sg_kda_workspace_bytes(1, M, K, n_qkvg, n_ab), x.device)
     st = _lib.load().kda_projection_overlap(
         _ptr(x), _ptr(packed_w), _ptr(w_b), _ptr(qkvg), _ptr(beta), _ptr(g1), M, K, n_qkvg, n_ab,
         rank, n_b, _ptr(wsm), wsm_bytes, _ptr(wsa), wsa_bytes, _stream(main_stream, x.device),

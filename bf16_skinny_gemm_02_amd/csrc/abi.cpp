@@ -36,6 +36,13 @@ int check_output2(const void* p, int64_t ld, int64_t min_ld) {
   return SG_OK;
 }
 
+// Kernels address a weight tile (at most 32 rows) and the whole activation
+// through 32-bit buffer offsets: both spans must stay below 2^31 bytes.
+bool spans_ok(int64_t rows, int64_t ld, int64_t K) {
+  if (rows <= 0) return true;
+  return ((rows - 1) * ld + K) * 2 < (int64_t(1) << 31);
+}
+
 int check_workspace(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return SG_OK;
   if (ws == nullptr || ws_bytes < need) return SG_ERR_WORKSPACE;
@@ -100,6 +107,7 @@ int validate_gemm(const sg_bf16* A, int64_t lda, const sg_bf16* W, int64_t ldw, 
   if ((st = check_output2(C, ldc, N)) != SG_OK) return st;
   if (R != nullptr && (st = check_output2(R, ldr, N)) != SG_OK) return st;
   if (user_cfg != nullptr && !same_config(*user_cfg, *cfg)) return SG_ERR_UNSUPPORTED;
+  if (!spans_ok(M, lda, K) || !spans_ok(32, ldw, K)) return SG_ERR_UNSUPPORTED;
   return check_workspace(ws, ws_bytes, sg_workspace_bytes(SG_OP_GEMM, M, N, K));
 }
 
@@ -123,9 +131,8 @@ int validate_fab_fb(const sg_bf16* x, const sg_bf16* w_ab, const sg_bf16* w_b, s
                     void* ws, size_t ws_bytes, bool* empty) {
   *empty = false;
   if (M < 0 || K < 0 || n_b < 0 || rank <= 0 || n_ab <= rank) return SG_ERR_INVALID_ARG;
-  if (rank % 8 != 0 || rank > 512) return SG_ERR_UNSUPPORTED;
+  if (rank % 8 != 0 || rank > sg::kFbMaxRank) return SG_ERR_UNSUPPORTED;
   if (K % 8 != 0 || M > 256) return SG_ERR_UNSUPPORTED;
-  if (static_cast<int64_t>(M) * rank > sg::kFbMaxMRank) return SG_ERR_UNSUPPORTED;
   if (M == 0) {
     *empty = true;
     return SG_OK;
@@ -216,23 +223,25 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
                                       int n_b, void* ws_main, size_t ws_main_bytes, void* ws_aux,
                                       size_t ws_aux_bytes, sg_stream_t main_stream,
                                       sg_stream_t aux_stream, sg_event_t fork, sg_event_t join) {
-  if (M < 0 || K < 0 || n_qkvg < 0) return SG_ERR_INVALID_ARG;
-  // Validate both branches completely before anything is enqueued.
-  sg_config_t c;
-  bool empty_q = false, empty_f = false;
-  const sg_bf16* w_qkvg = packed_w;
-  const sg_bf16* w_ab = packed_w ? packed_w + static_cast<int64_t>(n_qkvg) * K : nullptr;
-  int st = validate_gemm(x, K, w_qkvg, K, nullptr, n_qkvg, qkvg, n_qkvg, M, n_qkvg, K, nullptr,
-                         ws_main, ws_main_bytes, &c, &empty_q);
-  if (st != SG_OK) return st;
-  st = validate_fab_fb(x, w_ab, w_b, beta, g1, nullptr, M, K, n_ab, rank, n_b, ws_aux, ws_aux_bytes,
-                       &empty_f);
+  // ---- validation of both branches, before anything is enqueued ----
+  if (M < 0 || K < 0 || n_qkvg < 0 || n_b < 0 || rank <= 0 || n_ab <= rank)
+    return SG_ERR_INVALID_ARG;
+  if (rank % 8 != 0 || rank > sg::kFbMaxRank) return SG_ERR_UNSUPPORTED;
+  sg_config_t c;  // the packed [n_qkvg + n_ab] projection's configuration
+  int st = sg_select(M, n_qkvg + n_ab, K, 0, &c);
   if (st != SG_OK) return st;
   if (M == 0) return SG_OK;
-  // The two workspaces are used concurrently: they must not overlap.
-  const size_t need_main = sg_workspace_bytes(SG_OP_GEMM, M, n_qkvg, K);
-  const size_t need_aux = sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K);
-  if (need_main > 0 && need_aux > 0) {
+  if ((st = check_operand16(x, K, K)) != SG_OK) return st;
+  if ((st = check_operand16(packed_w, K, K)) != SG_OK) return st;
+  if ((st = check_operand16(w_b, rank, rank)) != SG_OK) return st;
+  if (n_qkvg > 0 && (st = check_output2(qkvg, n_qkvg, n_qkvg)) != SG_OK) return st;
+  if ((st = check_output2(beta, n_ab - rank, n_ab - rank)) != SG_OK) return st;
+  if (n_b > 0 && (st = check_output2(g1, n_b, n_b)) != SG_OK) return st;
+  const size_t need_main = sg_kda_workspace_bytes(0, M, K, n_qkvg, n_ab);
+  const size_t need_aux = sg_kda_workspace_bytes(1, M, K, n_qkvg, n_ab);
+  if ((st = check_workspace(ws_main, ws_main_bytes, need_main)) != SG_OK) return st;
+  if ((st = check_workspace(ws_aux, ws_aux_bytes, need_aux)) != SG_OK) return st;
+  if (need_main > 0) {  // the two workspaces are used concurrently
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(ws_main), a1 = a0 + need_main;
     const uintptr_t b0 = reinterpret_cast<uintptr_t>(ws_aux), b1 = b0 + need_aux;
     if (a0 < b1 && b0 < a1) return SG_ERR_INVALID_ARG;
@@ -243,29 +252,82 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
   hipEvent_t ef = static_cast<hipEvent_t>(fork);
   hipEvent_t ej = static_cast<hipEvent_t>(join);
   const bool concurrent = sa != nullptr && ef != nullptr && ej != nullptr;
+  const bool split = c.k_split > 1;
+  const int64_t p_elems = static_cast<int64_t>(M) * n_ab;
+  uint16_t* pbuf = static_cast<uint16_t*>(ws_aux);  // bf16 P = [f_a | beta], [M, n_ab]
+  float* aux_part = reinterpret_cast<float*>(static_cast<char*>(ws_aux) +
+                                             sg::ws_round(static_cast<size_t>(p_elems) * 2));
+  const sg_bf16* w_ab = packed_w + static_cast<int64_t>(n_qkvg) * K;
 
-  DotProblem p{};
-  p.a = x;
-  p.lda = K;
-  p.w = w_qkvg;
-  p.ldw = K;
-  p.out = qkvg;
-  p.ldc = n_qkvg;
-  p.ldr = n_qkvg;
-  p.M = M;
-  p.N = n_qkvg;
-  p.K = K;
+  // Both schedules run every row with the packed configuration, so each
+  // output element is computed by the same instruction sequence either way:
+  // the results are bitwise identical.
+  DotProblem q{};
+  q.a = x;
+  q.lda = K;
+  q.w = packed_w;
+  q.ldw = K;
+  q.out = qkvg;
+  q.ldc = n_qkvg;
+  q.ldr = n_qkvg;
+  q.M = M;
+  q.K = K;
 
+  sg::FbProblem fb{};
+  fb.M = M;
+  fb.n_ab = n_ab;
+  fb.rank = rank;
+  fb.n_b = n_b;
+  fb.w_b = w_b;
+  fb.beta = beta;
+  fb.g1 = g1;
+
+  if (!concurrent && !split) {
+    // One packed launch: Q/K/V/G rows to qkvg, F_A/beta rows to P; then F_B.
+    q.N = n_qkvg + n_ab;
+    q.out2 = pbuf;
+    q.ldc2 = n_ab;
+    q.n_split = n_qkvg > 0 ? n_qkvg : 0;
+    if (n_qkvg == 0) {
+      q.out = pbuf;
+      q.ldc = n_ab;
+    }
+    if ((st = enqueue_dot(q, c, nullptr, sm)) != SG_OK) return st;
+    fb.p_bf16 = pbuf;
+    return hip_status(sg::launch_fab_fb_tail(fb, sm));
+  }
+
+  // Two launches over the two row ranges (main: Q/K/V/G, aux: F_A/beta).
+  auto run_fab = [&](hipStream_t s) -> int {
+    DotProblem f = q;
+    f.w = w_ab;
+    f.row_origin = n_qkvg;
+    f.N = n_ab;
+    f.out = pbuf;
+    f.ldc = n_ab;
+    f.ldr = n_ab;
+    if (split) {
+      f.partial = aux_part;
+      hipError_t e = (c.kind == SG_KIND_MFMA_TILE) ? sg::launch_mfma(f, c, s) : sg::launch_gemv(f, c, s);
+      if (e != hipSuccess) return SG_ERR_HIP;
+      fb.partial = aux_part;
+      fb.S = c.k_split;
+    } else {
+      int r = enqueue_dot(f, c, nullptr, s);
+      if (r != SG_OK) return r;
+      fb.p_bf16 = pbuf;
+    }
+    return hip_status(sg::launch_fab_fb_tail(fb, s));
+  };
+  q.N = n_qkvg;
   if (!concurrent) {
-    if (!empty_q && (st = enqueue_dot(p, c, ws_main, sm)) != SG_OK) return st;
-    return enqueue_fab_fb(x, w_ab, w_b, nullptr, beta, g1, M, K, n_ab, rank, n_b, ws_aux, sm);
+    if (n_qkvg > 0 && (st = enqueue_dot(q, c, ws_main, sm)) != SG_OK) return st;
+    return run_fab(sm);
   }
   if (hipEventRecord(ef, sm) != hipSuccess) return SG_ERR_HIP;
   if (hipStreamWaitEvent(sa, ef, 0) != hipSuccess) return SG_ERR_HIP;
-  if (!empty_q && (st = enqueue_dot(p, c, ws_main, sm)) != SG_OK) return st;
-  if ((st = enqueue_fab_fb(x, w_ab, w_b, nullptr, beta, g1, M, K, n_ab, rank, n_b, ws_aux, sa)) !=
-      SG_OK)
-    return st;
+  if (n_qkvg > 0 && (st = enqueue_dot(q, c, ws_main, sm)) != SG_OK) return st;
+  if ((st = run_fab(sa)) != SG_OK) return st;
   if (hipEventRecord(ej, sa) != hipSuccess) return SG_ERR_HIP;
   if (hipStreamWaitEvent(sm, ej, 0) != hipSuccess) return SG_ERR_HIP;
   return SG_OK;
@@ -291,9 +353,10 @@ extern "C" int latent_moe_tail(const sg_bf16* latent, const sg_bf16* gamma, floa
   if ((st = check_workspace(ws, ws_bytes, need)) != SG_OK) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (c.kind == SG_KIND_MFMA_TILE) {
-    // RMSNorm into a bf16 buffer at the start of the workspace, then the MFMA
-    // GEMM with the shared-expert add in its epilogue.
+  if (c.kind == SG_KIND_MFMA_TILE || c.k_split > 1) {
+    // RMSNorm into a bf16 buffer at the start of the workspace, then the GEMM
+    // with the shared-expert add in its epilogue (the MFMA tile, or a GEMV
+    // whose K-range is split).
     const size_t norm_bytes = (static_cast<size_t>(M) * d_latent * sizeof(uint16_t) + 255) & ~size_t(255);
     sg::NormProblem np{latent, gamma, static_cast<uint16_t*>(ws), M, d_latent, eps};
     if (sg::launch_rmsnorm(np, s) != hipSuccess) return SG_ERR_HIP;
@@ -311,8 +374,8 @@ extern "C" int latent_moe_tail(const sg_bf16* latent, const sg_bf16* gamma, floa
     p.K = d_latent;
     return enqueue_dot(p, c, static_cast<char*>(ws) + norm_bytes, s);
   }
-  // M <= 16: one GEMV launch that normalises the latent on the fly.  The
-  // small-K GEMV has no fold, so small latents use the GEMV kernel too.
+  // One GEMV launch that stages the latent in LDS and normalises it there.
+  // The small-K GEMV has no fold, so small latents use the GEMV kernel too.
   if (c.kind == SG_KIND_GEMV_SMALLK) {
     c.kind = SG_KIND_GEMV_SPLITK;
     c.rows = 1;

@@ -41,11 +41,18 @@ int effective_split(int steps, int want) {
   return ceil_div(steps, per);
 }
 
+constexpr int kStageKiB = 128;       // LDS a GEMV workgroup may stage activations in
+
 int gemv_rows_for(int M) {
   if (M <= 2) return 1;
   if (M <= 8) return 2;
   return 4;
 }
+
+// Weight steps (512 k) a GEMV wave holds, and k-steps (32 k) an MFMA wave
+// keeps in flight.
+int gemv_ring_depth(int rows) { return rows == 1 ? 16 : (rows == 2 ? 14 : 7); }
+int mfma_ring_depth(int mb) { return mb <= 2 ? 12 : (mb <= 4 ? 8 : (mb <= 8 ? 4 : 2)); }
 
 }  // namespace
 
@@ -75,24 +82,35 @@ extern "C" int sg_select(int M, int N, int K, int has_residual, sg_config_t* out
       c.k_unroll = 1;
       c.grid = ceil_div(N, kWaves * c.rows);
     } else {
+      // A workgroup holds every weight step of its K-range in registers (at
+      // most gemv_ring_depth(rows) steps of 512) and its activation rows for
+      // that range in LDS (M KiB per step, at most kStageKiB): K is split
+      // across workgroups until both fit.
       const int steps = ceil_div(K8, 64);
+      int want;
       if (N >= kGemvRowMinN) {
         c.kind = SG_KIND_GEMV_ROW;
         c.rows = gemv_rows_for(M);
-        c.k_split = 1;
+        want = 1;
       } else {
         c.kind = SG_KIND_GEMV_SPLITK;
         c.rows = 1;
-        c.k_split = effective_split(steps, ceil_div(kGemvWaveTarget, N));
+        want = ceil_div(kGemvWaveTarget, N);
       }
-      c.k_unroll = 16 / c.rows;
-      c.grid = ceil_div(N, kWaves * c.rows) * c.k_split;
+      const int depth = gemv_ring_depth(c.rows);
+      const int max_sps = (kStageKiB / M < depth) ? kStageKiB / M : depth;
+      const int need = ceil_div(steps, max_sps);
+      c.k_split = effective_split(steps, want > need ? want : need);
+      const int sps = ceil_div(steps, c.k_split);
+      c.waves = (M * sps > kStageKiB / 2) ? 2 * kWaves : kWaves;
+      c.k_unroll = depth;
+      c.grid = ceil_div(N, c.waves * c.rows) * c.k_split;
     }
   } else {
     c.kind = SG_KIND_MFMA_TILE;
     c.m_tile = 16 * ceil_div(M, 16);
     c.rows = 1;
-    c.k_unroll = 8;
+    c.k_unroll = mfma_ring_depth(c.m_tile / 16);
     const int tiles = ceil_div(N, 16 * c.rows);
     const int ksteps = ceil_div(K, 32);
     if (tiles >= kMfmaNoSplitTiles) {
@@ -124,6 +142,7 @@ namespace sg {
 
 // Workspace regions start on 256-byte boundaries.
 size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+size_t ws_round(size_t b) { return round256(b); }
 
 }  // namespace sg
 
@@ -142,12 +161,13 @@ extern "C" size_t sg_workspace_bytes(int op, int M, int N, int K) {
       return sg::round256(s * plane);
     }
     case SG_OP_LATENT_TAIL: {
-      // M > 16: the bf16 normalised latent [M,K], then any split partials.
-      // M <= 16: the GEMV normalises on the fly; only split partials.
+      // The GEMV normalises on the fly when it covers the whole row in one
+      // workgroup (k_split == 1); otherwise the bf16 normalised latent [M,K]
+      // goes to the workspace first, followed by any split partials.
       const size_t part = (c.k_split > 1 && c.kind != SG_KIND_GEMV_SMALLK) ? sg::round256(S * plane) : 0;
-      if (c.kind == SG_KIND_MFMA_TILE)
+      if (c.kind == SG_KIND_MFMA_TILE || c.k_split > 1)
         return sg::round256(static_cast<size_t>(M) * static_cast<size_t>(K) * 2) + part;
-      return part;
+      return 0;
     }
     default:
       return 0;
@@ -167,3 +187,17 @@ extern "C" const char* sg_strerror(int status) {
 }
 
 extern "C" const char* sg_version(void) { return "0.1.0"; }
+
+extern "C" size_t sg_kda_workspace_bytes(int which, int M, int K, int n_qkvg, int n_ab) {
+  if (M <= 0 || K < 0 || n_qkvg < 0 || n_ab <= 0) return 0;
+  sg_config_t c;
+  if (sg_select(M, n_qkvg + n_ab, K, 0, &c) != SG_OK || c.kind == SG_KIND_NONE) return 0;
+  const size_t S = static_cast<size_t>(c.k_split > 1 ? c.k_split : 0);
+  const size_t m = static_cast<size_t>(M);
+  if (which == 0)  // main: Q/K/V/G split-K partials
+    return S ? sg::round256(S * m * static_cast<size_t>(n_qkvg) * sizeof(float)) : 0;
+  if (which == 1)  // aux: bf16 P [M, n_ab], then F_A/beta split-K partials
+    return sg::round256(m * static_cast<size_t>(n_ab) * 2) +
+           (S ? sg::round256(S * m * static_cast<size_t>(n_ab) * sizeof(float)) : 0);
+  return 0;
+}

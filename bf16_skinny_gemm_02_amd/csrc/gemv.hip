@@ -6,22 +6,30 @@
 // projection of "Overlap low-M TP8 KDA projections" (_KdaSkinnyNGemm, which
 // splits the work finely because N is small).
 //
-// Mapping: one wave owns R consecutive weight rows and a range of K.  The 64
-// lanes cover 64 consecutive 16-byte chunks of each row per step (one fully
-// coalesced 1 KiB global_load_dwordx4 per row), so a step covers 512 K.  Each
-// lane keeps U steps of weight chunks in flight (non-temporal loads), reads the
-// matching activation chunks through the cache (they are shared by every
-// wave), and accumulates acc[m][r] in fp32 with v_dot2c_f32_bf16.  The 64
-// per-lane partial sums are then combined with a DPP / permlane butterfly and
-// lane (m*R + r) stores output (m, r).  No LDS and no barriers.
+// Mapping.  A workgroup of NW waves owns NW*R consecutive weight rows and one
+// K-range (all of K, or 1/k_split of it).  A "step" is 512 consecutive k: the
+// 64 lanes of a wave read 64 consecutive 16-byte chunks of one weight row,
+// one fully coalesced 1 KiB global_load_dwordx4.
 //
-// Split-K (grid.y > 1): wave (row group, s) covers steps
+//  1. Each wave issues every weight chunk of its R rows over the workgroup's
+//     K-range at once (non-temporal loads: each weight byte is used once).
+//     The table keeps the K-range within D steps (a whole 7168-wide row for
+//     R <= 2), so the whole weight stream is requested before the first
+//     product and there is nothing to refill: no waits inside the loop.  On
+//     MI355X a plain streaming read of the same bytes is only ~5% faster.
+//  2. The workgroup stages its activation rows for the K-range in LDS with
+//     direct global->LDS loads (no registers); the products read them back
+//     with ds_read_b128.
+//  3. acc[m][r] accumulates in fp32 with v_dot2c_f32_bf16; a DPP / permlane
+//     butterfly sums the 64 lanes and lane (m*R + r) stores output (m, r).
+//
+// Split-K (grid.y > 1): workgroup (row group, s) covers steps
 // [s*sps, (s+1)*sps) and stores fp32 partials for a later fixed-order sum.
 //
-// Fold (latent-MoE tail, RMSNorm -> up-projection): the activation is the
-// latent L.  The wave first sums L[m,k]^2 over the whole row (its lanes hold
-// every chunk of it), forms r[m] = rsqrt(sum / K + eps), and then feeds the
-// dot product with n = bf16(L * r * gamma), the bf16 normalised latent the
+// Fold (latent-MoE tail, RMSNorm -> up-projection): the staged activation is
+// the latent L over the whole row.  Every wave sums L[m,k]^2 from LDS in the
+// same order, r[m] = rsqrt(sum / K + eps), and the workgroup rewrites LDS in
+// place with n = bf16(L * r * gamma), the bf16 normalised latent the
 // up-projection consumes.  One launch, no workspace.
 #include "sg_device.h"
 #include "sg_launch.h"
@@ -40,123 +48,137 @@ struct GemvArgs {
   int64_t ldc;
   const uint16_t* gamma;
   float* partial;
+  uint16_t* out2;
+  int64_t ldc2;
+  int n_split;
   int N, K;
   int sps;  // steps per split
   float eps;
 };
 
-constexpr int kGemvWaves = 4;
-
-template <int M, int R, int U, bool FOLD>
-__global__ __launch_bounds__(kGemvWaves * kWave) void gemv_kernel(GemvArgs g) {
-  const int lane = lane_id();
-  const int n0 = (static_cast<int>(blockIdx.x) * kGemvWaves + wave_id()) * R;
-  if (n0 >= g.N) return;  // wave-uniform; the kernel uses no barriers
+template <int M, int R, int NW, int D, bool FOLD>
+__global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs g) {
+  extern __shared__ u32x4 xs[];  // [M][row_chunks] 16-byte chunks of the activation
+  constexpr int kThreads = NW * kWave;
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & (kWave - 1);
+  const int wave = wave_id();
+  const int n0 = (static_cast<int>(blockIdx.x) * NW + wave) * R;
+  const bool active = n0 < g.N;
 
   const int K8 = g.K >> 3;
   const int nsteps = (K8 + kWave - 1) / kWave;
   const int s_begin = static_cast<int>(blockIdx.y) * g.sps;
   const int s_end = min(nsteps, s_begin + g.sps);
+  const int nst = max(0, s_end - s_begin);  // <= D (the table guarantees it)
+  const int row_chunks = nst * kWave;
+  const int total = M * row_chunks;
+  const int c_base = s_begin * kWave;
 
-  const uint16_t* wrow[R];
-  bool rvalid[R];
+  // 1. Every weight chunk of the workgroup's K-range, issued up front (the
+  //    range is at most D steps, so nothing is reloaded later).  Buffer
+  //    loads: rows past N, chunks past K and steps past the range read zero.
+  const int wg_row0 = static_cast<int>(blockIdx.x) * NW * R;
+  const int wg_rows = min(NW * R, g.N - wg_row0);
+  const rsrc_t wres = make_rsrc(g.w + static_cast<int64_t>(wg_row0) * g.ldw,
+                                static_cast<uint32_t>(((wg_rows - 1) * g.ldw + g.K) * 2));
+  u32x4 wr[D][R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    rvalid[r] = (n0 + r) < g.N;
-    wrow[r] = g.w + static_cast<int64_t>(rvalid[r] ? n0 + r : n0) * g.ldw;
+  for (int j = 0; j < D; ++j) {
+    const int c = c_base + j * kWave + lane;
+    const bool kok = (j < nst) && (c < K8);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = wave * R + r;
+      const uint32_t off =
+          (kok && row < wg_rows) ? static_cast<uint32_t>((row * g.ldw + c * 8) * 2) : kOob;
+      wr[j][r] = buf_load_nt(wres, off);
+    }
   }
 
+  // 2. Activation rows of the range into LDS, one 1 KiB step-block per wave
+  //    instruction, straight from global memory to LDS (no registers).  The
+  //    last, partial step of a ragged K goes through registers with zeros.
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint16_t* xrow = g.a + m * g.lda;
+    for (int t = wave; t < nst; t += NW) {
+      const int c0 = c_base + t * kWave;
+      u32x4* dst = xs + m * row_chunks + t * kWave;
+      if (c0 + kWave <= K8) {
+        // Address-space casts: global source, LDS destination.
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1)))*)(xrow + static_cast<int64_t>(c0 + lane) * 8),
+            (void __attribute__((address_space(3)))*)(dst), 16, 0, 0);
+      } else {
+        const int c = c0 + lane;
+        dst[lane] = (c < K8) ? load_cached(xrow + static_cast<int64_t>(c) * 8) : zero4();
+      }
+    }
+  }
+  __syncthreads();
+
+  if constexpr (FOLD) {
+    // RMSNorm over the whole row (the host runs the fold with one split).
+    float rs[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float ss = 0.f;
+      for (int c = lane; c < row_chunks; c += kWave) {
+        const u32x4 v = xs[m * row_chunks + c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float l0 = bf16_lo(v[i]), l1 = bf16_hi(v[i]);
+          ss = fmaf(l0, l0, ss);
+          ss = fmaf(l1, l1, ss);
+        }
+      }
+      rs[m] = __frsqrt_rn(wave_allreduce(ss) / static_cast<float>(g.K) + g.eps);
+    }
+    __syncthreads();  // every wave has read the raw latent
+    for (int q = tid; q < total; q += kThreads) {
+      const int m = q / row_chunks;
+      const int c = q - m * row_chunks;
+      if (c < K8) {
+        const u32x4 v = xs[q];
+        const u32x4 gv = load_cached(g.gamma + static_cast<int64_t>(c) * 8);
+        float r = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < M; ++mm) r = (mm == m) ? rs[mm] : r;
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[i] = pack_bf16x2(bf16_lo(v[i]) * r * bf16_lo(gv[i]), bf16_hi(v[i]) * r * bf16_hi(gv[i]));
+        xs[q] = o;
+      }
+    }
+    __syncthreads();
+  }
+  if (!active) return;  // no barrier follows
+
+  // 3. Products: every weight step is already in flight.
   float acc[M][R];
 #pragma unroll
   for (int m = 0; m < M; ++m)
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[m][r] = 0.f;
-
-  // RMSNorm scale of each latent row over the full K (every split needs it).
-  float rscale[M];
-  if constexpr (FOLD) {
 #pragma unroll
-    for (int m = 0; m < M; ++m) rscale[m] = 0.f;
-    for (int st = 0; st < nsteps; ++st) {
-      const int c = st * kWave + lane;
-      if (c < K8) {
+  for (int j = 0; j < D; ++j) {
+    if (j < nst) {
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const u32x4 lv = load_cached(g.a + m * g.lda + static_cast<int64_t>(c) * 8);
+      for (int m = 0; m < M; ++m) {
+        const u32x4 xv = xs[m * row_chunks + j * kWave + lane];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float l0 = bf16_lo(lv[i]), l1 = bf16_hi(lv[i]);
-            rscale[m] = fmaf(l0, l0, rscale[m]);
-            rscale[m] = fmaf(l1, l1, rscale[m]);
-          }
-        }
+        for (int r = 0; r < R; ++r) acc[m][r] = dot8(xv, wr[j][r], acc[m][r]);
       }
-    }
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-      rscale[m] = __frsqrt_rn(wave_allreduce(rscale[m]) / static_cast<float>(g.K) + g.eps);
-  }
-
-  for (int s0 = s_begin; s0 < s_end; s0 += U) {
-    u32x4 wv[U][R];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = (s0 + u) * kWave + lane;
-      const bool ok = (s0 + u < s_end) && (c < K8);
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-        wv[u][r] = (ok && rvalid[r]) ? load_nt(wrow[r] + static_cast<int64_t>(c) * 8) : zero4();
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = (s0 + u) * kWave + lane;
-      const bool ok = (s0 + u < s_end) && (c < K8);
-      u32x4 xv[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m)
-        xv[m] = ok ? load_cached(g.a + m * g.lda + static_cast<int64_t>(c) * 8) : zero4();
-      if constexpr (FOLD) {
-        const u32x4 gv = ok ? load_cached(g.gamma + static_cast<int64_t>(c) * 8) : zero4();
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          u32x4 nv;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            nv[i] = pack_bf16x2(bf16_lo(xv[m][i]) * rscale[m] * bf16_lo(gv[i]),
-                                bf16_hi(xv[m][i]) * rscale[m] * bf16_hi(gv[i]));
-          xv[m] = nv;
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < M; ++m)
-#pragma unroll
-        for (int r = 0; r < R; ++r) acc[m][r] = dot8(xv[m], wv[u][r], acc[m][r]);
-      // Keep the next step's activation loads below this point: only one
-      // step of activation chunks is live at a time.
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // Cross-lane sums: every lane ends up with every (m, r) total.
+  // 4. Cross-lane sums: every lane ends up with every (m, r) total.
 #pragma unroll
   for (int m = 0; m < M; ++m)
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[m][r] = wave_allreduce(acc[m][r]);
-
-  if (g.partial != nullptr) {
-    // Lane j stores partial (m, r) = (j / R, j % R).
-    float v = 0.f;
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int r = 0; r < R; ++r) v = (lane == m * R + r) ? acc[m][r] : v;
-    if (lane < M * R) {
-      const int m = lane / R, r = lane % R;
-      if (n0 + r < g.N)
-        g.partial[(static_cast<int64_t>(blockIdx.y) * M + m) * g.N + n0 + r] = v;
-    }
-    return;
-  }
 
   float v = 0.f;
 #pragma unroll
@@ -167,39 +189,63 @@ __global__ __launch_bounds__(kGemvWaves * kWave) void gemv_kernel(GemvArgs g) {
     const int m = lane / R, r = lane % R;
     const int n = n0 + r;
     if (n < g.N) {
-      if (g.res != nullptr) v += bf16_to_f32(g.res[m * g.ldr + n]);
-      g.out[m * g.ldc + n] = f32_to_bf16(v);
+      if (g.partial != nullptr) {
+        g.partial[(static_cast<int64_t>(blockIdx.y) * M + m) * g.N + n] = v;
+      } else {
+        if (g.res != nullptr) v += bf16_to_f32(g.res[m * g.ldr + n]);
+        if (g.n_split > 0 && n >= g.n_split)
+          g.out2[m * g.ldc2 + (n - g.n_split)] = f32_to_bf16(v);
+        else
+          g.out[m * g.ldc + n] = f32_to_bf16(v);
+      }
     }
   }
 }
 
-// Steps of 16-byte chunks each lane keeps in flight: R * U = 16 chunks
-// (64 VGPRs of weights).
-template <int R>
-constexpr int unroll_for() { return 16 / R; }
+// Weight steps a wave holds (the largest K-range, in 512-wide steps, the
+// table gives one workgroup): 16, 14, 7 steps for R = 1, 2, 4 rows, i.e. at
+// most 112 VGPRs of weights, and a whole 7168-wide row for R <= 2.
+constexpr int gemv_depth(int R) { return R == 1 ? 16 : (R == 2 ? 14 : 7); }
 
-template <int M, int R, bool FOLD>
-hipError_t launch_mr(const GemvArgs& g, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_kernel<M, R, unroll_for<R>(), FOLD>), grid, dim3(kGemvWaves * kWave), 0,
-                     s, g);
+template <int M, int R, int NW, bool FOLD>
+hipError_t launch_inst(const GemvArgs& g, dim3 grid, size_t lds, hipStream_t s) {
+  constexpr int D = gemv_depth(R);
+  auto kern = gemv_kernel<M, R, NW, D, FOLD>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+      static_cast<int>(kGemvMaxLds));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, grid, dim3(NW * kWave), lds, s, g);
   return hipGetLastError();
 }
 
 template <int M, bool FOLD>
-hipError_t launch_m(const GemvArgs& g, int R, dim3 grid, hipStream_t s) {
-  switch (R) {
-    case 1: return launch_mr<M, 1, FOLD>(g, grid, s);
-    case 2: return launch_mr<M, 2, FOLD>(g, grid, s);
-    case 4: return launch_mr<M, 4, FOLD>(g, grid, s);
-    default: return hipErrorInvalidValue;
+hipError_t launch_m(const GemvArgs& g, int R, int NW, dim3 grid, size_t lds, hipStream_t s) {
+  if (NW == 4) {
+    switch (R) {
+      case 1: return launch_inst<M, 1, 4, FOLD>(g, grid, lds, s);
+      case 2: return launch_inst<M, 2, 4, FOLD>(g, grid, lds, s);
+      case 4: return launch_inst<M, 4, 4, FOLD>(g, grid, lds, s);
+      default: return hipErrorInvalidValue;
+    }
   }
+  if (NW == 8) {
+    switch (R) {
+      case 1: return launch_inst<M, 1, 8, FOLD>(g, grid, lds, s);
+      case 2: return launch_inst<M, 2, 8, FOLD>(g, grid, lds, s);
+      case 4: return launch_inst<M, 4, 8, FOLD>(g, grid, lds, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 template <bool FOLD>
-hipError_t launch_fold(const GemvArgs& g, int M, int R, dim3 grid, hipStream_t s) {
+hipError_t launch_fold(const GemvArgs& g, int M, int R, int NW, dim3 grid, size_t lds,
+                       hipStream_t s) {
   switch (M) {
 #define SG_CASE(mm) \
-  case mm: return launch_m<mm, FOLD>(g, R, grid, s);
+  case mm: return launch_m<mm, FOLD>(g, R, NW, grid, lds, s);
     SG_CASE(1) SG_CASE(2) SG_CASE(3) SG_CASE(4) SG_CASE(5) SG_CASE(6) SG_CASE(7) SG_CASE(8)
     SG_CASE(9) SG_CASE(10) SG_CASE(11) SG_CASE(12) SG_CASE(13) SG_CASE(14) SG_CASE(15) SG_CASE(16)
 #undef SG_CASE
@@ -208,6 +254,22 @@ hipError_t launch_fold(const GemvArgs& g, int M, int R, dim3 grid, hipStream_t s
 }
 
 }  // namespace
+
+size_t gemv_lds_bytes(int M, int K, int k_split) {
+  const int K8 = K >> 3;
+  const int nsteps = (K8 + kWave - 1) / kWave;
+  const int S = k_split > 0 ? k_split : 1;
+  const int sps = nsteps > 0 ? (nsteps + S - 1) / S : 0;
+  return static_cast<size_t>(M) * sps * kWave * 16;
+}
+
+bool gemv_fits(int M, int K, int k_split, int rows) {
+  const int K8 = K >> 3;
+  const int nsteps = (K8 + kWave - 1) / kWave;
+  const int S = k_split > 0 ? k_split : 1;
+  const int sps = nsteps > 0 ? (nsteps + S - 1) / S : 0;
+  return gemv_lds_bytes(M, K, k_split) <= kGemvMaxLds && sps <= gemv_depth(rows);
+}
 
 hipError_t launch_gemv(const DotProblem& p, const sg_config_t& cfg, hipStream_t s) {
   GemvArgs g;
@@ -221,18 +283,22 @@ hipError_t launch_gemv(const DotProblem& p, const sg_config_t& cfg, hipStream_t 
   g.ldc = p.ldc;
   g.gamma = p.gamma;
   g.partial = p.partial;
+  g.out2 = p.out2;
+  g.ldc2 = p.ldc2;
+  g.n_split = p.n_split;
   g.N = p.N;
   g.K = p.K;
   g.eps = p.eps;
   const int K8 = p.K >> 3;
   const int nsteps = (K8 + kWave - 1) / kWave;
   const int S = cfg.k_split > 0 ? cfg.k_split : 1;
-  g.sps = (nsteps + S - 1) / S;
-  if (g.sps < 1) g.sps = 1;
-  const int rows_per_wg = kGemvWaves * cfg.rows;
+  g.sps = nsteps > 0 ? (nsteps + S - 1) / S : 1;
+  if (!gemv_fits(p.M, p.K, S, cfg.rows)) return hipErrorInvalidValue;
+  const size_t lds = gemv_lds_bytes(p.M, p.K, S);
+  const int rows_per_wg = cfg.waves * cfg.rows;
   const dim3 grid((p.N + rows_per_wg - 1) / rows_per_wg, S);
-  if (p.gamma != nullptr) return launch_fold<true>(g, p.M, cfg.rows, grid, s);
-  return launch_fold<false>(g, p.M, cfg.rows, grid, s);
+  if (p.gamma != nullptr) return launch_fold<true>(g, p.M, cfg.rows, cfg.waves, grid, lds, s);
+  return launch_fold<false>(g, p.M, cfg.rows, cfg.waves, grid, lds, s);
 }
 
 }  // namespace sg

@@ -14,9 +14,9 @@
 //
 // Workgroup = 4 waves on one 16*NB-row weight tile.  The workgroup's K-range
 // (all of K, or 1/k_split of it) is cut into 4 contiguous pieces, one per
-// wave; each wave keeps U k-steps of weights in flight.  The four wave
-// partials are summed through LDS in the fixed order 0,1,2,3, so results do
-// not depend on timing.
+// wave; each wave keeps a ring of D k-steps of weight and activation
+// fragments in flight.  The four wave partials are summed through LDS in the
+// fixed order 0,1,2,3, so results do not depend on timing.
 //
 // The latent-MoE tail reaches this kernel with its activation already
 // normalised (bf16 RMSNorm output from the norm kernel), so the epilogue only
@@ -37,7 +37,11 @@ struct MfmaArgs {
   uint16_t* out;
   int64_t ldc;
   float* partial;
+  uint16_t* out2;
+  int64_t ldc2;
+  int n_split;
   int M, N, K;
+  int row_origin;  // absolute index of weight row 0 (sets the k-order rotation)
   int sps;  // k-steps per split
 };
 
@@ -49,7 +53,7 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <int MB, int NB, int U>
+template <int MB, int NB, int D, int NKT>
 __global__ __launch_bounds__(kMfmaWaves * kWave) void mfma_kernel(MfmaArgs g) {
   constexpr int kRegs = MB * NB * 4;
   __shared__ float red[(kMfmaWaves - 1) * kRegs * kWave];
@@ -67,22 +71,26 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void mfma_kernel(MfmaArgs g) {
   const int per = (len + kMfmaWaves - 1) / kMfmaWaves;
   const int w_begin = s_begin + wave * per;
   const int w_end = min(s_end, w_begin + per);
+  const int nk = max(0, w_end - w_begin);
 
-  const uint16_t* wrow[NB];
-  bool nvalid[NB];
+  // Buffer resources: the workgroup's weight tile and the activation.  A
+  // row past N or M, a chunk past K and a step past the wave's range all map
+  // to kOob and read as zero.
+  const int tile_rows = min(16 * NB, g.N - n_base);
+  const rsrc_t wres = make_rsrc(g.w + static_cast<int64_t>(n_base) * g.ldw,
+                                static_cast<uint32_t>(((tile_rows - 1) * g.ldw + g.K) * 2));
+  const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(((g.M - 1) * g.lda + g.K) * 2));
+  uint32_t wbase[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int n = n_base + 16 * b + rl;
-    nvalid[b] = n < g.N;
-    wrow[b] = g.w + static_cast<int64_t>(nvalid[b] ? n : 0) * g.ldw;
+    const int row = 16 * b + rl;
+    wbase[b] = row < tile_rows ? static_cast<uint32_t>(row * g.ldw * 2) : kOob;
   }
-  const uint16_t* arow[MB];
-  bool mvalid[MB];
+  uint32_t xbase[MB];
 #pragma unroll
   for (int a = 0; a < MB; ++a) {
     const int m = 16 * a + rl;
-    mvalid[a] = m < g.M;
-    arow[a] = g.a + static_cast<int64_t>(mvalid[a] ? m : 0) * g.lda;
+    xbase[a] = m < g.M ? static_cast<uint32_t>(m * g.lda * 2) : kOob;
   }
 
   f32x4 acc[MB][NB];
@@ -91,30 +99,66 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void mfma_kernel(MfmaArgs g) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int ks0 = w_begin; ks0 < w_end; ks0 += U) {
-    u32x4 wv[U][NB];
+  // Ring of D k-steps: weight and activation fragments of step t are issued
+  // together, D steps before they are consumed, so waiting for one step never
+  // waits on a load issued for a later step.  No load sits in a branch.
+  // Every workgroup reads the same activation lines; if all of them walked K
+  // in the same order they would request the same lines at the same moment
+  // and queue at one L2 channel.  Each wave therefore starts its K-range at
+  // an offset set by its absolute 16-row tile (workgroups of one XCD are 8
+  // tiles apart) and wraps around.  The offset depends only on which rows the
+  // tile holds, so a row's sum is formed in the same order in every launch.
+  const int tile = (g.row_origin + n_base) >> 4;
+  const int rot = nk > 0 ? ((tile >> 3) * 23 + (tile & 7) * 7) % nk : 0;
+  auto koff = [&](int t) -> uint32_t {
+    int tt = t + rot;
+    tt = tt >= nk ? tt - nk : tt;
+    const int c = (w_begin + tt) * 4 + kg;
+    return (t < nk && c < K8) ? static_cast<uint32_t>(c * 16) : kOob;
+  };
+  auto wfrag = [&](uint32_t ko, int b) -> u32x4 {
+    return buf_load_nt(wres, (ko == kOob || wbase[b] == kOob) ? kOob : wbase[b] + ko);
+  };
+  auto xfrag = [&](uint32_t ko, int a) -> u32x4 {
+    return buf_load(xres, (ko == kOob || xbase[a] == kOob) ? kOob : xbase[a] + ko);
+  };
+
+  u32x4 wr[D][NB];
+  u32x4 xr[D][MB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = (ks0 + u) * 4 + kg;
-      const bool ok = (ks0 + u < w_end) && (c < K8);
+  for (int j = 0; j < D; ++j) {
+    const uint32_t ko = koff(j);
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        wv[u][b] = (ok && nvalid[b]) ? load_nt(wrow[b] + static_cast<int64_t>(c) * 8) : zero4();
-    }
+    for (int b = 0; b < NB; ++b) wr[j][b] = wfrag(ko, b);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = (ks0 + u) * 4 + kg;
-      const bool ok = (ks0 + u < w_end) && (c < K8);
-      u32x4 xv[MB];
+    for (int a = 0; a < MB; ++a) xr[j][a] = xfrag(ko, a);
+  }
+
+  // One ring pass: consume slot j, refill it with the step D ahead, in
+  // program order, so the loads complete in the order the steps need them.
+  auto pass = [&](int tb) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int t = tb + j;
 #pragma unroll
       for (int a = 0; a < MB; ++a)
-        xv[a] = (ok && mvalid[a]) ? load_cached(arow[a] + static_cast<int64_t>(c) * 8) : zero4();
 #pragma unroll
-      for (int a = 0; a < MB; ++a)
+        for (int b = 0; b < NB; ++b) acc[a][b] = mfma16(wr[j][b], xr[j][a], acc[a][b]);
+      const uint32_t ko = koff(t + D);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[a][b] = mfma16(wv[u][b], xv[a], acc[a][b]);
+      for (int b = 0; b < NB; ++b) wr[j][b] = wfrag(ko, b);
+#pragma unroll
+      for (int a = 0; a < MB; ++a) xr[j][a] = xfrag(ko, a);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  if constexpr (NKT > 0) {
+    // Known step count: straight-line code, so every wait is exact (a loop
+    // head would merge the pending-load state of two paths and drain).
+#pragma unroll
+    for (int tb = 0; tb < NKT; tb += D) pass(tb);
+  } else {
+    for (int tb = 0; tb < nk; tb += D) pass(tb);
   }
 
   // Fixed-order sum of the four wave partials.
@@ -169,16 +213,34 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void mfma_kernel(MfmaArgs g) {
         if (n < g.N) {
           float val = acc[a][b][v];
           if (g.res != nullptr) val += bf16_to_f32(g.res[m * g.ldr + n]);
-          g.out[m * g.ldc + n] = f32_to_bf16(val);
+          if (g.n_split > 0 && n >= g.n_split)
+            g.out2[m * g.ldc2 + (n - g.n_split)] = f32_to_bf16(val);
+          else
+            g.out[m * g.ldc + n] = f32_to_bf16(val);
         }
       }
   }
 }
 
+// Ring depth: the weight fragment plus MB activation fragments per k-step,
+// D steps deep, within the register budget of one wave per SIMD.
 template <int MB>
-hipError_t launch_mb(const MfmaArgs& g, int NB, dim3 grid, hipStream_t s) {
+constexpr int ring_depth() {
+  return MB <= 2 ? 12 : (MB <= 4 ? 8 : (MB <= 8 ? 4 : 2));
+}
+
+template <int MB>
+hipError_t launch_mb(const MfmaArgs& g, int NB, int per_wave, dim3 grid, hipStream_t s) {
   if (NB != 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mfma_kernel<MB, 1, 8>), grid, dim3(kMfmaWaves * kWave), 0, s, g);
+  constexpr int D = ring_depth<MB>();
+  // Straight-line instances for the per-wave step counts of the model's
+  // shapes (K = 7168 and K = 2048 without a split); a loop otherwise.
+  if (per_wave > 16 && per_wave <= 56)
+    hipLaunchKernelGGL((mfma_kernel<MB, 1, D, 56>), grid, dim3(kMfmaWaves * kWave), 0, s, g);
+  else if (per_wave <= 16)
+    hipLaunchKernelGGL((mfma_kernel<MB, 1, D, 16>), grid, dim3(kMfmaWaves * kWave), 0, s, g);
+  else
+    hipLaunchKernelGGL((mfma_kernel<MB, 1, D, 0>), grid, dim3(kMfmaWaves * kWave), 0, s, g);
   return hipGetLastError();
 }
 
@@ -195,9 +257,13 @@ hipError_t launch_mfma(const DotProblem& p, const sg_config_t& cfg, hipStream_t 
   g.out = p.out;
   g.ldc = p.ldc;
   g.partial = p.partial;
+  g.out2 = p.out2;
+  g.ldc2 = p.ldc2;
+  g.n_split = p.n_split;
   g.M = p.M;
   g.N = p.N;
   g.K = p.K;
+  g.row_origin = p.row_origin;
   const int KS = (p.K + kKStep - 1) / kKStep;
   const int S = cfg.k_split > 0 ? cfg.k_split : 1;
   g.sps = (KS + S - 1) / S;
@@ -206,9 +272,10 @@ hipError_t launch_mfma(const DotProblem& p, const sg_config_t& cfg, hipStream_t 
   const int NB = cfg.rows;
   const int rows_per_wg = 16 * NB;
   const dim3 grid((p.N + rows_per_wg - 1) / rows_per_wg, S);
+  const int per_wave = (g.sps + kMfmaWaves - 1) / kMfmaWaves;
   switch (MB) {
 #define SG_CASE(mb) \
-  case mb: return launch_mb<mb>(g, NB, grid, s);
+  case mb: return launch_mb<mb>(g, NB, per_wave, grid, s);
     SG_CASE(1) SG_CASE(2) SG_CASE(3) SG_CASE(4) SG_CASE(5) SG_CASE(6) SG_CASE(7) SG_CASE(8)
     SG_CASE(9) SG_CASE(10) SG_CASE(11) SG_CASE(12) SG_CASE(13) SG_CASE(14) SG_CASE(15) SG_CASE(16)
 #undef SG_CASE

@@ -31,6 +31,33 @@ __device__ __forceinline__ u32x4 load_cached(const uint16_t* p) {
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
+// ---- buffer loads ------------------------------------------------------------
+//
+// A buffer resource bounds a region of num_records bytes; a load whose offset
+// lies past it returns zeros without touching memory.  Ragged rows, the K
+// tail and steps past a wave's range therefore become an integer select on
+// the offset (kOob) instead of a branch around the load.  Loads outside
+// branches let the compiler wait for exactly the loads a value depends on
+// rather than for every outstanding load.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOob = 0x80000000u;  // any offset >= num_records reads zeros
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // 0x00020000: raw (untyped) 32-bit data, the gfx9 descriptor word 3 value.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// Non-temporal (streaming) 16-byte load: weights, each byte used once.
+__device__ __forceinline__ u32x4 buf_load_nt(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 2));
+}
+
+// Cached 16-byte load: activations, reused by every workgroup.
+__device__ __forceinline__ u32x4 buf_load(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+
 // ---- bf16 <-> fp32 ---------------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
@@ -117,6 +144,11 @@ __device__ __forceinline__ float wave_allreduce(float v) {
 }
 
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & (kWave - 1); }
-__device__ __forceinline__ int wave_id() { return static_cast<int>(threadIdx.x) >> 6; }
+// The wave index is the same for all 64 lanes; reading it through
+// readfirstlane puts it (and everything derived from it: K-ranges, trip
+// counts) in scalar registers, so loops over it are scalar loops.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+}
 
 }  // namespace sg

@@ -30,7 +30,20 @@ struct DotProblem {
   // Split-K partials: when non-NULL the kernel writes fp32 partial sums
   // partial[s][m][n] (s < k_split) instead of the bf16 output.
   float* partial;
+  // Split output: rows n >= n_split go to out2[m * ldc2 + (n - n_split)]
+  // instead of out (used by the packed KDA projection, whose F_A/beta rows
+  // form a separate tensor).  n_split <= 0 disables it.
+  uint16_t* out2;
+  int64_t ldc2;
+  int n_split;
+  // Absolute index of weight row 0 when w points into a larger matrix (the
+  // F_A/beta rows of the packed KDA weight): kernels that order their K loop
+  // by row position use it so a row is summed the same way in every launch.
+  int row_origin;
 };
+
+// Workspace regions start on 256-byte boundaries.
+size_t ws_round(size_t bytes);
 
 // Workspace layout for split-K partials of a [M,N] problem with S splits.
 inline size_t partial_floats(int S, int M, int N) { return (size_t)S * M * N; }
@@ -51,11 +64,13 @@ struct ReduceProblem {
 };
 hipError_t launch_reduce(const ReduceProblem& p, hipStream_t s);
 
-// F_B stage of the KDA F_A/beta -> F_B branch: reduces the F_A/beta split-K
-// partials (fixed order), rounds P to bf16, stores beta (and f_a when
-// requested), and computes g1 = bf16(f_a @ w_b^T) with f_a held in LDS.
+// F_B stage of the KDA F_A/beta -> F_B branch.  The F_A/beta projection
+// P [M, n_ab] arrives either as fp32 split-K partials (partial != NULL,
+// summed in fixed order) or as bf16 (p_bf16).  The stage stores beta = P[:,
+// rank:] (and f_a = P[:, :rank] when requested) and g1 = bf16(f_a @ w_b^T).
 struct FbProblem {
-  const float* partial;     // [S][M][n_ab]
+  const float* partial;     // [S][M][n_ab], or NULL
+  const uint16_t* p_bf16;   // [M][n_ab] when partial == NULL
   int S, M, n_ab, rank, n_b;
   const uint16_t* w_b;      // [n_b, rank]
   uint16_t* f_a;            // [M, rank], nullable
@@ -75,7 +90,17 @@ struct NormProblem {
 };
 hipError_t launch_rmsnorm(const NormProblem& p, hipStream_t s);
 
-// Largest M * rank the F_B stage keeps in LDS.
-constexpr int kFbMaxMRank = 32768;
+// F_B stage tiling: activation rows per workgroup, g1 rows per workgroup,
+// largest rank (f_a width) it supports.
+constexpr int kFbMGroup = 4;
+constexpr int kFbRowsPerWg = 64;
+constexpr int kFbMaxRank = 512;
+
+// GEMV activation staging: a workgroup keeps its K-range of the activation in
+// LDS (at most this many bytes) and holds every weight step of that range in
+// registers; the table sizes k_split so that both fit.
+constexpr size_t kGemvMaxLds = 128 * 1024;
+size_t gemv_lds_bytes(int M, int K, int k_split);
+bool gemv_fits(int M, int K, int k_split, int rows);
 
 }  // namespace sg

@@ -43,6 +43,9 @@ struct SmallkArgs {
   int64_t ldr;
   uint16_t* out;
   int64_t ldc;
+  uint16_t* out2;
+  int64_t ldc2;
+  int n_split;
   int M, N, K;
 };
 
@@ -62,13 +65,17 @@ __global__ __launch_bounds__(kSmallkWaves * kWave) void smallk_kernel(SmallkArgs
     float v = group_sum<G>(dot8(xv, wv, 0.f));
     if (nvalid && j == 0) {
       if (g.res != nullptr) v += bf16_to_f32(g.res[m * g.ldr + n]);
-      g.out[m * g.ldc + n] = f32_to_bf16(v);
+      if (g.n_split > 0 && n >= g.n_split)
+        g.out2[m * g.ldc2 + (n - g.n_split)] = f32_to_bf16(v);
+      else
+        g.out[m * g.ldc + n] = f32_to_bf16(v);
     }
   }
 }
 
 struct FbArgs {
   const float* partial;
+  const uint16_t* p_bf16;
   int S, M, n_ab, rank, n_b;
   const uint16_t* w_b;
   uint16_t* f_a;
@@ -76,52 +83,76 @@ struct FbArgs {
   uint16_t* g1;
 };
 
-template <int G>
+// Sum of the S split-K partials p[0], p[plane], ..., in the fixed order
+// s = 0, 1, ..., S-1 (eight independent loads in flight at a time).
+__device__ __forceinline__ float sum_splits(const float* p, int64_t plane, int S) {
+  float acc = 0.f;
+  int s = 0;
+  for (; s + 8 <= S; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = p[(s + i) * plane];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += v[i];
+  }
+  for (; s < S; ++s) acc += p[s * plane];
+  return acc;
+}
+
+// Workgroup (x, y) computes g1 rows [x*kFbRowsPerWg, (x+1)*kFbRowsPerWg) for
+// activation rows [y*kFbMGroup, (y+1)*kFbMGroup): it forms only those rows'
+// bf16 P (summing the F_A/beta partials in fixed order when PARTIALS, so
+// every workgroup agrees bit for bit, else reading the bf16 P), keeps f_a in
+// LDS, and workgroups with x == 0 also store beta (and f_a).
+template <int G, bool PARTIALS>
 __global__ __launch_bounds__(kSmallkWaves * kWave) void fab_fb_tail_kernel(FbArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t fa_lds[kFbMaxMRank];
+  __shared__ __attribute__((aligned(16))) uint16_t fa_lds[kFbMGroup * kFbMaxRank];
   const int tid = static_cast<int>(threadIdx.x);
   const int nthreads = kSmallkWaves * kWave;
   const int64_t plane = static_cast<int64_t>(g.M) * g.n_ab;
+  const int m0 = static_cast<int>(blockIdx.y) * kFbMGroup;
+  const int mg = min(kFbMGroup, g.M - m0);
+  const bool first = blockIdx.x == 0;
 
-  // 1. f_a = bf16(sum_s partial[s][m][r]) for r < rank, fixed order s = 0..S-1.
-  const int mr = g.M * g.rank;
-  for (int idx = tid; idx < mr; idx += nthreads) {
-    const int m = idx / g.rank, r = idx - m * g.rank;
-    const float* p = g.partial + static_cast<int64_t>(m) * g.n_ab + r;
-    float acc = 0.f;
-    for (int s = 0; s < g.S; ++s) acc += p[s * plane];
-    const uint16_t b = f32_to_bf16(acc);
-    fa_lds[idx] = b;
-    if (blockIdx.x == 0 && g.f_a != nullptr) g.f_a[idx] = b;
-  }
-  // 2. beta = bf16(sum_s partial[s][m][rank + h]) (workgroup 0 only).
-  if (blockIdx.x == 0) {
-    const int nbeta = g.n_ab - g.rank;
-    const int mb = g.M * nbeta;
-    for (int idx = tid; idx < mb; idx += nthreads) {
-      const int m = idx / nbeta, h = idx - m * nbeta;
-      const float* p = g.partial + static_cast<int64_t>(m) * g.n_ab + g.rank + h;
-      float acc = 0.f;
-      for (int s = 0; s < g.S; ++s) acc += p[s * plane];
-      g.beta[idx] = f32_to_bf16(acc);
+  // 1. P = bf16(sum_s partial[s][m][j]) for this workgroup's rows; all n_ab
+  //    columns in the first column of workgroups, the rank f_a columns elsewhere.
+  const int cols = first ? g.n_ab : g.rank;
+  for (int idx = tid; idx < mg * cols; idx += nthreads) {
+    const int mm = idx / cols, j = idx - mm * cols;
+    const int m = m0 + mm;
+    uint16_t b;
+    if constexpr (PARTIALS)
+      b = f32_to_bf16(sum_splits(g.partial + static_cast<int64_t>(m) * g.n_ab + j, plane, g.S));
+    else
+      b = g.p_bf16[static_cast<int64_t>(m) * g.n_ab + j];
+    if (j < g.rank) {
+      fa_lds[mm * g.rank + j] = b;
+      if (first && g.f_a != nullptr) g.f_a[static_cast<int64_t>(m) * g.rank + j] = b;
+    } else {
+      g.beta[static_cast<int64_t>(m) * (g.n_ab - g.rank) + (j - g.rank)] = b;
     }
   }
   __syncthreads();
 
-  // 3. g1[m, i] = bf16(sum_r f_a[m, r] * w_b[i, r]).
+  // 2. g1[m, i] = bf16(sum_r f_a[m, r] * w_b[i, r]); each weight chunk is
+  //    loaded once and used for every activation row of the group.
   const int lane = lane_id();
   const int j = lane & (G - 1);
-  const int rows_per_wave = kWave / G;
-  const int i = (static_cast<int>(blockIdx.x) * kSmallkWaves + wave_id()) * rows_per_wave + lane / G;
   const int K8 = g.rank >> 3;
-  const bool ivalid = i < g.n_b;
   const bool cvalid = j < K8;
-  const u32x4 wv =
-      (ivalid && cvalid) ? load_nt(g.w_b + static_cast<int64_t>(i) * g.rank + j * 8) : zero4();
-  for (int m = 0; m < g.M; ++m) {
-    const u32x4 xv = cvalid ? *reinterpret_cast<const u32x4*>(fa_lds + m * g.rank + j * 8) : zero4();
-    const float v = group_sum<G>(dot8(xv, wv, 0.f));
-    if (ivalid && j == 0) g.g1[static_cast<int64_t>(m) * g.n_b + i] = f32_to_bf16(v);
+  constexpr int kRowsPerPass = kSmallkWaves * (kWave / G);
+  const int i_base = static_cast<int>(blockIdx.x) * kFbRowsPerWg + wave_id() * (kWave / G) + lane / G;
+  for (int off = 0; off < kFbRowsPerWg; off += kRowsPerPass) {
+    const int i = i_base + off;
+    const bool ivalid = i < g.n_b;
+    const u32x4 wv =
+        (ivalid && cvalid) ? load_nt(g.w_b + static_cast<int64_t>(i) * g.rank + j * 8) : zero4();
+    for (int mm = 0; mm < mg; ++mm) {
+      const u32x4 xv =
+          cvalid ? *reinterpret_cast<const u32x4*>(fa_lds + mm * g.rank + j * 8) : zero4();
+      const float v = group_sum<G>(dot8(xv, wv, 0.f));
+      if (ivalid && j == 0) g.g1[static_cast<int64_t>(m0 + mm) * g.n_b + i] = f32_to_bf16(v);
+    }
   }
 }
 
@@ -142,7 +173,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs g) {
     const int m = static_cast<int>(idx / g.N);
     const int n = static_cast<int>(idx - static_cast<int64_t>(m) * g.N);
     float acc = 0.f;
-    for (int s = 0; s < g.S; ++s) acc += g.partial[s * plane + idx];
+    acc = sum_splits(g.partial + idx, plane, g.S);
     if (g.res != nullptr) acc += bf16_to_f32(g.res[m * g.ldr + n]);
     g.out[m * g.ldc + n] = f32_to_bf16(acc);
   }
@@ -198,11 +229,13 @@ hipError_t launch_smallk_g(const SmallkArgs& g, hipStream_t s) {
 
 template <int G>
 hipError_t launch_fb_g(const FbArgs& g, hipStream_t s) {
-  const int rows_per_wg = kSmallkWaves * (kWave / G);
-  // At least one workgroup: workgroup 0 also stores beta and f_a.
-  const int blocks = (g.n_b + rows_per_wg - 1) / rows_per_wg;
-  const dim3 grid(blocks > 0 ? blocks : 1);
-  hipLaunchKernelGGL((fab_fb_tail_kernel<G>), grid, dim3(kSmallkWaves * kWave), 0, s, g);
+  // At least one column of workgroups: it also stores beta and f_a.
+  const int bx = (g.n_b + kFbRowsPerWg - 1) / kFbRowsPerWg;
+  const dim3 grid(bx > 0 ? bx : 1, (g.M + kFbMGroup - 1) / kFbMGroup);
+  if (g.partial != nullptr)
+    hipLaunchKernelGGL((fab_fb_tail_kernel<G, true>), grid, dim3(kSmallkWaves * kWave), 0, s, g);
+  else
+    hipLaunchKernelGGL((fab_fb_tail_kernel<G, false>), grid, dim3(kSmallkWaves * kWave), 0, s, g);
   return hipGetLastError();
 }
 
@@ -210,7 +243,8 @@ hipError_t launch_fb_g(const FbArgs& g, hipStream_t s) {
 
 hipError_t launch_smallk(const DotProblem& p, const sg_config_t& cfg, hipStream_t s) {
   (void)cfg;
-  SmallkArgs g{p.a, p.lda, p.w, p.ldw, p.res, p.ldr, p.out, p.ldc, p.M, p.N, p.K};
+  SmallkArgs g{p.a,    p.lda,  p.w,       p.ldw, p.res, p.ldr, p.out,
+               p.ldc,  p.out2, p.ldc2,    p.n_split, p.M, p.N, p.K};
   switch (lanes_for(p.K >> 3)) {
     case 1: return launch_smallk_g<1>(g, s);
     case 2: return launch_smallk_g<2>(g, s);
@@ -223,7 +257,7 @@ hipError_t launch_smallk(const DotProblem& p, const sg_config_t& cfg, hipStream_
 }
 
 hipError_t launch_fab_fb_tail(const FbProblem& p, hipStream_t s) {
-  FbArgs g{p.partial, p.S, p.M, p.n_ab, p.rank, p.n_b, p.w_b, p.f_a, p.beta, p.g1};
+  FbArgs g{p.partial, p.p_bf16, p.S, p.M, p.n_ab, p.rank, p.n_b, p.w_b, p.f_a, p.beta, p.g1};
   switch (lanes_for(p.rank >> 3)) {
     case 1: return launch_fb_g<1>(g, s);
     case 2: return launch_fb_g<2>(g, s);

@@ -133,6 +133,11 @@ int sg_overlap_max_tokens(void);
  * error. */
 size_t sg_workspace_bytes(int op, int M, int N, int K);
 
+/* Bytes of device workspace kda_projection_overlap needs: which = 0 for
+ * ws_main (Q/K/V/G split-K partials, 0 when unsplit), 1 for ws_aux (the
+ * bf16 F_A/beta projection [M, n_ab] plus its split-K partials). */
+size_t sg_kda_workspace_bytes(int which, int M, int K, int n_qkvg, int n_ab);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *sg_strerror(int status);
 
@@ -177,17 +182,21 @@ int kda_fab_fb_proj(const sg_bf16 *x, const sg_bf16 *w_ab, const sg_bf16 *w_b,
                     void *ws, size_t ws_bytes, sg_stream_t stream);
 
 /* Concurrent KDA projection [P3 low_latency_gemm.py
- * run_kda_projection_overlap]: kda_qkvg_proj on packed_w rows [0, n_qkvg) on
- * `main`, and kda_fab_fb_proj on packed_w rows [n_qkvg, n_qkvg + n_ab) with
- * w_b on `aux`.  Fork: `fork` is recorded on main and waited on by aux; join:
- * `join` is recorded on aux and waited on by main, so that every output is
- * complete in main's order when the call's work retires.  If aux, fork or
- * join is NULL the two branches run one after the other on main (the
- * reference's fallback).  Outputs are bitwise identical either way.
- * packed_w [n_qkvg + n_ab, K] contiguous; qkvg [M,n_qkvg]; beta, g1 as in
- * kda_fab_fb_proj (f_a is not returned, as in the reference).  ws_main needs
- * sg_workspace_bytes(SG_OP_GEMM, M, n_qkvg, K) and ws_aux
- * sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K); they must not overlap. */
+ * run_kda_projection_overlap; kda.py forward fallback]:
+ *   qkvg = bf16(x @ packed_w[0:n_qkvg]^T)                    on `main`
+ *   P    = bf16(x @ packed_w[n_qkvg:n_qkvg+n_ab]^T), beta = P[:, rank:],
+ *   g1   = bf16(P[:, :rank] @ w_b^T)                          on `aux`
+ * Fork: `fork` is recorded on main and waited on by aux; join: `join` is
+ * recorded on aux and waited on by main, so every output is complete in
+ * main's order once the call's work retires.  If aux, fork or join is NULL
+ * the call runs on main alone: one packed GEMM over all n_qkvg + n_ab rows
+ * (the reference's sequential path), then F_B.  Every row is computed with
+ * the configuration sg_select gives the packed shape (M, n_qkvg + n_ab, K)
+ * in both schedules, so the outputs are bitwise identical either way.
+ * packed_w [n_qkvg + n_ab, K] contiguous; qkvg [M,n_qkvg]; beta
+ * [M,n_ab-rank]; g1 [M,n_b]; w_b [n_b,rank]; 0 < rank < n_ab, rank % 8 == 0,
+ * rank <= 512.  ws_main needs sg_kda_workspace_bytes(0, ...) bytes (often 0)
+ * and ws_aux sg_kda_workspace_bytes(1, ...); they must not overlap. */
 int kda_projection_overlap(const sg_bf16 *x, const sg_bf16 *packed_w, const sg_bf16 *w_b,
                            sg_bf16 *qkvg, sg_bf16 *beta, sg_bf16 *g1,
                            int M, int K, int n_qkvg, int n_ab, int rank, int n_b,

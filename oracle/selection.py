@@ -15,11 +15,16 @@ Rule, for C[M,N] = A[M,K] W[N,K]^T:
     lanes per weight row; rows = 64 / G rows per wave; k_split = 1;
     k_unroll = 1; grid = ceil(N / (4 * rows)); m_tile = M.
   * M <= 16, K > 256: steps = ceil((K/8) / 64).
-      - N >= 1024: GEMV_ROW, rows = 1 (M <= 2), 2 (M <= 8) or 4; k_split = 1.
-      - N < 1024: GEMV_SPLITK, rows = 1, k_split = split(steps, ceil(2048 / N)).
-    k_unroll = 16 / rows; grid = ceil(N / (4 * rows)) * k_split; m_tile = M.
+      - N >= 1024: GEMV_ROW, rows = 1 (M <= 2), 2 (M <= 8) or 4; want = 1.
+      - N < 1024: GEMV_SPLITK, rows = 1, want = ceil(2048 / N).
+      depth = 16, 14, 7 for rows = 1, 2, 4 (k_unroll = depth);
+      max_sps = min(floor(128 / M), depth), need = ceil(steps / max_sps),
+      k_split = split(steps, max(want, need)), sps = ceil(steps / k_split);
+      waves = 8 if M * sps > 64 else 4.
+      grid = ceil(N / (waves * rows)) * k_split; m_tile = M.
   * 17 <= M <= 256: MFMA_TILE, m_tile = 16 * ceil(M / 16), rows = 1,
-    k_unroll = 8, tiles = ceil(N / 16), ksteps = ceil(K / 32).
+    k_unroll = 12, 8, 4, 2 for m_tile/16 <= 2, <= 4, <= 8, above;
+    tiles = ceil(N / 16), ksteps = ceil(K / 32).
       - tiles >= 192: k_split = 1.
       - else want = min(ceil(256 / tiles), max(1, floor(ksteps / 8))),
         k_split = split(ksteps, want).
@@ -76,11 +81,19 @@ def select(M: int, N: int, K: int, has_residual: bool = False):
             steps = _cdiv(K // 8, 64)
             if N >= 1024:
                 rows = 1 if M <= 2 else (2 if M <= 8 else 4)
-                cfg.update(kind=GEMV_ROW, rows=rows, k_split=1)
+                cfg.update(kind=GEMV_ROW, rows=rows)
+                want = 1
             else:
-                cfg.update(kind=GEMV_SPLITK, rows=1, k_split=_split(steps, _cdiv(2048, N)))
-            cfg["k_unroll"] = 16 // cfg["rows"]
-            cfg["grid"] = _cdiv(N, 4 * cfg["rows"]) * cfg["k_split"]
+                cfg.update(kind=GEMV_SPLITK, rows=1)
+                want = _cdiv(2048, N)
+            depth = {1: 16, 2: 14, 4: 7}[cfg["rows"]]
+            max_sps = min(128 // M, depth)
+            need = _cdiv(steps, max_sps)
+            cfg["k_split"] = _split(steps, max(want, need))
+            sps = _cdiv(steps, cfg["k_split"])
+            cfg["waves"] = 8 if M * sps > 64 else 4
+            cfg["k_unroll"] = depth
+            cfg["grid"] = _cdiv(N, cfg["waves"] * cfg["rows"]) * cfg["k_split"]
     else:
         tiles = _cdiv(N, 16)
         ksteps = _cdiv(K, 32)
@@ -89,7 +102,9 @@ def select(M: int, N: int, K: int, has_residual: bool = False):
         else:
             want = min(_cdiv(256, tiles), max(1, ksteps // 8))
             ks = _split(ksteps, want)
-        cfg.update(kind=MFMA_TILE, m_tile=16 * _cdiv(M, 16), rows=1, k_unroll=8, k_split=ks,
+        mb = _cdiv(M, 16)
+        depth = 12 if mb <= 2 else (8 if mb <= 4 else (4 if mb <= 8 else 2))
+        cfg.update(kind=MFMA_TILE, m_tile=16 * mb, rows=1, k_unroll=depth, k_split=ks,
                    grid=tiles * ks)
     return OK, cfg
 

@@ -177,15 +177,17 @@ def test_overlap_graph_replay(device, M):
     q = torch.empty_like(q_e)
     g1 = torch.empty_like(g1_e)
     beta = torch.empty_like(b_e)
-    ws_aux = torch.empty(sg.sg_workspace_bytes(sg.SG_OP_FAB_FB, M, 136, synth.HIDDEN),
+    ws_aux = torch.empty(sg.sg_kda_workspace_bytes(1, M, synth.HIDDEN, 4096, 136),
                          dtype=torch.uint8, device=device)
+    ws_main = torch.empty(max(sg.sg_kda_workspace_bytes(0, M, synth.HIDDEN, 4096, 136), 256),
+                          dtype=torch.uint8, device=device)
     side = torch.cuda.Stream(device)
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=side):
             sg.kda_projection_overlap(xd, pd, wbd, qkvg=q, g1=g1, beta=beta, ws_aux=ws_aux,
-                                      aux_stream=aux, fork=fork, join=join)
+                                      ws_main=ws_main, aux_stream=aux, fork=fork, join=join)
     torch.cuda.current_stream().wait_stream(side)
     for rep in range(4):
         for t in (q, g1, beta):

@@ -196,7 +196,6 @@ def test_fab_fb_validation(lib):
     assert _fab(lib, rank=124) == E.SG_ERR_UNSUPPORTED
     assert _fab(lib, rank=520, n_ab=600) == E.SG_ERR_UNSUPPORTED
     assert _fab(lib, M=300) == E.SG_ERR_UNSUPPORTED
-    assert _fab(lib, M=256, rank=256, n_ab=300) == E.SG_ERR_UNSUPPORTED  # f_a too big for LDS
     assert _fab(lib, x=NUL) == E.SG_ERR_INVALID_ARG
     assert _fab(lib, beta=NUL) == E.SG_ERR_INVALID_ARG
     assert _fab(lib, g1=NUL) == E.SG_ERR_INVALID_ARG
@@ -207,7 +206,9 @@ def test_fab_fb_validation(lib):
 
 def test_overlap_validation(lib):
     E = _lib
-    need_aux = lib.sg_workspace_bytes(_lib.SG_OP_FAB_FB, 2, 136, 7168)
+    need_aux = lib.sg_kda_workspace_bytes(1, 2, 7168, 4096, 136)
+    assert need_aux >= 2 * 136 * 2
+    assert lib.sg_kda_workspace_bytes(0, 2, 7168, 4096, 136) == 0
 
     def ov(**kw):
         args = dict(x=A16, packed=B16, w_b=C16, qkvg=ctypes.c_void_p(0x80000),
