@@ -21,8 +21,8 @@ import torch
 
 from . import _lib
 from ._lib import (SG_KIND_GEMV_ROW, SG_KIND_GEMV_SMALLK, SG_KIND_GEMV_SPLITK,  # noqa: F401
-                   SG_KIND_MFMA_TILE, SG_KIND_NONE, SG_OP_FAB_FB, SG_OP_GEMM,
-                   SG_OP_LATENT_TAIL, SgConfig)
+                   SG_KIND_MFMA_DIRECT, SG_KIND_MFMA_TILE, SG_KIND_MFMA_WAVESPLIT, SG_KIND_NONE,
+                   SG_OP_FAB_FB, SG_OP_GEMM, SG_OP_LATENT_TAIL, SgConfig)
 
 __all__ = [
     "sg_select", "sg_overlap_gate", "sg_overlap_max_tokens", "sg_workspace_bytes",

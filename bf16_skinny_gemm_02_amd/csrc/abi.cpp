@@ -36,8 +36,9 @@ int check_output2(const void* p, int64_t ld, int64_t min_ld) {
   return SG_OK;
 }
 
-// Kernels address a weight tile (at most 32 rows) and the whole activation
+// Kernels address a weight tile (at most 64 rows) and the whole activation
 // through 32-bit buffer offsets: both spans must stay below 2^31 bytes.
+constexpr int64_t kMaxTileRows = 64;
 bool spans_ok(int64_t rows, int64_t ld, int64_t K) {
   if (rows <= 0) return true;
   return ((rows - 1) * ld + K) * 2 < (int64_t(1) << 31);
@@ -55,36 +56,42 @@ bool same_config(const sg_config_t& a, const sg_config_t& b) {
          a.k_split == b.k_split && a.grid == b.grid;
 }
 
+bool is_mfma(int kind) {
+  return kind == SG_KIND_MFMA_TILE || kind == SG_KIND_MFMA_WAVESPLIT || kind == SG_KIND_MFMA_DIRECT;
+}
+
+// The main kernel of configuration c, with the problem's epilogue as given
+// (p.partial set means fp32 partials).
+hipError_t launch_main(const DotProblem& p, const sg_config_t& c, hipStream_t s) {
+  if (is_mfma(c.kind)) return sg::launch_mfma(p, c, s);
+  if (c.kind == SG_KIND_GEMV_SMALLK) return sg::launch_smallk(p, c, s);
+  return sg::launch_gemv(p, c, s);
+}
+
 // Enqueue out = a @ w^T (+res) with configuration c.  ws holds the split-K
 // partials when c.k_split > 1 (size checked by the caller).
 int enqueue_dot(DotProblem p, const sg_config_t& c, void* ws, hipStream_t s) {
-  switch (c.kind) {
-    case SG_KIND_NONE:
-      return SG_OK;
-    case SG_KIND_GEMV_SMALLK:
-      return hip_status(sg::launch_smallk(p, c, s));
-    case SG_KIND_GEMV_ROW:
-    case SG_KIND_GEMV_SPLITK:
-    case SG_KIND_MFMA_TILE: {
-      const bool split = c.k_split > 1;
-      if (split) p.partial = static_cast<float*>(ws);
-      hipError_t e = (c.kind == SG_KIND_MFMA_TILE) ? sg::launch_mfma(p, c, s) : sg::launch_gemv(p, c, s);
-      if (e != hipSuccess) return SG_ERR_HIP;
-      if (!split) return SG_OK;
-      sg::ReduceProblem r{};
-      r.partial = p.partial;
-      r.S = c.k_split;
-      r.M = p.M;
-      r.N = p.N;
-      r.res = p.res;
-      r.ldr = p.ldr;
-      r.out = p.out;
-      r.ldc = p.ldc;
-      return hip_status(sg::launch_reduce(r, s));
-    }
-    default:
-      return SG_ERR_UNSUPPORTED;
-  }
+  if (c.kind == SG_KIND_NONE) return SG_OK;
+  if (c.kind == SG_KIND_GEMV_SMALLK) return hip_status(sg::launch_smallk(p, c, s));
+  if (c.kind != SG_KIND_GEMV_ROW && c.kind != SG_KIND_GEMV_SPLITK && !is_mfma(c.kind))
+    return SG_ERR_UNSUPPORTED;
+  const bool split = c.k_split > 1;
+  if (split) p.partial = static_cast<float*>(ws);
+  if (launch_main(p, c, s) != hipSuccess) return SG_ERR_HIP;
+  if (!split) return SG_OK;
+  sg::ReduceProblem r{};
+  r.partial = p.partial;
+  r.S = c.k_split;
+  r.M = p.M;
+  r.N = p.N;
+  r.res = p.res;
+  r.ldr = p.ldr;
+  r.out = p.out;
+  r.ldc = p.ldc;
+  r.out2 = p.out2;
+  r.ldc2 = p.ldc2;
+  r.n_split = p.n_split;
+  return hip_status(sg::launch_reduce(r, s));
 }
 
 // Validation of skinny_gemm arguments; fills *cfg on success.
@@ -107,19 +114,32 @@ int validate_gemm(const sg_bf16* A, int64_t lda, const sg_bf16* W, int64_t ldw, 
   if ((st = check_output2(C, ldc, N)) != SG_OK) return st;
   if (R != nullptr && (st = check_output2(R, ldr, N)) != SG_OK) return st;
   if (user_cfg != nullptr && !same_config(*user_cfg, *cfg)) return SG_ERR_UNSUPPORTED;
-  if (!spans_ok(M, lda, K) || !spans_ok(32, ldw, K)) return SG_ERR_UNSUPPORTED;
+  if (!spans_ok(M, lda, K) || !spans_ok(kMaxTileRows, ldw, K)) return SG_ERR_UNSUPPORTED;
   return check_workspace(ws, ws_bytes, sg_workspace_bytes(SG_OP_GEMM, M, N, K));
 }
 
 // The F_A/beta stage configuration: the table's choice, run in partial mode.
-// The small-K kernel has no partial mode, so that case uses the GEMV kernel
-// with one split.
+// The small-K kernel has no partial mode, so that case runs the kernel the
+// table uses for K > 256 at the same M, without a K split.
 sg_config_t fab_config(int M, int n_ab, int K) {
   sg_config_t c;
   sg_select(M, n_ab, K, 0, &c);
   if (c.kind == SG_KIND_GEMV_SMALLK) {
-    c.kind = SG_KIND_GEMV_SPLITK;
-    c.rows = 1;
+    if (M == 1) {
+      c.kind = SG_KIND_GEMV_SPLITK;
+      c.m_tile = 1;
+      c.rows = 1;
+      c.waves = 4;
+      c.k_unroll = 16;
+      c.grid = (n_ab + 3) / 4;
+    } else {
+      c.kind = SG_KIND_MFMA_WAVESPLIT;
+      c.m_tile = 4 * ((M + 3) / 4);
+      c.rows = 16;
+      c.waves = 4;
+      c.k_unroll = 4;
+      c.grid = (n_ab + 15) / 16;
+    }
     c.k_split = 1;
   }
   if (c.k_split < 1) c.k_split = 1;
@@ -161,8 +181,7 @@ int enqueue_fab_fb(const sg_bf16* x, const sg_bf16* w_ab, const sg_bf16* w_b, sg
   p.N = n_ab;
   p.K = K;
   p.partial = static_cast<float*>(ws);
-  hipError_t e = (c.kind == SG_KIND_MFMA_TILE) ? sg::launch_mfma(p, c, s) : sg::launch_gemv(p, c, s);
-  if (e != hipSuccess) return SG_ERR_HIP;
+  if (launch_main(p, c, s) != hipSuccess) return SG_ERR_HIP;
   sg::FbProblem fb{};
   fb.partial = p.partial;
   fb.S = c.k_split;
@@ -282,8 +301,9 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
   fb.beta = beta;
   fb.g1 = g1;
 
-  if (!concurrent && !split) {
-    // One packed launch: Q/K/V/G rows to qkvg, F_A/beta rows to P; then F_B.
+  if (!concurrent) {
+    // One packed launch: Q/K/V/G rows to qkvg, F_A/beta rows to P (through
+    // the split-K reduction when K is split, partials in ws_main); then F_B.
     q.N = n_qkvg + n_ab;
     q.out2 = pbuf;
     q.ldc2 = n_ab;
@@ -292,7 +312,7 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
       q.out = pbuf;
       q.ldc = n_ab;
     }
-    if ((st = enqueue_dot(q, c, nullptr, sm)) != SG_OK) return st;
+    if ((st = enqueue_dot(q, c, ws_main, sm)) != SG_OK) return st;
     fb.p_bf16 = pbuf;
     return hip_status(sg::launch_fab_fb_tail(fb, sm));
   }
@@ -301,15 +321,13 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
   auto run_fab = [&](hipStream_t s) -> int {
     DotProblem f = q;
     f.w = w_ab;
-    f.row_origin = n_qkvg;
     f.N = n_ab;
     f.out = pbuf;
     f.ldc = n_ab;
     f.ldr = n_ab;
     if (split) {
       f.partial = aux_part;
-      hipError_t e = (c.kind == SG_KIND_MFMA_TILE) ? sg::launch_mfma(f, c, s) : sg::launch_gemv(f, c, s);
-      if (e != hipSuccess) return SG_ERR_HIP;
+      if (launch_main(f, c, s) != hipSuccess) return SG_ERR_HIP;
       fb.partial = aux_part;
       fb.S = c.k_split;
     } else {
@@ -320,10 +338,6 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
     return hip_status(sg::launch_fab_fb_tail(fb, s));
   };
   q.N = n_qkvg;
-  if (!concurrent) {
-    if (n_qkvg > 0 && (st = enqueue_dot(q, c, ws_main, sm)) != SG_OK) return st;
-    return run_fab(sm);
-  }
   if (hipEventRecord(ef, sm) != hipSuccess) return SG_ERR_HIP;
   if (hipStreamWaitEvent(sa, ef, 0) != hipSuccess) return SG_ERR_HIP;
   if (n_qkvg > 0 && (st = enqueue_dot(q, c, ws_main, sm)) != SG_OK) return st;
@@ -349,14 +363,18 @@ extern "C" int latent_moe_tail(const sg_bf16* latent, const sg_bf16* gamma, floa
   if ((st = check_operand16(w_up, d_latent, d_latent)) != SG_OK) return st;
   if ((st = check_output2(out, d_hidden, d_hidden)) != SG_OK) return st;
   if (shared != nullptr && (st = check_output2(shared, d_hidden, d_hidden)) != SG_OK) return st;
+  const bool fold = (M == 1) && (c.kind == SG_KIND_GEMV_SMALLK ||
+                                 ((c.kind == SG_KIND_GEMV_ROW || c.kind == SG_KIND_GEMV_SPLITK) &&
+                                  c.k_split == 1));
+  if (!fold && d_latent > sg::kNormMaxD) return SG_ERR_UNSUPPORTED;
+  if (!fold && !spans_ok(kMaxTileRows, d_latent, d_latent)) return SG_ERR_UNSUPPORTED;
   const size_t need = sg_workspace_bytes(SG_OP_LATENT_TAIL, M, d_hidden, d_latent);
   if ((st = check_workspace(ws, ws_bytes, need)) != SG_OK) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (c.kind == SG_KIND_MFMA_TILE || c.k_split > 1) {
+  if (!fold) {
     // RMSNorm into a bf16 buffer at the start of the workspace, then the GEMM
-    // with the shared-expert add in its epilogue (the MFMA tile, or a GEMV
-    // whose K-range is split).
+    // with the shared-expert add in its epilogue.
     const size_t norm_bytes = (static_cast<size_t>(M) * d_latent * sizeof(uint16_t) + 255) & ~size_t(255);
     sg::NormProblem np{latent, gamma, static_cast<uint16_t*>(ws), M, d_latent, eps};
     if (sg::launch_rmsnorm(np, s) != hipSuccess) return SG_ERR_HIP;
@@ -374,11 +392,14 @@ extern "C" int latent_moe_tail(const sg_bf16* latent, const sg_bf16* gamma, floa
     p.K = d_latent;
     return enqueue_dot(p, c, static_cast<char*>(ws) + norm_bytes, s);
   }
-  // One GEMV launch that stages the latent in LDS and normalises it there.
-  // The small-K GEMV has no fold, so small latents use the GEMV kernel too.
+  // One GEMV launch (M = 1, whole row in one workgroup) that stages the
+  // latent in LDS and normalises it there.  The small-K GEMV has no fold, so
+  // a small latent uses the GEMV kernel too.
   if (c.kind == SG_KIND_GEMV_SMALLK) {
     c.kind = SG_KIND_GEMV_SPLITK;
+    c.m_tile = 1;
     c.rows = 1;
+    c.waves = 4;
     c.k_split = 1;
   }
   DotProblem p{};

@@ -15,13 +15,18 @@
 
 namespace {
 
-constexpr int kWaves = 4;            // waves per workgroup for every kind
-constexpr int kGemvRowMinN = 1024;   // below this N the GEMV splits K
+constexpr int kWaves = 4;            // waves per workgroup unless a kind sets its own
+constexpr int kGemvRowMinN = 1024;   // below this N the M = 1 GEMV splits K
 constexpr int kGemvWaveTarget = 2048;  // waves the split-K GEMV aims for
 constexpr int kSmallK = 256;         // K at or below this: small-K GEMV
-constexpr int kMfmaNoSplitTiles = 192;  // weight tiles that fill the chip alone
-constexpr int kMfmaTileTarget = 256; // workgroups the MFMA split aims for
-constexpr int kMfmaMinStepsPerSplit = 8;
+constexpr int kGemvDepth = 16;       // 512-wide weight steps an M = 1 GEMV wave holds
+// MFMA ring kernels.  A chunk is 4 k-steps of 32 (128 k).
+constexpr int kWgTarget = 224;       // workgroups a launch aims for (256 CUs, one each)
+constexpr int kNoSplitTiles = 192;   // this many tiles fill the chip without a K split
+constexpr int kSplitMaxTiles = 320;  // WAVESPLIT up to this many 16-row tiles
+constexpr int kSplitRing = 4;        // WAVESPLIT ring slots
+constexpr int kWideRing = 4;         // TILE ring slots for M <= 16 (2 waves, 32 rows)
+constexpr int kTileRing = 3;         // TILE ring slots for 16 < M <= 64 (4 waves, 64 rows)
 constexpr int kOverlapMaxTokens = 32;
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -41,18 +46,19 @@ int effective_split(int steps, int want) {
   return ceil_div(steps, per);
 }
 
-constexpr int kStageKiB = 128;       // LDS a GEMV workgroup may stage activations in
-
-int gemv_rows_for(int M) {
-  if (M <= 2) return 1;
-  if (M <= 8) return 2;
-  return 4;
+// K split for `tiles` workgroup tiles: none once the tiles fill the chip,
+// otherwise enough ranges for about kWgTarget workgroups, each range at
+// least min_steps k-steps long.
+int mfma_split(int tiles, int ksteps, int min_steps) {
+  if (tiles >= kNoSplitTiles) return 1;
+  int cap = ksteps / min_steps;
+  if (cap < 1) cap = 1;
+  int want = ceil_div(kWgTarget, tiles);
+  if (want > cap) want = cap;
+  return effective_split(ksteps, want);
 }
 
-// Weight steps (512 k) a GEMV wave holds, and k-steps (32 k) an MFMA wave
-// keeps in flight.
-int gemv_ring_depth(int rows) { return rows == 1 ? 16 : (rows == 2 ? 14 : 7); }
-int mfma_ring_depth(int mb) { return mb <= 2 ? 12 : (mb <= 4 ? 8 : (mb <= 8 ? 4 : 2)); }
+int direct_ring_depth(int mb) { return mb <= 8 ? 4 : 2; }
 
 }  // namespace
 
@@ -70,58 +76,74 @@ extern "C" int sg_select(int M, int N, int K, int has_residual, sg_config_t* out
     return SG_OK;
   }
   const int K8 = K / 8;
+  const int ksteps = ceil_div(K, 32);
   c.waves = kWaves;
   c.nt_weights = 1;
-  if (M <= 16) {
+  if (M <= 16 && K <= kSmallK) {
+    c.kind = SG_KIND_GEMV_SMALLK;
     c.m_tile = M;
-    if (K <= kSmallK) {
-      c.kind = SG_KIND_GEMV_SMALLK;
-      const int G = pow2_ceil(K8 > 0 ? K8 : 1);
-      c.rows = 64 / G;
-      c.k_split = 1;
-      c.k_unroll = 1;
-      c.grid = ceil_div(N, kWaves * c.rows);
+    const int G = pow2_ceil(K8 > 0 ? K8 : 1);
+    c.rows = 64 / G;
+    c.k_split = 1;
+    c.k_unroll = 1;
+    c.grid = ceil_div(N, kWaves * c.rows);
+  } else if (M == 1) {
+    // A workgroup holds every weight step of its K-range in registers (at
+    // most kGemvDepth steps of 512) and the activation for that range in
+    // LDS: K is split across workgroups until both fit.
+    const int steps = ceil_div(K8, 64);
+    int want;
+    if (N >= kGemvRowMinN) {
+      c.kind = SG_KIND_GEMV_ROW;
+      want = 1;
     } else {
-      // A workgroup holds every weight step of its K-range in registers (at
-      // most gemv_ring_depth(rows) steps of 512) and its activation rows for
-      // that range in LDS (M KiB per step, at most kStageKiB): K is split
-      // across workgroups until both fit.
-      const int steps = ceil_div(K8, 64);
-      int want;
-      if (N >= kGemvRowMinN) {
-        c.kind = SG_KIND_GEMV_ROW;
-        c.rows = gemv_rows_for(M);
-        want = 1;
-      } else {
-        c.kind = SG_KIND_GEMV_SPLITK;
-        c.rows = 1;
-        want = ceil_div(kGemvWaveTarget, N);
-      }
-      const int depth = gemv_ring_depth(c.rows);
-      const int max_sps = (kStageKiB / M < depth) ? kStageKiB / M : depth;
-      const int need = ceil_div(steps, max_sps);
-      c.k_split = effective_split(steps, want > need ? want : need);
-      const int sps = ceil_div(steps, c.k_split);
-      c.waves = (M * sps > kStageKiB / 2) ? 2 * kWaves : kWaves;
-      c.k_unroll = depth;
-      c.grid = ceil_div(N, c.waves * c.rows) * c.k_split;
+      c.kind = SG_KIND_GEMV_SPLITK;
+      want = ceil_div(kGemvWaveTarget, N);
     }
-  } else {
+    c.m_tile = 1;
+    c.rows = 1;
+    const int need = ceil_div(steps, kGemvDepth);
+    c.k_split = effective_split(steps, want > need ? want : need);
+    c.k_unroll = kGemvDepth;
+    c.grid = ceil_div(N, c.waves * c.rows) * c.k_split;
+  } else if (M <= 16) {
+    c.m_tile = 4 * ceil_div(M, 4);
+    const int tiles16 = ceil_div(N, 16);
+    if (tiles16 <= kSplitMaxTiles) {
+      // Each wave walks a quarter of the workgroup's K-range: at least one
+      // chunk (4 k-steps) per wave.
+      c.kind = SG_KIND_MFMA_WAVESPLIT;
+      c.rows = 16;
+      c.waves = 4;
+      c.k_unroll = kSplitRing;
+      c.k_split = mfma_split(tiles16, ksteps, 16);
+      c.grid = tiles16 * c.k_split;
+    } else {
+      c.kind = SG_KIND_MFMA_TILE;
+      c.rows = 32;
+      c.waves = 2;
+      c.k_unroll = kWideRing;
+      const int tiles = ceil_div(N, c.rows);
+      c.k_split = mfma_split(tiles, ksteps, 4);
+      c.grid = tiles * c.k_split;
+    }
+  } else if (M <= 64) {
     c.kind = SG_KIND_MFMA_TILE;
     c.m_tile = 16 * ceil_div(M, 16);
+    c.rows = 64;
+    c.waves = 4;
+    c.k_unroll = kTileRing;
+    const int tiles = ceil_div(N, c.rows);
+    c.k_split = mfma_split(tiles, ksteps, 4);
+    c.grid = tiles * c.k_split;
+  } else {
+    c.kind = SG_KIND_MFMA_DIRECT;
+    const int mb = ceil_div(M, 16);
+    c.m_tile = 16 * mb;
     c.rows = 1;
-    c.k_unroll = mfma_ring_depth(c.m_tile / 16);
-    const int tiles = ceil_div(N, 16 * c.rows);
-    const int ksteps = ceil_div(K, 32);
-    if (tiles >= kMfmaNoSplitTiles) {
-      c.k_split = 1;
-    } else {
-      int want = ceil_div(kMfmaTileTarget, tiles);
-      int cap = ksteps / kMfmaMinStepsPerSplit;
-      if (cap < 1) cap = 1;
-      if (want > cap) want = cap;
-      c.k_split = effective_split(ksteps, want);
-    }
+    c.k_unroll = direct_ring_depth(mb);
+    const int tiles = ceil_div(N, 16);
+    c.k_split = mfma_split(tiles, ksteps, 32);
     c.grid = tiles * c.k_split;
   }
   *out = c;
@@ -161,13 +183,15 @@ extern "C" size_t sg_workspace_bytes(int op, int M, int N, int K) {
       return sg::round256(s * plane);
     }
     case SG_OP_LATENT_TAIL: {
-      // The GEMV normalises on the fly when it covers the whole row in one
-      // workgroup (k_split == 1); otherwise the bf16 normalised latent [M,K]
-      // goes to the workspace first, followed by any split partials.
+      // M = 1 with the whole row in one workgroup: the GEMV normalises the
+      // latent in LDS (no workspace).  Otherwise the bf16 normalised latent
+      // [M,K] goes to the workspace first, followed by any split partials.
+      const bool gemv1 = (M == 1) && (c.kind == SG_KIND_GEMV_SMALLK ||
+                                      ((c.kind == SG_KIND_GEMV_ROW || c.kind == SG_KIND_GEMV_SPLITK) &&
+                                       c.k_split == 1));
+      if (gemv1) return 0;
       const size_t part = (c.k_split > 1 && c.kind != SG_KIND_GEMV_SMALLK) ? sg::round256(S * plane) : 0;
-      if (c.kind == SG_KIND_MFMA_TILE || c.k_split > 1)
-        return sg::round256(static_cast<size_t>(M) * static_cast<size_t>(K) * 2) + part;
-      return 0;
+      return sg::round256(static_cast<size_t>(M) * static_cast<size_t>(K) * 2) + part;
     }
     default:
       return 0;
@@ -194,8 +218,8 @@ extern "C" size_t sg_kda_workspace_bytes(int which, int M, int K, int n_qkvg, in
   if (sg_select(M, n_qkvg + n_ab, K, 0, &c) != SG_OK || c.kind == SG_KIND_NONE) return 0;
   const size_t S = static_cast<size_t>(c.k_split > 1 ? c.k_split : 0);
   const size_t m = static_cast<size_t>(M);
-  if (which == 0)  // main: Q/K/V/G split-K partials
-    return S ? sg::round256(S * m * static_cast<size_t>(n_qkvg) * sizeof(float)) : 0;
+  if (which == 0)  // main: split-K partials of the packed projection
+    return S ? sg::round256(S * m * static_cast<size_t>(n_qkvg + n_ab) * sizeof(float)) : 0;
   if (which == 1)  // aux: bf16 P [M, n_ab], then F_A/beta split-K partials
     return sg::round256(m * static_cast<size_t>(n_ab) * 2) +
            (S ? sg::round256(S * m * static_cast<size_t>(n_ab) * sizeof(float)) : 0);

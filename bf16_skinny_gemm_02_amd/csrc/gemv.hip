@@ -1,4 +1,4 @@
-// Row-parallel and split-K GEMV for M <= 16 (gfx950).
+// Row-parallel and split-K GEMV for one activation row (gfx950).
 //
 // out[m,n] = sum_k a[m,k] * w[n,k]  for a handful of activation rows m, the
 // decode-time projection of "Kimi K3 support, phase 1" (CuteSkinnyGemm, where
@@ -219,38 +219,13 @@ hipError_t launch_inst(const GemvArgs& g, dim3 grid, size_t lds, hipStream_t s) 
   return hipGetLastError();
 }
 
-template <int M, bool FOLD>
-hipError_t launch_m(const GemvArgs& g, int R, int NW, dim3 grid, size_t lds, hipStream_t s) {
-  if (NW == 4) {
-    switch (R) {
-      case 1: return launch_inst<M, 1, 4, FOLD>(g, grid, lds, s);
-      case 2: return launch_inst<M, 2, 4, FOLD>(g, grid, lds, s);
-      case 4: return launch_inst<M, 4, 4, FOLD>(g, grid, lds, s);
-      default: return hipErrorInvalidValue;
-    }
-  }
-  if (NW == 8) {
-    switch (R) {
-      case 1: return launch_inst<M, 1, 8, FOLD>(g, grid, lds, s);
-      case 2: return launch_inst<M, 2, 8, FOLD>(g, grid, lds, s);
-      case 4: return launch_inst<M, 4, 8, FOLD>(g, grid, lds, s);
-      default: return hipErrorInvalidValue;
-    }
-  }
-  return hipErrorInvalidValue;
-}
-
+// The table sends only M = 1 here (one row per wave, 4 waves); wider M
+// goes to the MFMA kernels.
 template <bool FOLD>
 hipError_t launch_fold(const GemvArgs& g, int M, int R, int NW, dim3 grid, size_t lds,
                        hipStream_t s) {
-  switch (M) {
-#define SG_CASE(mm) \
-  case mm: return launch_m<mm, FOLD>(g, R, NW, grid, lds, s);
-    SG_CASE(1) SG_CASE(2) SG_CASE(3) SG_CASE(4) SG_CASE(5) SG_CASE(6) SG_CASE(7) SG_CASE(8)
-    SG_CASE(9) SG_CASE(10) SG_CASE(11) SG_CASE(12) SG_CASE(13) SG_CASE(14) SG_CASE(15) SG_CASE(16)
-#undef SG_CASE
-    default: return hipErrorInvalidValue;
-  }
+  if (M == 1 && R == 1 && NW == 4) return launch_inst<1, 1, 4, FOLD>(g, grid, lds, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

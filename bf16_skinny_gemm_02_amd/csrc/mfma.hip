@@ -1,26 +1,45 @@
-// bf16 MFMA tile path for 16 < M <= 256 (gfx950, v_mfma_f32_16x16x32_bf16).
+// bf16 MFMA paths for 2 <= M <= 256 (gfx950, v_mfma_f32_16x16x32_bf16).
 //
-// out[m,n] = sum_k a[m,k] * w[n,k] is a dense contraction once M exceeds a
-// GEMV's handful of rows, so it goes to the matrix cores.  Operand layout of
-// the 16x16x32 instruction: lane l supplies row (l % 16) and the eight
-// consecutive k of group (l / 16) of the 16x32 A operand, and the same for
-// the columns of B; lane l receives D[4*(l/16) + v][l % 16], v = 0..3.
-// Because the weights are [N,K] with K contiguous, a lane's eight k of one
-// weight row are one 16-byte global load, so the A operand (weights, rows =
-// n) is loaded straight from HBM into registers in MFMA order -- no LDS
-// transpose.  The B operand is the activation (columns = m), loaded the same
-// way from the cache.  D[n][m] then gives each lane four consecutive n of one
-// output row.
+// out[m,n] = sum_k a[m,k] * w[n,k] is a dense contraction once more than one
+// activation row shares each weight byte, so the products go to the matrix
+// cores; the weight stream from HBM stays the bound up to M = 64.
 //
-// Workgroup = 4 waves on one 16*NB-row weight tile.  The workgroup's K-range
-// (all of K, or 1/k_split of it) is cut into 4 contiguous pieces, one per
-// wave; each wave keeps a ring of D k-steps of weight and activation
-// fragments in flight.  The four wave partials are summed through LDS in the
-// fixed order 0,1,2,3, so results do not depend on timing.
+// Operand layout of v_mfma_f32_16x16x32_bf16: lane l supplies row (l % 16)
+// and the eight consecutive k of group (l / 16) of the 16x32 A operand, the
+// same for the 16 columns of B, and receives D[4*(l/16) + v][l % 16],
+// v = 0..3.  A = 16 weight rows (n), B = 16 activation rows (m): each lane
+// ends with four consecutive n of one output row m.
 //
-// The latent-MoE tail reaches this kernel with its activation already
-// normalised (bf16 RMSNorm output from the norm kernel), so the epilogue only
-// adds the shared-expert partial.
+// Three kernels:
+//
+//  * tile_kernel (SG_KIND_MFMA_TILE): a workgroup of NW waves owns 16*NW
+//    weight rows (wave w: rows 16w..16w+15) and one K-range (all of K, or
+//    1/k_split of it).  The range is walked in chunks of 4 k-steps (128 k,
+//    256 bytes of a row).  For every chunk the weight tile and the activation
+//    rows are copied straight from global memory into one slot of a C-slot
+//    LDS ring (buffer_load ... lds, no registers, 1 KiB per instruction:
+//    4 rows x 256 contiguous bytes), C-1 chunks ahead of the products.  All
+//    waves share the activation copy; one barrier per chunk.
+//  * wsplit_kernel (SG_KIND_MFMA_WAVESPLIT, M <= 16): a workgroup owns 16
+//    weight rows; its 4 waves each walk a quarter of the K-range with a
+//    private LDS ring (16 weight rows + the M activation rows per slot), so
+//    the loop has no barrier.  The four wave sums meet in LDS in the fixed
+//    order 0,1,2,3 at the end: no split-K partials and no second launch.
+//  * direct_kernel (SG_KIND_MFMA_DIRECT, M > 64): each wave loads weight and
+//    activation fragments straight into registers; 4 waves split the K-range
+//    and sum through LDS in fixed order.
+//
+// LDS layout of one ring slot: rows of 16 pieces of 16 bytes.  Piece c of row
+// r is stored at position c ^ (r & 15): the 16 lanes that read piece c of 16
+// consecutive rows (one MFMA operand) hit 16 different 16-byte bank groups.
+// The copies realise the swizzle on the global side: the lane that fills
+// position p of row r loads piece p ^ (r & 15).
+//
+// Every kernel either stores bf16 (with the optional residual and the split
+// output of the packed KDA projection) or fp32 split-K partials
+// partial[s][m][n] for a later fixed-order sum.  Each output element's sum is
+// formed in an order that depends only on K and the configuration, never on
+// timing or on which tile holds the row.
 #include "sg_device.h"
 #include "sg_launch.h"
 
@@ -41,51 +60,262 @@ struct MfmaArgs {
   int64_t ldc2;
   int n_split;
   int M, N, K;
-  int row_origin;  // absolute index of weight row 0 (sets the k-order rotation)
-  int sps;  // k-steps per split
+  int sps;  // k-steps (32 k) per split
 };
 
-constexpr int kMfmaWaves = 4;
-constexpr int kKStep = 32;
+constexpr int kKStep = 32;       // k per MFMA
+constexpr int kChunkSteps = 4;   // k-steps per LDS ring chunk
+constexpr int kPieces = 16;      // 16-byte pieces of a row per chunk (256 bytes)
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <int MB, int NB, int D, int NKT>
-__global__ __launch_bounds__(kMfmaWaves * kWave) void mfma_kernel(MfmaArgs g) {
-  constexpr int kRegs = MB * NB * 4;
-  __shared__ float red[(kMfmaWaves - 1) * kRegs * kWave];
+// Stores the four outputs (m, n0 .. n0+3) a lane holds.
+__device__ __forceinline__ void store4(const MfmaArgs& g, const f32x4& acc, int m, int n0, int split) {
+  if (m >= g.M) return;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int n = n0 + v;
+    if (n >= g.N) continue;
+    if (g.partial != nullptr) {
+      g.partial[(static_cast<int64_t>(split) * g.M + m) * g.N + n] = acc[v];
+    } else {
+      float val = acc[v];
+      if (g.res != nullptr) val += bf16_to_f32(g.res[m * g.ldr + n]);
+      if (g.n_split > 0 && n >= g.n_split)
+        g.out2[m * g.ldc2 + (n - g.n_split)] = f32_to_bf16(val);
+      else
+        g.out[m * g.ldc + n] = f32_to_bf16(val);
+    }
+  }
+}
+
+// ---- shared-activation LDS tile ------------------------------------------------
+
+// MB: 16-row activation blocks (m_tile = 16*MB); NW: waves = 16-row weight
+// blocks per workgroup; C: ring slots; XQ: activation rows copied per chunk,
+// in groups of 4 (XQ*4 >= M).
+template <int MB, int NW, int C, int XQ>
+__global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaArgs g) {
+  extern __shared__ u32x4 lds[];
+  constexpr int WROWS = 16 * NW;
+  constexpr int XROWS = 4 * XQ;
+  constexpr int SLOT = (WROWS + XROWS) * kPieces;
+  constexpr int XJ = (XQ + NW - 1) / NW;  // activation copies per wave per chunk
+  constexpr int P = 4 + XJ;               // copies per wave per chunk
+  constexpr int kInFlight = (C - 2) * P;  // copies allowed pending when a chunk is read
+  static_assert(XROWS <= 16 * MB && XROWS > 16 * (MB - 1), "activation rows");
+  static_assert(C >= 2, "ring");
 
   const int lane = lane_id();
   const int wave = wave_id();
   const int rl = lane & 15;
   const int kg = lane >> 4;
-  const int n_base = static_cast<int>(blockIdx.x) * 16 * NB;
+  const int K8 = g.K >> 3;
+  const int KS = (g.K + kKStep - 1) / kKStep;
+  const int s_begin = static_cast<int>(blockIdx.y) * g.sps;
+  const int nk = max(0, min(KS, s_begin + g.sps) - s_begin);
+  const int npieces = nk * 4;
+  const int nch = (nk + kChunkSteps - 1) / kChunkSteps;
+  const int c0 = s_begin * 4;
+  const int tile_row0 = static_cast<int>(blockIdx.x) * WROWS;
+  const int tile_rows = min(WROWS, g.N - tile_row0);
+
+  const rsrc_t wres = make_rsrc(g.w + static_cast<int64_t>(tile_row0) * g.ldw,
+                                static_cast<uint32_t>(((tile_rows - 1) * g.ldw + g.K) * 2));
+  const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(((g.M - 1) * g.lda + g.K) * 2));
+  const int dr = lane >> 4;   // row within a 4-row copy
+  const int dp = lane & 15;   // position within the row
+
+  // Copies of chunk q into slot q % C: this wave's 16 weight rows (4 copies)
+  // and its share of the activation row groups.  Chunks past the range read
+  // zeros (no memory traffic), so every wave issues the same count.
+  auto issue = [&](int q) {
+    u32x4* slot = lds + (q % C) * SLOT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wave + 4 * i + dr;
+      const int pc = kPieces * q + (dp ^ (r & 15));
+      const uint32_t off = (r < tile_rows && pc < npieces && c0 + pc < K8)
+                               ? static_cast<uint32_t>((r * g.ldw + (c0 + pc) * 8) * 2)
+                               : kOob;
+      copy16_to_lds_nt(wres, slot + (16 * wave + 4 * i) * kPieces, off);
+    }
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) {
+      const int grp = (wave + NW * j) % XQ;  // a repeated group rewrites identical bytes
+      const int m = 4 * grp + dr;
+      const int pc = kPieces * q + (dp ^ (m & 15));
+      const uint32_t off = (m < g.M && pc < npieces && c0 + pc < K8)
+                               ? static_cast<uint32_t>((m * g.lda + (c0 + pc) * 8) * 2)
+                               : kOob;
+      copy16_to_lds(xres, slot + (WROWS + 4 * grp) * kPieces, off);
+    }
+  };
+
+#pragma unroll
+  for (int q = 0; q < C - 1; ++q) issue(q);
+
+  f32x4 acc[MB];
+#pragma unroll
+  for (int a = 0; a < MB; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int wrow = (16 * wave + rl) * kPieces;
+  for (int q = 0; q < nch; ++q) {
+    // Chunk q has landed for this wave; the barrier makes it so for all, and
+    // also means every wave has finished reading slot (q - 1) % C, which the
+    // next copy overwrites.
+    wait_vmcnt<kInFlight>();
+    __builtin_amdgcn_s_barrier();
+    issue(q + C - 1);
+    const u32x4* slot = lds + (q % C) * SLOT;
+    u32x4 wf[kChunkSteps], xf[kChunkSteps][MB];
+#pragma unroll
+    for (int t = 0; t < kChunkSteps; ++t) {
+      wf[t] = slot[wrow + ((4 * t + kg) ^ rl)];
+#pragma unroll
+      for (int a = 0; a < MB; ++a) {
+        // Rows past the copied ones only feed outputs that are not stored.
+        const int xr = (16 * a + rl < XROWS) ? 16 * a + rl : XROWS - 1;
+        xf[t][a] = slot[(WROWS + xr) * kPieces + ((4 * t + kg) ^ (xr & 15))];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kChunkSteps; ++t)
+#pragma unroll
+      for (int a = 0; a < MB; ++a) acc[a] = mfma16(wf[t], xf[t][a], acc[a]);
+  }
+  wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
+
+  const int n0 = tile_row0 + 16 * wave + 4 * kg;
+#pragma unroll
+  for (int a = 0; a < MB; ++a) store4(g, acc[a], 16 * a + rl, n0, static_cast<int>(blockIdx.y));
+}
+
+// ---- wave-split LDS tile (M <= 16) ------------------------------------------------
+
+constexpr int kSplitWaves = 4;
+
+template <int XQ, int C>
+__global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaArgs g) {
+  extern __shared__ u32x4 lds[];
+  constexpr int XROWS = 4 * XQ;
+  constexpr int SLOT = (16 + XROWS) * kPieces;
+  constexpr int P = 4 + XQ;
+  constexpr int kInFlight = (C - 2) * P;
+  static_assert(XQ >= 1 && XQ <= 4 && C >= 2, "configuration");
+
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int rl = lane & 15;
+  const int kg = lane >> 4;
+  const int K8 = g.K >> 3;
+  const int KS = (g.K + kKStep - 1) / kKStep;
+  const int s_begin = static_cast<int>(blockIdx.y) * g.sps;
+  const int len = max(0, min(KS, s_begin + g.sps) - s_begin);
+  const int per = (len + kSplitWaves - 1) / kSplitWaves;
+  const int w_begin = s_begin + wave * per;
+  const int nk = max(0, min(s_begin + len, w_begin + per) - w_begin);
+  const int npieces = nk * 4;
+  const int nch = (nk + kChunkSteps - 1) / kChunkSteps;
+  const int c0 = w_begin * 4;
+  const int row0 = static_cast<int>(blockIdx.x) * 16;
+  const int rows = min(16, g.N - row0);
+  u32x4* ring = lds + wave * C * SLOT;
+
+  const rsrc_t wres = make_rsrc(g.w + static_cast<int64_t>(row0) * g.ldw,
+                                static_cast<uint32_t>(((rows - 1) * g.ldw + g.K) * 2));
+  const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(((g.M - 1) * g.lda + g.K) * 2));
+  const int dr = lane >> 4;
+  const int dp = lane & 15;
+  auto issue = [&](int q) {
+    u32x4* slot = ring + (q % C) * SLOT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * i + dr;
+      const int pc = kPieces * q + (dp ^ r);
+      const uint32_t off = (r < rows && pc < npieces && c0 + pc < K8)
+                               ? static_cast<uint32_t>((r * g.ldw + (c0 + pc) * 8) * 2)
+                               : kOob;
+      copy16_to_lds_nt(wres, slot + 4 * i * kPieces, off);
+    }
+#pragma unroll
+    for (int j = 0; j < XQ; ++j) {
+      const int m = 4 * j + dr;
+      const int pc = kPieces * q + (dp ^ m);
+      const uint32_t off = (m < g.M && pc < npieces && c0 + pc < K8)
+                               ? static_cast<uint32_t>((m * g.lda + (c0 + pc) * 8) * 2)
+                               : kOob;
+      copy16_to_lds(xres, slot + (16 + 4 * j) * kPieces, off);
+    }
+  };
+
+#pragma unroll
+  for (int q = 0; q < C - 1; ++q) issue(q);
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int xr = rl < XROWS ? rl : XROWS - 1;
+  for (int q = 0; q < nch; ++q) {
+    wait_vmcnt<kInFlight>();  // this wave's chunk q has landed (its own ring)
+    const u32x4* slot = ring + (q % C) * SLOT;
+    u32x4 wf[kChunkSteps], xf[kChunkSteps];
+#pragma unroll
+    for (int t = 0; t < kChunkSteps; ++t) {
+      wf[t] = slot[rl * kPieces + ((4 * t + kg) ^ rl)];
+      xf[t] = slot[(16 + xr) * kPieces + ((4 * t + kg) ^ xr)];
+    }
+    wait_lgkmcnt0();  // the slot is in registers before the copy below refills the ring
+    issue(q + C - 1);
+#pragma unroll
+    for (int t = 0; t < kChunkSteps; ++t) acc = mfma16(wf[t], xf[t], acc);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // every ring is drained: LDS is reused for the wave sums
+
+  float* red = reinterpret_cast<float*>(lds);
+  if (wave > 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[((wave - 1) * 4 + v) * kWave + lane] = acc[v];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kSplitWaves - 1; ++w)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] += red[(w * 4 + v) * kWave + lane];
+  store4(g, acc, rl, row0 + 4 * kg, static_cast<int>(blockIdx.y));
+}
+
+// ---- register-fragment kernel (M > 64) ------------------------------------------
+
+constexpr int kDirectWaves = 4;
+
+template <int MB, int D, int NKT>
+__global__ __launch_bounds__(kDirectWaves * kWave) void direct_kernel(MfmaArgs g) {
+  constexpr int kRegs = MB * 4;
+  __shared__ float red[(kDirectWaves - 1) * kRegs * kWave];
+
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int rl = lane & 15;
+  const int kg = lane >> 4;
+  const int n_base = static_cast<int>(blockIdx.x) * 16;
   const int K8 = g.K >> 3;
   const int KS = (g.K + kKStep - 1) / kKStep;
   const int s_begin = static_cast<int>(blockIdx.y) * g.sps;
   const int s_end = min(KS, s_begin + g.sps);
   const int len = max(0, s_end - s_begin);
-  const int per = (len + kMfmaWaves - 1) / kMfmaWaves;
+  const int per = (len + kDirectWaves - 1) / kDirectWaves;
   const int w_begin = s_begin + wave * per;
   const int w_end = min(s_end, w_begin + per);
   const int nk = max(0, w_end - w_begin);
 
-  // Buffer resources: the workgroup's weight tile and the activation.  A
-  // row past N or M, a chunk past K and a step past the wave's range all map
-  // to kOob and read as zero.
-  const int tile_rows = min(16 * NB, g.N - n_base);
+  const int tile_rows = min(16, g.N - n_base);
   const rsrc_t wres = make_rsrc(g.w + static_cast<int64_t>(n_base) * g.ldw,
                                 static_cast<uint32_t>(((tile_rows - 1) * g.ldw + g.K) * 2));
   const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(((g.M - 1) * g.lda + g.K) * 2));
-  uint32_t wbase[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int row = 16 * b + rl;
-    wbase[b] = row < tile_rows ? static_cast<uint32_t>(row * g.ldw * 2) : kOob;
-  }
+  const uint32_t wbase = rl < tile_rows ? static_cast<uint32_t>(rl * g.ldw * 2) : kOob;
   uint32_t xbase[MB];
 #pragma unroll
   for (int a = 0; a < MB; ++a) {
@@ -93,68 +323,46 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void mfma_kernel(MfmaArgs g) {
     xbase[a] = m < g.M ? static_cast<uint32_t>(m * g.lda * 2) : kOob;
   }
 
-  f32x4 acc[MB][NB];
+  f32x4 acc[MB];
 #pragma unroll
-  for (int a = 0; a < MB; ++a)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < MB; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Ring of D k-steps: weight and activation fragments of step t are issued
-  // together, D steps before they are consumed, so waiting for one step never
-  // waits on a load issued for a later step.  No load sits in a branch.
-  // Every workgroup reads the same activation lines; if all of them walked K
-  // in the same order they would request the same lines at the same moment
-  // and queue at one L2 channel.  Each wave therefore starts its K-range at
-  // an offset set by its absolute 16-row tile (workgroups of one XCD are 8
-  // tiles apart) and wraps around.  The offset depends only on which rows the
-  // tile holds, so a row's sum is formed in the same order in every launch.
-  const int tile = (g.row_origin + n_base) >> 4;
-  const int rot = nk > 0 ? ((tile >> 3) * 23 + (tile & 7) * 7) % nk : 0;
+  // together D steps before they are consumed; no load sits in a branch.
   auto koff = [&](int t) -> uint32_t {
-    int tt = t + rot;
-    tt = tt >= nk ? tt - nk : tt;
-    const int c = (w_begin + tt) * 4 + kg;
+    const int c = (w_begin + t) * 4 + kg;
     return (t < nk && c < K8) ? static_cast<uint32_t>(c * 16) : kOob;
   };
-  auto wfrag = [&](uint32_t ko, int b) -> u32x4 {
-    return buf_load_nt(wres, (ko == kOob || wbase[b] == kOob) ? kOob : wbase[b] + ko);
+  auto wfrag = [&](uint32_t ko) -> u32x4 {
+    return buf_load_nt(wres, (ko == kOob || wbase == kOob) ? kOob : wbase + ko);
   };
   auto xfrag = [&](uint32_t ko, int a) -> u32x4 {
     return buf_load(xres, (ko == kOob || xbase[a] == kOob) ? kOob : xbase[a] + ko);
   };
-
-  u32x4 wr[D][NB];
+  u32x4 wr[D];
   u32x4 xr[D][MB];
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     const uint32_t ko = koff(j);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) wr[j][b] = wfrag(ko, b);
+    wr[j] = wfrag(ko);
 #pragma unroll
     for (int a = 0; a < MB; ++a) xr[j][a] = xfrag(ko, a);
   }
-
-  // One ring pass: consume slot j, refill it with the step D ahead, in
-  // program order, so the loads complete in the order the steps need them.
   auto pass = [&](int tb) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int t = tb + j;
 #pragma unroll
-      for (int a = 0; a < MB; ++a)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acc[a][b] = mfma16(wr[j][b], xr[j][a], acc[a][b]);
+      for (int a = 0; a < MB; ++a) acc[a] = mfma16(wr[j], xr[j][a], acc[a]);
       const uint32_t ko = koff(t + D);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) wr[j][b] = wfrag(ko, b);
+      wr[j] = wfrag(ko);
 #pragma unroll
       for (int a = 0; a < MB; ++a) xr[j][a] = xfrag(ko, a);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   if constexpr (NKT > 0) {
-    // Known step count: straight-line code, so every wait is exact (a loop
-    // head would merge the pending-load state of two paths and drain).
+    // Known step count: straight-line code, so every wait is exact.
 #pragma unroll
     for (int tb = 0; tb < NKT; tb += D) pass(tb);
   } else {
@@ -167,84 +375,70 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void mfma_kernel(MfmaArgs g) {
 #pragma unroll
     for (int a = 0; a < MB; ++a)
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) dst[((a * NB + b) * 4 + v) * kWave + lane] = acc[a][b][v];
+      for (int v = 0; v < 4; ++v) dst[(a * 4 + v) * kWave + lane] = acc[a][v];
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int w = 0; w < kMfmaWaves - 1; ++w) {
+  for (int w = 0; w < kDirectWaves - 1; ++w) {
     const float* src = red + w * kRegs * kWave;
 #pragma unroll
     for (int a = 0; a < MB; ++a)
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[a][b][v] += src[((a * NB + b) * 4 + v) * kWave + lane];
+      for (int v = 0; v < 4; ++v) acc[a][v] += src[(a * 4 + v) * kWave + lane];
   }
-
-  if (g.partial != nullptr) {
-    const int64_t s = blockIdx.y;
 #pragma unroll
-    for (int a = 0; a < MB; ++a) {
-      const int m = 16 * a + rl;
-      if (m >= g.M) continue;
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int n = n_base + 16 * b + 4 * kg + v;
-          if (n < g.N) g.partial[(s * g.M + m) * g.N + n] = acc[a][b][v];
-        }
-    }
-    return;
-  }
-
-#pragma unroll
-  for (int a = 0; a < MB; ++a) {
-    const int m = 16 * a + rl;
-    if (m >= g.M) continue;
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int n = n_base + 16 * b + 4 * kg + v;
-        if (n < g.N) {
-          float val = acc[a][b][v];
-          if (g.res != nullptr) val += bf16_to_f32(g.res[m * g.ldr + n]);
-          if (g.n_split > 0 && n >= g.n_split)
-            g.out2[m * g.ldc2 + (n - g.n_split)] = f32_to_bf16(val);
-          else
-            g.out[m * g.ldc + n] = f32_to_bf16(val);
-        }
-      }
-  }
+  for (int a = 0; a < MB; ++a) store4(g, acc[a], 16 * a + rl, n_base + 4 * kg, static_cast<int>(blockIdx.y));
 }
 
-// Ring depth: the weight fragment plus MB activation fragments per k-step,
-// D steps deep, within the register budget of one wave per SIMD.
-template <int MB>
-constexpr int ring_depth() {
-  return MB <= 2 ? 12 : (MB <= 4 ? 8 : (MB <= 8 ? 4 : 2));
+// ---- launchers -------------------------------------------------------------------
+
+// One attribute call per kernel instance (the ring can exceed the default
+// 64 KiB of dynamic LDS).
+template <int MB, int NW, int C, int XQ>
+hipError_t launch_tile_inst(const MfmaArgs& g, dim3 grid, hipStream_t s) {
+  auto kern = tile_kernel<MB, NW, C, XQ>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+      static_cast<int>(kMfmaMaxLds));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, grid, dim3(NW * kWave), tile_lds_bytes(NW, C, XQ), s, g);
+  return hipGetLastError();
+}
+
+template <int XQ, int C>
+hipError_t launch_wsplit_inst(const MfmaArgs& g, dim3 grid, hipStream_t s) {
+  auto kern = wsplit_kernel<XQ, C>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+      static_cast<int>(kMfmaMaxLds));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, grid, dim3(kSplitWaves * kWave), wsplit_lds_bytes(C, XQ), s, g);
+  return hipGetLastError();
 }
 
 template <int MB>
-hipError_t launch_mb(const MfmaArgs& g, int NB, int per_wave, dim3 grid, hipStream_t s) {
-  if (NB != 1) return hipErrorInvalidValue;
-  constexpr int D = ring_depth<MB>();
-  // Straight-line instances for the per-wave step counts of the model's
-  // shapes (K = 7168 and K = 2048 without a split); a loop otherwise.
+hipError_t launch_direct_mb(const MfmaArgs& g, int per_wave, dim3 grid, hipStream_t s) {
+  constexpr int D = MB <= 8 ? 4 : 2;
+  const dim3 block(kDirectWaves * kWave);
   if (per_wave > 16 && per_wave <= 56)
-    hipLaunchKernelGGL((mfma_kernel<MB, 1, D, 56>), grid, dim3(kMfmaWaves * kWave), 0, s, g);
+    hipLaunchKernelGGL((direct_kernel<MB, D, 56>), grid, block, 0, s, g);
   else if (per_wave <= 16)
-    hipLaunchKernelGGL((mfma_kernel<MB, 1, D, 16>), grid, dim3(kMfmaWaves * kWave), 0, s, g);
+    hipLaunchKernelGGL((direct_kernel<MB, D, 16>), grid, block, 0, s, g);
   else
-    hipLaunchKernelGGL((mfma_kernel<MB, 1, D, 0>), grid, dim3(kMfmaWaves * kWave), 0, s, g);
+    hipLaunchKernelGGL((direct_kernel<MB, D, 0>), grid, block, 0, s, g);
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t tile_lds_bytes(int nw, int c, int xq) {
+  return static_cast<size_t>(c) * (16 * nw + 4 * xq) * kPieces * 16;
+}
+
+size_t wsplit_lds_bytes(int c, int xq) {
+  return static_cast<size_t>(kSplitWaves) * c * (16 + 4 * xq) * kPieces * 16;
+}
 
 hipError_t launch_mfma(const DotProblem& p, const sg_config_t& cfg, hipStream_t s) {
   MfmaArgs g;
@@ -263,24 +457,64 @@ hipError_t launch_mfma(const DotProblem& p, const sg_config_t& cfg, hipStream_t 
   g.M = p.M;
   g.N = p.N;
   g.K = p.K;
-  g.row_origin = p.row_origin;
   const int KS = (p.K + kKStep - 1) / kKStep;
   const int S = cfg.k_split > 0 ? cfg.k_split : 1;
   g.sps = (KS + S - 1) / S;
   if (g.sps < 1) g.sps = 1;
-  const int MB = cfg.m_tile / 16;
-  const int NB = cfg.rows;
-  const int rows_per_wg = 16 * NB;
-  const dim3 grid((p.N + rows_per_wg - 1) / rows_per_wg, S);
-  const int per_wave = (g.sps + kMfmaWaves - 1) / kMfmaWaves;
-  switch (MB) {
-#define SG_CASE(mb) \
-  case mb: return launch_mb<mb>(g, NB, per_wave, grid, s);
-    SG_CASE(1) SG_CASE(2) SG_CASE(3) SG_CASE(4) SG_CASE(5) SG_CASE(6) SG_CASE(7) SG_CASE(8)
-    SG_CASE(9) SG_CASE(10) SG_CASE(11) SG_CASE(12) SG_CASE(13) SG_CASE(14) SG_CASE(15) SG_CASE(16)
-#undef SG_CASE
-    default: return hipErrorInvalidValue;
+  if (p.M > cfg.m_tile || cfg.m_tile <= 0) return hipErrorInvalidValue;
+
+  if (cfg.kind == SG_KIND_MFMA_TILE) {
+    const int NW = cfg.waves, C = cfg.k_unroll, XQ = cfg.m_tile / 4;
+    if (cfg.rows != 16 * NW || (cfg.m_tile % 4) != 0) return hipErrorInvalidValue;
+    const dim3 grid((p.N + cfg.rows - 1) / cfg.rows, S);
+    // The instances the configuration table uses.
+    if (NW == 2 && C == 4) {
+      switch (XQ) {
+        case 1: return launch_tile_inst<1, 2, 4, 1>(g, grid, s);
+        case 2: return launch_tile_inst<1, 2, 4, 2>(g, grid, s);
+        case 3: return launch_tile_inst<1, 2, 4, 3>(g, grid, s);
+        case 4: return launch_tile_inst<1, 2, 4, 4>(g, grid, s);
+        default: break;
+      }
+    }
+    if (NW == 4 && C == 3) {
+      switch (XQ) {
+        case 8: return launch_tile_inst<2, 4, 3, 8>(g, grid, s);
+        case 12: return launch_tile_inst<3, 4, 3, 12>(g, grid, s);
+        case 16: return launch_tile_inst<4, 4, 3, 16>(g, grid, s);
+        default: break;
+      }
+    }
+    return hipErrorInvalidValue;
   }
+  if (cfg.kind == SG_KIND_MFMA_WAVESPLIT) {
+    const int C = cfg.k_unroll, XQ = cfg.m_tile / 4;
+    if (cfg.rows != 16 || cfg.waves != kSplitWaves || (cfg.m_tile % 4) != 0 || C != 4)
+      return hipErrorInvalidValue;
+    const dim3 grid((p.N + 15) / 16, S);
+    switch (XQ) {
+      case 1: return launch_wsplit_inst<1, 4>(g, grid, s);
+      case 2: return launch_wsplit_inst<2, 4>(g, grid, s);
+      case 3: return launch_wsplit_inst<3, 4>(g, grid, s);
+      case 4: return launch_wsplit_inst<4, 4>(g, grid, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (cfg.kind == SG_KIND_MFMA_DIRECT) {
+    const int MB = cfg.m_tile / 16;
+    if (cfg.rows != 1 || (cfg.m_tile % 16) != 0) return hipErrorInvalidValue;
+    const dim3 grid((p.N + 15) / 16, S);
+    const int per_wave = (g.sps + kDirectWaves - 1) / kDirectWaves;
+    switch (MB) {
+#define SG_CASE(mb) \
+  case mb: return launch_direct_mb<mb>(g, per_wave, grid, s);
+      SG_CASE(5) SG_CASE(6) SG_CASE(7) SG_CASE(8) SG_CASE(9) SG_CASE(10) SG_CASE(11) SG_CASE(12)
+      SG_CASE(13) SG_CASE(14) SG_CASE(15) SG_CASE(16)
+#undef SG_CASE
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace sg

@@ -151,4 +151,31 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
 }
 
+// ---- global -> LDS copies ----------------------------------------------------
+//
+// buffer_load_dwordx4 ... lds: each lane's 16 bytes go from the buffer offset
+// it names straight into LDS at dst + 16 * lane (dst is the same for the whole
+// wave), without passing through registers.  An offset past the buffer writes
+// zeros.  The copy is counted by vmcnt; the compiler does not order LDS reads
+// after it, so callers wait with wait_vmcnt<> (and a barrier when another
+// wave reads the data).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void copy16_to_lds(rsrc_t r, void* lds_dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_dst, 16, static_cast<int>(off), 0, 0, 0);
+}
+// Same, non-temporal (weights).
+__device__ __forceinline__ void copy16_to_lds_nt(rsrc_t r, void* lds_dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_dst, 16, static_cast<int>(off), 0, 0, 2);
+}
+
+// s_waitcnt with only one counter constrained (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the others left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 }  // namespace sg

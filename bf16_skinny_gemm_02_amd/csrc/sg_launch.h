@@ -36,10 +36,6 @@ struct DotProblem {
   uint16_t* out2;
   int64_t ldc2;
   int n_split;
-  // Absolute index of weight row 0 when w points into a larger matrix (the
-  // F_A/beta rows of the packed KDA weight): kernels that order their K loop
-  // by row position use it so a row is summed the same way in every launch.
-  int row_origin;
 };
 
 // Workspace regions start on 256-byte boundaries.
@@ -52,8 +48,16 @@ hipError_t launch_gemv(const DotProblem& p, const sg_config_t& cfg, hipStream_t 
 hipError_t launch_smallk(const DotProblem& p, const sg_config_t& cfg, hipStream_t s);
 hipError_t launch_mfma(const DotProblem& p, const sg_config_t& cfg, hipStream_t s);
 
+// LDS of the MFMA ring kernels: the shared-activation tile (nw waves, c ring
+// slots, 4*xq activation rows) and the wave-split tile (4 private rings).
+// The configuration table keeps both within kMfmaMaxLds.
+constexpr size_t kMfmaMaxLds = 160 * 1024;
+size_t tile_lds_bytes(int nw, int c, int xq);
+size_t wsplit_lds_bytes(int c, int xq);
+
 // out[m,n] = bf16( sum_{s<S} partial[s][m][n] + res[m,n] ).  The sum runs
-// over s = 0..S-1 in order (deterministic).
+// over s = 0..S-1 in order (deterministic).  Columns n >= n_split (when
+// n_split > 0) go to out2[m * ldc2 + n - n_split] instead.
 struct ReduceProblem {
   const float* partial;
   int S, M, N;
@@ -61,6 +65,9 @@ struct ReduceProblem {
   int64_t ldr;
   uint16_t* out;
   int64_t ldc;
+  uint16_t* out2;
+  int64_t ldc2;
+  int n_split;
 };
 hipError_t launch_reduce(const ReduceProblem& p, hipStream_t s);
 
@@ -80,7 +87,7 @@ struct FbProblem {
 hipError_t launch_fab_fb_tail(const FbProblem& p, hipStream_t s);
 
 // RMSNorm of the latent rows into a bf16 buffer: n[m,k] = bf16(L[m,k] * r[m] *
-// gamma[k]), r[m] = rsqrt(mean_k L[m,k]^2 + eps).
+// gamma[k]), r[m] = rsqrt(mean_k L[m,k]^2 + eps).  d <= kNormMaxD.
 struct NormProblem {
   const uint16_t* latent;   // [M,d] contiguous
   const uint16_t* gamma;    // [d]
@@ -89,11 +96,11 @@ struct NormProblem {
   float eps;
 };
 hipError_t launch_rmsnorm(const NormProblem& p, hipStream_t s);
+constexpr int kNormMaxD = 8192;
 
-// F_B stage tiling: activation rows per workgroup, g1 rows per workgroup,
-// largest rank (f_a width) it supports.
+// F_B stage tiling: activation rows per workgroup, largest rank (f_a width)
+// it supports.
 constexpr int kFbMGroup = 4;
-constexpr int kFbRowsPerWg = 64;
 constexpr int kFbMaxRank = 512;
 
 // GEMV activation staging: a workgroup keeps its K-range of the activation in

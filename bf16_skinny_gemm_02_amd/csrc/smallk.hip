@@ -99,11 +99,17 @@ __device__ __forceinline__ float sum_splits(const float* p, int64_t plane, int S
   return acc;
 }
 
-// Workgroup (x, y) computes g1 rows [x*kFbRowsPerWg, (x+1)*kFbRowsPerWg) for
-// activation rows [y*kFbMGroup, (y+1)*kFbMGroup): it forms only those rows'
-// bf16 P (summing the F_A/beta partials in fixed order when PARTIALS, so
-// every workgroup agrees bit for bit, else reading the bf16 P), keeps f_a in
-// LDS, and workgroups with x == 0 also store beta (and f_a).
+// Rows of w_b one F_B workgroup covers: one row per group of G lanes, every
+// lane of the workgroup busy, a single pass.
+template <int G>
+constexpr int fb_rows_per_wg() { return kSmallkWaves * (kWave / G); }
+
+// Workgroup (x, y) computes g1 rows [x*R, (x+1)*R), R = fb_rows_per_wg<G>(),
+// for activation rows [y*kFbMGroup, (y+1)*kFbMGroup).  Its w_b chunk is
+// requested first, so that load overlaps forming P: the rows' bf16 P (the
+// F_A/beta partials summed in fixed order when PARTIALS, so every workgroup
+// agrees bit for bit, else the bf16 P as stored); f_a goes to LDS, and
+// workgroups with x == 0 also store beta (and f_a).
 template <int G, bool PARTIALS>
 __global__ __launch_bounds__(kSmallkWaves * kWave) void fab_fb_tail_kernel(FbArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t fa_lds[kFbMGroup * kFbMaxRank];
@@ -114,45 +120,41 @@ __global__ __launch_bounds__(kSmallkWaves * kWave) void fab_fb_tail_kernel(FbArg
   const int mg = min(kFbMGroup, g.M - m0);
   const bool first = blockIdx.x == 0;
 
-  // 1. P = bf16(sum_s partial[s][m][j]) for this workgroup's rows; all n_ab
-  //    columns in the first column of workgroups, the rank f_a columns elsewhere.
-  const int cols = first ? g.n_ab : g.rank;
-  for (int idx = tid; idx < mg * cols; idx += nthreads) {
-    const int mm = idx / cols, j = idx - mm * cols;
-    const int m = m0 + mm;
-    uint16_t b;
-    if constexpr (PARTIALS)
-      b = f32_to_bf16(sum_splits(g.partial + static_cast<int64_t>(m) * g.n_ab + j, plane, g.S));
-    else
-      b = g.p_bf16[static_cast<int64_t>(m) * g.n_ab + j];
-    if (j < g.rank) {
-      fa_lds[mm * g.rank + j] = b;
-      if (first && g.f_a != nullptr) g.f_a[static_cast<int64_t>(m) * g.rank + j] = b;
-    } else {
-      g.beta[static_cast<int64_t>(m) * (g.n_ab - g.rank) + (j - g.rank)] = b;
-    }
-  }
-  __syncthreads();
-
-  // 2. g1[m, i] = bf16(sum_r f_a[m, r] * w_b[i, r]); each weight chunk is
-  //    loaded once and used for every activation row of the group.
   const int lane = lane_id();
   const int j = lane & (G - 1);
   const int K8 = g.rank >> 3;
   const bool cvalid = j < K8;
-  constexpr int kRowsPerPass = kSmallkWaves * (kWave / G);
-  const int i_base = static_cast<int>(blockIdx.x) * kFbRowsPerWg + wave_id() * (kWave / G) + lane / G;
-  for (int off = 0; off < kFbRowsPerWg; off += kRowsPerPass) {
-    const int i = i_base + off;
-    const bool ivalid = i < g.n_b;
-    const u32x4 wv =
-        (ivalid && cvalid) ? load_nt(g.w_b + static_cast<int64_t>(i) * g.rank + j * 8) : zero4();
-    for (int mm = 0; mm < mg; ++mm) {
-      const u32x4 xv =
-          cvalid ? *reinterpret_cast<const u32x4*>(fa_lds + mm * g.rank + j * 8) : zero4();
-      const float v = group_sum<G>(dot8(xv, wv, 0.f));
-      if (ivalid && j == 0) g.g1[static_cast<int64_t>(m0 + mm) * g.n_b + i] = f32_to_bf16(v);
+  const int i = static_cast<int>(blockIdx.x) * fb_rows_per_wg<G>() + wave_id() * (kWave / G) + lane / G;
+  const bool ivalid = i < g.n_b;
+  const u32x4 wv =
+      (ivalid && cvalid) ? load_nt(g.w_b + static_cast<int64_t>(i) * g.rank + j * 8) : zero4();
+
+  // 1. P = bf16(sum_s partial[s][m][j]) for this workgroup's rows; all n_ab
+  //    columns in the first column of workgroups, the rank f_a columns elsewhere.
+  const int cols = first ? g.n_ab : g.rank;
+  for (int idx = tid; idx < mg * cols; idx += nthreads) {
+    const int mm = idx / cols, jj = idx - mm * cols;
+    const int m = m0 + mm;
+    uint16_t b;
+    if constexpr (PARTIALS)
+      b = f32_to_bf16(sum_splits(g.partial + static_cast<int64_t>(m) * g.n_ab + jj, plane, g.S));
+    else
+      b = g.p_bf16[static_cast<int64_t>(m) * g.n_ab + jj];
+    if (jj < g.rank) {
+      fa_lds[mm * g.rank + jj] = b;
+      if (first && g.f_a != nullptr) g.f_a[static_cast<int64_t>(m) * g.rank + jj] = b;
+    } else {
+      g.beta[static_cast<int64_t>(m) * (g.n_ab - g.rank) + (jj - g.rank)] = b;
     }
+  }
+  __syncthreads();
+
+  // 2. g1[m, i] = bf16(sum_r f_a[m, r] * w_b[i, r]): the weight chunk is used
+  //    for every activation row of the group.
+  for (int mm = 0; mm < mg; ++mm) {
+    const u32x4 xv = cvalid ? *reinterpret_cast<const u32x4*>(fa_lds + mm * g.rank + j * 8) : zero4();
+    const float v = group_sum<G>(dot8(xv, wv, 0.f));
+    if (ivalid && j == 0) g.g1[static_cast<int64_t>(m0 + mm) * g.n_b + i] = f32_to_bf16(v);
   }
 }
 
@@ -163,52 +165,106 @@ struct ReduceArgs {
   int64_t ldr;
   uint16_t* out;
   int64_t ldc;
+  uint16_t* out2;
+  int64_t ldc2;
+  int n_split;
 };
 
+// Four consecutive elements (flat index over [M][N]) per thread.  The
+// residual is requested before the partial sums so the two loads overlap;
+// the S partials are summed in the fixed order s = 0..S-1.
+template <bool VEC>
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs g) {
   const int64_t total = static_cast<int64_t>(g.M) * g.N;
-  const int64_t plane = total;
-  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; idx < total;
-       idx += static_cast<int64_t>(gridDim.x) * 256) {
-    const int m = static_cast<int>(idx / g.N);
-    const int n = static_cast<int>(idx - static_cast<int64_t>(m) * g.N);
-    float acc = 0.f;
-    acc = sum_splits(g.partial + idx, plane, g.S);
-    if (g.res != nullptr) acc += bf16_to_f32(g.res[m * g.ldr + n]);
-    g.out[m * g.ldc + n] = f32_to_bf16(acc);
+  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (e0 >= total) return;
+  int mm[4], nn[4];
+  float r[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int64_t e = e0 + v;
+    mm[v] = static_cast<int>(e / g.N);
+    nn[v] = static_cast<int>(e - static_cast<int64_t>(mm[v]) * g.N);
+    if (g.res != nullptr && e < total) r[v] = bf16_to_f32(g.res[mm[v] * g.ldr + nn[v]]);
+  }
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (VEC) {
+    // total % 4 == 0: every plane starts 16-byte aligned.
+    const f32x4* p = reinterpret_cast<const f32x4*>(g.partial + e0);
+    const int64_t plane4 = total / 4;
+    int s = 0;
+    for (; s + 4 <= g.S; s += 4) {
+      f32x4 t[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) t[k] = p[(s + k) * plane4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] += t[k][v];
+    }
+    for (; s < g.S; ++s) {
+      const f32x4 t = p[s * plane4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] += t[v];
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (e0 + v < total) acc[v] = sum_splits(g.partial + e0 + v, total, g.S);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    if (e0 + v >= total) break;
+    const float val = g.res != nullptr ? acc[v] + r[v] : acc[v];
+    if (g.n_split > 0 && nn[v] >= g.n_split)
+      g.out2[mm[v] * g.ldc2 + (nn[v] - g.n_split)] = f32_to_bf16(val);
+    else
+      g.out[mm[v] * g.ldc + nn[v]] = f32_to_bf16(val);
   }
 }
 
-// One workgroup per latent row: sum of squares with a fixed-order tree
-// (wave butterfly, then the four wave sums in order), then the bf16 output.
+// One workgroup per latent row.  The row and gamma are loaded once, into
+// registers (up to kNormChunks 16-byte chunks per thread, d <= 8192), then
+// the sum of squares in a fixed-order tree (per-thread order, wave
+// butterfly, the four wave sums in order) and the bf16 output.
+constexpr int kNormChunks = 4;
+
 __global__ __launch_bounds__(256) void rmsnorm_kernel(NormProblem p) {
   __shared__ float wsum[4];
   const int m = static_cast<int>(blockIdx.x);
   const uint16_t* row = p.latent + static_cast<int64_t>(m) * p.d;
+  uint16_t* orow = p.out + static_cast<int64_t>(m) * p.d;
   const int d8 = p.d >> 3;
-  float ss = 0.f;
-  for (int c = static_cast<int>(threadIdx.x); c < d8; c += 256) {
-    const u32x4 v = load_cached(row + c * 8);
+  const int tid = static_cast<int>(threadIdx.x);
+  u32x4 v[kNormChunks], gv[kNormChunks];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float l0 = bf16_lo(v[i]), l1 = bf16_hi(v[i]);
+  for (int i = 0; i < kNormChunks; ++i) {
+    const int c = tid + 256 * i;
+    v[i] = c < d8 ? load_cached(row + c * 8) : zero4();
+    gv[i] = c < d8 ? load_cached(p.gamma + c * 8) : zero4();
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNormChunks; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float l0 = bf16_lo(v[i][q]), l1 = bf16_hi(v[i][q]);
       ss = fmaf(l0, l0, ss);
       ss = fmaf(l1, l1, ss);
     }
-  }
   ss = wave_allreduce(ss);
   if (lane_id() == 0) wsum[wave_id()] = ss;
   __syncthreads();
   const float total = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
   const float r = __frsqrt_rn(total / static_cast<float>(p.d) + p.eps);
-  uint16_t* orow = p.out + static_cast<int64_t>(m) * p.d;
-  for (int c = static_cast<int>(threadIdx.x); c < d8; c += 256) {
-    const u32x4 v = load_cached(row + c * 8);
-    const u32x4 gv = load_cached(p.gamma + c * 8);
+#pragma unroll
+  for (int i = 0; i < kNormChunks; ++i) {
+    const int c = tid + 256 * i;
+    if (c >= d8) break;
     u32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = pack_bf16x2(bf16_lo(v[i]) * r * bf16_lo(gv[i]), bf16_hi(v[i]) * r * bf16_hi(gv[i]));
+    for (int q = 0; q < 4; ++q)
+      o[q] = pack_bf16x2(bf16_lo(v[i][q]) * r * bf16_lo(gv[i][q]), bf16_hi(v[i][q]) * r * bf16_hi(gv[i][q]));
     *reinterpret_cast<u32x4*>(orow + c * 8) = o;
   }
 }
@@ -230,7 +286,8 @@ hipError_t launch_smallk_g(const SmallkArgs& g, hipStream_t s) {
 template <int G>
 hipError_t launch_fb_g(const FbArgs& g, hipStream_t s) {
   // At least one column of workgroups: it also stores beta and f_a.
-  const int bx = (g.n_b + kFbRowsPerWg - 1) / kFbRowsPerWg;
+  constexpr int R = fb_rows_per_wg<G>();
+  const int bx = (g.n_b + R - 1) / R;
   const dim3 grid(bx > 0 ? bx : 1, (g.M + kFbMGroup - 1) / kFbMGroup);
   if (g.partial != nullptr)
     hipLaunchKernelGGL((fab_fb_tail_kernel<G, true>), grid, dim3(kSmallkWaves * kWave), 0, s, g);
@@ -271,16 +328,20 @@ hipError_t launch_fab_fb_tail(const FbProblem& p, hipStream_t s) {
 }
 
 hipError_t launch_reduce(const ReduceProblem& p, hipStream_t s) {
-  ReduceArgs g{p.partial, p.S, p.M, p.N, p.res, p.ldr, p.out, p.ldc};
+  ReduceArgs g{p.partial, p.S, p.M, p.N, p.res, p.ldr, p.out, p.ldc, p.out2, p.ldc2, p.n_split};
   const int64_t total = static_cast<int64_t>(p.M) * p.N;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 2048) blocks = 2048;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, g);
+  const int64_t blocks = (total + 1023) / 1024;
+  if (blocks < 1) return hipSuccess;
+  const bool vec = (total % 4) == 0 && (reinterpret_cast<uintptr_t>(p.partial) & 15u) == 0;
+  if (vec)
+    hipLaunchKernelGGL(reduce_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL(reduce_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm(const NormProblem& p, hipStream_t s) {
+  if ((p.d >> 3) > 256 * kNormChunks) return hipErrorInvalidValue;
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(static_cast<unsigned>(p.M)), dim3(256), 0, s, p);
   return hipGetLastError();
 }

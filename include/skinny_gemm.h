@@ -69,23 +69,31 @@ enum {
 
 /* Kernel families a configuration can name. */
 enum {
-    SG_KIND_NONE = 0,         /* empty problem: nothing to launch */
-    SG_KIND_GEMV_ROW = 1,     /* M <= 16: one wave streams whole weight rows */
-    SG_KIND_GEMV_SPLITK = 2,  /* M <= 16, small N: K split across waves */
-    SG_KIND_GEMV_SMALLK = 3,  /* M <= 16, K <= 256: several rows per wave */
-    SG_KIND_MFMA_TILE = 4     /* 16 < M <= 256: bf16 MFMA tiles */
+    SG_KIND_NONE = 0,           /* empty problem: nothing to launch */
+    SG_KIND_GEMV_ROW = 1,       /* M == 1: one wave streams whole weight rows */
+    SG_KIND_GEMV_SPLITK = 2,    /* M == 1, small N: K split across workgroups */
+    SG_KIND_GEMV_SMALLK = 3,    /* M <= 16, K <= 256: several rows per wave */
+    SG_KIND_MFMA_TILE = 4,      /* bf16 MFMA, weight and activation chunks staged
+                                   in an LDS ring shared by the workgroup */
+    SG_KIND_MFMA_WAVESPLIT = 5, /* bf16 MFMA, M <= 16: 16 weight rows per
+                                   workgroup, each wave a private LDS ring over
+                                   a quarter of K, summed in LDS */
+    SG_KIND_MFMA_DIRECT = 6     /* bf16 MFMA, M > 64: fragments loaded straight
+                                   into registers */
 };
 
 /* Launch configuration chosen per (M, N, K): the analogue of the reference's
  * SkinnyGemmConfig [P1 skinny_gemm.py].  Fields not used by a kind are 0.
  *   kind     SG_KIND_*
- *   m_tile   rows of the activation the kernel instance is built for
- *            (GEMV: M; MFMA: M rounded up to a multiple of 16)
- *   rows     GEMV: weight rows per wave; MFMA: 16-row weight blocks per wave
+ *   m_tile   activation rows the kernel instance is built for: M (GEMV),
+ *            M rounded up to 4 (TILE and WAVESPLIT with M <= 16), M rounded
+ *            up to 16 (MFMA otherwise)
+ *   rows     weight rows per wave (GEMV) or per workgroup (MFMA TILE and
+ *            WAVESPLIT); 1 for DIRECT (one 16-row block per workgroup)
  *   waves    waves (64 lanes) per workgroup
  *   k_split  workgroups that split K; > 1 means fp32 partials in workspace
- *   k_unroll 16-byte weight chunks (GEMV) or 32-deep k-steps (MFMA) each
- *            lane keeps in flight
+ *   k_unroll GEMV: 512-wide weight steps a wave holds; TILE / WAVESPLIT: LDS
+ *            ring slots (chunks of 128 k); DIRECT: 32-deep k-steps in flight
  *   grid     workgroups launched by the main kernel
  *   nt_weights 1 = weights are read with non-temporal (streaming) loads */
 typedef struct {
@@ -134,8 +142,9 @@ int sg_overlap_max_tokens(void);
 size_t sg_workspace_bytes(int op, int M, int N, int K);
 
 /* Bytes of device workspace kda_projection_overlap needs: which = 0 for
- * ws_main (Q/K/V/G split-K partials, 0 when unsplit), 1 for ws_aux (the
- * bf16 F_A/beta projection [M, n_ab] plus its split-K partials). */
+ * ws_main (split-K partials of the packed projection [k_split][M][n_qkvg +
+ * n_ab] fp32, 0 when unsplit), 1 for ws_aux (the bf16 F_A/beta projection
+ * [M, n_ab] plus its split-K partials). */
 size_t sg_kda_workspace_bytes(int which, int M, int K, int n_qkvg, int n_ab);
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -214,9 +223,11 @@ int kda_projection_overlap(const sg_bf16 *x, const sg_bf16 *packed_w, const sg_b
  * latent [M,d_latent], gamma [d_latent], w_up [d_hidden,d_latent], shared
  * [M,d_hidden] (nullable: no add), out [M,d_hidden]; all contiguous.  eps
  * must be finite and > 0, d_latent > 0.  out may alias shared exactly.
- * For M <= 16 one kernel normalises on the fly; for M > 16 the normalised
- * latent is written to the workspace (sg_workspace_bytes(SG_OP_LATENT_TAIL,
- * M, d_hidden, d_latent)) and consumed by the MFMA GEMM. */
+ * For M == 1 (when one workgroup covers the whole latent row) one GEMV
+ * kernel normalises on the fly; otherwise the normalised latent is written
+ * to the workspace (sg_workspace_bytes(SG_OP_LATENT_TAIL, M, d_hidden,
+ * d_latent)) by a norm kernel and consumed by the GEMM; that path needs
+ * d_latent <= 8192 (SG_ERR_UNSUPPORTED otherwise). */
 int latent_moe_tail(const sg_bf16 *latent, const sg_bf16 *gamma, float eps,
                     const sg_bf16 *w_up, const sg_bf16 *shared, sg_bf16 *out,
                     int M, int d_latent, int d_hidden,

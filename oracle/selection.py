@@ -10,35 +10,39 @@ dispatcher must agree with it field by field.
 Rule, for C[M,N] = A[M,K] W[N,K]^T:
   * M, N or K negative -> INVALID_ARG.  K not a multiple of 8 -> UNSUPPORTED.
     M > 256 -> UNSUPPORTED.  M == 0 or N == 0 -> kind NONE, every field 0.
-  * Otherwise waves = 4 and nt_weights = 1, and
+  * Otherwise nt_weights = 1, waves = 4 unless stated, ksteps = ceil(K / 32),
+    and
   * M <= 16, K <= 256: GEMV_SMALLK.  G = smallest power of two >= max(K/8, 1)
     lanes per weight row; rows = 64 / G rows per wave; k_split = 1;
     k_unroll = 1; grid = ceil(N / (4 * rows)); m_tile = M.
-  * M <= 16, K > 256: steps = ceil((K/8) / 64).
-      - N >= 1024: GEMV_ROW, rows = 1 (M <= 2), 2 (M <= 8) or 4; want = 1.
-      - N < 1024: GEMV_SPLITK, rows = 1, want = ceil(2048 / N).
-      depth = 16, 14, 7 for rows = 1, 2, 4 (k_unroll = depth);
-      max_sps = min(floor(128 / M), depth), need = ceil(steps / max_sps),
-      k_split = split(steps, max(want, need)), sps = ceil(steps / k_split);
-      waves = 8 if M * sps > 64 else 4.
-      grid = ceil(N / (waves * rows)) * k_split; m_tile = M.
-  * 17 <= M <= 256: MFMA_TILE, m_tile = 16 * ceil(M / 16), rows = 1,
-    k_unroll = 12, 8, 4, 2 for m_tile/16 <= 2, <= 4, <= 8, above;
-    tiles = ceil(N / 16), ksteps = ceil(K / 32).
-      - tiles >= 192: k_split = 1.
-      - else want = min(ceil(256 / tiles), max(1, floor(ksteps / 8))),
-        k_split = split(ksteps, want).
+  * M == 1 (K > 256): steps = ceil((K/8) / 64).
+      - N >= 1024: GEMV_ROW, want = 1.
+      - N < 1024: GEMV_SPLITK, want = ceil(2048 / N).
+      need = ceil(steps / 16), k_split = split(steps, max(want, need)),
+      m_tile = 1, rows = 1, k_unroll = 16, grid = ceil(N / 4) * k_split.
+  * 2 <= M <= 16: m_tile = 4 * ceil(M / 4), tiles16 = ceil(N / 16).
+      - tiles16 <= 320: MFMA_WAVESPLIT, rows = 16, waves = 4, k_unroll = 4,
+        k_split = msplit(tiles16, 16), grid = tiles16 * k_split.
+      - else MFMA_TILE, rows = 32, waves = 2, k_unroll = 4,
+        tiles = ceil(N / 32), k_split = msplit(tiles, 4), grid = tiles * k_split.
+  * 17 <= M <= 64: MFMA_TILE, m_tile = 16 * ceil(M / 16), rows = 64, waves = 4,
+    k_unroll = 3, tiles = ceil(N / 64), k_split = msplit(tiles, 4),
     grid = tiles * k_split.
+  * 65 <= M <= 256: MFMA_DIRECT, m_tile = 16 * ceil(M / 16), rows = 1,
+    k_unroll = 4 if m_tile <= 128 else 2, tiles = ceil(N / 16),
+    k_split = msplit(tiles, 32), grid = tiles * k_split.
+  * msplit(tiles, min_steps): 1 if tiles >= 192; else
+    split(ksteps, min(ceil(224 / tiles), max(1, floor(ksteps / min_steps)))).
   * split(steps, want): 1 if steps <= 0 or want <= 1; else with
     w = min(want, steps) and per = ceil(steps / w), ceil(steps / per).
 
-Overlap gate: enabled and 0 < M <= 32 and x contiguous and an aux stream and
-the event pair are present.
+Overlap gate: enabled and 0 < M <= OVERLAP_MAX_TOKENS and x contiguous and an
+aux stream and the event pair are present.
 """
 from __future__ import annotations
 
 OK, INVALID_ARG, UNSUPPORTED = 0, -1, -2
-NONE, GEMV_ROW, GEMV_SPLITK, GEMV_SMALLK, MFMA_TILE = 0, 1, 2, 3, 4
+NONE, GEMV_ROW, GEMV_SPLITK, GEMV_SMALLK, MFMA_TILE, MFMA_WAVESPLIT, MFMA_DIRECT = 0, 1, 2, 3, 4, 5, 6
 OVERLAP_MAX_TOKENS = 32
 
 FIELDS = ("kind", "m_tile", "rows", "waves", "k_split", "k_unroll", "grid", "nt_weights")
@@ -69,43 +73,52 @@ def select(M: int, N: int, K: int, has_residual: bool = False):
         return OK, cfg
     cfg["waves"] = 4
     cfg["nt_weights"] = 1
-    if M <= 16:
-        cfg["m_tile"] = M
-        if K <= 256:
-            g = 1
-            while g < max(K // 8, 1):
-                g *= 2
-            cfg.update(kind=GEMV_SMALLK, rows=64 // g, k_split=1, k_unroll=1)
-            cfg["grid"] = _cdiv(N, 4 * cfg["rows"])
-        else:
-            steps = _cdiv(K // 8, 64)
-            if N >= 1024:
-                rows = 1 if M <= 2 else (2 if M <= 8 else 4)
-                cfg.update(kind=GEMV_ROW, rows=rows)
-                want = 1
-            else:
-                cfg.update(kind=GEMV_SPLITK, rows=1)
-                want = _cdiv(2048, N)
-            depth = {1: 16, 2: 14, 4: 7}[cfg["rows"]]
-            max_sps = min(128 // M, depth)
-            need = _cdiv(steps, max_sps)
-            cfg["k_split"] = _split(steps, max(want, need))
-            sps = _cdiv(steps, cfg["k_split"])
-            cfg["waves"] = 8 if M * sps > 64 else 4
-            cfg["k_unroll"] = depth
-            cfg["grid"] = _cdiv(N, cfg["waves"] * cfg["rows"]) * cfg["k_split"]
-    else:
-        tiles = _cdiv(N, 16)
-        ksteps = _cdiv(K, 32)
+    ksteps = _cdiv(K, 32)
+
+    def msplit(tiles: int, min_steps: int) -> int:
         if tiles >= 192:
-            ks = 1
+            return 1
+        cap = max(1, ksteps // min_steps)
+        return _split(ksteps, min(_cdiv(224, tiles), cap))
+
+    if M <= 16 and K <= 256:
+        g = 1
+        while g < max(K // 8, 1):
+            g *= 2
+        cfg.update(kind=GEMV_SMALLK, m_tile=M, rows=64 // g, k_split=1, k_unroll=1)
+        cfg["grid"] = _cdiv(N, 4 * cfg["rows"])
+    elif M == 1:
+        steps = _cdiv(K // 8, 64)
+        if N >= 1024:
+            kind, want = GEMV_ROW, 1
         else:
-            want = min(_cdiv(256, tiles), max(1, ksteps // 8))
-            ks = _split(ksteps, want)
+            kind, want = GEMV_SPLITK, _cdiv(2048, N)
+        ks = _split(steps, max(want, _cdiv(steps, 16)))
+        cfg.update(kind=kind, m_tile=1, rows=1, k_split=ks, k_unroll=16,
+                   grid=_cdiv(N, 4) * ks)
+    elif M <= 16:
+        cfg["m_tile"] = 4 * _cdiv(M, 4)
+        tiles16 = _cdiv(N, 16)
+        if tiles16 <= 320:
+            ks = msplit(tiles16, 16)
+            cfg.update(kind=MFMA_WAVESPLIT, rows=16, waves=4, k_unroll=4, k_split=ks,
+                       grid=tiles16 * ks)
+        else:
+            tiles = _cdiv(N, 32)
+            ks = msplit(tiles, 4)
+            cfg.update(kind=MFMA_TILE, rows=32, waves=2, k_unroll=4, k_split=ks,
+                       grid=tiles * ks)
+    elif M <= 64:
+        tiles = _cdiv(N, 64)
+        ks = msplit(tiles, 4)
+        cfg.update(kind=MFMA_TILE, m_tile=16 * _cdiv(M, 16), rows=64, waves=4, k_unroll=3,
+                   k_split=ks, grid=tiles * ks)
+    else:
         mb = _cdiv(M, 16)
-        depth = 12 if mb <= 2 else (8 if mb <= 4 else (4 if mb <= 8 else 2))
-        cfg.update(kind=MFMA_TILE, m_tile=16 * mb, rows=1, k_unroll=depth, k_split=ks,
-                   grid=tiles * ks)
+        tiles = _cdiv(N, 16)
+        ks = msplit(tiles, 32)
+        cfg.update(kind=MFMA_DIRECT, m_tile=16 * mb, rows=1, k_unroll=4 if mb <= 8 else 2,
+                   k_split=ks, grid=tiles * ks)
     return OK, cfg
 
 

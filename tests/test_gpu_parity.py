@@ -26,13 +26,15 @@ def _say(*a):
 # ---- skinny_gemm over every kind, with ragged shapes --------------------------------
 
 GEMM_CASES = [
-    # (M, N, K, residual)  -- GEMV_ROW / SPLITK / SMALLK / MFMA, ragged N and K
+    # (M, N, K, residual)  -- GEMV_ROW / SPLITK / SMALLK, MFMA WAVESPLIT / TILE /
+    # DIRECT, ragged N and K
     (1, 1030, 1000, False), (2, 1500, 2056, True), (3, 1024, 520, False), (4, 1100, 7168, True),
     (5, 77, 3000, False), (8, 300, 1000, True), (11, 2000, 264, False), (16, 1100, 4104, True),
     (16, 40, 8, False), (4, 64, 136, True), (1, 5, 248, False), (7, 9, 256, True),
     (17, 300, 1000, False), (31, 100, 2056, True), (33, 520, 264, False), (64, 1024, 1000, True),
     (100, 77, 4104, False), (256, 300, 520, True), (255, 129, 96, False), (48, 3000, 40, True),
     (16, 1, 7168, False), (20, 1, 64, True), (3, 7, 0, True),
+    (6, 5200, 1000, True), (13, 7170, 2056, False), (20, 9000, 512, True), (2, 4100, 7176, False),
 ]
 
 

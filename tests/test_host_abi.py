@@ -98,11 +98,22 @@ def test_select_null_out(lib):
     assert lib.sg_select(1, 1, 8, 0, None) == _lib.SG_ERR_INVALID_ARG
 
 
+def _kind_for(M):
+    if M == 1:
+        return selection.GEMV_ROW
+    if M <= 16:
+        return selection.MFMA_WAVESPLIT
+    return selection.MFMA_TILE if M <= 64 else selection.MFMA_DIRECT
+
+
 def test_kind_follows_m_boundaries():
     for M in range(1, 257):
         st, cfg = selection.select(M, 4096, 7168)
         assert st == selection.OK
-        assert cfg["kind"] == (selection.GEMV_ROW if M <= 16 else selection.MFMA_TILE)
+        assert cfg["kind"] == _kind_for(M), M
+    # A wide N moves M <= 16 to the shared-activation tile (32 rows per workgroup).
+    assert selection.select(8, 7168, 2048)[1]["kind"] == selection.MFMA_TILE
+    assert selection.select(8, 7168, 2048)[1]["rows"] == 32
     assert selection.select(257, 4096, 7168)[0] == selection.UNSUPPORTED
     assert selection.select(0, 4096, 7168)[1]["kind"] == selection.NONE
 
@@ -114,9 +125,11 @@ def test_overlap_gate_matches_oracle(lib):
 
 
 def test_workspace_bytes(lib):
-    # QKVG at decode sizes needs no workspace; F_A/beta always keeps partials.
+    # QKVG for M <= 16 needs no workspace (one launch, no K split); the
+    # 64-row tile for M > 16 splits K four ways; F_A/beta always keeps partials.
     assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, 1, 4096, 7168) == 0
-    assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, 64, 4096, 7168) == 0
+    assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, 8, 4096, 7168) == 0
+    assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, 64, 4096, 7168) == 4 * 64 * 4096 * 4
     for M in (1, 2, 4, 8, 16, 32):
         st, cfg = selection.select(M, 136, 7168)
         need = lib.sg_workspace_bytes(_lib.SG_OP_FAB_FB, M, 136, 7168)
