@@ -3,16 +3,21 @@
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
 One step is one pass of the whole hot path over the decode batch sizes
-M in {1, 2, 3, 4, 8, 16, 17, 32, 64}: for every M, the concurrent KDA projection
-(packed Q/K/V/G on the main stream || F_A/beta -> F_B on an aux stream, event
-fork/join) and the latent-MoE tail (RMSNorm -> up-projection -> shared add).
+M in {1, 2, 3, 4, 8, 16, 17, 32, 64}: for every M, the KDA projection (Q/K/V/G
+and F_A/beta -> F_B) in the schedule the overlap gate picks for that M, and the
+latent-MoE tail (RMSNorm -> up-projection -> shared add).  With the gate
+closed (its measured setting on MI355X) the projection runs on one stream: the
+Q/K/V/G and F_A/beta rows as two segments of one launch, then F_B.
 Each (op, M) is a hipGraph of R back-to-back calls that cycle through R copies
 of the weights, with R chosen so that the copies span >= 512 MiB: the 256 MiB
 Infinity Cache cannot hold them, so the weights stream from HBM on every call.
 Inputs are resident in HBM before timing starts.
 
 Reported ``value``: mean microseconds per KDA projection call over the M sweep
-(the metric's unit).  The same line carries the per-M breakdown (projection,
+(the metric's unit).  ``--comparators`` adds, per M, the forced two-stream
+schedule (fork/join events, F_A/beta -> F_B on an aux stream), the forced
+single-stream schedule, and a plain packed GEMM followed by a second GEMM for
+F_B.  The same line carries the per-M breakdown (projection,
 tail, GB/s, fraction of HBM peak), the roofline of the dominant kernel (the
 Q/K/V/G GEMV at M = 1, timed with HIP events on its own stream) and the CPU
 oracle timed on this host.
@@ -81,7 +86,7 @@ def copies_for(weight_bytes):
 
 
 class ProjectionCase:
-    """R concurrent KDA projection calls at batch M, one weight copy each."""
+    """R KDA projection calls at batch M, one weight copy each."""
 
     def __init__(self, M, device, aux, fork, join):
         x, packed, w_b = synth.overlap_inputs(M)
@@ -237,7 +242,9 @@ def main():
     fork, join = sg.HipEvent(), sg.HipEvent()
     proj = {M: ProjectionCase(M, device, aux, fork, join) for M in M_SWEEP}
     tail = {M: TailCase(M, device) for M in M_SWEEP}
-    g_proj = {M: capture(lambda r, c=proj[M]: c.call(r), proj[M].R, main_stream) for M in M_SWEEP}
+    gate = {M: sg.sg_overlap_gate(M, True, True, True, True) for M in M_SWEEP}
+    g_proj = {M: capture(lambda r, c=proj[M], conc=gate[M]: c.call(r, concurrent=conc), proj[M].R,
+                         main_stream) for M in M_SWEEP}
     g_tail = {M: capture(lambda r, c=tail[M]: c.call(r), tail[M].R, main_stream) for M in M_SWEEP}
     print("[bench] graphs captured", file=sys.stderr, flush=True)
 
@@ -291,6 +298,7 @@ def main():
             "tail_hbm_frac": round(tail_bytes(M) / (tu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "tail_tflops": round(tail_flops(M) / (tu * 1e-6) / 1e12, 2),
             "weight_copies": [proj[M].R, tail[M].R],
+            "schedule": "two_stream" if gate[M] else "one_stream",
         }
     value = sum(b["proj_us"] for b in breakdown.values()) / len(M_SWEEP)
     ms_per_step = wall * 1000.0 / args.steps
@@ -298,8 +306,10 @@ def main():
     if args.comparators:
         for M in M_SWEEP:
             c = proj[M]
-            g_s1 = capture(lambda r, c=c: c.call(r, concurrent=False), c.R, main_stream)
-            s1 = time_graph(g_s1, main_stream, 10) * 1000.0 / c.R
+            g_two = capture(lambda r, c=c: c.call(r, concurrent=True), c.R, main_stream)
+            two = time_graph(g_two, main_stream, 10) * 1000.0 / c.R
+            g_one = capture(lambda r, c=c: c.call(r, concurrent=False), c.R, main_stream)
+            one = time_graph(g_one, main_stream, 10) * 1000.0 / c.R
             pw = c.packed
             out_packed = torch.empty((M, N_QKVG + N_AB), dtype=torch.bfloat16, device=device)
             g1_s2 = torch.empty((M, N_B), dtype=torch.bfloat16, device=device)
@@ -313,10 +323,10 @@ def main():
             g_s2 = capture(s2_call, c.R, main_stream)
             s2 = time_graph(g_s2, main_stream, 10) * 1000.0 / c.R
             b = breakdown[str(M)]
-            b["s1_us"] = round(s1, 3)
-            b["s2_us"] = round(s2, 3)
-            b["speedup_vs_s1"] = round(s1 / b["proj_us"], 3)
-            b["speedup_vs_s2"] = round(s2 / b["proj_us"], 3)
+            b["two_stream_us"] = round(two, 3)
+            b["one_stream_us"] = round(one, 3)
+            b["packed_gemm_then_fb_us"] = round(s2, 3)
+            b["two_stream_speedup_vs_one_stream"] = round(one / two, 3)
 
     leg = qkvg_kernel_leg(device)
     roofline = {"bound": "hbm", "achieved": round(leg["gbs"], 1), "peak": HBM_PEAK_GBS,
@@ -339,11 +349,11 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "kda_decode_projection_sweep",
-            "description": "concurrent KDA projection (packed QKVG [4096,7168] on main || "
-                           "F_A/beta [136,7168] -> F_B [1024,128] on aux, hipGraph) per M, plus "
-                           "the latent-MoE tail (RMSNorm 2048 -> up-proj [7168,2048] + shared "
-                           "add) per M; value = mean us per projection call over the sweep; "
-                           "weights cold (rotated over >= 512 MiB)",
+            "description": "KDA projection per M in the schedule the overlap gate picks (QKVG "
+                           "[4096,7168] and F_A/beta [136,7168] -> F_B [1024,128], hipGraph), "
+                           "plus the latent-MoE tail (RMSNorm 2048 -> up-proj [7168,2048] + "
+                           "shared add) per M; value = mean us per projection call over the "
+                           "sweep; weights cold (rotated over >= 512 MiB)",
             "m_sweep": M_SWEEP, "hidden": K, "n_qkvg": N_QKVG, "n_ab": N_AB, "rank": RANK,
             "n_b": N_B, "d_latent": D_LAT, "d_hidden": D_HID, "parallelism": "single_gpu",
         },

@@ -246,10 +246,11 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
   if (M < 0 || K < 0 || n_qkvg < 0 || n_b < 0 || rank <= 0 || n_ab <= rank)
     return SG_ERR_INVALID_ARG;
   if (rank % 8 != 0 || rank > sg::kFbMaxRank) return SG_ERR_UNSUPPORTED;
-  sg_config_t c;  // the packed [n_qkvg + n_ab] projection's configuration
-  int st = sg_select(M, n_qkvg + n_ab, K, 0, &c);
+  sg_config_t cq;  // the Q/K/V/G rows: the table's configuration for [n_qkvg, K]
+  int st = sg_select(M, n_qkvg, K, 0, &cq);
   if (st != SG_OK) return st;
   if (M == 0) return SG_OK;
+  const sg_config_t cf = fab_config(M, n_ab, K);  // F_A/beta rows, as kda_fab_fb_proj
   if ((st = check_operand16(x, K, K)) != SG_OK) return st;
   if ((st = check_operand16(packed_w, K, K)) != SG_OK) return st;
   if ((st = check_operand16(w_b, rank, rank)) != SG_OK) return st;
@@ -260,7 +261,7 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
   const size_t need_aux = sg_kda_workspace_bytes(1, M, K, n_qkvg, n_ab);
   if ((st = check_workspace(ws_main, ws_main_bytes, need_main)) != SG_OK) return st;
   if ((st = check_workspace(ws_aux, ws_aux_bytes, need_aux)) != SG_OK) return st;
-  if (need_main > 0) {  // the two workspaces are used concurrently
+  if (need_main > 0) {  // the two workspaces may be used concurrently
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(ws_main), a1 = a0 + need_main;
     const uintptr_t b0 = reinterpret_cast<uintptr_t>(ws_aux), b1 = b0 + need_aux;
     if (a0 < b1 && b0 < a1) return SG_ERR_INVALID_ARG;
@@ -271,16 +272,10 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
   hipEvent_t ef = static_cast<hipEvent_t>(fork);
   hipEvent_t ej = static_cast<hipEvent_t>(join);
   const bool concurrent = sa != nullptr && ef != nullptr && ej != nullptr;
-  const bool split = c.k_split > 1;
-  const int64_t p_elems = static_cast<int64_t>(M) * n_ab;
-  uint16_t* pbuf = static_cast<uint16_t*>(ws_aux);  // bf16 P = [f_a | beta], [M, n_ab]
-  float* aux_part = reinterpret_cast<float*>(static_cast<char*>(ws_aux) +
-                                             sg::ws_round(static_cast<size_t>(p_elems) * 2));
-  const sg_bf16* w_ab = packed_w + static_cast<int64_t>(n_qkvg) * K;
+  const bool have_q = n_qkvg > 0 && cq.kind != SG_KIND_NONE;
+  const bool split_q = have_q && cq.k_split > 1;
 
-  // Both schedules run every row with the packed configuration, so each
-  // output element is computed by the same instruction sequence either way:
-  // the results are bitwise identical.
+  // Q/K/V/G rows with their own configuration (split-K partials in ws_main).
   DotProblem q{};
   q.a = x;
   q.lda = K;
@@ -290,9 +285,31 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
   q.ldc = n_qkvg;
   q.ldr = n_qkvg;
   q.M = M;
+  q.N = n_qkvg;
   q.K = K;
+  if (split_q) q.partial = static_cast<float*>(ws_main);
+  sg::ReduceProblem red{};
+  red.partial = static_cast<const float*>(ws_main);
+  red.S = cq.k_split;
+  red.M = M;
+  red.N = n_qkvg;
+  red.out = qkvg;
+  red.ldc = n_qkvg;
+
+  // F_A/beta rows: always fp32 partials in ws_aux, summed by the F_B stage.
+  DotProblem f{};
+  f.a = x;
+  f.lda = K;
+  f.w = packed_w + static_cast<int64_t>(n_qkvg) * K;
+  f.ldw = K;
+  f.M = M;
+  f.N = n_ab;
+  f.K = K;
+  f.partial = static_cast<float*>(ws_aux);
 
   sg::FbProblem fb{};
+  fb.partial = f.partial;
+  fb.S = cf.k_split;
   fb.M = M;
   fb.n_ab = n_ab;
   fb.rank = rank;
@@ -301,47 +318,39 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
   fb.beta = beta;
   fb.g1 = g1;
 
+  // Each output element is computed by the same kernel code over the same
+  // K-ranges, and every split-K sum runs in the same fixed order, in both
+  // schedules: the results are bitwise identical.
   if (!concurrent) {
-    // One packed launch: Q/K/V/G rows to qkvg, F_A/beta rows to P (through
-    // the split-K reduction when K is split, partials in ws_main); then F_B.
-    q.N = n_qkvg + n_ab;
-    q.out2 = pbuf;
-    q.ldc2 = n_ab;
-    q.n_split = n_qkvg > 0 ? n_qkvg : 0;
-    if (n_qkvg == 0) {
-      q.out = pbuf;
-      q.ldc = n_ab;
+    // One launch for both row ranges when their configurations name the same
+    // kernel instance (two segments of one grid: the small F_A/beta problem
+    // fills in beside the Q/K/V/G tiles instead of trailing them), then one
+    // launch for F_B and the Q/K/V/G split-K reduction.
+    const DotProblem segs[2] = {q, f};
+    const sg_config_t cfgs[2] = {cq, cf};
+    hipError_t e = hipSuccess;
+    if (have_q && is_mfma(cq.kind) && is_mfma(cf.kind) && sg::mfma_same_instance(cq, cf)) {
+      e = sg::launch_mfma(segs, cfgs, 2, sm);
+    } else if (have_q && !is_mfma(cq.kind) && cq.kind != SG_KIND_GEMV_SMALLK &&
+               !is_mfma(cf.kind) && sg::gemv_same_instance(cq, cf)) {
+      e = sg::launch_gemv(segs, cfgs, 2, sm);
+    } else {
+      if (have_q && launch_main(q, cq, sm) != hipSuccess) return SG_ERR_HIP;
+      e = launch_main(f, cf, sm);
     }
-    if ((st = enqueue_dot(q, c, ws_main, sm)) != SG_OK) return st;
-    fb.p_bf16 = pbuf;
+    if (e != hipSuccess) return SG_ERR_HIP;
+    if (split_q) fb.red = &red;
     return hip_status(sg::launch_fab_fb_tail(fb, sm));
   }
 
-  // Two launches over the two row ranges (main: Q/K/V/G, aux: F_A/beta).
-  auto run_fab = [&](hipStream_t s) -> int {
-    DotProblem f = q;
-    f.w = w_ab;
-    f.N = n_ab;
-    f.out = pbuf;
-    f.ldc = n_ab;
-    f.ldr = n_ab;
-    if (split) {
-      f.partial = aux_part;
-      if (launch_main(f, c, s) != hipSuccess) return SG_ERR_HIP;
-      fb.partial = aux_part;
-      fb.S = c.k_split;
-    } else {
-      int r = enqueue_dot(f, c, nullptr, s);
-      if (r != SG_OK) return r;
-      fb.p_bf16 = pbuf;
-    }
-    return hip_status(sg::launch_fab_fb_tail(fb, s));
-  };
-  q.N = n_qkvg;
   if (hipEventRecord(ef, sm) != hipSuccess) return SG_ERR_HIP;
   if (hipStreamWaitEvent(sa, ef, 0) != hipSuccess) return SG_ERR_HIP;
-  if (n_qkvg > 0 && (st = enqueue_dot(q, c, ws_main, sm)) != SG_OK) return st;
-  if ((st = run_fab(sa)) != SG_OK) return st;
+  if (have_q) {
+    if (launch_main(q, cq, sm) != hipSuccess) return SG_ERR_HIP;
+    if (split_q && sg::launch_reduce(red, sm) != hipSuccess) return SG_ERR_HIP;
+  }
+  if (launch_main(f, cf, sa) != hipSuccess) return SG_ERR_HIP;
+  if (sg::launch_fab_fb_tail(fb, sa) != hipSuccess) return SG_ERR_HIP;
   if (hipEventRecord(ej, sa) != hipSuccess) return SG_ERR_HIP;
   if (hipStreamWaitEvent(sm, ej, 0) != hipSuccess) return SG_ERR_HIP;
   return SG_OK;

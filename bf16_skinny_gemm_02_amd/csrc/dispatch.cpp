@@ -27,7 +27,13 @@ constexpr int kSplitMaxTiles = 320;  // WAVESPLIT up to this many 16-row tiles
 constexpr int kSplitRing = 4;        // WAVESPLIT ring slots
 constexpr int kWideRing = 4;         // TILE ring slots for M <= 16 (2 waves, 32 rows)
 constexpr int kTileRing = 3;         // TILE ring slots for 16 < M <= 64 (4 waves, 64 rows)
-constexpr int kOverlapMaxTokens = 32;
+// Largest M for which the two-stream projection is worth its fork/join.  On
+// MI355X the concurrent schedule measured slower than the single-stream one
+// (two segments in one launch, then F_B) at every decode M from 1 to 64:
+// the event pair costs more than the overlap recovers, and the LDS-resident
+// main kernel leaves no room beside it for the aux branch's workgroups.  The
+// gate therefore stays closed; the concurrent path remains available.
+constexpr int kOverlapMaxTokens = 0;
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -124,7 +130,7 @@ extern "C" int sg_select(int M, int N, int K, int has_residual, sg_config_t* out
       c.waves = 2;
       c.k_unroll = kWideRing;
       const int tiles = ceil_div(N, c.rows);
-      c.k_split = mfma_split(tiles, ksteps, 4);
+      c.k_split = mfma_split(tiles, ksteps, 8);
       c.grid = tiles * c.k_split;
     }
   } else if (M <= 64) {
@@ -134,7 +140,7 @@ extern "C" int sg_select(int M, int N, int K, int has_residual, sg_config_t* out
     c.waves = 4;
     c.k_unroll = kTileRing;
     const int tiles = ceil_div(N, c.rows);
-    c.k_split = mfma_split(tiles, ksteps, 4);
+    c.k_split = mfma_split(tiles, ksteps, 8);
     c.grid = tiles * c.k_split;
   } else {
     c.kind = SG_KIND_MFMA_DIRECT;
@@ -214,14 +220,12 @@ extern "C" const char* sg_version(void) { return "0.1.0"; }
 
 extern "C" size_t sg_kda_workspace_bytes(int which, int M, int K, int n_qkvg, int n_ab) {
   if (M <= 0 || K < 0 || n_qkvg < 0 || n_ab <= 0) return 0;
-  sg_config_t c;
-  if (sg_select(M, n_qkvg + n_ab, K, 0, &c) != SG_OK || c.kind == SG_KIND_NONE) return 0;
-  const size_t S = static_cast<size_t>(c.k_split > 1 ? c.k_split : 0);
-  const size_t m = static_cast<size_t>(M);
-  if (which == 0)  // main: split-K partials of the packed projection
-    return S ? sg::round256(S * m * static_cast<size_t>(n_qkvg + n_ab) * sizeof(float)) : 0;
-  if (which == 1)  // aux: bf16 P [M, n_ab], then F_A/beta split-K partials
-    return sg::round256(m * static_cast<size_t>(n_ab) * 2) +
-           (S ? sg::round256(S * m * static_cast<size_t>(n_ab) * sizeof(float)) : 0);
+  if (which == 0) {  // main: Q/K/V/G split-K partials
+    sg_config_t c;
+    if (n_qkvg == 0 || sg_select(M, n_qkvg, K, 0, &c) != SG_OK || c.kind == SG_KIND_NONE) return 0;
+    return sg_workspace_bytes(SG_OP_GEMM, M, n_qkvg, K);
+  }
+  if (which == 1)  // aux: F_A/beta partials, as kda_fab_fb_proj
+    return sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K);
   return 0;
 }

@@ -56,19 +56,37 @@ struct GemvArgs {
   float eps;
 };
 
+// One launch covers one or two segments (independent problems sharing a
+// flat grid, segment 1's workgroups after segment 0's).  Within a segment,
+// workgroup `local` takes row group local % groups of K-range local / groups.
+struct GemvSeg {
+  GemvArgs g;
+  int groups;
+  int wg_begin;  // first workgroup of the segment (INT_MAX: unused)
+};
+struct GemvLaunch {
+  GemvSeg seg[2];
+};
+
 template <int M, int R, int NW, int D, bool FOLD>
-__global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs g) {
+__global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
+  const int b = static_cast<int>(blockIdx.x);
+  const GemvSeg sgm = (b >= L.seg[1].wg_begin) ? L.seg[1] : L.seg[0];  // into registers once
+  const GemvArgs g = sgm.g;
+  const int local = b - sgm.wg_begin;
+  const int split = local / sgm.groups;
+  const int group = local - split * sgm.groups;
   extern __shared__ u32x4 xs[];  // [M][row_chunks] 16-byte chunks of the activation
   constexpr int kThreads = NW * kWave;
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & (kWave - 1);
   const int wave = wave_id();
-  const int n0 = (static_cast<int>(blockIdx.x) * NW + wave) * R;
+  const int n0 = (group * NW + wave) * R;
   const bool active = n0 < g.N;
 
   const int K8 = g.K >> 3;
   const int nsteps = (K8 + kWave - 1) / kWave;
-  const int s_begin = static_cast<int>(blockIdx.y) * g.sps;
+  const int s_begin = split * g.sps;
   const int s_end = min(nsteps, s_begin + g.sps);
   const int nst = max(0, s_end - s_begin);  // <= D (the table guarantees it)
   const int row_chunks = nst * kWave;
@@ -78,7 +96,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs g) {
   // 1. Every weight chunk of the workgroup's K-range, issued up front (the
   //    range is at most D steps, so nothing is reloaded later).  Buffer
   //    loads: rows past N, chunks past K and steps past the range read zero.
-  const int wg_row0 = static_cast<int>(blockIdx.x) * NW * R;
+  const int wg_row0 = group * NW * R;
   const int wg_rows = min(NW * R, g.N - wg_row0);
   const rsrc_t wres = make_rsrc(g.w + static_cast<int64_t>(wg_row0) * g.ldw,
                                 static_cast<uint32_t>(((wg_rows - 1) * g.ldw + g.K) * 2));
@@ -190,7 +208,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs g) {
     const int n = n0 + r;
     if (n < g.N) {
       if (g.partial != nullptr) {
-        g.partial[(static_cast<int64_t>(blockIdx.y) * M + m) * g.N + n] = v;
+        g.partial[(static_cast<int64_t>(split) * M + m) * g.N + n] = v;
       } else {
         if (g.res != nullptr) v += bf16_to_f32(g.res[m * g.ldr + n]);
         if (g.n_split > 0 && n >= g.n_split)
@@ -208,7 +226,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvArgs g) {
 constexpr int gemv_depth(int R) { return R == 1 ? 16 : (R == 2 ? 14 : 7); }
 
 template <int M, int R, int NW, bool FOLD>
-hipError_t launch_inst(const GemvArgs& g, dim3 grid, size_t lds, hipStream_t s) {
+hipError_t launch_inst(const GemvLaunch& g, dim3 grid, size_t lds, hipStream_t s) {
   constexpr int D = gemv_depth(R);
   auto kern = gemv_kernel<M, R, NW, D, FOLD>;
   static const hipError_t attr = hipFuncSetAttribute(
@@ -222,7 +240,7 @@ hipError_t launch_inst(const GemvArgs& g, dim3 grid, size_t lds, hipStream_t s) 
 // The table sends only M = 1 here (one row per wave, 4 waves); wider M
 // goes to the MFMA kernels.
 template <bool FOLD>
-hipError_t launch_fold(const GemvArgs& g, int M, int R, int NW, dim3 grid, size_t lds,
+hipError_t launch_fold(const GemvLaunch& g, int M, int R, int NW, dim3 grid, size_t lds,
                        hipStream_t s) {
   if (M == 1 && R == 1 && NW == 4) return launch_inst<1, 1, 4, FOLD>(g, grid, lds, s);
   return hipErrorInvalidValue;
@@ -246,34 +264,67 @@ bool gemv_fits(int M, int K, int k_split, int rows) {
   return gemv_lds_bytes(M, K, k_split) <= kGemvMaxLds && sps <= gemv_depth(rows);
 }
 
+bool gemv_same_instance(const sg_config_t& a, const sg_config_t& b) {
+  return (a.kind == SG_KIND_GEMV_ROW || a.kind == SG_KIND_GEMV_SPLITK) &&
+         (b.kind == SG_KIND_GEMV_ROW || b.kind == SG_KIND_GEMV_SPLITK) && a.rows == b.rows &&
+         a.waves == b.waves && a.m_tile == b.m_tile;
+}
+
+hipError_t launch_gemv(const DotProblem* segs, const sg_config_t* cfgs, int nseg, hipStream_t s) {
+  if (nseg < 1 || nseg > 2) return hipErrorInvalidValue;
+  if (nseg == 2 && (!gemv_same_instance(cfgs[0], cfgs[1]) || segs[0].M != segs[1].M ||
+                    (segs[0].gamma == nullptr) != (segs[1].gamma == nullptr)))
+    return hipErrorInvalidValue;
+  GemvLaunch L;
+  int wgs = 0;
+  size_t lds = 0;
+  for (int i = 0; i < 2; ++i) {
+    GemvSeg& sgm = L.seg[i];
+    if (i >= nseg) {
+      sgm = L.seg[0];
+      sgm.wg_begin = INT32_MAX;
+      continue;
+    }
+    const DotProblem& p = segs[i];
+    const sg_config_t& cfg = cfgs[i];
+    GemvArgs& g = sgm.g;
+    g.a = p.a;
+    g.lda = p.lda;
+    g.w = p.w;
+    g.ldw = p.ldw;
+    g.res = p.res;
+    g.ldr = p.ldr;
+    g.out = p.out;
+    g.ldc = p.ldc;
+    g.gamma = p.gamma;
+    g.partial = p.partial;
+    g.out2 = p.out2;
+    g.ldc2 = p.ldc2;
+    g.n_split = p.n_split;
+    g.N = p.N;
+    g.K = p.K;
+    g.eps = p.eps;
+    const int K8 = p.K >> 3;
+    const int nsteps = (K8 + kWave - 1) / kWave;
+    const int S = cfg.k_split > 0 ? cfg.k_split : 1;
+    g.sps = nsteps > 0 ? (nsteps + S - 1) / S : 1;
+    if (!gemv_fits(p.M, p.K, S, cfg.rows)) return hipErrorInvalidValue;
+    const size_t seg_lds = gemv_lds_bytes(p.M, p.K, S);
+    if (seg_lds > lds) lds = seg_lds;
+    const int rows_per_wg = cfg.waves * cfg.rows;
+    sgm.groups = (p.N + rows_per_wg - 1) / rows_per_wg;
+    if (sgm.groups <= 0) return hipErrorInvalidValue;
+    sgm.wg_begin = wgs;
+    wgs += sgm.groups * S;
+  }
+  if (wgs <= 0) return hipSuccess;
+  const dim3 grid(wgs);
+  if (segs[0].gamma != nullptr) return launch_fold<true>(L, segs[0].M, cfgs[0].rows, cfgs[0].waves, grid, lds, s);
+  return launch_fold<false>(L, segs[0].M, cfgs[0].rows, cfgs[0].waves, grid, lds, s);
+}
+
 hipError_t launch_gemv(const DotProblem& p, const sg_config_t& cfg, hipStream_t s) {
-  GemvArgs g;
-  g.a = p.a;
-  g.lda = p.lda;
-  g.w = p.w;
-  g.ldw = p.ldw;
-  g.res = p.res;
-  g.ldr = p.ldr;
-  g.out = p.out;
-  g.ldc = p.ldc;
-  g.gamma = p.gamma;
-  g.partial = p.partial;
-  g.out2 = p.out2;
-  g.ldc2 = p.ldc2;
-  g.n_split = p.n_split;
-  g.N = p.N;
-  g.K = p.K;
-  g.eps = p.eps;
-  const int K8 = p.K >> 3;
-  const int nsteps = (K8 + kWave - 1) / kWave;
-  const int S = cfg.k_split > 0 ? cfg.k_split : 1;
-  g.sps = nsteps > 0 ? (nsteps + S - 1) / S : 1;
-  if (!gemv_fits(p.M, p.K, S, cfg.rows)) return hipErrorInvalidValue;
-  const size_t lds = gemv_lds_bytes(p.M, p.K, S);
-  const int rows_per_wg = cfg.waves * cfg.rows;
-  const dim3 grid((p.N + rows_per_wg - 1) / rows_per_wg, S);
-  if (p.gamma != nullptr) return launch_fold<true>(g, p.M, cfg.rows, cfg.waves, grid, lds, s);
-  return launch_fold<false>(g, p.M, cfg.rows, cfg.waves, grid, lds, s);
+  return launch_gemv(&p, &cfg, 1, s);
 }
 
 }  // namespace sg

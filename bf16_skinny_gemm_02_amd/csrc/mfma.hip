@@ -63,6 +63,30 @@ struct MfmaArgs {
   int sps;  // k-steps (32 k) per split
 };
 
+// One launch covers one or two segments: independent problems whose
+// workgroups share a flat grid, segment 1's after segment 0's.  Within a
+// segment, workgroup `local` takes tile local % tiles of K-range
+// local / tiles.
+struct MfmaSeg {
+  MfmaArgs g;
+  int tiles;
+  int wg_begin;  // first workgroup of the segment (INT_MAX: unused)
+};
+struct MfmaLaunch {
+  MfmaSeg seg[2];
+};
+
+// The segment's arguments are copied into registers once (uniform values in
+// SGPRs), so nothing re-reads the kernel arguments inside the loops.
+__device__ __forceinline__ MfmaArgs pick_segment(const MfmaLaunch& L, int& tile, int& split) {
+  const int b = static_cast<int>(blockIdx.x);
+  const MfmaSeg sg = (b >= L.seg[1].wg_begin) ? L.seg[1] : L.seg[0];
+  const int local = b - sg.wg_begin;
+  split = local / sg.tiles;
+  tile = local - split * sg.tiles;
+  return sg.g;
+}
+
 constexpr int kKStep = 32;       // k per MFMA
 constexpr int kChunkSteps = 4;   // k-steps per LDS ring chunk
 constexpr int kPieces = 16;      // 16-byte pieces of a row per chunk (256 bytes)
@@ -98,8 +122,10 @@ __device__ __forceinline__ void store4(const MfmaArgs& g, const f32x4& acc, int 
 // blocks per workgroup; C: ring slots; XQ: activation rows copied per chunk,
 // in groups of 4 (XQ*4 >= M).
 template <int MB, int NW, int C, int XQ>
-__global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaArgs g) {
+__global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaLaunch L) {
   extern __shared__ u32x4 lds[];
+  int tile, split;
+  const MfmaArgs g = pick_segment(L, tile, split);
   constexpr int WROWS = 16 * NW;
   constexpr int XROWS = 4 * XQ;
   constexpr int SLOT = (WROWS + XROWS) * kPieces;
@@ -115,12 +141,12 @@ __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaArgs g) {
   const int kg = lane >> 4;
   const int K8 = g.K >> 3;
   const int KS = (g.K + kKStep - 1) / kKStep;
-  const int s_begin = static_cast<int>(blockIdx.y) * g.sps;
+  const int s_begin = split * g.sps;
   const int nk = max(0, min(KS, s_begin + g.sps) - s_begin);
   const int npieces = nk * 4;
   const int nch = (nk + kChunkSteps - 1) / kChunkSteps;
   const int c0 = s_begin * 4;
-  const int tile_row0 = static_cast<int>(blockIdx.x) * WROWS;
+  const int tile_row0 = tile * WROWS;
   const int tile_rows = min(WROWS, g.N - tile_row0);
 
   const rsrc_t wres = make_rsrc(g.w + static_cast<int64_t>(tile_row0) * g.ldw,
@@ -190,7 +216,7 @@ __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaArgs g) {
 
   const int n0 = tile_row0 + 16 * wave + 4 * kg;
 #pragma unroll
-  for (int a = 0; a < MB; ++a) store4(g, acc[a], 16 * a + rl, n0, static_cast<int>(blockIdx.y));
+  for (int a = 0; a < MB; ++a) store4(g, acc[a], 16 * a + rl, n0, split);
 }
 
 // ---- wave-split LDS tile (M <= 16) ------------------------------------------------
@@ -198,8 +224,10 @@ __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaArgs g) {
 constexpr int kSplitWaves = 4;
 
 template <int XQ, int C>
-__global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaArgs g) {
+__global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch L) {
   extern __shared__ u32x4 lds[];
+  int tile, split;
+  const MfmaArgs g = pick_segment(L, tile, split);
   constexpr int XROWS = 4 * XQ;
   constexpr int SLOT = (16 + XROWS) * kPieces;
   constexpr int P = 4 + XQ;
@@ -212,7 +240,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaArgs g)
   const int kg = lane >> 4;
   const int K8 = g.K >> 3;
   const int KS = (g.K + kKStep - 1) / kKStep;
-  const int s_begin = static_cast<int>(blockIdx.y) * g.sps;
+  const int s_begin = split * g.sps;
   const int len = max(0, min(KS, s_begin + g.sps) - s_begin);
   const int per = (len + kSplitWaves - 1) / kSplitWaves;
   const int w_begin = s_begin + wave * per;
@@ -220,7 +248,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaArgs g)
   const int npieces = nk * 4;
   const int nch = (nk + kChunkSteps - 1) / kChunkSteps;
   const int c0 = w_begin * 4;
-  const int row0 = static_cast<int>(blockIdx.x) * 16;
+  const int row0 = tile * 16;
   const int rows = min(16, g.N - row0);
   u32x4* ring = lds + wave * C * SLOT;
 
@@ -284,7 +312,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaArgs g)
   for (int w = 0; w < kSplitWaves - 1; ++w)
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[v] += red[(w * 4 + v) * kWave + lane];
-  store4(g, acc, rl, row0 + 4 * kg, static_cast<int>(blockIdx.y));
+  store4(g, acc, rl, row0 + 4 * kg, split);
 }
 
 // ---- register-fragment kernel (M > 64) ------------------------------------------
@@ -292,18 +320,20 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaArgs g)
 constexpr int kDirectWaves = 4;
 
 template <int MB, int D, int NKT>
-__global__ __launch_bounds__(kDirectWaves * kWave) void direct_kernel(MfmaArgs g) {
+__global__ __launch_bounds__(kDirectWaves * kWave) void direct_kernel(MfmaLaunch L) {
   constexpr int kRegs = MB * 4;
+  int tile, split;
+  const MfmaArgs g = pick_segment(L, tile, split);
   __shared__ float red[(kDirectWaves - 1) * kRegs * kWave];
 
   const int lane = lane_id();
   const int wave = wave_id();
   const int rl = lane & 15;
   const int kg = lane >> 4;
-  const int n_base = static_cast<int>(blockIdx.x) * 16;
+  const int n_base = tile * 16;
   const int K8 = g.K >> 3;
   const int KS = (g.K + kKStep - 1) / kKStep;
-  const int s_begin = static_cast<int>(blockIdx.y) * g.sps;
+  const int s_begin = split * g.sps;
   const int s_end = min(KS, s_begin + g.sps);
   const int len = max(0, s_end - s_begin);
   const int per = (len + kDirectWaves - 1) / kDirectWaves;
@@ -388,7 +418,7 @@ __global__ __launch_bounds__(kDirectWaves * kWave) void direct_kernel(MfmaArgs g
       for (int v = 0; v < 4; ++v) acc[a][v] += src[(a * 4 + v) * kWave + lane];
   }
 #pragma unroll
-  for (int a = 0; a < MB; ++a) store4(g, acc[a], 16 * a + rl, n_base + 4 * kg, static_cast<int>(blockIdx.y));
+  for (int a = 0; a < MB; ++a) store4(g, acc[a], 16 * a + rl, n_base + 4 * kg, split);
 }
 
 // ---- launchers -------------------------------------------------------------------
@@ -396,38 +426,45 @@ __global__ __launch_bounds__(kDirectWaves * kWave) void direct_kernel(MfmaArgs g
 // One attribute call per kernel instance (the ring can exceed the default
 // 64 KiB of dynamic LDS).
 template <int MB, int NW, int C, int XQ>
-hipError_t launch_tile_inst(const MfmaArgs& g, dim3 grid, hipStream_t s) {
+hipError_t launch_tile_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
   auto kern = tile_kernel<MB, NW, C, XQ>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       static_cast<int>(kMfmaMaxLds));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, grid, dim3(NW * kWave), tile_lds_bytes(NW, C, XQ), s, g);
+  hipLaunchKernelGGL(kern, dim3(wgs), dim3(NW * kWave), tile_lds_bytes(NW, C, XQ), s, L);
   return hipGetLastError();
 }
 
 template <int XQ, int C>
-hipError_t launch_wsplit_inst(const MfmaArgs& g, dim3 grid, hipStream_t s) {
+hipError_t launch_wsplit_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
   auto kern = wsplit_kernel<XQ, C>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       static_cast<int>(kMfmaMaxLds));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, grid, dim3(kSplitWaves * kWave), wsplit_lds_bytes(C, XQ), s, g);
+  hipLaunchKernelGGL(kern, dim3(wgs), dim3(kSplitWaves * kWave), wsplit_lds_bytes(C, XQ), s, L);
   return hipGetLastError();
 }
 
 template <int MB>
-hipError_t launch_direct_mb(const MfmaArgs& g, int per_wave, dim3 grid, hipStream_t s) {
+hipError_t launch_direct_mb(const MfmaLaunch& L, int per_wave, int wgs, hipStream_t s) {
   constexpr int D = MB <= 8 ? 4 : 2;
   const dim3 block(kDirectWaves * kWave);
   if (per_wave > 16 && per_wave <= 56)
-    hipLaunchKernelGGL((direct_kernel<MB, D, 56>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((direct_kernel<MB, D, 56>), dim3(wgs), block, 0, s, L);
   else if (per_wave <= 16)
-    hipLaunchKernelGGL((direct_kernel<MB, D, 16>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((direct_kernel<MB, D, 16>), dim3(wgs), block, 0, s, L);
   else
-    hipLaunchKernelGGL((direct_kernel<MB, D, 0>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((direct_kernel<MB, D, 0>), dim3(wgs), block, 0, s, L);
   return hipGetLastError();
+}
+
+int ksteps_of(int K) { return (K + kKStep - 1) / kKStep; }
+
+// Weight rows one workgroup of this configuration covers.
+int rows_per_wg(const sg_config_t& c) {
+  return c.kind == SG_KIND_MFMA_TILE ? c.rows : 16;
 }
 
 }  // namespace
@@ -440,48 +477,75 @@ size_t wsplit_lds_bytes(int c, int xq) {
   return static_cast<size_t>(kSplitWaves) * c * (16 + 4 * xq) * kPieces * 16;
 }
 
-hipError_t launch_mfma(const DotProblem& p, const sg_config_t& cfg, hipStream_t s) {
-  MfmaArgs g;
-  g.a = p.a;
-  g.lda = p.lda;
-  g.w = p.w;
-  g.ldw = p.ldw;
-  g.res = p.res;
-  g.ldr = p.ldr;
-  g.out = p.out;
-  g.ldc = p.ldc;
-  g.partial = p.partial;
-  g.out2 = p.out2;
-  g.ldc2 = p.ldc2;
-  g.n_split = p.n_split;
-  g.M = p.M;
-  g.N = p.N;
-  g.K = p.K;
-  const int KS = (p.K + kKStep - 1) / kKStep;
-  const int S = cfg.k_split > 0 ? cfg.k_split : 1;
-  g.sps = (KS + S - 1) / S;
-  if (g.sps < 1) g.sps = 1;
-  if (p.M > cfg.m_tile || cfg.m_tile <= 0) return hipErrorInvalidValue;
+bool mfma_same_instance(const sg_config_t& a, const sg_config_t& b) {
+  return a.kind == b.kind && a.m_tile == b.m_tile && a.rows == b.rows && a.waves == b.waves &&
+         a.k_unroll == b.k_unroll;
+}
+
+hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg, hipStream_t s) {
+  if (nseg < 1 || nseg > 2) return hipErrorInvalidValue;
+  const sg_config_t& cfg = cfgs[0];
+  if (nseg == 2 && !mfma_same_instance(cfgs[0], cfgs[1])) return hipErrorInvalidValue;
+  MfmaLaunch L;
+  int wgs = 0;
+  int max_sps = 0;
+  for (int i = 0; i < 2; ++i) {
+    MfmaSeg& sgm = L.seg[i];
+    if (i >= nseg) {
+      sgm = L.seg[0];
+      sgm.wg_begin = INT32_MAX;
+      continue;
+    }
+    const DotProblem& p = segs[i];
+    const sg_config_t& c = cfgs[i];
+    if (p.M > c.m_tile || c.m_tile <= 0) return hipErrorInvalidValue;
+    MfmaArgs& g = sgm.g;
+    g.a = p.a;
+    g.lda = p.lda;
+    g.w = p.w;
+    g.ldw = p.ldw;
+    g.res = p.res;
+    g.ldr = p.ldr;
+    g.out = p.out;
+    g.ldc = p.ldc;
+    g.partial = p.partial;
+    g.out2 = p.out2;
+    g.ldc2 = p.ldc2;
+    g.n_split = p.n_split;
+    g.M = p.M;
+    g.N = p.N;
+    g.K = p.K;
+    const int KS = ksteps_of(p.K);
+    const int S = c.k_split > 0 ? c.k_split : 1;
+    g.sps = (KS + S - 1) / S;
+    if (g.sps < 1) g.sps = 1;
+    if (g.sps > max_sps) max_sps = g.sps;
+    const int rows = rows_per_wg(c);
+    sgm.tiles = (p.N + rows - 1) / rows;
+    sgm.wg_begin = wgs;
+    if (sgm.tiles <= 0) return hipErrorInvalidValue;
+    wgs += sgm.tiles * S;
+  }
+  if (wgs <= 0) return hipSuccess;
 
   if (cfg.kind == SG_KIND_MFMA_TILE) {
     const int NW = cfg.waves, C = cfg.k_unroll, XQ = cfg.m_tile / 4;
     if (cfg.rows != 16 * NW || (cfg.m_tile % 4) != 0) return hipErrorInvalidValue;
-    const dim3 grid((p.N + cfg.rows - 1) / cfg.rows, S);
     // The instances the configuration table uses.
     if (NW == 2 && C == 4) {
       switch (XQ) {
-        case 1: return launch_tile_inst<1, 2, 4, 1>(g, grid, s);
-        case 2: return launch_tile_inst<1, 2, 4, 2>(g, grid, s);
-        case 3: return launch_tile_inst<1, 2, 4, 3>(g, grid, s);
-        case 4: return launch_tile_inst<1, 2, 4, 4>(g, grid, s);
+        case 1: return launch_tile_inst<1, 2, 4, 1>(L, wgs, s);
+        case 2: return launch_tile_inst<1, 2, 4, 2>(L, wgs, s);
+        case 3: return launch_tile_inst<1, 2, 4, 3>(L, wgs, s);
+        case 4: return launch_tile_inst<1, 2, 4, 4>(L, wgs, s);
         default: break;
       }
     }
     if (NW == 4 && C == 3) {
       switch (XQ) {
-        case 8: return launch_tile_inst<2, 4, 3, 8>(g, grid, s);
-        case 12: return launch_tile_inst<3, 4, 3, 12>(g, grid, s);
-        case 16: return launch_tile_inst<4, 4, 3, 16>(g, grid, s);
+        case 8: return launch_tile_inst<2, 4, 3, 8>(L, wgs, s);
+        case 12: return launch_tile_inst<3, 4, 3, 12>(L, wgs, s);
+        case 16: return launch_tile_inst<4, 4, 3, 16>(L, wgs, s);
         default: break;
       }
     }
@@ -491,23 +555,22 @@ hipError_t launch_mfma(const DotProblem& p, const sg_config_t& cfg, hipStream_t 
     const int C = cfg.k_unroll, XQ = cfg.m_tile / 4;
     if (cfg.rows != 16 || cfg.waves != kSplitWaves || (cfg.m_tile % 4) != 0 || C != 4)
       return hipErrorInvalidValue;
-    const dim3 grid((p.N + 15) / 16, S);
     switch (XQ) {
-      case 1: return launch_wsplit_inst<1, 4>(g, grid, s);
-      case 2: return launch_wsplit_inst<2, 4>(g, grid, s);
-      case 3: return launch_wsplit_inst<3, 4>(g, grid, s);
-      case 4: return launch_wsplit_inst<4, 4>(g, grid, s);
+      case 1: return launch_wsplit_inst<1, 4>(L, wgs, s);
+      case 2: return launch_wsplit_inst<2, 4>(L, wgs, s);
+      case 3: return launch_wsplit_inst<3, 4>(L, wgs, s);
+      case 4: return launch_wsplit_inst<4, 4>(L, wgs, s);
       default: return hipErrorInvalidValue;
     }
   }
   if (cfg.kind == SG_KIND_MFMA_DIRECT) {
     const int MB = cfg.m_tile / 16;
     if (cfg.rows != 1 || (cfg.m_tile % 16) != 0) return hipErrorInvalidValue;
-    const dim3 grid((p.N + 15) / 16, S);
-    const int per_wave = (g.sps + kDirectWaves - 1) / kDirectWaves;
+    // The straight-line instance must cover every segment's per-wave steps.
+    const int per_wave = (max_sps + kDirectWaves - 1) / kDirectWaves;
     switch (MB) {
 #define SG_CASE(mb) \
-  case mb: return launch_direct_mb<mb>(g, per_wave, grid, s);
+  case mb: return launch_direct_mb<mb>(L, per_wave, wgs, s);
       SG_CASE(5) SG_CASE(6) SG_CASE(7) SG_CASE(8) SG_CASE(9) SG_CASE(10) SG_CASE(11) SG_CASE(12)
       SG_CASE(13) SG_CASE(14) SG_CASE(15) SG_CASE(16)
 #undef SG_CASE
@@ -515,6 +578,10 @@ hipError_t launch_mfma(const DotProblem& p, const sg_config_t& cfg, hipStream_t 
     }
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_mfma(const DotProblem& p, const sg_config_t& cfg, hipStream_t s) {
+  return launch_mfma(&p, &cfg, 1, s);
 }
 
 }  // namespace sg

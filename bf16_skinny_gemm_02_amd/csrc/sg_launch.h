@@ -48,6 +48,16 @@ hipError_t launch_gemv(const DotProblem& p, const sg_config_t& cfg, hipStream_t 
 hipError_t launch_smallk(const DotProblem& p, const sg_config_t& cfg, hipStream_t s);
 hipError_t launch_mfma(const DotProblem& p, const sg_config_t& cfg, hipStream_t s);
 
+// Segmented launches: nseg (1 or 2) independent problems in one grid, each
+// with its own configuration (k_split, grid); both must name the same kernel
+// instance (*_same_instance), which lets two shapes that would each leave the
+// chip partly idle, or spill a few workgroups into a second wave, run as one
+// wave of work.
+bool gemv_same_instance(const sg_config_t& a, const sg_config_t& b);
+bool mfma_same_instance(const sg_config_t& a, const sg_config_t& b);
+hipError_t launch_gemv(const DotProblem* segs, const sg_config_t* cfgs, int nseg, hipStream_t s);
+hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg, hipStream_t s);
+
 // LDS of the MFMA ring kernels: the shared-activation tile (nw waves, c ring
 // slots, 4*xq activation rows) and the wave-split tile (4 private rings).
 // The configuration table keeps both within kMfmaMaxLds.
@@ -83,6 +93,9 @@ struct FbProblem {
   uint16_t* f_a;            // [M, rank], nullable
   uint16_t* beta;           // [M, n_ab - rank]
   uint16_t* g1;             // [M, n_b]
+  // Optional: a split-K reduction run by extra workgroups of the same
+  // launch (the Q/K/V/G partials of the packed projection).
+  const ReduceProblem* red;
 };
 hipError_t launch_fab_fb_tail(const FbProblem& p, hipStream_t s);
 

@@ -84,79 +84,23 @@ struct FbArgs {
 };
 
 // Sum of the S split-K partials p[0], p[plane], ..., in the fixed order
-// s = 0, 1, ..., S-1 (eight independent loads in flight at a time).
+// s = 0, 1, ..., S-1.  Loads go out kSumBatch at a time, so a sum over S
+// partials costs ceil(S / kSumBatch) memory round trips, not S.
+constexpr int kSumBatch = 16;
+
 __device__ __forceinline__ float sum_splits(const float* p, int64_t plane, int S) {
   float acc = 0.f;
-  int s = 0;
-  for (; s + 8 <= S; s += 8) {
-    float v[8];
+  for (int s = 0; s < S; s += kSumBatch) {
+    float v[kSumBatch];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = p[(s + i) * plane];
+    for (int i = 0; i < kSumBatch; ++i) v[i] = (s + i < S) ? p[(s + i) * plane] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc += v[i];
+    for (int i = 0; i < kSumBatch; ++i)
+      if (s + i < S) acc += v[i];
   }
-  for (; s < S; ++s) acc += p[s * plane];
   return acc;
 }
 
-// Rows of w_b one F_B workgroup covers: one row per group of G lanes, every
-// lane of the workgroup busy, a single pass.
-template <int G>
-constexpr int fb_rows_per_wg() { return kSmallkWaves * (kWave / G); }
-
-// Workgroup (x, y) computes g1 rows [x*R, (x+1)*R), R = fb_rows_per_wg<G>(),
-// for activation rows [y*kFbMGroup, (y+1)*kFbMGroup).  Its w_b chunk is
-// requested first, so that load overlaps forming P: the rows' bf16 P (the
-// F_A/beta partials summed in fixed order when PARTIALS, so every workgroup
-// agrees bit for bit, else the bf16 P as stored); f_a goes to LDS, and
-// workgroups with x == 0 also store beta (and f_a).
-template <int G, bool PARTIALS>
-__global__ __launch_bounds__(kSmallkWaves * kWave) void fab_fb_tail_kernel(FbArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t fa_lds[kFbMGroup * kFbMaxRank];
-  const int tid = static_cast<int>(threadIdx.x);
-  const int nthreads = kSmallkWaves * kWave;
-  const int64_t plane = static_cast<int64_t>(g.M) * g.n_ab;
-  const int m0 = static_cast<int>(blockIdx.y) * kFbMGroup;
-  const int mg = min(kFbMGroup, g.M - m0);
-  const bool first = blockIdx.x == 0;
-
-  const int lane = lane_id();
-  const int j = lane & (G - 1);
-  const int K8 = g.rank >> 3;
-  const bool cvalid = j < K8;
-  const int i = static_cast<int>(blockIdx.x) * fb_rows_per_wg<G>() + wave_id() * (kWave / G) + lane / G;
-  const bool ivalid = i < g.n_b;
-  const u32x4 wv =
-      (ivalid && cvalid) ? load_nt(g.w_b + static_cast<int64_t>(i) * g.rank + j * 8) : zero4();
-
-  // 1. P = bf16(sum_s partial[s][m][j]) for this workgroup's rows; all n_ab
-  //    columns in the first column of workgroups, the rank f_a columns elsewhere.
-  const int cols = first ? g.n_ab : g.rank;
-  for (int idx = tid; idx < mg * cols; idx += nthreads) {
-    const int mm = idx / cols, jj = idx - mm * cols;
-    const int m = m0 + mm;
-    uint16_t b;
-    if constexpr (PARTIALS)
-      b = f32_to_bf16(sum_splits(g.partial + static_cast<int64_t>(m) * g.n_ab + jj, plane, g.S));
-    else
-      b = g.p_bf16[static_cast<int64_t>(m) * g.n_ab + jj];
-    if (jj < g.rank) {
-      fa_lds[mm * g.rank + jj] = b;
-      if (first && g.f_a != nullptr) g.f_a[static_cast<int64_t>(m) * g.rank + jj] = b;
-    } else {
-      g.beta[static_cast<int64_t>(m) * (g.n_ab - g.rank) + (jj - g.rank)] = b;
-    }
-  }
-  __syncthreads();
-
-  // 2. g1[m, i] = bf16(sum_r f_a[m, r] * w_b[i, r]): the weight chunk is used
-  //    for every activation row of the group.
-  for (int mm = 0; mm < mg; ++mm) {
-    const u32x4 xv = cvalid ? *reinterpret_cast<const u32x4*>(fa_lds + mm * g.rank + j * 8) : zero4();
-    const float v = group_sum<G>(dot8(xv, wv, 0.f));
-    if (ivalid && j == 0) g.g1[static_cast<int64_t>(m0 + mm) * g.n_b + i] = f32_to_bf16(v);
-  }
-}
 
 struct ReduceArgs {
   const float* partial;
@@ -174,9 +118,9 @@ struct ReduceArgs {
 // residual is requested before the partial sums so the two loads overlap;
 // the S partials are summed in the fixed order s = 0..S-1.
 template <bool VEC>
-__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs g) {
+__device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
   const int64_t total = static_cast<int64_t>(g.M) * g.N;
-  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  const int64_t e0 = (static_cast<int64_t>(block) * 256 + threadIdx.x) * 4;
   if (e0 >= total) return;
   int mm[4], nn[4];
   float r[4] = {0.f, 0.f, 0.f, 0.f};
@@ -220,6 +164,106 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs g) {
       g.out2[mm[v] * g.ldc2 + (nn[v] - g.n_split)] = f32_to_bf16(val);
     else
       g.out[mm[v] * g.ldc + nn[v]] = f32_to_bf16(val);
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs g) {
+  reduce_block<VEC>(g, static_cast<int>(blockIdx.x));
+}
+
+// Rows of w_b one F_B workgroup covers: one row per group of G lanes, every
+// lane of the workgroup busy, a single pass.
+template <int G>
+constexpr int fb_rows_per_wg() { return kSmallkWaves * (kWave / G); }
+
+// P elements one F_B thread forms per pass (4 rows x 136 columns = 544 fit in
+// one pass of 256 threads x 3).
+constexpr int kFbPer = 3;
+
+// Workgroup (x, y) computes g1 rows [x*R, (x+1)*R), R = fb_rows_per_wg<G>(),
+// for activation rows [y*kFbMGroup, (y+1)*kFbMGroup).  Its w_b chunk is
+// requested first, so that load overlaps forming P: the rows' bf16 P (the
+// F_A/beta partials summed in fixed order when PARTIALS, so every workgroup
+// agrees bit for bit, else the bf16 P as stored); f_a goes to LDS, and
+// workgroups with x == 0 also store beta (and f_a).
+//
+// RED (0 none, 1 vector, 2 scalar): the first red_wgs workgroups instead run
+// the split-K reduction of another problem (the Q/K/V/G projection that ran
+// beside F_A/beta), so both epilogues take one launch.
+template <int G, bool PARTIALS, int RED>
+__global__ __launch_bounds__(kSmallkWaves * kWave) void fab_fb_tail_kernel(FbArgs g, ReduceArgs red,
+                                                                           int red_wgs, int fbx) {
+  __shared__ __attribute__((aligned(16))) uint16_t fa_lds[kFbMGroup * kFbMaxRank];
+  int b = static_cast<int>(blockIdx.x);
+  if constexpr (RED != 0) {
+    if (b < red_wgs) {
+      reduce_block<RED == 1>(red, b);
+      return;
+    }
+    b -= red_wgs;
+  }
+  const int bx = b % fbx;
+  const int by = b / fbx;
+  const int tid = static_cast<int>(threadIdx.x);
+  const int nthreads = kSmallkWaves * kWave;
+  const int64_t plane = static_cast<int64_t>(g.M) * g.n_ab;
+  const int m0 = by * kFbMGroup;
+  const int mg = min(kFbMGroup, g.M - m0);
+  const bool first = bx == 0;
+
+  const int lane = lane_id();
+  const int j = lane & (G - 1);
+  const int K8 = g.rank >> 3;
+  const bool cvalid = j < K8;
+  const int i = bx * fb_rows_per_wg<G>() + wave_id() * (kWave / G) + lane / G;
+  const bool ivalid = i < g.n_b;
+  const u32x4 wv =
+      (ivalid && cvalid) ? load_nt(g.w_b + static_cast<int64_t>(i) * g.rank + j * 8) : zero4();
+
+  // 1. P = bf16(sum_s partial[s][m][j]) for this workgroup's rows; all n_ab
+  //    columns in the first column of workgroups, the rank f_a columns
+  //    elsewhere.  kFbPer elements per thread per pass, their loads issued
+  //    together.
+  const int cols = first ? g.n_ab : g.rank;
+  const int count = mg * cols;
+  for (int base = 0; base < count; base += kFbPer * nthreads) {
+    uint16_t b[kFbPer];
+#pragma unroll
+    for (int e = 0; e < kFbPer; ++e) {
+      const int idx = base + e * nthreads + tid;
+      b[e] = 0;
+      if (idx < count) {
+        const int mm = idx / cols, jj = idx - mm * cols;
+        const int64_t off = static_cast<int64_t>(m0 + mm) * g.n_ab + jj;
+        if constexpr (PARTIALS)
+          b[e] = f32_to_bf16(sum_splits(g.partial + off, plane, g.S));
+        else
+          b[e] = g.p_bf16[off];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kFbPer; ++e) {
+      const int idx = base + e * nthreads + tid;
+      if (idx >= count) continue;
+      const int mm = idx / cols, jj = idx - mm * cols;
+      const int m = m0 + mm;
+      if (jj < g.rank) {
+        fa_lds[mm * g.rank + jj] = b[e];
+        if (first && g.f_a != nullptr) g.f_a[static_cast<int64_t>(m) * g.rank + jj] = b[e];
+      } else {
+        g.beta[static_cast<int64_t>(m) * (g.n_ab - g.rank) + (jj - g.rank)] = b[e];
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. g1[m, i] = bf16(sum_r f_a[m, r] * w_b[i, r]): the weight chunk is used
+  //    for every activation row of the group.
+  for (int mm = 0; mm < mg; ++mm) {
+    const u32x4 xv = cvalid ? *reinterpret_cast<const u32x4*>(fa_lds + mm * g.rank + j * 8) : zero4();
+    const float v = group_sum<G>(dot8(xv, wv, 0.f));
+    if (ivalid && j == 0) g.g1[static_cast<int64_t>(m0 + mm) * g.n_b + i] = f32_to_bf16(v);
   }
 }
 
@@ -284,16 +328,40 @@ hipError_t launch_smallk_g(const SmallkArgs& g, hipStream_t s) {
 }
 
 template <int G>
-hipError_t launch_fb_g(const FbArgs& g, hipStream_t s) {
+hipError_t launch_fb_g(const FbArgs& g, const ReduceArgs& r, int red_wgs, int red_mode, hipStream_t s) {
   // At least one column of workgroups: it also stores beta and f_a.
   constexpr int R = fb_rows_per_wg<G>();
   const int bx = (g.n_b + R - 1) / R;
-  const dim3 grid(bx > 0 ? bx : 1, (g.M + kFbMGroup - 1) / kFbMGroup);
-  if (g.partial != nullptr)
-    hipLaunchKernelGGL((fab_fb_tail_kernel<G, true>), grid, dim3(kSmallkWaves * kWave), 0, s, g);
-  else
-    hipLaunchKernelGGL((fab_fb_tail_kernel<G, false>), grid, dim3(kSmallkWaves * kWave), 0, s, g);
+  const int fbx = bx > 0 ? bx : 1;
+  const int fby = (g.M + kFbMGroup - 1) / kFbMGroup;
+  const dim3 grid(red_wgs + fbx * fby);
+  const dim3 block(kSmallkWaves * kWave);
+#define SG_FB(P, RM) hipLaunchKernelGGL((fab_fb_tail_kernel<G, P, RM>), grid, block, 0, s, g, r, red_wgs, fbx)
+  if (g.partial != nullptr) {
+    if (red_mode == 1) SG_FB(true, 1);
+    else if (red_mode == 2) SG_FB(true, 2);
+    else SG_FB(true, 0);
+  } else {
+    if (red_mode == 1) SG_FB(false, 1);
+    else if (red_mode == 2) SG_FB(false, 2);
+    else SG_FB(false, 0);
+  }
+#undef SG_FB
   return hipGetLastError();
+}
+
+int reduce_blocks(const ReduceProblem& p) {
+  const int64_t total = static_cast<int64_t>(p.M) * p.N;
+  return static_cast<int>((total + 1023) / 1024);
+}
+
+bool reduce_vec(const ReduceProblem& p) {
+  const int64_t total = static_cast<int64_t>(p.M) * p.N;
+  return (total % 4) == 0 && (reinterpret_cast<uintptr_t>(p.partial) & 15u) == 0;
+}
+
+ReduceArgs reduce_args(const ReduceProblem& p) {
+  return ReduceArgs{p.partial, p.S, p.M, p.N, p.res, p.ldr, p.out, p.ldc, p.out2, p.ldc2, p.n_split};
 }
 
 }  // namespace
@@ -315,25 +383,30 @@ hipError_t launch_smallk(const DotProblem& p, const sg_config_t& cfg, hipStream_
 
 hipError_t launch_fab_fb_tail(const FbProblem& p, hipStream_t s) {
   FbArgs g{p.partial, p.p_bf16, p.S, p.M, p.n_ab, p.rank, p.n_b, p.w_b, p.f_a, p.beta, p.g1};
+  ReduceArgs r{};
+  int red_wgs = 0, red_mode = 0;
+  if (p.red != nullptr && reduce_blocks(*p.red) > 0) {
+    r = reduce_args(*p.red);
+    red_wgs = reduce_blocks(*p.red);
+    red_mode = reduce_vec(*p.red) ? 1 : 2;
+  }
   switch (lanes_for(p.rank >> 3)) {
-    case 1: return launch_fb_g<1>(g, s);
-    case 2: return launch_fb_g<2>(g, s);
-    case 4: return launch_fb_g<4>(g, s);
-    case 8: return launch_fb_g<8>(g, s);
-    case 16: return launch_fb_g<16>(g, s);
-    case 32: return launch_fb_g<32>(g, s);
-    case 64: return launch_fb_g<64>(g, s);
+    case 1: return launch_fb_g<1>(g, r, red_wgs, red_mode, s);
+    case 2: return launch_fb_g<2>(g, r, red_wgs, red_mode, s);
+    case 4: return launch_fb_g<4>(g, r, red_wgs, red_mode, s);
+    case 8: return launch_fb_g<8>(g, r, red_wgs, red_mode, s);
+    case 16: return launch_fb_g<16>(g, r, red_wgs, red_mode, s);
+    case 32: return launch_fb_g<32>(g, r, red_wgs, red_mode, s);
+    case 64: return launch_fb_g<64>(g, r, red_wgs, red_mode, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_reduce(const ReduceProblem& p, hipStream_t s) {
-  ReduceArgs g{p.partial, p.S, p.M, p.N, p.res, p.ldr, p.out, p.ldc, p.out2, p.ldc2, p.n_split};
-  const int64_t total = static_cast<int64_t>(p.M) * p.N;
-  const int64_t blocks = (total + 1023) / 1024;
+  const int blocks = reduce_blocks(p);
   if (blocks < 1) return hipSuccess;
-  const bool vec = (total % 4) == 0 && (reinterpret_cast<uintptr_t>(p.partial) & 15u) == 0;
-  if (vec)
+  const ReduceArgs g = reduce_args(p);
+  if (reduce_vec(p))
     hipLaunchKernelGGL(reduce_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, g);
   else
     hipLaunchKernelGGL(reduce_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, g);

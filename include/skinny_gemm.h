@@ -133,7 +133,9 @@ int sg_select(int M, int N, int K, int has_residual, sg_config_t *out);
 int sg_overlap_gate(int M, int x_contiguous, int have_aux_stream, int have_events, int enabled);
 
 /* The largest M for which sg_overlap_gate() opens (the analogue of
- * KDA_PROJECTION_OVERLAP_MAX_TOKENS [P3 low_latency_gemm.py]). */
+ * KDA_PROJECTION_OVERLAP_MAX_TOKENS [P3 low_latency_gemm.py]).  Set from
+ * measurement on MI355X: 0, the single-stream schedule was faster at every
+ * M tried (1..64), so the gate stays closed. */
 int sg_overlap_max_tokens(void);
 
 /* Bytes of device workspace the operation needs at this shape (0 if none).
@@ -142,9 +144,9 @@ int sg_overlap_max_tokens(void);
 size_t sg_workspace_bytes(int op, int M, int N, int K);
 
 /* Bytes of device workspace kda_projection_overlap needs: which = 0 for
- * ws_main (split-K partials of the packed projection [k_split][M][n_qkvg +
- * n_ab] fp32, 0 when unsplit), 1 for ws_aux (the bf16 F_A/beta projection
- * [M, n_ab] plus its split-K partials). */
+ * ws_main (the Q/K/V/G split-K partials, sg_workspace_bytes(SG_OP_GEMM, M,
+ * n_qkvg, K), 0 when unsplit), 1 for ws_aux (the F_A/beta partials,
+ * sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K)). */
 size_t sg_kda_workspace_bytes(int which, int M, int K, int n_qkvg, int n_ab);
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -198,10 +200,12 @@ int kda_fab_fb_proj(const sg_bf16 *x, const sg_bf16 *w_ab, const sg_bf16 *w_b,
  * Fork: `fork` is recorded on main and waited on by aux; join: `join` is
  * recorded on aux and waited on by main, so every output is complete in
  * main's order once the call's work retires.  If aux, fork or join is NULL
- * the call runs on main alone: one packed GEMM over all n_qkvg + n_ab rows
- * (the reference's sequential path), then F_B.  Every row is computed with
- * the configuration sg_select gives the packed shape (M, n_qkvg + n_ab, K)
- * in both schedules, so the outputs are bitwise identical either way.
+ * the call runs on main alone (the reference's sequential path): the
+ * Q/K/V/G rows and the F_A/beta rows as two segments of one launch, then one
+ * launch for F_B (and the Q/K/V/G split-K reduction).  The Q/K/V/G rows use
+ * sg_select(M, n_qkvg, K) and the F_A/beta rows the configuration of
+ * kda_fab_fb_proj in both schedules, so the outputs are bitwise identical
+ * either way.
  * packed_w [n_qkvg + n_ab, K] contiguous; qkvg [M,n_qkvg]; beta
  * [M,n_ab-rank]; g1 [M,n_b]; w_b [n_b,rank]; 0 < rank < n_ab, rank % 8 == 0,
  * rank <= 512.  ws_main needs sg_kda_workspace_bytes(0, ...) bytes (often 0)

@@ -24,9 +24,9 @@ Rule, for C[M,N] = A[M,K] W[N,K]^T:
       - tiles16 <= 320: MFMA_WAVESPLIT, rows = 16, waves = 4, k_unroll = 4,
         k_split = msplit(tiles16, 16), grid = tiles16 * k_split.
       - else MFMA_TILE, rows = 32, waves = 2, k_unroll = 4,
-        tiles = ceil(N / 32), k_split = msplit(tiles, 4), grid = tiles * k_split.
+        tiles = ceil(N / 32), k_split = msplit(tiles, 8), grid = tiles * k_split.
   * 17 <= M <= 64: MFMA_TILE, m_tile = 16 * ceil(M / 16), rows = 64, waves = 4,
-    k_unroll = 3, tiles = ceil(N / 64), k_split = msplit(tiles, 4),
+    k_unroll = 3, tiles = ceil(N / 64), k_split = msplit(tiles, 8),
     grid = tiles * k_split.
   * 65 <= M <= 256: MFMA_DIRECT, m_tile = 16 * ceil(M / 16), rows = 1,
     k_unroll = 4 if m_tile <= 128 else 2, tiles = ceil(N / 16),
@@ -43,7 +43,7 @@ from __future__ import annotations
 
 OK, INVALID_ARG, UNSUPPORTED = 0, -1, -2
 NONE, GEMV_ROW, GEMV_SPLITK, GEMV_SMALLK, MFMA_TILE, MFMA_WAVESPLIT, MFMA_DIRECT = 0, 1, 2, 3, 4, 5, 6
-OVERLAP_MAX_TOKENS = 32
+OVERLAP_MAX_TOKENS = 0
 
 FIELDS = ("kind", "m_tile", "rows", "waves", "k_split", "k_unroll", "grid", "nt_weights")
 
@@ -105,12 +105,12 @@ def select(M: int, N: int, K: int, has_residual: bool = False):
                        grid=tiles16 * ks)
         else:
             tiles = _cdiv(N, 32)
-            ks = msplit(tiles, 4)
+            ks = msplit(tiles, 8)
             cfg.update(kind=MFMA_TILE, rows=32, waves=2, k_unroll=4, k_split=ks,
                        grid=tiles * ks)
     elif M <= 64:
         tiles = _cdiv(N, 64)
-        ks = msplit(tiles, 4)
+        ks = msplit(tiles, 8)
         cfg.update(kind=MFMA_TILE, m_tile=16 * _cdiv(M, 16), rows=64, waves=4, k_unroll=3,
                    k_split=ks, grid=tiles * ks)
     else:

@@ -149,7 +149,7 @@ def test_fab_fb_lattice_bitwise(device, M):
 
 # ---- the concurrent projection ------------------------------------------------------------
 
-@pytest.mark.parametrize("M", [1, 4, 16, 32])
+@pytest.mark.parametrize("M", [1, 4, 16, 32, 64])
 def test_overlap_matches_sequential_and_oracle(device, M):
     _say(f"kda_projection_overlap M={M}")
     x, packed, w_b = synth.overlap_inputs(M)
@@ -201,6 +201,23 @@ def test_overlap_graph_replay(device, M):
         for a, b in ((q, q_e), (g1, g1_e), (beta, b_e)):
             assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {rep}"
         del junk
+
+
+@pytest.mark.parametrize("M", [1, 3, 8, 16, 17, 64])
+def test_sequential_projection_equals_separate_calls(device, M):
+    """The sequential KDA projection (Q/K/V/G and F_A/beta as two segments of
+    one launch, then F_B with the Q/K/V/G split-K reduction) uses the same
+    per-row configurations as kda_qkvg_proj and kda_fab_fb_proj: bit for bit
+    the same outputs."""
+    _say(f"sequential projection vs separate calls M={M}")
+    x, packed, w_b = synth.overlap_inputs(M)
+    xd, pd, wbd = dev(x, device), dev(packed, device), dev(w_b, device)
+    q_s, g1_s, b_s = sg.kda_projection_overlap(xd, pd, wbd)
+    q = sg.kda_qkvg_proj(xd, pd[:4096])
+    g1, beta = sg.kda_fab_fb_proj(xd, pd[4096:], wbd)
+    torch.cuda.synchronize()
+    for a, b in ((q_s, q), (g1_s, g1), (b_s, beta)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 def test_packed_projection_equals_split(device):

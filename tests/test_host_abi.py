@@ -119,7 +119,10 @@ def test_kind_follows_m_boundaries():
 
 
 def test_overlap_gate_matches_oracle(lib):
-    assert lib.sg_overlap_max_tokens() == selection.OVERLAP_MAX_TOKENS
+    # Measured on MI355X: the two-stream schedule never won, so the gate is
+    # closed at every M (the setting, not the rule, is what is pinned here).
+    assert lib.sg_overlap_max_tokens() == selection.OVERLAP_MAX_TOKENS == 0
+    assert not any(lib.sg_overlap_gate(M, 1, 1, 1, 1) for M in range(0, 300))
     for M, c, a, e, en in itertools.product(range(-1, 70), (0, 1), (0, 1), (0, 1), (0, 1)):
         assert bool(lib.sg_overlap_gate(M, c, a, e, en)) == selection.overlap_gate(M, c, a, e, en)
 
