@@ -25,6 +25,7 @@ oracle timed on this host.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -163,16 +164,37 @@ def time_graph(g, stream, reps):
 
 # ---- dominant-kernel roofline leg ---------------------------------------------------
 
-def qkvg_kernel_leg(device, reps=200):
-    """Average duration of the Q/K/V/G GEMV at M = 1 (config: x[1,7168] x W[4096,7168]^T),
-    back-to-back launches on one stream cycling cold weight copies, timed with
-    HIP events recorded on that stream."""
-    x, w = synth.qkvg_inputs(1, seed=1000 * synth.WL_QKVG_GEMV + 1)
+ROOFLINE_M = 8   # the wave-split MFMA tile serves M = 2..16, five of the nine sweep points
+
+# HBM traffic of the roofline kernel from two rocprofv3 --pmc runs of `bench.py --counters`
+# (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 KiB per dispatch; factors from a 256 MiB device copy),
+# summarised with the commands in profiles/qkvg_wsplit_m8_pmc_traffic.md.  Valid only for the
+# kernel sources it was measured on: any change to them reports traffic as null until the
+# counters are taken again.
+TRAFFIC_SOURCES = ("bf16_skinny_gemm_02_amd/csrc/mfma.hip", "bf16_skinny_gemm_02_amd/csrc/sg_device.h",
+                   "bf16_skinny_gemm_02_amd/csrc/dispatch.cpp")
+TRAFFIC_PMC = {"sources_sha256": "c04138aa98dfea5d089968a9cae44a07ed6309af1a3d58ffbe3ef3d071253373",
+               "bytes_per_launch": 59781890}
+
+
+def measured_traffic():
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        h.update((ROOT / rel).read_bytes())
+    return TRAFFIC_PMC["bytes_per_launch"] if h.hexdigest() == TRAFFIC_PMC["sources_sha256"] else None
+
+
+def qkvg_kernel_leg(device, M, reps=200):
+    """Average duration of the Q/K/V/G projection kernel at batch M
+    (x[M,7168] x W[4096,7168]^T, one launch per call for M <= 16), back-to-back
+    launches on one stream cycling cold weight copies, timed with HIP events
+    recorded on that stream."""
+    x, w = synth.qkvg_inputs(M, seed=1000 * synth.WL_QKVG_SWEEP + M)
     R = copies_for(2 * N_QKVG * K)
     xd = bf16_dev(x, device)
     w0 = bf16_dev(w, device)
     ws = [w0] + [w0.clone() for _ in range(R - 1)]
-    out = torch.empty((1, N_QKVG), dtype=torch.bfloat16, device=device)
+    out = torch.empty((M, N_QKVG), dtype=torch.bfloat16, device=device)
     stream = torch.cuda.Stream(device)
     g = capture(lambda r: sg.kda_qkvg_proj(xd, ws[r], out=out), R, stream)
     for _ in range(5):
@@ -180,9 +202,41 @@ def qkvg_kernel_leg(device, reps=200):
     torch.cuda.synchronize()
     ms = time_graph(g, stream, reps)
     us = ms * 1000.0 / R
-    gbs = qkvg_bytes(1) / (us * 1e-6) / 1e9
-    return {"kernel": "gemv_kernel<M=1,R=1> (kda_qkvg_proj M=1)", "us_per_launch": us,
-            "launches_timed": reps * R, "gbs": gbs}
+    gbs = qkvg_bytes(M) / (us * 1e-6) / 1e9
+    cfg = sg.sg_select(M, N_QKVG, K)
+    kinds = {sg.SG_KIND_GEMV_ROW: "gemv_kernel", sg.SG_KIND_MFMA_WAVESPLIT: "wsplit_kernel",
+             sg.SG_KIND_MFMA_TILE: "tile_kernel", sg.SG_KIND_MFMA_DIRECT: "direct_kernel"}
+    name = f"{kinds.get(cfg['kind'], '?')} (kda_qkvg_proj M={M}, {cfg['grid']} workgroups)"
+    return {"kernel": name, "us_per_launch": us, "launches_timed": reps * R, "gbs": gbs,
+            "bytes": qkvg_bytes(M)}
+
+
+COPY_BYTES = 256 << 20   # calibration copy: reads and writes exactly this many bytes
+
+
+def counters_mode(device):
+    """One eager pass for the PMC runs: three device-to-device copies of
+    COPY_BYTES (their FETCH_SIZE / WRITE_SIZE per dispatch calibrate the
+    counters against known traffic), then the roofline kernel once per cold
+    weight copy, twice over."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=device)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    M = ROOFLINE_M
+    x, w = synth.qkvg_inputs(M, seed=1000 * synth.WL_QKVG_SWEEP + M)
+    R = copies_for(2 * N_QKVG * K)
+    xd = bf16_dev(x, device)
+    w0 = bf16_dev(w, device)
+    ws = [w0] + [w0.clone() for _ in range(R - 1)]
+    out = torch.empty((M, N_QKVG), dtype=torch.bfloat16, device=device)
+    for _ in range(2):
+        for r in range(R):
+            sg.kda_qkvg_proj(xd, ws[r], out=out)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "roofline_m": M, "launches": 2 * R,
+                      "algorithmic_bytes_per_launch": qkvg_bytes(M)}), flush=True)
 
 
 # ---- CPU baseline -------------------------------------------------------------------
@@ -223,8 +277,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--comparators", action="store_true",
-                    help="also time the sequential paths (S1: same kernels on one stream; "
-                         "S2: packed N=4232 GEMM then F_B)")
+                    help="also time the forced two-stream and one-stream schedules and a plain "
+                         "packed GEMM followed by F_B")
+    ap.add_argument("--counters", action="store_true",
+                    help="counter-collection mode for rocprofv3 --pmc: a plain device copy of "
+                         "known size (calibration), then the roofline kernel launched eagerly "
+                         "over its cold weight copies; prints the byte counts and exits")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the hot path has no cross-GPU step (each TP8 rank's "
@@ -235,6 +293,9 @@ def main():
         sys.exit(2)
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
+    if args.counters:
+        counters_mode(device)
+        return
     print(f"[bench] building cases for M in {M_SWEEP}", file=sys.stderr, flush=True)
 
     main_stream = torch.cuda.Stream(device)
@@ -328,11 +389,17 @@ def main():
             b["packed_gemm_then_fb_us"] = round(s2, 3)
             b["two_stream_speedup_vs_one_stream"] = round(one / two, 3)
 
-    leg = qkvg_kernel_leg(device)
+    leg = qkvg_kernel_leg(device, ROOFLINE_M)
     roofline = {"bound": "hbm", "achieved": round(leg["gbs"], 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(leg["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(leg["gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(),
                 "kernel": leg["kernel"], "us_per_launch": round(leg["us_per_launch"], 3),
-                "algorithmic_bytes_per_launch": qkvg_bytes(1)}
+                "algorithmic_bytes_per_launch": leg["bytes"]}
+    gemv = qkvg_kernel_leg(device, 1)
+    roofline["gemv_m1"] = {"kernel": gemv["kernel"], "us_per_launch": round(gemv["us_per_launch"], 3),
+                           "achieved": round(gemv["gbs"], 1),
+                           "frac": round(gemv["gbs"] / HBM_PEAK_GBS, 4),
+                           "algorithmic_bytes_per_launch": gemv["bytes"]}
 
     result = {
         "metric": METRIC,
