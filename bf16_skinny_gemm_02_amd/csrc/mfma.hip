@@ -96,8 +96,27 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// The residual values of the four outputs (m, n0 .. n0+3) a lane will store,
+// requested when the kernel starts so that the epilogue does not wait a
+// memory round trip for them (zeros when there is no residual or the kernel
+// stores split-K partials).
+struct Res4 {
+  uint16_t v[4];
+};
+
+__device__ __forceinline__ Res4 load_res4(const MfmaArgs& g, int m, int n0) {
+  Res4 r;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int n = n0 + v;
+    r.v[v] = (g.res != nullptr && g.partial == nullptr && m < g.M && n < g.N) ? g.res[m * g.ldr + n] : 0;
+  }
+  return r;
+}
+
 // Stores the four outputs (m, n0 .. n0+3) a lane holds.
-__device__ __forceinline__ void store4(const MfmaArgs& g, const f32x4& acc, int m, int n0, int split) {
+__device__ __forceinline__ void store4(const MfmaArgs& g, const f32x4& acc, int m, int n0, int split,
+                                       const Res4& res) {
   if (m >= g.M) return;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
@@ -107,7 +126,7 @@ __device__ __forceinline__ void store4(const MfmaArgs& g, const f32x4& acc, int 
       g.partial[(static_cast<int64_t>(split) * g.M + m) * g.N + n] = acc[v];
     } else {
       float val = acc[v];
-      if (g.res != nullptr) val += bf16_to_f32(g.res[m * g.ldr + n]);
+      if (g.res != nullptr) val += bf16_to_f32(res.v[v]);
       if (g.n_split > 0 && n >= g.n_split)
         g.out2[m * g.ldc2 + (n - g.n_split)] = f32_to_bf16(val);
       else
@@ -184,6 +203,11 @@ __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaLaunch L) {
 #pragma unroll
   for (int q = 0; q < C - 1; ++q) issue(q);
 
+  const int n0 = tile_row0 + 16 * wave + 4 * kg;
+  Res4 res[MB];
+#pragma unroll
+  for (int a = 0; a < MB; ++a) res[a] = load_res4(g, 16 * a + rl, n0);
+
   f32x4 acc[MB];
 #pragma unroll
   for (int a = 0; a < MB; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -214,9 +238,8 @@ __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaLaunch L) {
   }
   wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
 
-  const int n0 = tile_row0 + 16 * wave + 4 * kg;
 #pragma unroll
-  for (int a = 0; a < MB; ++a) store4(g, acc[a], 16 * a + rl, n0, split);
+  for (int a = 0; a < MB; ++a) store4(g, acc[a], 16 * a + rl, n0, split, res[a]);
 }
 
 // ---- wave-split LDS tile (M <= 16) ------------------------------------------------
@@ -282,6 +305,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
 #pragma unroll
   for (int q = 0; q < C - 1; ++q) issue(q);
 
+  const Res4 res = load_res4(g, rl, row0 + 4 * kg);
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   const int xr = rl < XROWS ? rl : XROWS - 1;
   for (int q = 0; q < nch; ++q) {
@@ -312,7 +336,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
   for (int w = 0; w < kSplitWaves - 1; ++w)
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[v] += red[(w * 4 + v) * kWave + lane];
-  store4(g, acc, rl, row0 + 4 * kg, split);
+  store4(g, acc, rl, row0 + 4 * kg, split, res);
 }
 
 // ---- register-fragment kernel (M > 64) ------------------------------------------
@@ -418,7 +442,7 @@ __global__ __launch_bounds__(kDirectWaves * kWave) void direct_kernel(MfmaLaunch
       for (int v = 0; v < 4; ++v) acc[a][v] += src[(a * 4 + v) * kWave + lane];
   }
 #pragma unroll
-  for (int a = 0; a < MB; ++a) store4(g, acc[a], 16 * a + rl, n_base + 4 * kg, split);
+  for (int a = 0; a < MB; ++a) store4(g, acc[a], 16 * a + rl, n_base + 4 * kg, split, load_res4(g, 16 * a + rl, n_base + 4 * kg));
 }
 
 // ---- launchers -------------------------------------------------------------------

@@ -236,7 +236,7 @@ def test_packed_projection_equals_split(device):
 
 # ---- latent-MoE tail ----------------------------------------------------------------------
 
-@pytest.mark.parametrize("M", [1, 8, 64, 256])
+@pytest.mark.parametrize("M", [1, 2, 8, 13, 16, 17, 64, 256])
 def test_latent_tail_full_size(device, M):
     cfg = sg.sg_select(M, synth.D_HIDDEN, synth.D_LATENT)
     _say(f"latent_moe_tail M={M} cfg={cfg}")
@@ -275,9 +275,12 @@ def test_latent_tail_zero_weights_is_shared(device, M):
     assert np.array_equal(host(out), S)
 
 
-@pytest.mark.parametrize("M,d,D", [(5, 264, 900), (24, 520, 100), (2, 128, 64)])
+@pytest.mark.parametrize("M,d,D", [(5, 264, 900), (24, 520, 100), (2, 128, 64),
+                                   (3, 1000, 5200), (11, 4104, 6000), (16, 2048, 5136)])
 def test_latent_tail_other_shapes(device, M, d, D):
-    """Shapes that take the split-K and small-latent paths of the tail."""
+    """Shapes that take the split-K, small-latent and folded-RMSNorm (ragged
+    latent, wide output) paths of the tail."""
+    _say(f"latent_moe_tail M={M} d={d} D={D} cfg={sg.sg_select(M, D, d)}")
     L, gamma, w_up, S = synth.tail_inputs(M, seed=123 + M, d=d, D=D)
     out = nan_like((M, D), device)
     sg.latent_moe_tail(dev(L, device), dev(gamma, device), dev(w_up, device), dev(S, device),
