@@ -22,11 +22,12 @@ import torch
 from . import _lib
 from ._lib import (SG_KIND_GEMV_ROW, SG_KIND_GEMV_SMALLK, SG_KIND_GEMV_SPLITK,  # noqa: F401
                    SG_KIND_MFMA_DIRECT, SG_KIND_MFMA_TILE, SG_KIND_MFMA_WAVESPLIT, SG_KIND_NONE,
-                   SG_OP_FAB_FB, SG_OP_GEMM, SG_OP_LATENT_TAIL, SgConfig)
+                   SG_KDA_FAB, SG_KDA_FAB_ALONE, SG_KDA_QKVG, SG_OP_FAB_FB, SG_OP_GEMM,
+                   SG_OP_LATENT_TAIL, SgConfig)
 
 __all__ = [
     "sg_select", "sg_overlap_gate", "sg_overlap_max_tokens", "sg_workspace_bytes",
-    "sg_kda_workspace_bytes", "sg_version",
+    "sg_kda_select", "sg_kda_workspace_bytes", "sg_version",
     "skinny_gemm", "kda_qkvg_proj", "kda_fab_fb_proj", "kda_projection_overlap",
     "latent_moe_tail", "HipEvent", "library_path",
 ]
@@ -61,6 +62,16 @@ def sg_overlap_max_tokens() -> int:
 
 def sg_workspace_bytes(op: int, M: int, N: int, K: int) -> int:
     return int(_lib.load().sg_workspace_bytes(int(op), int(M), int(N), int(K)))
+
+
+def sg_kda_select(which: int, M: int, K: int, n_qkvg: int, n_ab: int) -> dict:
+    """The configuration a KDA projection entry point uses for one row range
+    (SG_KDA_QKVG, SG_KDA_FAB: kda_projection_overlap; SG_KDA_FAB_ALONE:
+    kda_fab_fb_proj)."""
+    cfg = SgConfig()
+    _lib.check(_lib.load().sg_kda_select(int(which), int(M), int(K), int(n_qkvg), int(n_ab),
+                                         ctypes.byref(cfg)), "sg_kda_select")
+    return cfg.as_dict()
 
 
 def sg_kda_workspace_bytes(which: int, M: int, K: int, n_qkvg: int, n_ab: int) -> int:

@@ -30,10 +30,14 @@ SG_OP_GEMM = 0
 SG_OP_FAB_FB = 1
 SG_OP_LATENT_TAIL = 2
 
+SG_KDA_QKVG = 0
+SG_KDA_FAB = 1
+SG_KDA_FAB_ALONE = 2
+
 # Every extern "C" symbol declared in include/skinny_gemm.h.
 EXPORTED_SYMBOLS = (
     "sg_select", "sg_overlap_gate", "sg_overlap_max_tokens", "sg_workspace_bytes",
-    "sg_kda_workspace_bytes",
+    "sg_kda_select", "sg_kda_workspace_bytes",
     "sg_strerror", "sg_version", "skinny_gemm", "kda_qkvg_proj", "kda_fab_fb_proj",
     "kda_projection_overlap", "latent_moe_tail",
 )
@@ -57,6 +61,7 @@ _PROTOS = {
     "sg_overlap_gate": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "sg_overlap_max_tokens": (_i32, []),
     "sg_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "sg_kda_select": (_i32, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(SgConfig)]),
     "sg_kda_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "sg_strerror": (ctypes.c_char_p, [_i32]),
     "sg_version": (ctypes.c_char_p, []),

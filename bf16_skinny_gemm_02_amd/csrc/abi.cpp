@@ -36,9 +36,9 @@ int check_output2(const void* p, int64_t ld, int64_t min_ld) {
   return SG_OK;
 }
 
-// Kernels address a weight tile (at most 64 rows) and the whole activation
+// Kernels address a weight tile (at most 128 rows) and the whole activation
 // through 32-bit buffer offsets: both spans must stay below 2^31 bytes.
-constexpr int64_t kMaxTileRows = 64;
+constexpr int64_t kMaxTileRows = 128;
 bool spans_ok(int64_t rows, int64_t ld, int64_t K) {
   if (rows <= 0) return true;
   return ((rows - 1) * ld + K) * 2 < (int64_t(1) << 31);
@@ -118,31 +118,11 @@ int validate_gemm(const sg_bf16* A, int64_t lda, const sg_bf16* W, int64_t ldw, 
   return check_workspace(ws, ws_bytes, sg_workspace_bytes(SG_OP_GEMM, M, N, K));
 }
 
-// The F_A/beta stage configuration: the table's choice, run in partial mode.
-// The small-K kernel has no partial mode, so that case runs the kernel the
-// table uses for K > 256 at the same M, without a K split.
+// The F_A/beta stage configuration of kda_fab_fb_proj (the table's choice,
+// run in partial mode).
 sg_config_t fab_config(int M, int n_ab, int K) {
   sg_config_t c;
-  sg_select(M, n_ab, K, 0, &c);
-  if (c.kind == SG_KIND_GEMV_SMALLK) {
-    if (M == 1) {
-      c.kind = SG_KIND_GEMV_SPLITK;
-      c.m_tile = 1;
-      c.rows = 1;
-      c.waves = 4;
-      c.k_unroll = 16;
-      c.grid = (n_ab + 3) / 4;
-    } else {
-      c.kind = SG_KIND_MFMA_WAVESPLIT;
-      c.m_tile = 4 * ((M + 3) / 4);
-      c.rows = 16;
-      c.waves = 4;
-      c.k_unroll = 4;
-      c.grid = (n_ab + 15) / 16;
-    }
-    c.k_split = 1;
-  }
-  if (c.k_split < 1) c.k_split = 1;
+  if (sg_kda_select(SG_KDA_FAB_ALONE, M, K, 0, n_ab, &c) != SG_OK) memset(&c, 0, sizeof c);
   return c;
 }
 
@@ -165,6 +145,7 @@ int validate_fab_fb(const sg_bf16* x, const sg_bf16* w_ab, const sg_bf16* w_b, s
   if (n_b > 0 && (st = check_output2(g1, n_b, n_b)) != SG_OK) return st;
   if (n_b == 0 && g1 != nullptr && !al2(g1)) return SG_ERR_MISALIGNED;
   if (f_a != nullptr && !al2(f_a)) return SG_ERR_MISALIGNED;
+  if (!spans_ok(M, K, K) || !spans_ok(kMaxTileRows, K, K)) return SG_ERR_UNSUPPORTED;
   return check_workspace(ws, ws_bytes, sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K));
 }
 
@@ -246,19 +227,20 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
   if (M < 0 || K < 0 || n_qkvg < 0 || n_b < 0 || rank <= 0 || n_ab <= rank)
     return SG_ERR_INVALID_ARG;
   if (rank % 8 != 0 || rank > sg::kFbMaxRank) return SG_ERR_UNSUPPORTED;
-  sg_config_t cq;  // the Q/K/V/G rows: the table's configuration for [n_qkvg, K]
-  int st = sg_select(M, n_qkvg, K, 0, &cq);
+  sg_config_t cq, cf;  // the two row ranges' configurations
+  int st = sg_kda_select(SG_KDA_QKVG, M, K, n_qkvg, n_ab, &cq);
   if (st != SG_OK) return st;
   if (M == 0) return SG_OK;
-  const sg_config_t cf = fab_config(M, n_ab, K);  // F_A/beta rows, as kda_fab_fb_proj
+  if ((st = sg_kda_select(SG_KDA_FAB, M, K, n_qkvg, n_ab, &cf)) != SG_OK) return st;
   if ((st = check_operand16(x, K, K)) != SG_OK) return st;
   if ((st = check_operand16(packed_w, K, K)) != SG_OK) return st;
   if ((st = check_operand16(w_b, rank, rank)) != SG_OK) return st;
   if (n_qkvg > 0 && (st = check_output2(qkvg, n_qkvg, n_qkvg)) != SG_OK) return st;
   if ((st = check_output2(beta, n_ab - rank, n_ab - rank)) != SG_OK) return st;
   if (n_b > 0 && (st = check_output2(g1, n_b, n_b)) != SG_OK) return st;
-  const size_t need_main = sg_kda_workspace_bytes(0, M, K, n_qkvg, n_ab);
-  const size_t need_aux = sg_kda_workspace_bytes(1, M, K, n_qkvg, n_ab);
+  if (!spans_ok(M, K, K) || !spans_ok(kMaxTileRows, K, K)) return SG_ERR_UNSUPPORTED;
+  const size_t need_main = sg_kda_workspace_bytes(SG_KDA_QKVG, M, K, n_qkvg, n_ab);
+  const size_t need_aux = sg_kda_workspace_bytes(SG_KDA_FAB, M, K, n_qkvg, n_ab);
   if ((st = check_workspace(ws_main, ws_main_bytes, need_main)) != SG_OK) return st;
   if ((st = check_workspace(ws_aux, ws_aux_bytes, need_aux)) != SG_OK) return st;
   if (need_main > 0) {  // the two workspaces may be used concurrently

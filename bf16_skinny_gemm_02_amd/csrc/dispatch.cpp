@@ -20,13 +20,22 @@ constexpr int kGemvRowMinN = 1024;   // below this N the M = 1 GEMV splits K
 constexpr int kGemvWaveTarget = 2048;  // waves the split-K GEMV aims for
 constexpr int kSmallK = 256;         // K at or below this: small-K GEMV
 constexpr int kGemvDepth = 16;       // 512-wide weight steps an M = 1 GEMV wave holds
+constexpr int kGemvDepth4 = 7;       // the same with four weight rows per wave
 // MFMA ring kernels.  A chunk is 4 k-steps of 32 (128 k).
 constexpr int kWgTarget = 224;       // workgroups a launch aims for (256 CUs, one each)
 constexpr int kNoSplitTiles = 192;   // this many tiles fill the chip without a K split
 constexpr int kSplitMaxTiles = 320;  // WAVESPLIT up to this many 16-row tiles
-constexpr int kSplitRing = 4;        // WAVESPLIT ring slots
+constexpr int kSplitPairTiles = 512; // ... or this many when two workgroups fit a CU (M <= 8)
+constexpr int kSplitRing = 3;        // WAVESPLIT ring slots
 constexpr int kWideRing = 4;         // TILE ring slots for M <= 16 (2 waves, 32 rows)
 constexpr int kTileRing = 3;         // TILE ring slots for 16 < M <= 64 (4 waves, 64 rows)
+// The packed KDA projection at 16 < M <= 64: both row ranges in 128-row tiles
+// (8 waves) with one K split, so that the two segments of the launch fit in a
+// single round of workgroups on 256 CUs.
+constexpr int kPairRows = 128;
+constexpr int kPairWaves = 8;
+constexpr int kPairRing = 3;
+constexpr int kPairWgs = 256;
 // Largest M for which the two-stream projection is worth its fork/join.  On
 // MI355X the concurrent schedule measured slower than the single-stream one
 // (two segments in one launch, then F_B) at every decode M from 1 to 64:
@@ -107,7 +116,9 @@ extern "C" int sg_select(int M, int N, int K, int has_residual, sg_config_t* out
       want = ceil_div(kGemvWaveTarget, N);
     }
     c.m_tile = 1;
-    c.rows = 1;
+    // Four rows per wave when a whole short row fits in the shallower
+    // register ring: fewer, longer workgroups (each stages the activation once).
+    c.rows = (c.kind == SG_KIND_GEMV_ROW && steps <= kGemvDepth4) ? 4 : 1;
     const int need = ceil_div(steps, kGemvDepth);
     c.k_split = effective_split(steps, want > need ? want : need);
     c.k_unroll = kGemvDepth;
@@ -115,9 +126,10 @@ extern "C" int sg_select(int M, int N, int K, int has_residual, sg_config_t* out
   } else if (M <= 16) {
     c.m_tile = 4 * ceil_div(M, 4);
     const int tiles16 = ceil_div(N, 16);
-    if (tiles16 <= kSplitMaxTiles) {
+    if (tiles16 <= kSplitMaxTiles || (c.m_tile <= 8 && tiles16 <= kSplitPairTiles)) {
       // Each wave walks a quarter of the workgroup's K-range: at least one
-      // chunk (4 k-steps) per wave.
+      // chunk (4 k-steps) per wave.  Up to M = 8 the 3-slot rings of two
+      // workgroups fit one CU's LDS, so up to 512 tiles run in one round.
       c.kind = SG_KIND_MFMA_WAVESPLIT;
       c.rows = 16;
       c.waves = 4;
@@ -218,14 +230,73 @@ extern "C" const char* sg_strerror(int status) {
 
 extern "C" const char* sg_version(void) { return "0.1.0"; }
 
+extern "C" int sg_kda_select(int which, int M, int K, int n_qkvg, int n_ab, sg_config_t* out) {
+  if (out == nullptr || which < SG_KDA_QKVG || which > SG_KDA_FAB_ALONE) return SG_ERR_INVALID_ARG;
+  if (M < 0 || K < 0 || n_qkvg < 0 || n_ab < 0) return SG_ERR_INVALID_ARG;
+  sg_config_t q, f;
+  int st = sg_select(M, n_qkvg, K, 0, &q);
+  if (st != SG_OK) return st;
+  if ((st = sg_select(M, n_ab, K, 0, &f)) != SG_OK) return st;
+  // The F_A/beta rows always leave fp32 partials for the F_B stage to sum, so
+  // the small-K kind (which has no partial output) is replaced by the kind
+  // the table uses for these M at larger K, over one K-range.
+  if (f.kind == SG_KIND_GEMV_SMALLK) {
+    if (M == 1) {
+      f.kind = SG_KIND_GEMV_SPLITK;
+      f.m_tile = 1;
+      f.rows = 1;
+      f.waves = kWaves;
+      f.k_unroll = kGemvDepth;
+      f.grid = ceil_div(n_ab, kWaves);
+    } else {
+      f.kind = SG_KIND_MFMA_WAVESPLIT;
+      f.m_tile = 4 * ceil_div(M, 4);
+      f.rows = 16;
+      f.waves = 4;
+      f.k_unroll = kSplitRing;
+      f.grid = ceil_div(n_ab, 16);
+    }
+    f.k_split = 1;
+  }
+  if (f.k_split < 1) f.k_split = 1;
+  if (which == SG_KDA_FAB_ALONE) {
+    *out = f;
+    return SG_OK;
+  }
+  // 16 < M <= 64: the table's 64-row tiles leave the Q/K/V/G rows alone
+  // filling the chip (256 workgroups), so the F_A/beta segment would start a
+  // second round.  Both ranges move to 128-row tiles with one K split sized so
+  // that all their workgroups run in one round.
+  if (q.kind == SG_KIND_MFMA_TILE && f.kind == SG_KIND_MFMA_TILE && q.rows == 64 && f.rows == 64) {
+    const int tq = ceil_div(n_qkvg, kPairRows), tf = ceil_div(n_ab, kPairRows);
+    const int ksteps = ceil_div(K, 32);
+    int want = kPairWgs / (tq + tf);
+    int cap = ksteps / 8;
+    if (cap < 1) cap = 1;
+    if (want > cap) want = cap;
+    const int S = effective_split(ksteps, want);
+    sg_config_t* both[2] = {&q, &f};
+    const int tiles[2] = {tq, tf};
+    for (int i = 0; i < 2; ++i) {
+      both[i]->rows = kPairRows;
+      both[i]->waves = kPairWaves;
+      both[i]->k_unroll = kPairRing;
+      both[i]->k_split = S;
+      both[i]->grid = tiles[i] * S;
+    }
+  }
+  *out = (which == SG_KDA_QKVG) ? q : f;
+  return SG_OK;
+}
+
 extern "C" size_t sg_kda_workspace_bytes(int which, int M, int K, int n_qkvg, int n_ab) {
   if (M <= 0 || K < 0 || n_qkvg < 0 || n_ab <= 0) return 0;
-  if (which == 0) {  // main: Q/K/V/G split-K partials
-    sg_config_t c;
-    if (n_qkvg == 0 || sg_select(M, n_qkvg, K, 0, &c) != SG_OK || c.kind == SG_KIND_NONE) return 0;
-    return sg_workspace_bytes(SG_OP_GEMM, M, n_qkvg, K);
-  }
-  if (which == 1)  // aux: F_A/beta partials, as kda_fab_fb_proj
-    return sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K);
-  return 0;
+  if (which != SG_KDA_QKVG && which != SG_KDA_FAB) return 0;
+  sg_config_t c;
+  if (sg_kda_select(which, M, K, n_qkvg, n_ab, &c) != SG_OK || c.kind == SG_KIND_NONE) return 0;
+  const int N = (which == SG_KDA_QKVG) ? n_qkvg : n_ab;
+  const size_t plane = static_cast<size_t>(M) * static_cast<size_t>(N) * sizeof(float);
+  // Q/K/V/G: split-K partials only when K is split.  F_A/beta: always partials.
+  if (which == SG_KDA_QKVG && c.k_split <= 1) return 0;
+  return sg::round256(static_cast<size_t>(c.k_split) * plane);
 }

@@ -27,7 +27,8 @@
 // [s*sps, (s+1)*sps) and stores fp32 partials for a later fixed-order sum.
 //
 // Fold (latent-MoE tail, RMSNorm -> up-projection): the staged activation is
-// the latent L over the whole row.  Every wave sums L[m,k]^2 from LDS in the
+// the latent L over the whole row, with gamma staged behind it in the same
+// step (both land with one round trip).  Every wave sums L[m,k]^2 from LDS in the
 // same order, r[m] = rsqrt(sum / K + eps), and the workgroup rewrites LDS in
 // place with n = bf16(L * r * gamma), the bf16 normalised latent the
 // up-projection consumes.  One launch, no workspace.
@@ -134,6 +135,22 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
       }
     }
   }
+  if constexpr (FOLD) {
+    // gamma over the same range, staged behind the activation rows in the
+    // same way, so the normalisation below waits for no second round trip.
+    for (int t = wave; t < nst; t += NW) {
+      const int c0 = c_base + t * kWave;
+      u32x4* dst = xs + total + t * kWave;
+      if (c0 + kWave <= K8) {
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1)))*)(g.gamma + static_cast<int64_t>(c0 + lane) * 8),
+            (void __attribute__((address_space(3)))*)(dst), 16, 0, 0);
+      } else {
+        const int c = c0 + lane;
+        dst[lane] = (c < K8) ? load_cached(g.gamma + static_cast<int64_t>(c) * 8) : zero4();
+      }
+    }
+  }
   __syncthreads();
 
   if constexpr (FOLD) {
@@ -159,7 +176,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
       const int c = q - m * row_chunks;
       if (c < K8) {
         const u32x4 v = xs[q];
-        const u32x4 gv = load_cached(g.gamma + static_cast<int64_t>(c) * 8);
+        const u32x4 gv = xs[total + c];
         float r = 0.f;
 #pragma unroll
         for (int mm = 0; mm < M; ++mm) r = (mm == m) ? rs[mm] : r;
@@ -237,31 +254,33 @@ hipError_t launch_inst(const GemvLaunch& g, dim3 grid, size_t lds, hipStream_t s
   return hipGetLastError();
 }
 
-// The table sends only M = 1 here (one row per wave, 4 waves); wider M
-// goes to the MFMA kernels.
+// The table sends only M = 1 here (4 waves; one weight row per wave, or four
+// when a whole row fits in 7 steps); wider M goes to the MFMA kernels.
 template <bool FOLD>
 hipError_t launch_fold(const GemvLaunch& g, int M, int R, int NW, dim3 grid, size_t lds,
                        hipStream_t s) {
   if (M == 1 && R == 1 && NW == 4) return launch_inst<1, 1, 4, FOLD>(g, grid, lds, s);
+  if (M == 1 && R == 4 && NW == 4) return launch_inst<1, 4, 4, FOLD>(g, grid, lds, s);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-size_t gemv_lds_bytes(int M, int K, int k_split) {
+// The activation rows of one K-range, plus gamma's when the RMSNorm is folded.
+size_t gemv_lds_bytes(int M, int K, int k_split, bool fold) {
   const int K8 = K >> 3;
   const int nsteps = (K8 + kWave - 1) / kWave;
   const int S = k_split > 0 ? k_split : 1;
   const int sps = nsteps > 0 ? (nsteps + S - 1) / S : 0;
-  return static_cast<size_t>(M) * sps * kWave * 16;
+  return static_cast<size_t>(M + (fold ? 1 : 0)) * sps * kWave * 16;
 }
 
-bool gemv_fits(int M, int K, int k_split, int rows) {
+bool gemv_fits(int M, int K, int k_split, int rows, bool fold) {
   const int K8 = K >> 3;
   const int nsteps = (K8 + kWave - 1) / kWave;
   const int S = k_split > 0 ? k_split : 1;
   const int sps = nsteps > 0 ? (nsteps + S - 1) / S : 0;
-  return gemv_lds_bytes(M, K, k_split) <= kGemvMaxLds && sps <= gemv_depth(rows);
+  return gemv_lds_bytes(M, K, k_split, fold) <= kGemvMaxLds && sps <= gemv_depth(rows);
 }
 
 bool gemv_same_instance(const sg_config_t& a, const sg_config_t& b) {
@@ -308,8 +327,9 @@ hipError_t launch_gemv(const DotProblem* segs, const sg_config_t* cfgs, int nseg
     const int nsteps = (K8 + kWave - 1) / kWave;
     const int S = cfg.k_split > 0 ? cfg.k_split : 1;
     g.sps = nsteps > 0 ? (nsteps + S - 1) / S : 1;
-    if (!gemv_fits(p.M, p.K, S, cfg.rows)) return hipErrorInvalidValue;
-    const size_t seg_lds = gemv_lds_bytes(p.M, p.K, S);
+    const bool fold = p.gamma != nullptr;
+    if (!gemv_fits(p.M, p.K, S, cfg.rows, fold)) return hipErrorInvalidValue;
+    const size_t seg_lds = gemv_lds_bytes(p.M, p.K, S, fold);
     if (seg_lds > lds) lds = seg_lds;
     const int rows_per_wg = cfg.waves * cfg.rows;
     sgm.groups = (p.N + rows_per_wg - 1) / rows_per_wg;

@@ -573,17 +573,25 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
         default: break;
       }
     }
+    if (NW == 8 && C == 3) {  // the packed KDA projection, 16 < M <= 64
+      switch (XQ) {
+        case 8: return launch_tile_inst<2, 8, 3, 8>(L, wgs, s);
+        case 12: return launch_tile_inst<3, 8, 3, 12>(L, wgs, s);
+        case 16: return launch_tile_inst<4, 8, 3, 16>(L, wgs, s);
+        default: break;
+      }
+    }
     return hipErrorInvalidValue;
   }
   if (cfg.kind == SG_KIND_MFMA_WAVESPLIT) {
     const int C = cfg.k_unroll, XQ = cfg.m_tile / 4;
-    if (cfg.rows != 16 || cfg.waves != kSplitWaves || (cfg.m_tile % 4) != 0 || C != 4)
+    if (cfg.rows != 16 || cfg.waves != kSplitWaves || (cfg.m_tile % 4) != 0 || C != 3)
       return hipErrorInvalidValue;
     switch (XQ) {
-      case 1: return launch_wsplit_inst<1, 4>(L, wgs, s);
-      case 2: return launch_wsplit_inst<2, 4>(L, wgs, s);
-      case 3: return launch_wsplit_inst<3, 4>(L, wgs, s);
-      case 4: return launch_wsplit_inst<4, 4>(L, wgs, s);
+      case 1: return launch_wsplit_inst<1, 3>(L, wgs, s);
+      case 2: return launch_wsplit_inst<2, 3>(L, wgs, s);
+      case 3: return launch_wsplit_inst<3, 3>(L, wgs, s);
+      case 4: return launch_wsplit_inst<4, 3>(L, wgs, s);
       default: return hipErrorInvalidValue;
     }
   }

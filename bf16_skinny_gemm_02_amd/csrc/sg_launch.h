@@ -120,7 +120,7 @@ constexpr int kFbMaxRank = 512;
 // LDS (at most this many bytes) and holds every weight step of that range in
 // registers; the table sizes k_split so that both fit.
 constexpr size_t kGemvMaxLds = 128 * 1024;
-size_t gemv_lds_bytes(int M, int K, int k_split);
-bool gemv_fits(int M, int K, int k_split, int rows);
+size_t gemv_lds_bytes(int M, int K, int k_split, bool fold);
+bool gemv_fits(int M, int K, int k_split, int rows, bool fold);
 
 }  // namespace sg

@@ -143,10 +143,36 @@ int sg_overlap_max_tokens(void);
  * error. */
 size_t sg_workspace_bytes(int op, int M, int N, int K);
 
-/* Bytes of device workspace kda_projection_overlap needs: which = 0 for
- * ws_main (the Q/K/V/G split-K partials, sg_workspace_bytes(SG_OP_GEMM, M,
- * n_qkvg, K), 0 when unsplit), 1 for ws_aux (the F_A/beta partials,
- * sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K)). */
+/* Row ranges of the KDA projection, for sg_kda_select() and
+ * sg_kda_workspace_bytes(). */
+enum {
+    SG_KDA_QKVG = 0,       /* Q/K/V/G rows in kda_projection_overlap */
+    SG_KDA_FAB = 1,        /* F_A/beta rows in kda_projection_overlap */
+    SG_KDA_FAB_ALONE = 2   /* F_A/beta rows in kda_fab_fb_proj */
+};
+
+/* Host-only, pure: the configurations the KDA projection entry points use,
+ * the analogue of the per-M KDA_QKVG_CONFIGS table and of the small-N
+ * kernel's own choice [P3 low_latency_gemm.py, kda_skinny_gemm.py].
+ *   SG_KDA_FAB_ALONE: sg_select(M, n_ab, K, 0), except that the small-K
+ *     kind, which has no partial output, becomes GEMV_SPLITK (M == 1) or
+ *     MFMA_WAVESPLIT (M > 1) over one K-range: the F_B stage always sums
+ *     fp32 partials.
+ *   SG_KDA_QKVG / SG_KDA_FAB: sg_select(M, n_qkvg, K, 0) and the
+ *     SG_KDA_FAB_ALONE configuration, except where both are the 64-row MFMA
+ *     tile (16 < M <= 64): then both ranges use 128-row tiles of 8 waves
+ *     with one K split S = split(ceil(K/32), min(256 / (t_q + t_f),
+ *     max(1, ceil(K/32) / 8))), t = ceil(rows / 128), so that the two
+ *     segments of the single-stream launch run in one round of workgroups.
+ * Returns SG_OK, SG_ERR_INVALID_ARG (NULL out, unknown which, negative
+ * sizes) or the status of sg_select for either range. */
+int sg_kda_select(int which, int M, int K, int n_qkvg, int n_ab, sg_config_t *out);
+
+/* Bytes of device workspace kda_projection_overlap needs: which =
+ * SG_KDA_QKVG for ws_main (the Q/K/V/G split-K partials, k_split * M *
+ * n_qkvg * 4 rounded up to 256, 0 when unsplit), SG_KDA_FAB for ws_aux (the
+ * F_A/beta partials, k_split * M * n_ab * 4 rounded up to 256), with the
+ * configurations of sg_kda_select().  0 for any other which. */
 size_t sg_kda_workspace_bytes(int which, int M, int K, int n_qkvg, int n_ab);
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -202,14 +228,16 @@ int kda_fab_fb_proj(const sg_bf16 *x, const sg_bf16 *w_ab, const sg_bf16 *w_b,
  * main's order once the call's work retires.  If aux, fork or join is NULL
  * the call runs on main alone (the reference's sequential path): the
  * Q/K/V/G rows and the F_A/beta rows as two segments of one launch, then one
- * launch for F_B (and the Q/K/V/G split-K reduction).  The Q/K/V/G rows use
- * sg_select(M, n_qkvg, K) and the F_A/beta rows the configuration of
- * kda_fab_fb_proj in both schedules, so the outputs are bitwise identical
- * either way.
+ * launch for F_B (and the Q/K/V/G split-K reduction).  Both schedules use the
+ * configurations sg_kda_select(SG_KDA_QKVG / SG_KDA_FAB, ...), so their
+ * outputs are bitwise identical; where those equal the standalone
+ * configurations (sg_select and SG_KDA_FAB_ALONE) they are also bitwise
+ * identical to kda_qkvg_proj + kda_fab_fb_proj.
  * packed_w [n_qkvg + n_ab, K] contiguous; qkvg [M,n_qkvg]; beta
  * [M,n_ab-rank]; g1 [M,n_b]; w_b [n_b,rank]; 0 < rank < n_ab, rank % 8 == 0,
- * rank <= 512.  ws_main needs sg_kda_workspace_bytes(0, ...) bytes (often 0)
- * and ws_aux sg_kda_workspace_bytes(1, ...); they must not overlap. */
+ * rank <= 512.  ws_main needs sg_kda_workspace_bytes(SG_KDA_QKVG, ...) bytes
+ * (often 0) and ws_aux sg_kda_workspace_bytes(SG_KDA_FAB, ...); they must
+ * not overlap. */
 int kda_projection_overlap(const sg_bf16 *x, const sg_bf16 *packed_w, const sg_bf16 *w_b,
                            sg_bf16 *qkvg, sg_bf16 *beta, sg_bf16 *g1,
                            int M, int K, int n_qkvg, int n_ab, int rank, int n_b,

@@ -19,10 +19,12 @@ Rule, for C[M,N] = A[M,K] W[N,K]^T:
       - N >= 1024: GEMV_ROW, want = 1.
       - N < 1024: GEMV_SPLITK, want = ceil(2048 / N).
       need = ceil(steps / 16), k_split = split(steps, max(want, need)),
-      m_tile = 1, rows = 1, k_unroll = 16, grid = ceil(N / 4) * k_split.
+      m_tile = 1, rows = 4 if GEMV_ROW and steps <= 7 else 1, k_unroll = 16,
+      grid = ceil(N / (4 * rows)) * k_split.
   * 2 <= M <= 16: m_tile = 4 * ceil(M / 4), tiles16 = ceil(N / 16).
-      - tiles16 <= 320: MFMA_WAVESPLIT, rows = 16, waves = 4, k_unroll = 4,
-        k_split = msplit(tiles16, 16), grid = tiles16 * k_split.
+      - tiles16 <= 320, or m_tile <= 8 and tiles16 <= 512: MFMA_WAVESPLIT,
+        rows = 16, waves = 4, k_unroll = 3, k_split = msplit(tiles16, 16),
+        grid = tiles16 * k_split.
       - else MFMA_TILE, rows = 32, waves = 2, k_unroll = 4,
         tiles = ceil(N / 32), k_split = msplit(tiles, 8), grid = tiles * k_split.
   * 17 <= M <= 64: MFMA_TILE, m_tile = 16 * ceil(M / 16), rows = 64, waves = 4,
@@ -38,6 +40,20 @@ Rule, for C[M,N] = A[M,K] W[N,K]^T:
 
 Overlap gate: enabled and 0 < M <= OVERLAP_MAX_TOKENS and x contiguous and an
 aux stream and the event pair are present.
+
+KDA projection row ranges (kda_select; which = 0 Q/K/V/G and 1 F_A/beta in the
+packed projection, 2 F_A/beta alone):
+  * f = select(M, n_ab, K); a GEMV_SMALLK f becomes, with k_split = 1,
+    GEMV_SPLITK (M == 1: m_tile 1, rows 1, waves 4, k_unroll 16,
+    grid ceil(n_ab / 4)) or MFMA_WAVESPLIT (M > 1: m_tile 4 ceil(M / 4),
+    rows 16, waves 4, k_unroll 3, grid ceil(n_ab / 16)); k_split >= 1.
+  * which 2: f.  Otherwise q = select(M, n_qkvg, K), and if q and f are both
+    MFMA_TILE with rows 64: with t_q = ceil(n_qkvg / 128), t_f =
+    ceil(n_ab / 128), ksteps = ceil(K / 32), S = split(ksteps,
+    min(256 // (t_q + t_f), max(1, ksteps // 8))), both get rows 128,
+    waves 8, k_unroll 3, k_split S, grid t * S.
+  * workspace: Q/K/V/G k_split * M * n_qkvg * 4 (0 when k_split <= 1),
+    F_A/beta k_split * M * n_ab * 4, each rounded up to 256.
 """
 from __future__ import annotations
 
@@ -94,14 +110,15 @@ def select(M: int, N: int, K: int, has_residual: bool = False):
         else:
             kind, want = GEMV_SPLITK, _cdiv(2048, N)
         ks = _split(steps, max(want, _cdiv(steps, 16)))
-        cfg.update(kind=kind, m_tile=1, rows=1, k_split=ks, k_unroll=16,
-                   grid=_cdiv(N, 4) * ks)
+        rows = 4 if (kind == GEMV_ROW and steps <= 7) else 1
+        cfg.update(kind=kind, m_tile=1, rows=rows, k_split=ks, k_unroll=16,
+                   grid=_cdiv(N, 4 * rows) * ks)
     elif M <= 16:
         cfg["m_tile"] = 4 * _cdiv(M, 4)
         tiles16 = _cdiv(N, 16)
-        if tiles16 <= 320:
+        if tiles16 <= 320 or (cfg["m_tile"] <= 8 and tiles16 <= 512):
             ks = msplit(tiles16, 16)
-            cfg.update(kind=MFMA_WAVESPLIT, rows=16, waves=4, k_unroll=4, k_split=ks,
+            cfg.update(kind=MFMA_WAVESPLIT, rows=16, waves=4, k_unroll=3, k_split=ks,
                        grid=tiles16 * ks)
         else:
             tiles = _cdiv(N, 32)
@@ -126,3 +143,44 @@ def overlap_gate(M: int, x_contiguous: bool, have_aux: bool, have_events: bool,
                  enabled: bool = True) -> bool:
     return bool(enabled and 0 < M <= OVERLAP_MAX_TOKENS and x_contiguous and have_aux
                 and have_events)
+
+
+def kda_select(which: int, M: int, K: int, n_qkvg: int, n_ab: int):
+    """Returns (status, config dict or None) for one row range of the KDA projection."""
+    if which not in (0, 1, 2) or M < 0 or K < 0 or n_qkvg < 0 or n_ab < 0:
+        return INVALID_ARG, None
+    st, q = select(M, n_qkvg, K)
+    if st != OK:
+        return st, None
+    st, f = select(M, n_ab, K)
+    if st != OK:
+        return st, None
+    if f["kind"] == GEMV_SMALLK:
+        if M == 1:
+            f.update(kind=GEMV_SPLITK, m_tile=1, rows=1, waves=4, k_unroll=16, grid=_cdiv(n_ab, 4))
+        else:
+            f.update(kind=MFMA_WAVESPLIT, m_tile=4 * _cdiv(M, 4), rows=16, waves=4, k_unroll=3,
+                     grid=_cdiv(n_ab, 16))
+        f["k_split"] = 1
+    f["k_split"] = max(f["k_split"], 1)
+    if which == 2:
+        return OK, f
+    if q["kind"] == MFMA_TILE and f["kind"] == MFMA_TILE and q["rows"] == 64 and f["rows"] == 64:
+        tq, tf = _cdiv(n_qkvg, 128), _cdiv(n_ab, 128)
+        ksteps = _cdiv(K, 32)
+        S = _split(ksteps, min(256 // (tq + tf), max(1, ksteps // 8)))
+        for c, t in ((q, tq), (f, tf)):
+            c.update(rows=128, waves=8, k_unroll=3, k_split=S, grid=t * S)
+    return OK, (q if which == 0 else f)
+
+
+def kda_workspace_bytes(which: int, M: int, K: int, n_qkvg: int, n_ab: int) -> int:
+    if M <= 0 or K < 0 or n_qkvg < 0 or n_ab <= 0 or which not in (0, 1):
+        return 0
+    st, c = kda_select(which, M, K, n_qkvg, n_ab)
+    if st != OK or c["kind"] == NONE:
+        return 0
+    if which == 0 and c["k_split"] <= 1:
+        return 0
+    n = n_qkvg if which == 0 else n_ab
+    return -(-(c["k_split"] * M * n * 4) // 256) * 256

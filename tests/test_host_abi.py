@@ -111,11 +111,61 @@ def test_kind_follows_m_boundaries():
         st, cfg = selection.select(M, 4096, 7168)
         assert st == selection.OK
         assert cfg["kind"] == _kind_for(M), M
-    # A wide N moves M <= 16 to the shared-activation tile (32 rows per workgroup).
-    assert selection.select(8, 7168, 2048)[1]["kind"] == selection.MFMA_TILE
-    assert selection.select(8, 7168, 2048)[1]["rows"] == 32
+    # A wide N moves M <= 16 to the shared-activation tile (32 rows per
+    # workgroup), except up to M = 8 while two wave-split workgroups fit a CU.
+    assert selection.select(12, 7168, 2048)[1]["kind"] == selection.MFMA_TILE
+    assert selection.select(12, 7168, 2048)[1]["rows"] == 32
+    assert selection.select(8, 7168, 2048)[1]["kind"] == selection.MFMA_WAVESPLIT
+    assert selection.select(8, 9000, 2048)[1]["kind"] == selection.MFMA_TILE
+    # M = 1 takes four rows per wave when a whole row fits seven 512-wide steps.
+    assert selection.select(1, 7168, 2048)[1]["rows"] == 4
+    assert selection.select(1, 7168, 2048)[1]["grid"] == 448
+    assert selection.select(1, 4096, 7168)[1]["rows"] == 1
     assert selection.select(257, 4096, 7168)[0] == selection.UNSUPPORTED
     assert selection.select(0, 4096, 7168)[1]["kind"] == selection.NONE
+
+
+KDA_SHAPES = [(7168, 4096, 136), (7168, 4096, 140), (7168, 4096, 144), (2048, 1024, 136),
+              (128, 512, 136), (7168, 0, 136), (264, 64, 16), (7168, 4096, 0), (1000, 300, 40),
+              (7168, 40000, 136), (8, 8, 8), (520, 4096, 260)]
+
+
+def _c_kda_select(lib, which, M, K, nq, nab):
+    cfg = _lib.SgConfig()
+    st = lib.sg_kda_select(which, M, K, nq, nab, ctypes.byref(cfg))
+    return st, cfg.as_dict()
+
+
+def test_kda_select_matches_oracle(lib):
+    checked = 0
+    for (K, nq, nab), M, which in itertools.product(KDA_SHAPES, range(-1, 260), (-1, 0, 1, 2, 3)):
+        st_c, cfg_c = _c_kda_select(lib, which, M, K, nq, nab)
+        st_o, cfg_o = selection.kda_select(which, M, K, nq, nab)
+        assert st_c == st_o, (which, M, K, nq, nab)
+        if st_o == selection.OK:
+            assert cfg_c == cfg_o, (which, M, K, nq, nab, cfg_c, cfg_o)
+        checked += 1
+        for w in (0, 1):
+            if which == w:
+                assert lib.sg_kda_workspace_bytes(w, M, K, nq, nab) == \
+                    selection.kda_workspace_bytes(w, M, K, nq, nab), (w, M, K, nq, nab)
+    assert checked > 10000
+    assert lib.sg_kda_select(0, 1, 8, 8, 8, None) == _lib.SG_ERR_INVALID_ARG
+
+
+def test_kda_select_pairs_the_projection_tiles():
+    # 16 < M <= 64 at the KDA shapes: both ranges in 128-row tiles, one K split,
+    # (32 + 2) * 7 = 238 workgroups: one round on 256 CUs.
+    for M in (17, 32, 48, 64):
+        _, q = selection.kda_select(0, M, 7168, 4096, 136)
+        _, f = selection.kda_select(1, M, 7168, 4096, 136)
+        assert (q["rows"], q["waves"], q["k_split"], q["grid"]) == (128, 8, 7, 224)
+        assert (f["rows"], f["waves"], f["k_split"], f["grid"]) == (128, 8, 7, 14)
+        # the standalone calls keep the table's 64-row tiles
+        assert selection.select(M, 4096, 7168)[1]["rows"] == 64
+        assert selection.kda_select(2, M, 7168, 4096, 136)[1]["rows"] == 64
+    for M in (1, 8, 16, 65):
+        assert selection.kda_select(0, M, 7168, 4096, 136)[1] == selection.select(M, 4096, 7168)[1]
 
 
 def test_overlap_gate_matches_oracle(lib):
