@@ -205,7 +205,7 @@ def qkvg_kernel_leg(device, M, reps=200):
     gbs = qkvg_bytes(M) / (us * 1e-6) / 1e9
     cfg = sg.sg_select(M, N_QKVG, K)
     kinds = {sg.SG_KIND_GEMV_ROW: "gemv_kernel", sg.SG_KIND_MFMA_WAVESPLIT: "wsplit_kernel",
-             sg.SG_KIND_MFMA_TILE: "tile_kernel", sg.SG_KIND_MFMA_DIRECT: "direct_kernel"}
+             sg.SG_KIND_MFMA_TILE: "tile_kernel", sg.SG_KIND_MFMA_BLOCK: "block_kernel"}
     name = f"{kinds.get(cfg['kind'], '?')} (kda_qkvg_proj M={M}, {cfg['grid']} workgroups)"
     return {"kernel": name, "us_per_launch": us, "launches_timed": reps * R, "gbs": gbs,
             "bytes": qkvg_bytes(M)}

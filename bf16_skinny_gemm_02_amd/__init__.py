@@ -20,8 +20,8 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (SG_KIND_GEMV_ROW, SG_KIND_GEMV_SMALLK, SG_KIND_GEMV_SPLITK,  # noqa: F401
-                   SG_KIND_MFMA_DIRECT, SG_KIND_MFMA_TILE, SG_KIND_MFMA_WAVESPLIT, SG_KIND_NONE,
+from ._lib import (SG_KIND_MFMA_BLOCK, SG_KIND_GEMV_ROW, SG_KIND_GEMV_SMALLK, SG_KIND_GEMV_SPLITK,  # noqa: F401
+                   SG_KIND_MFMA_TILE, SG_KIND_MFMA_WAVESPLIT, SG_KIND_NONE,
                    SG_KDA_FAB, SG_KDA_FAB_ALONE, SG_KDA_QKVG, SG_OP_FAB_FB, SG_OP_GEMM,
                    SG_OP_LATENT_TAIL, SgConfig)
 

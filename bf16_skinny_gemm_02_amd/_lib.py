@@ -24,7 +24,7 @@ SG_KIND_GEMV_SPLITK = 2
 SG_KIND_GEMV_SMALLK = 3
 SG_KIND_MFMA_TILE = 4
 SG_KIND_MFMA_WAVESPLIT = 5
-SG_KIND_MFMA_DIRECT = 6
+SG_KIND_MFMA_BLOCK = 6
 
 SG_OP_GEMM = 0
 SG_OP_FAB_FB = 1

@@ -57,7 +57,7 @@ bool same_config(const sg_config_t& a, const sg_config_t& b) {
 }
 
 bool is_mfma(int kind) {
-  return kind == SG_KIND_MFMA_TILE || kind == SG_KIND_MFMA_WAVESPLIT || kind == SG_KIND_MFMA_DIRECT;
+  return kind == SG_KIND_MFMA_TILE || kind == SG_KIND_MFMA_WAVESPLIT || kind == SG_KIND_MFMA_BLOCK;
 }
 
 // The main kernel of configuration c, with the problem's epilogue as given

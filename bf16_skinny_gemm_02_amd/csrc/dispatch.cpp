@@ -29,6 +29,9 @@ constexpr int kSplitPairTiles = 512; // ... or this many when two workgroups fit
 constexpr int kSplitRing = 3;        // WAVESPLIT ring slots
 constexpr int kWideRing = 4;         // TILE ring slots for M <= 16 (2 waves, 32 rows)
 constexpr int kTileRing = 3;         // TILE ring slots for 16 < M <= 64 (4 waves, 64 rows)
+constexpr int kBlockRows = 64;       // BLOCK (M > 64): weight rows per workgroup
+constexpr int kBlockM = 128;         // ... and activation rows per workgroup
+constexpr int kBlockRing = 3;
 // The packed KDA projection at 16 < M <= 64: both row ranges in 128-row tiles
 // (8 waves) with one K split, so that the two segments of the launch fit in a
 // single round of workgroups on 256 CUs.
@@ -73,7 +76,6 @@ int mfma_split(int tiles, int ksteps, int min_steps) {
   return effective_split(ksteps, want);
 }
 
-int direct_ring_depth(int mb) { return mb <= 8 ? 4 : 2; }
 
 }  // namespace
 
@@ -155,13 +157,14 @@ extern "C" int sg_select(int M, int N, int K, int has_residual, sg_config_t* out
     c.k_split = mfma_split(tiles, ksteps, 8);
     c.grid = tiles * c.k_split;
   } else {
-    c.kind = SG_KIND_MFMA_DIRECT;
-    const int mb = ceil_div(M, 16);
-    c.m_tile = 16 * mb;
-    c.rows = 1;
-    c.k_unroll = direct_ring_depth(mb);
-    const int tiles = ceil_div(N, 16);
-    c.k_split = mfma_split(tiles, ksteps, 32);
+    // Two-dimensional blocks: the activation is shared by 64 weight rows and
+    // each weight tile by 128 activation rows.
+    c.kind = SG_KIND_MFMA_BLOCK;
+    c.m_tile = kBlockM * ceil_div(M, kBlockM);
+    c.rows = kBlockRows;
+    c.k_unroll = kBlockRing;
+    const int tiles = ceil_div(N, kBlockRows) * ceil_div(M, kBlockM);
+    c.k_split = mfma_split(tiles, ksteps, 8);
     c.grid = tiles * c.k_split;
   }
   *out = c;

@@ -10,7 +10,8 @@
 // v = 0..3.  A = 16 weight rows (n), B = 16 activation rows (m): each lane
 // ends with four consecutive n of one output row m.
 //
-// Three kernels:
+// Three kernels, all staging both operands through an LDS ring filled by
+// direct global->LDS copies:
 //
 //  * tile_kernel (SG_KIND_MFMA_TILE): a workgroup of NW waves owns 16*NW
 //    weight rows (wave w: rows 16w..16w+15) and one K-range (all of K, or
@@ -25,9 +26,9 @@
 //    private LDS ring (16 weight rows + the M activation rows per slot), so
 //    the loop has no barrier.  The four wave sums meet in LDS in the fixed
 //    order 0,1,2,3 at the end: no split-K partials and no second launch.
-//  * direct_kernel (SG_KIND_MFMA_DIRECT, M > 64): each wave loads weight and
-//    activation fragments straight into registers; 4 waves split the K-range
-//    and sum through LDS in fixed order.
+//  * block_kernel (SG_KIND_MFMA_BLOCK, M > 64): tile_kernel's ring over a
+//    two-dimensional block, 64 weight rows x 128 activation rows, each wave
+//    a 32 x 64 corner of it.
 //
 // LDS layout of one ring slot: rows of 16 pieces of 16 bytes.  Piece c of row
 // r is stored at position c ^ (r & 15): the 16 lanes that read piece c of 16
@@ -339,110 +340,133 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
   store4(g, acc, rl, row0 + 4 * kg, split, res);
 }
 
-// ---- register-fragment kernel (M > 64) ------------------------------------------
+// ---- two-dimensional LDS block tile (M > 64) ----------------------------------------
 
-constexpr int kDirectWaves = 4;
+// A workgroup of 4 waves owns a block of kBlkRows weight rows x kBlkM
+// activation rows and one K-range; wave w computes weight rows 32 (w & 1) ..
+// +31 against activation rows 64 (w >> 1) .. +63 (2 x 4 MFMA tiles), so each
+// k-step reads 6 fragments from LDS for 8 MFMAs.  The ring is tile_kernel's:
+// chunks of 128 k, both operands copied global->LDS (weights non-temporal),
+// one barrier per chunk.
+constexpr int kBlkRows = 64;
+constexpr int kBlkM = 128;
+constexpr int kBlkWaves = 4;
 
-template <int MB, int D, int NKT>
-__global__ __launch_bounds__(kDirectWaves * kWave) void direct_kernel(MfmaLaunch L) {
-  constexpr int kRegs = MB * 4;
+// Workgroup -> (weight tile, activation block).  Consecutive workgroups go to
+// the 8 XCDs in turn, so the activation blocks of one weight tile are given
+// to workgroups 8 apart: the same XCD, whose L2 then serves the tile's second
+// read.
+__device__ __forceinline__ void block_coords(int tile, int ntiles, int mblocks, int& nt, int& mb) {
+  const int G = 8 * mblocks;
+  const int grp = tile / G;
+  const int r = tile - grp * G;
+  const int nrem = min(8, ntiles - grp * 8);
+  mb = r / nrem;
+  nt = grp * 8 + (r - mb * nrem);
+}
+
+template <int C>
+__global__ __launch_bounds__(kBlkWaves * kWave) void block_kernel(MfmaLaunch L) {
+  extern __shared__ u32x4 lds[];
   int tile, split;
   const MfmaArgs g = pick_segment(L, tile, split);
-  __shared__ float red[(kDirectWaves - 1) * kRegs * kWave];
+  constexpr int SLOT = (kBlkRows + kBlkM) * kPieces;
+  constexpr int WC = kBlkRows / 4 / kBlkWaves;  // weight copies per wave per chunk
+  constexpr int XC = kBlkM / 4 / kBlkWaves;     // activation copies per wave per chunk
+  constexpr int kInFlight = (C - 2) * (WC + XC);
+  static_assert(C >= 2, "ring");
 
   const int lane = lane_id();
   const int wave = wave_id();
   const int rl = lane & 15;
   const int kg = lane >> 4;
-  const int n_base = tile * 16;
+  const int ntiles = (g.N + kBlkRows - 1) / kBlkRows;
+  const int mblocks = (g.M + kBlkM - 1) / kBlkM;
+  int nt, mb;
+  block_coords(tile, ntiles, mblocks, nt, mb);
   const int K8 = g.K >> 3;
   const int KS = (g.K + kKStep - 1) / kKStep;
   const int s_begin = split * g.sps;
-  const int s_end = min(KS, s_begin + g.sps);
-  const int len = max(0, s_end - s_begin);
-  const int per = (len + kDirectWaves - 1) / kDirectWaves;
-  const int w_begin = s_begin + wave * per;
-  const int w_end = min(s_end, w_begin + per);
-  const int nk = max(0, w_end - w_begin);
+  const int nk = max(0, min(KS, s_begin + g.sps) - s_begin);
+  const int npieces = nk * 4;
+  const int nch = (nk + kChunkSteps - 1) / kChunkSteps;
+  const int c0 = s_begin * 4;
+  const int row0 = nt * kBlkRows;
+  const int tile_rows = min(kBlkRows, g.N - row0);
+  const int m0 = mb * kBlkM;
+  const int m_rows = min(kBlkM, g.M - m0);
 
-  const int tile_rows = min(16, g.N - n_base);
-  const rsrc_t wres = make_rsrc(g.w + static_cast<int64_t>(n_base) * g.ldw,
+  const rsrc_t wres = make_rsrc(g.w + static_cast<int64_t>(row0) * g.ldw,
                                 static_cast<uint32_t>(((tile_rows - 1) * g.ldw + g.K) * 2));
-  const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(((g.M - 1) * g.lda + g.K) * 2));
-  const uint32_t wbase = rl < tile_rows ? static_cast<uint32_t>(rl * g.ldw * 2) : kOob;
-  uint32_t xbase[MB];
+  const rsrc_t xres = make_rsrc(g.a + static_cast<int64_t>(m0) * g.lda,
+                                static_cast<uint32_t>(((m_rows - 1) * g.lda + g.K) * 2));
+  const int dr = lane >> 4;
+  const int dp = lane & 15;
+  auto issue = [&](int q) {
+    u32x4* slot = lds + (q % C) * SLOT;
 #pragma unroll
-  for (int a = 0; a < MB; ++a) {
-    const int m = 16 * a + rl;
-    xbase[a] = m < g.M ? static_cast<uint32_t>(m * g.lda * 2) : kOob;
-  }
-
-  f32x4 acc[MB];
+    for (int i = 0; i < WC; ++i) {
+      const int r = 4 * (wave * WC + i) + dr;
+      const int pc = kPieces * q + (dp ^ (r & 15));
+      const uint32_t off = (r < tile_rows && pc < npieces && c0 + pc < K8)
+                               ? static_cast<uint32_t>((r * g.ldw + (c0 + pc) * 8) * 2)
+                               : kOob;
+      copy16_to_lds_nt(wres, slot + 4 * (wave * WC + i) * kPieces, off);
+    }
 #pragma unroll
-  for (int a = 0; a < MB; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Ring of D k-steps: weight and activation fragments of step t are issued
-  // together D steps before they are consumed; no load sits in a branch.
-  auto koff = [&](int t) -> uint32_t {
-    const int c = (w_begin + t) * 4 + kg;
-    return (t < nk && c < K8) ? static_cast<uint32_t>(c * 16) : kOob;
-  };
-  auto wfrag = [&](uint32_t ko) -> u32x4 {
-    return buf_load_nt(wres, (ko == kOob || wbase == kOob) ? kOob : wbase + ko);
-  };
-  auto xfrag = [&](uint32_t ko, int a) -> u32x4 {
-    return buf_load(xres, (ko == kOob || xbase[a] == kOob) ? kOob : xbase[a] + ko);
-  };
-  u32x4 wr[D];
-  u32x4 xr[D][MB];
-#pragma unroll
-  for (int j = 0; j < D; ++j) {
-    const uint32_t ko = koff(j);
-    wr[j] = wfrag(ko);
-#pragma unroll
-    for (int a = 0; a < MB; ++a) xr[j][a] = xfrag(ko, a);
-  }
-  auto pass = [&](int tb) {
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-      const int t = tb + j;
-#pragma unroll
-      for (int a = 0; a < MB; ++a) acc[a] = mfma16(wr[j], xr[j][a], acc[a]);
-      const uint32_t ko = koff(t + D);
-      wr[j] = wfrag(ko);
-#pragma unroll
-      for (int a = 0; a < MB; ++a) xr[j][a] = xfrag(ko, a);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < XC; ++j) {
+      const int m = 4 * (wave * XC + j) + dr;
+      const int pc = kPieces * q + (dp ^ (m & 15));
+      const uint32_t off = (m < m_rows && pc < npieces && c0 + pc < K8)
+                               ? static_cast<uint32_t>((m * g.lda + (c0 + pc) * 8) * 2)
+                               : kOob;
+      copy16_to_lds(xres, slot + (kBlkRows + 4 * (wave * XC + j)) * kPieces, off);
     }
   };
-  if constexpr (NKT > 0) {
-    // Known step count: straight-line code, so every wait is exact.
-#pragma unroll
-    for (int tb = 0; tb < NKT; tb += D) pass(tb);
-  } else {
-    for (int tb = 0; tb < nk; tb += D) pass(tb);
-  }
 
-  // Fixed-order sum of the four wave partials.
-  if (wave > 0) {
-    float* dst = red + (wave - 1) * kRegs * kWave;
 #pragma unroll
-    for (int a = 0; a < MB; ++a)
+  for (int q = 0; q < C - 1; ++q) issue(q);
+
+  const int wr0 = 32 * (wave & 1);   // this wave's first weight row in the block
+  const int xr0 = 64 * (wave >> 1);  // and first activation row
+  Res4 res[2][4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) dst[(a * 4 + v) * kWave + lane] = acc[a][v];
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      res[i][j] = load_res4(g, m0 + xr0 + 16 * j + rl, row0 + wr0 + 16 * i + 4 * kg);
+
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < nch; ++q) {
+    wait_vmcnt<kInFlight>();
+    __builtin_amdgcn_s_barrier();
+    issue(q + C - 1);
+    const u32x4* slot = lds + (q % C) * SLOT;
+#pragma unroll
+    for (int t = 0; t < kChunkSteps; ++t) {
+      const int pos = (4 * t + kg) ^ rl;  // every fragment row is 16-aligned + rl
+      u32x4 wf[2], xf[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) wf[i] = slot[(wr0 + 16 * i + rl) * kPieces + pos];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xf[j] = slot[(kBlkRows + xr0 + 16 * j + rl) * kPieces + pos];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(wf[i], xf[j], acc[i][j]);
+    }
   }
-  __syncthreads();
-  if (wave != 0) return;
+  wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
+
 #pragma unroll
-  for (int w = 0; w < kDirectWaves - 1; ++w) {
-    const float* src = red + w * kRegs * kWave;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int a = 0; a < MB; ++a)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[a][v] += src[(a * 4 + v) * kWave + lane];
-  }
-#pragma unroll
-  for (int a = 0; a < MB; ++a) store4(g, acc[a], 16 * a + rl, n_base + 4 * kg, split, load_res4(g, 16 * a + rl, n_base + 4 * kg));
+    for (int j = 0; j < 4; ++j)
+      store4(g, acc[i][j], m0 + xr0 + 16 * j + rl, row0 + wr0 + 16 * i + 4 * kg, split, res[i][j]);
 }
 
 // ---- launchers -------------------------------------------------------------------
@@ -471,30 +495,36 @@ hipError_t launch_wsplit_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int MB>
-hipError_t launch_direct_mb(const MfmaLaunch& L, int per_wave, int wgs, hipStream_t s) {
-  constexpr int D = MB <= 8 ? 4 : 2;
-  const dim3 block(kDirectWaves * kWave);
-  if (per_wave > 16 && per_wave <= 56)
-    hipLaunchKernelGGL((direct_kernel<MB, D, 56>), dim3(wgs), block, 0, s, L);
-  else if (per_wave <= 16)
-    hipLaunchKernelGGL((direct_kernel<MB, D, 16>), dim3(wgs), block, 0, s, L);
-  else
-    hipLaunchKernelGGL((direct_kernel<MB, D, 0>), dim3(wgs), block, 0, s, L);
+template <int C>
+hipError_t launch_block_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
+  auto kern = block_kernel<C>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+      static_cast<int>(kMfmaMaxLds));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(wgs), dim3(kBlkWaves * kWave), block_lds_bytes(C), s, L);
   return hipGetLastError();
 }
 
 int ksteps_of(int K) { return (K + kKStep - 1) / kKStep; }
 
-// Weight rows one workgroup of this configuration covers.
-int rows_per_wg(const sg_config_t& c) {
-  return c.kind == SG_KIND_MFMA_TILE ? c.rows : 16;
+// Workgroup tiles of one K-range: 16 * NW (TILE) or 16 (WAVESPLIT) weight
+// rows each, or (BLOCK) 64 weight rows x 128 activation rows.
+int tiles_of(const sg_config_t& c, int M, int N) {
+  if (c.kind == SG_KIND_MFMA_BLOCK)
+    return ((N + kBlkRows - 1) / kBlkRows) * ((M + kBlkM - 1) / kBlkM);
+  const int rows = c.kind == SG_KIND_MFMA_TILE ? c.rows : 16;
+  return (N + rows - 1) / rows;
 }
 
 }  // namespace
 
 size_t tile_lds_bytes(int nw, int c, int xq) {
   return static_cast<size_t>(c) * (16 * nw + 4 * xq) * kPieces * 16;
+}
+
+size_t block_lds_bytes(int c) {
+  return static_cast<size_t>(c) * (kBlkRows + kBlkM) * kPieces * 16;
 }
 
 size_t wsplit_lds_bytes(int c, int xq) {
@@ -544,8 +574,7 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
     g.sps = (KS + S - 1) / S;
     if (g.sps < 1) g.sps = 1;
     if (g.sps > max_sps) max_sps = g.sps;
-    const int rows = rows_per_wg(c);
-    sgm.tiles = (p.N + rows - 1) / rows;
+    sgm.tiles = tiles_of(c, p.M, p.N);
     sgm.wg_begin = wgs;
     if (sgm.tiles <= 0) return hipErrorInvalidValue;
     wgs += sgm.tiles * S;
@@ -595,19 +624,10 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
       default: return hipErrorInvalidValue;
     }
   }
-  if (cfg.kind == SG_KIND_MFMA_DIRECT) {
-    const int MB = cfg.m_tile / 16;
-    if (cfg.rows != 1 || (cfg.m_tile % 16) != 0) return hipErrorInvalidValue;
-    // The straight-line instance must cover every segment's per-wave steps.
-    const int per_wave = (max_sps + kDirectWaves - 1) / kDirectWaves;
-    switch (MB) {
-#define SG_CASE(mb) \
-  case mb: return launch_direct_mb<mb>(L, per_wave, wgs, s);
-      SG_CASE(5) SG_CASE(6) SG_CASE(7) SG_CASE(8) SG_CASE(9) SG_CASE(10) SG_CASE(11) SG_CASE(12)
-      SG_CASE(13) SG_CASE(14) SG_CASE(15) SG_CASE(16)
-#undef SG_CASE
-      default: return hipErrorInvalidValue;
-    }
+  if (cfg.kind == SG_KIND_MFMA_BLOCK) {
+    if (cfg.rows != kBlkRows || cfg.waves != kBlkWaves || cfg.m_tile % kBlkM != 0) return hipErrorInvalidValue;
+    if (cfg.k_unroll == 3) return launch_block_inst<3>(L, wgs, s);
+    return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }

@@ -64,6 +64,7 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
 constexpr size_t kMfmaMaxLds = 160 * 1024;
 size_t tile_lds_bytes(int nw, int c, int xq);
 size_t wsplit_lds_bytes(int c, int xq);
+size_t block_lds_bytes(int c);
 
 // out[m,n] = bf16( sum_{s<S} partial[s][m][n] + res[m,n] ).  The sum runs
 // over s = 0..S-1 in order (deterministic).  Columns n >= n_split (when

@@ -78,8 +78,9 @@ enum {
     SG_KIND_MFMA_WAVESPLIT = 5, /* bf16 MFMA, M <= 16: 16 weight rows per
                                    workgroup, each wave a private LDS ring over
                                    a quarter of K, summed in LDS */
-    SG_KIND_MFMA_DIRECT = 6     /* bf16 MFMA, M > 64: fragments loaded straight
-                                   into registers */
+    SG_KIND_MFMA_BLOCK = 6      /* bf16 MFMA, M > 64: 64 weight rows x 128
+                                   activation rows per workgroup, both staged
+                                   in an LDS ring */
 };
 
 /* Launch configuration chosen per (M, N, K): the analogue of the reference's
@@ -87,13 +88,14 @@ enum {
  *   kind     SG_KIND_*
  *   m_tile   activation rows the kernel instance is built for: M (GEMV),
  *            M rounded up to 4 (TILE and WAVESPLIT with M <= 16), M rounded
- *            up to 16 (MFMA otherwise)
+ *            up to 16 (TILE otherwise), M rounded up to 128 (BLOCK: blocks of
+ *            128 activation rows, one per workgroup)
  *   rows     weight rows per wave (GEMV) or per workgroup (MFMA TILE and
- *            WAVESPLIT); 1 for DIRECT (one 16-row block per workgroup)
+ *            WAVESPLIT, BLOCK: 64 with 128 activation rows)
  *   waves    waves (64 lanes) per workgroup
  *   k_split  workgroups that split K; > 1 means fp32 partials in workspace
  *   k_unroll GEMV: 512-wide weight steps a wave holds; TILE / WAVESPLIT: LDS
- *            ring slots (chunks of 128 k); DIRECT: 32-deep k-steps in flight
+ *            ring slots (chunks of 128 k); BLOCK: the same
  *   grid     workgroups launched by the main kernel
  *   nt_weights 1 = weights are read with non-temporal (streaming) loads */
 typedef struct {

@@ -30,9 +30,9 @@ Rule, for C[M,N] = A[M,K] W[N,K]^T:
   * 17 <= M <= 64: MFMA_TILE, m_tile = 16 * ceil(M / 16), rows = 64, waves = 4,
     k_unroll = 3, tiles = ceil(N / 64), k_split = msplit(tiles, 8),
     grid = tiles * k_split.
-  * 65 <= M <= 256: MFMA_DIRECT, m_tile = 16 * ceil(M / 16), rows = 1,
-    k_unroll = 4 if m_tile <= 128 else 2, tiles = ceil(N / 16),
-    k_split = msplit(tiles, 32), grid = tiles * k_split.
+  * 65 <= M <= 256: MFMA_BLOCK, m_tile = 128 * ceil(M / 128), rows = 64,
+    waves = 4, k_unroll = 3, tiles = ceil(N / 64) * ceil(M / 128),
+    k_split = msplit(tiles, 8), grid = tiles * k_split.
   * msplit(tiles, min_steps): 1 if tiles >= 192; else
     split(ksteps, min(ceil(224 / tiles), max(1, floor(ksteps / min_steps)))).
   * split(steps, want): 1 if steps <= 0 or want <= 1; else with
@@ -58,7 +58,7 @@ packed projection, 2 F_A/beta alone):
 from __future__ import annotations
 
 OK, INVALID_ARG, UNSUPPORTED = 0, -1, -2
-NONE, GEMV_ROW, GEMV_SPLITK, GEMV_SMALLK, MFMA_TILE, MFMA_WAVESPLIT, MFMA_DIRECT = 0, 1, 2, 3, 4, 5, 6
+NONE, GEMV_ROW, GEMV_SPLITK, GEMV_SMALLK, MFMA_TILE, MFMA_WAVESPLIT, MFMA_BLOCK = 0, 1, 2, 3, 4, 5, 6
 OVERLAP_MAX_TOKENS = 0
 
 FIELDS = ("kind", "m_tile", "rows", "waves", "k_split", "k_unroll", "grid", "nt_weights")
@@ -131,11 +131,10 @@ def select(M: int, N: int, K: int, has_residual: bool = False):
         cfg.update(kind=MFMA_TILE, m_tile=16 * _cdiv(M, 16), rows=64, waves=4, k_unroll=3,
                    k_split=ks, grid=tiles * ks)
     else:
-        mb = _cdiv(M, 16)
-        tiles = _cdiv(N, 16)
-        ks = msplit(tiles, 32)
-        cfg.update(kind=MFMA_DIRECT, m_tile=16 * mb, rows=1, k_unroll=4 if mb <= 8 else 2,
-                   k_split=ks, grid=tiles * ks)
+        tiles = _cdiv(N, 64) * _cdiv(M, 128)
+        ks = msplit(tiles, 8)
+        cfg.update(kind=MFMA_BLOCK, m_tile=128 * _cdiv(M, 128), rows=64, k_unroll=3, k_split=ks,
+                   grid=tiles * ks)
     return OK, cfg
 
 

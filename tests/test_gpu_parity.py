@@ -27,7 +27,7 @@ def _say(*a):
 
 GEMM_CASES = [
     # (M, N, K, residual)  -- GEMV_ROW / SPLITK / SMALLK, MFMA WAVESPLIT / TILE /
-    # DIRECT, ragged N and K
+    # BLOCK, ragged N and K
     (1, 1030, 1000, False), (2, 1500, 2056, True), (3, 1024, 520, False), (4, 1100, 7168, True),
     (5, 77, 3000, False), (8, 300, 1000, True), (11, 2000, 264, False), (16, 1100, 4104, True),
     (16, 40, 8, False), (4, 64, 136, True), (1, 5, 248, False), (7, 9, 256, True),
@@ -35,6 +35,7 @@ GEMM_CASES = [
     (100, 77, 4104, False), (256, 300, 520, True), (255, 129, 96, False), (48, 3000, 40, True),
     (16, 1, 7168, False), (20, 1, 64, True), (3, 7, 0, True),
     (6, 5200, 1000, True), (13, 7170, 2056, False), (20, 9000, 512, True), (2, 4100, 7176, False),
+    (130, 1000, 2056, True), (200, 4100, 520, False), (65, 7168, 2048, True), (129, 64, 1032, False),
 ]
 
 
@@ -91,7 +92,7 @@ def test_qkvg_full_size(device, M):
     assert cosine(g, ex) > 0.9999
 
 
-@pytest.mark.parametrize("M", [1, 3, 16, 17, 64])
+@pytest.mark.parametrize("M", [1, 3, 16, 17, 64, 100, 256])
 def test_qkvg_lattice_bitwise(device, M):
     """On the integer lattice fp32 accumulation is exact in any order, so the
     GPU must equal the oracle bit for bit."""
@@ -269,7 +270,7 @@ def test_packed_projection_equals_split(device):
 
 # ---- latent-MoE tail ----------------------------------------------------------------------
 
-@pytest.mark.parametrize("M", [1, 2, 8, 13, 16, 17, 64, 256])
+@pytest.mark.parametrize("M", [1, 2, 8, 13, 16, 17, 64, 130, 256])
 def test_latent_tail_full_size(device, M):
     cfg = sg.sg_select(M, synth.D_HIDDEN, synth.D_LATENT)
     _say(f"latent_moe_tail M={M} cfg={cfg}")

@@ -103,7 +103,7 @@ def _kind_for(M):
         return selection.GEMV_ROW
     if M <= 16:
         return selection.MFMA_WAVESPLIT
-    return selection.MFMA_TILE if M <= 64 else selection.MFMA_DIRECT
+    return selection.MFMA_TILE if M <= 64 else selection.MFMA_BLOCK
 
 
 def test_kind_follows_m_boundaries():
