@@ -14,13 +14,17 @@ Infinity Cache cannot hold them, so the weights stream from HBM on every call.
 Inputs are resident in HBM before timing starts.
 
 Reported ``value``: mean microseconds per KDA projection call over the M sweep
-(the metric's unit).  ``--comparators`` adds, per M, the forced two-stream
-schedule (fork/join events, F_A/beta -> F_B on an aux stream), the forced
-single-stream schedule, and a plain packed GEMM followed by a second GEMM for
-F_B.  The same line carries the per-M breakdown (projection,
-tail, GB/s, fraction of HBM peak), the roofline of the dominant kernel (the
-Q/K/V/G GEMV at M = 1, timed with HIP events on its own stream) and the CPU
-oracle timed on this host.
+(the metric's unit).  Within each timed step the projection graphs of the
+whole sweep run back to back between two events, then the tail graphs between
+the next two: ``value`` is the projection half's time over its calls,
+``tail_us_per_call`` the tail half's.  The per-M ``breakdown`` (projection and
+tail µs, GB/s, fraction of HBM peak) is measured after the timed region, each
+graph replayed back to back.  ``--comparators`` adds, per M, the forced
+two-stream schedule (fork/join events, F_A/beta -> F_B on an aux stream), the
+forced single-stream schedule, and a plain packed GEMM followed by a second
+GEMM for F_B.  The line also carries the roofline of the dominant kernel (the
+wave-split MFMA tile at M = 8, with the M = 1 GEMV beside it, each timed with
+HIP events on its own stream) and the CPU oracle timed on this host.
 """
 from __future__ import annotations
 
@@ -149,11 +153,16 @@ def capture(fn, R, stream):
     return g
 
 
-def time_graph(g, stream, reps):
-    """Mean ms per replay, timed with events on the replay stream."""
+def time_graph(g, stream, reps, warm=3):
+    """Mean ms per replay, timed with events on the replay stream.  `warm`
+    untimed replays go first: the GPU is busy (and at its working clocks)
+    when the start event is reached, and the host's submission of the first
+    timed replay is not counted."""
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
+        for _ in range(warm):
+            g.replay()
         start.record(stream)
         for _ in range(reps):
             g.replay()
@@ -163,6 +172,8 @@ def time_graph(g, stream, reps):
 
 
 # ---- dominant-kernel roofline leg ---------------------------------------------------
+
+BREAKDOWN_REPS = 20
 
 ROOFLINE_M = 8   # the wave-split MFMA tile serves M = 2..16, five of the nine sweep points
 
@@ -319,36 +330,38 @@ def main():
             step()
     torch.cuda.synchronize()
 
-    # Timed region: exactly `steps` steps, synchronised on both sides.  Events
-    # on the replay stream bracket each graph; they are read after the region.
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in M_SWEEP]
-           for _ in range(args.steps)]
+    # Timed region: exactly `steps` steps, synchronised on both sides.  Within
+    # a step the projection graphs of the whole sweep run back to back, then
+    # the tail graphs; three events on the replay stream split the step into
+    # its two halves (an event between every graph would stall the stream at
+    # each boundary).  They are read after the region.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     with torch.cuda.stream(main_stream):
         for st in range(args.steps):
-            for i, M in enumerate(M_SWEEP):
-                e = evs[st][i]
-                e[0].record(main_stream)
+            e = evs[st]
+            e[0].record(main_stream)
+            for M in M_SWEEP:
                 g_proj[M].replay()
-                e[1].record(main_stream)
+            e[1].record(main_stream)
+            for M in M_SWEEP:
                 g_tail[M].replay()
-                e[2].record(main_stream)
+            e[2].record(main_stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    t_proj = {M: 0.0 for M in M_SWEEP}
-    t_tail = {M: 0.0 for M in M_SWEEP}
-    for st in range(args.steps):
-        for i, M in enumerate(M_SWEEP):
-            e = evs[st][i]
-            t_proj[M] += e[0].elapsed_time(e[1])
-            t_tail[M] += e[1].elapsed_time(e[2])
+    t_proj_all = sum(e[0].elapsed_time(e[1]) for e in evs)
+    t_tail_all = sum(e[1].elapsed_time(e[2]) for e in evs)
+    calls_proj = args.steps * sum(proj[M].R for M in M_SWEEP)
+    calls_tail = args.steps * sum(tail[M].R for M in M_SWEEP)
     print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
+    # Per-M breakdown (after the timed region): each graph replayed back to
+    # back, timed with events on the replay stream.
     breakdown = {}
     for M in M_SWEEP:
-        pu = t_proj[M] * 1000.0 / (args.steps * proj[M].R)
-        tu = t_tail[M] * 1000.0 / (args.steps * tail[M].R)
+        pu = time_graph(g_proj[M], main_stream, BREAKDOWN_REPS) * 1000.0 / proj[M].R
+        tu = time_graph(g_tail[M], main_stream, BREAKDOWN_REPS) * 1000.0 / tail[M].R
         breakdown[str(M)] = {
             "proj_us": round(pu, 3),
             "proj_gbs": round(proj_bytes(M) / (pu * 1e-6) / 1e9, 1),
@@ -361,7 +374,10 @@ def main():
             "weight_copies": [proj[M].R, tail[M].R],
             "schedule": "two_stream" if gate[M] else "one_stream",
         }
-    value = sum(b["proj_us"] for b in breakdown.values()) / len(M_SWEEP)
+    # Every projection graph holds the same number of calls, so this is also
+    # the mean over the sweep of the per-M time per call.
+    value = t_proj_all * 1000.0 / calls_proj
+    tail_value = t_tail_all * 1000.0 / calls_tail
     ms_per_step = wall * 1000.0 / args.steps
 
     if args.comparators:
@@ -425,6 +441,7 @@ def main():
             "n_b": N_B, "d_latent": D_LAT, "d_hidden": D_HID, "parallelism": "single_gpu",
         },
         "roofline": roofline,
+        "tail_us_per_call": round(tail_value, 3),
         "breakdown": breakdown,
     }
     if not args.no_cpu_baseline:

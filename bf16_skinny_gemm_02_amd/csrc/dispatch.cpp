@@ -32,7 +32,7 @@ constexpr int kTileRing = 3;         // TILE ring slots for 16 < M <= 64 (4 wave
 constexpr int kBlockRows = 64;       // BLOCK (M > 64): weight rows per workgroup
 constexpr int kBlockM = 128;         // ... and activation rows per workgroup
 constexpr int kBlockRing = 3;
-// The packed KDA projection at 16 < M <= 64: both row ranges in 128-row tiles
+// The packed KDA projection at 2 <= M <= 64: both row ranges in 128-row tiles
 // (8 waves) with one K split, so that the two segments of the launch fit in a
 // single round of workgroups on 256 CUs.
 constexpr int kPairRows = 128;
@@ -266,11 +266,13 @@ extern "C" int sg_kda_select(int which, int M, int K, int n_qkvg, int n_ab, sg_c
     *out = f;
     return SG_OK;
   }
-  // 16 < M <= 64: the table's 64-row tiles leave the Q/K/V/G rows alone
-  // filling the chip (256 workgroups), so the F_A/beta segment would start a
-  // second round.  Both ranges move to 128-row tiles with one K split sized so
-  // that all their workgroups run in one round.
-  if (q.kind == SG_KIND_MFMA_TILE && f.kind == SG_KIND_MFMA_TILE && q.rows == 64 && f.rows == 64) {
+  // 2 <= M <= 64: the table's wave-split and 64-row tiles give the Q/K/V/G
+  // rows alone 256 workgroups, one per CU, so the F_A/beta segment would start
+  // a second round.  Both ranges move to 128-row tiles with one K split sized
+  // so that all their workgroups run in one round.
+  const bool q_small = q.kind == SG_KIND_MFMA_WAVESPLIT || q.kind == SG_KIND_MFMA_TILE;
+  const bool f_small = f.kind == SG_KIND_MFMA_WAVESPLIT || f.kind == SG_KIND_MFMA_TILE;
+  if (q_small && f_small) {
     const int tq = ceil_div(n_qkvg, kPairRows), tf = ceil_div(n_ab, kPairRows);
     const int ksteps = ceil_div(K, 32);
     int want = kPairWgs / (tq + tf);
@@ -281,6 +283,8 @@ extern "C" int sg_kda_select(int which, int M, int K, int n_qkvg, int n_ab, sg_c
     sg_config_t* both[2] = {&q, &f};
     const int tiles[2] = {tq, tf};
     for (int i = 0; i < 2; ++i) {
+      both[i]->kind = SG_KIND_MFMA_TILE;
+      both[i]->m_tile = M <= 16 ? 4 * ceil_div(M, 4) : 16 * ceil_div(M, 16);
       both[i]->rows = kPairRows;
       both[i]->waves = kPairWaves;
       both[i]->k_unroll = kPairRing;

@@ -602,8 +602,12 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
         default: break;
       }
     }
-    if (NW == 8 && C == 3) {  // the packed KDA projection, 16 < M <= 64
+    if (NW == 8 && C == 3) {  // the packed KDA projection, 2 <= M <= 64
       switch (XQ) {
+        case 1: return launch_tile_inst<1, 8, 3, 1>(L, wgs, s);
+        case 2: return launch_tile_inst<1, 8, 3, 2>(L, wgs, s);
+        case 3: return launch_tile_inst<1, 8, 3, 3>(L, wgs, s);
+        case 4: return launch_tile_inst<1, 8, 3, 4>(L, wgs, s);
         case 8: return launch_tile_inst<2, 8, 3, 8>(L, wgs, s);
         case 12: return launch_tile_inst<3, 8, 3, 12>(L, wgs, s);
         case 16: return launch_tile_inst<4, 8, 3, 16>(L, wgs, s);

@@ -161,9 +161,10 @@ enum {
  *     MFMA_WAVESPLIT (M > 1) over one K-range: the F_B stage always sums
  *     fp32 partials.
  *   SG_KDA_QKVG / SG_KDA_FAB: sg_select(M, n_qkvg, K, 0) and the
- *     SG_KDA_FAB_ALONE configuration, except where both are the 64-row MFMA
- *     tile (16 < M <= 64): then both ranges use 128-row tiles of 8 waves
- *     with one K split S = split(ceil(K/32), min(256 / (t_q + t_f),
+ *     SG_KDA_FAB_ALONE configuration, except where both are MFMA_WAVESPLIT
+ *     or MFMA_TILE (2 <= M <= 64): then both ranges use MFMA_TILE with
+ *     128-row tiles of 8 waves (m_tile M rounded up to 4 for M <= 16, to 16
+ *     above) and one K split S = split(ceil(K/32), min(256 / (t_q + t_f),
  *     max(1, ceil(K/32) / 8))), t = ceil(rows / 128), so that the two
  *     segments of the single-stream launch run in one round of workgroups.
  * Returns SG_OK, SG_ERR_INVALID_ARG (NULL out, unknown which, negative

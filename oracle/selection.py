@@ -48,10 +48,11 @@ packed projection, 2 F_A/beta alone):
     grid ceil(n_ab / 4)) or MFMA_WAVESPLIT (M > 1: m_tile 4 ceil(M / 4),
     rows 16, waves 4, k_unroll 3, grid ceil(n_ab / 16)); k_split >= 1.
   * which 2: f.  Otherwise q = select(M, n_qkvg, K), and if q and f are both
-    MFMA_TILE with rows 64: with t_q = ceil(n_qkvg / 128), t_f =
+    MFMA_WAVESPLIT or MFMA_TILE: with t_q = ceil(n_qkvg / 128), t_f =
     ceil(n_ab / 128), ksteps = ceil(K / 32), S = split(ksteps,
-    min(256 // (t_q + t_f), max(1, ksteps // 8))), both get rows 128,
-    waves 8, k_unroll 3, k_split S, grid t * S.
+    min(256 // (t_q + t_f), max(1, ksteps // 8))), both become MFMA_TILE with
+    m_tile 4 ceil(M / 4) (M <= 16) or 16 ceil(M / 16), rows 128, waves 8,
+    k_unroll 3, k_split S, grid t * S.
   * workspace: Q/K/V/G k_split * M * n_qkvg * 4 (0 when k_split <= 1),
     F_A/beta k_split * M * n_ab * 4, each rounded up to 256.
 """
@@ -164,12 +165,15 @@ def kda_select(which: int, M: int, K: int, n_qkvg: int, n_ab: int):
     f["k_split"] = max(f["k_split"], 1)
     if which == 2:
         return OK, f
-    if q["kind"] == MFMA_TILE and f["kind"] == MFMA_TILE and q["rows"] == 64 and f["rows"] == 64:
+    small = (MFMA_WAVESPLIT, MFMA_TILE)
+    if q["kind"] in small and f["kind"] in small:
         tq, tf = _cdiv(n_qkvg, 128), _cdiv(n_ab, 128)
         ksteps = _cdiv(K, 32)
         S = _split(ksteps, min(256 // (tq + tf), max(1, ksteps // 8)))
+        mt = 4 * _cdiv(M, 4) if M <= 16 else 16 * _cdiv(M, 16)
         for c, t in ((q, tq), (f, tf)):
-            c.update(rows=128, waves=8, k_unroll=3, k_split=S, grid=t * S)
+            c.update(kind=MFMA_TILE, m_tile=mt, rows=128, waves=8, k_unroll=3, k_split=S,
+                     grid=t * S)
     return OK, (q if which == 0 else f)
 
 

@@ -154,17 +154,18 @@ def test_kda_select_matches_oracle(lib):
 
 
 def test_kda_select_pairs_the_projection_tiles():
-    # 16 < M <= 64 at the KDA shapes: both ranges in 128-row tiles, one K split,
+    # 2 <= M <= 64 at the KDA shapes: both ranges in 128-row tiles, one K split,
     # (32 + 2) * 7 = 238 workgroups: one round on 256 CUs.
-    for M in (17, 32, 48, 64):
+    for M in (2, 3, 8, 12, 16, 17, 32, 48, 64):
         _, q = selection.kda_select(0, M, 7168, 4096, 136)
         _, f = selection.kda_select(1, M, 7168, 4096, 136)
         assert (q["rows"], q["waves"], q["k_split"], q["grid"]) == (128, 8, 7, 224)
         assert (f["rows"], f["waves"], f["k_split"], f["grid"]) == (128, 8, 7, 14)
-        # the standalone calls keep the table's 64-row tiles
-        assert selection.select(M, 4096, 7168)[1]["rows"] == 64
-        assert selection.kda_select(2, M, 7168, 4096, 136)[1]["rows"] == 64
-    for M in (1, 8, 16, 65):
+        assert q["m_tile"] == (4 * -(-M // 4) if M <= 16 else 16 * -(-M // 16))
+        # the standalone calls keep the table's own kernels
+        assert selection.select(M, 4096, 7168)[1]["rows"] in (16, 64)
+        assert selection.kda_select(2, M, 7168, 4096, 136)[1]["rows"] in (16, 64)
+    for M in (1, 65, 256):
         assert selection.kda_select(0, M, 7168, 4096, 136)[1] == selection.select(M, 4096, 7168)[1]
 
 
@@ -272,13 +273,16 @@ def test_fab_fb_validation(lib):
 
 def test_overlap_validation(lib):
     E = _lib
-    need_aux = lib.sg_kda_workspace_bytes(1, 2, 7168, 4096, 136)
-    assert need_aux >= 2 * 136 * 2
-    assert lib.sg_kda_workspace_bytes(0, 2, 7168, 4096, 136) == 0
+    # M = 1: the Q/K/V/G rows need no workspace; M = 2: the paired tiles split
+    # K, so both ranges leave partials.
+    need_aux = lib.sg_kda_workspace_bytes(1, 1, 7168, 4096, 136)
+    assert need_aux >= 136 * 4
+    assert lib.sg_kda_workspace_bytes(0, 1, 7168, 4096, 136) == 0
+    assert lib.sg_kda_workspace_bytes(0, 2, 7168, 4096, 136) == 7 * 2 * 4096 * 4
 
     def ov(**kw):
         args = dict(x=A16, packed=B16, w_b=C16, qkvg=ctypes.c_void_p(0x80000),
-                    beta=ctypes.c_void_p(0x60000), g1=ctypes.c_void_p(0x70000), M=2, K=7168,
+                    beta=ctypes.c_void_p(0x60000), g1=ctypes.c_void_p(0x70000), M=1, K=7168,
                     n_qkvg=4096, n_ab=136, rank=128, n_b=1024, wsm=NUL, wsm_b=0,
                     wsa=ctypes.c_void_p(0x90000), wsa_b=need_aux)
         args.update(kw)
@@ -291,6 +295,7 @@ def test_overlap_validation(lib):
     assert ov(packed=NUL) == E.SG_ERR_INVALID_ARG
     assert ov(qkvg=NUL) == E.SG_ERR_INVALID_ARG
     assert ov(wsa=NUL) == E.SG_ERR_WORKSPACE
+    assert ov(M=2) == E.SG_ERR_WORKSPACE            # ws_main missing
     assert ov(rank=100) == E.SG_ERR_UNSUPPORTED
     assert ov(M=0) == E.SG_OK
 
