@@ -357,12 +357,31 @@ extern "C" int latent_moe_tail(const sg_bf16* latent, const sg_bf16* gamma, floa
   const bool fold = (M == 1) && (c.kind == SG_KIND_GEMV_SMALLK ||
                                  ((c.kind == SG_KIND_GEMV_ROW || c.kind == SG_KIND_GEMV_SPLITK) &&
                                   c.k_split == 1));
-  if (!fold && d_latent > sg::kNormMaxD) return SG_ERR_UNSUPPORTED;
+  // 2 <= M <= 16 on the wave-split MFMA tile: the kernel normalises in registers.
+  const bool mfma_fold = c.kind == SG_KIND_MFMA_WAVESPLIT && sg::wsplit_fold_fits(d_latent, c.k_split);
+  if (!fold && !mfma_fold && d_latent > sg::kNormMaxD) return SG_ERR_UNSUPPORTED;
   if (!fold && !spans_ok(kMaxTileRows, d_latent, d_latent)) return SG_ERR_UNSUPPORTED;
   const size_t need = sg_workspace_bytes(SG_OP_LATENT_TAIL, M, d_hidden, d_latent);
   if ((st = check_workspace(ws, ws_bytes, need)) != SG_OK) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mfma_fold) {
+    DotProblem p{};
+    p.a = latent;
+    p.lda = d_latent;
+    p.w = w_up;
+    p.ldw = d_latent;
+    p.res = shared;
+    p.ldr = d_hidden;
+    p.out = out;
+    p.ldc = d_hidden;
+    p.M = M;
+    p.N = d_hidden;
+    p.K = d_latent;
+    p.gamma = gamma;
+    p.eps = eps;
+    return enqueue_dot(p, c, ws, s);
+  }
   if (!fold) {
     // RMSNorm into a bf16 buffer at the start of the workspace, then the GEMM
     // with the shared-expert add in its epilogue.

@@ -62,6 +62,8 @@ struct MfmaArgs {
   int n_split;
   int M, N, K;
   int sps;  // k-steps (32 k) per split
+  const uint16_t* gamma;  // RMSNorm fold (wave-split kernel): gamma[K], else unused
+  float eps;
 };
 
 // One launch covers one or two segments: independent problems whose
@@ -246,8 +248,19 @@ __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaLaunch L) {
 // ---- wave-split LDS tile (M <= 16) ------------------------------------------------
 
 constexpr int kSplitWaves = 4;
+// RMSNorm fold: the latent row is read in at most this many 16-byte chunks
+// per lane (d_latent <= 2048), and one wave's K-range of gamma fits one copy.
+constexpr int kFoldChunks = 4;
+constexpr int kFoldMaxK = kFoldChunks * kWave * 8;
 
-template <int XQ, int C>
+// NORM (the latent-MoE tail): the activation rows are the raw latent L.  Each
+// wave first computes r[m] = 1/sqrt(mean(L[m,:]^2) + eps) for the rows it
+// owns (m = wave + 4j), from whole rows read into registers while its ring's
+// first chunks are in flight, and stages its K-range of gamma in LDS; every
+// activation fragment is then normalised in registers, n = bf16((L * r) *
+// gamma), before its MFMA: the rounding of the bf16 normalised latent that a
+// separate RMSNorm kernel would store.
+template <int XQ, int C, bool NORM>
 __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch L) {
   extern __shared__ u32x4 lds[];
   int tile, split;
@@ -281,6 +294,15 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
   const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(((g.M - 1) * g.lda + g.K) * 2));
   const int dr = lane >> 4;
   const int dp = lane & 15;
+  // Behind the rings (NORM): 64 gamma pieces per wave, then r[16].
+  u32x4* gam = lds + kSplitWaves * C * SLOT + wave * kWave;
+  float* rsc = reinterpret_cast<float*>(lds + kSplitWaves * C * SLOT + kSplitWaves * kWave);
+  if constexpr (NORM) {
+    const rsrc_t gres = make_rsrc(g.gamma, static_cast<uint32_t>(g.K * 2));
+    const uint32_t off =
+        (lane < npieces && c0 + lane < K8) ? static_cast<uint32_t>((c0 + lane) * 16) : kOob;
+    copy16_to_lds(gres, gam, off);
+  }
   auto issue = [&](int q) {
     u32x4* slot = ring + (q % C) * SLOT;
 #pragma unroll
@@ -306,6 +328,40 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
 #pragma unroll
   for (int q = 0; q < C - 1; ++q) issue(q);
 
+  float rn = 0.f;  // NORM: r of this lane's activation row (0 past the rows)
+  if constexpr (NORM) {
+    u32x4 lv[XQ][kFoldChunks];
+#pragma unroll
+    for (int j = 0; j < XQ; ++j) {
+      const int m = wave + 4 * j;
+#pragma unroll
+      for (int i = 0; i < kFoldChunks; ++i) {
+        const int c = lane + kWave * i;
+        const uint32_t off =
+            (m < g.M && c < K8) ? static_cast<uint32_t>((m * g.lda + c * 8) * 2) : kOob;
+        lv[j][i] = buf_load(xres, off);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < XQ; ++j) {
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < kFoldChunks; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float l0 = bf16_lo(lv[j][i][e]), l1 = bf16_hi(lv[j][i][e]);
+          ss = fmaf(l0, l0, ss);
+          ss = fmaf(l1, l1, ss);
+        }
+      ss = wave_allreduce(ss);
+      const int m = wave + 4 * j;
+      if (lane == 0)
+        rsc[m] = m < g.M ? __frsqrt_rn(ss / static_cast<float>(g.K) + g.eps) : 0.f;
+    }
+    __syncthreads();  // r of every row is in LDS
+    rn = rl < XROWS ? rsc[rl] : 0.f;
+  }
+
   const Res4 res = load_res4(g, rl, row0 + 4 * kg);
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   const int xr = rl < XROWS ? rl : XROWS - 1;
@@ -317,6 +373,18 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
     for (int t = 0; t < kChunkSteps; ++t) {
       wf[t] = slot[rl * kPieces + ((4 * t + kg) ^ rl)];
       xf[t] = slot[(16 + xr) * kPieces + ((4 * t + kg) ^ xr)];
+    }
+    if constexpr (NORM) {
+#pragma unroll
+      for (int t = 0; t < kChunkSteps; ++t) {
+        const u32x4 gv = gam[kPieces * q + 4 * t + kg];
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = pack_bf16x2(bf16_lo(xf[t][e]) * rn * bf16_lo(gv[e]),
+                             bf16_hi(xf[t][e]) * rn * bf16_hi(gv[e]));
+        xf[t] = o;
+      }
     }
     wait_lgkmcnt0();  // the slot is in registers before the copy below refills the ring
     issue(q + C - 1);
@@ -484,15 +552,26 @@ hipError_t launch_tile_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int XQ, int C>
+template <int XQ, int C, bool NORM>
 hipError_t launch_wsplit_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
-  auto kern = wsplit_kernel<XQ, C>;
+  auto kern = wsplit_kernel<XQ, C, NORM>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       static_cast<int>(kMfmaMaxLds));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(wgs), dim3(kSplitWaves * kWave), wsplit_lds_bytes(C, XQ), s, L);
+  hipLaunchKernelGGL(kern, dim3(wgs), dim3(kSplitWaves * kWave), wsplit_lds_bytes(C, XQ, NORM), s, L);
   return hipGetLastError();
+}
+
+template <bool NORM>
+hipError_t launch_wsplit_xq(const MfmaLaunch& L, int XQ, int wgs, hipStream_t s) {
+  switch (XQ) {
+    case 1: return launch_wsplit_inst<1, 3, NORM>(L, wgs, s);
+    case 2: return launch_wsplit_inst<2, 3, NORM>(L, wgs, s);
+    case 3: return launch_wsplit_inst<3, 3, NORM>(L, wgs, s);
+    case 4: return launch_wsplit_inst<4, 3, NORM>(L, wgs, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int C>
@@ -527,8 +606,18 @@ size_t block_lds_bytes(int c) {
   return static_cast<size_t>(c) * (kBlkRows + kBlkM) * kPieces * 16;
 }
 
-size_t wsplit_lds_bytes(int c, int xq) {
-  return static_cast<size_t>(kSplitWaves) * c * (16 + 4 * xq) * kPieces * 16;
+size_t wsplit_lds_bytes(int c, int xq, bool norm) {
+  const size_t rings = static_cast<size_t>(kSplitWaves) * c * (16 + 4 * xq) * kPieces * 16;
+  return rings + (norm ? kSplitWaves * kWave * 16 + 16 * sizeof(float) : 0);
+}
+
+bool wsplit_fold_fits(int K, int k_split) {
+  // Whole latent rows in kFoldChunks chunks per lane; each wave's K-range of
+  // gamma in one 64-piece copy (at most 16 k-steps per wave).
+  const int ks = ksteps_of(K);
+  const int S = k_split > 0 ? k_split : 1;
+  const int sps = (ks + S - 1) / S;
+  return K > 0 && K <= kFoldMaxK && (sps + kSplitWaves - 1) / kSplitWaves <= 16;
 }
 
 bool mfma_same_instance(const sg_config_t& a, const sg_config_t& b) {
@@ -569,6 +658,8 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
     g.M = p.M;
     g.N = p.N;
     g.K = p.K;
+    g.gamma = p.gamma;
+    g.eps = p.eps;
     const int KS = ksteps_of(p.K);
     const int S = c.k_split > 0 ? c.k_split : 1;
     g.sps = (KS + S - 1) / S;
@@ -580,6 +671,8 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
     wgs += sgm.tiles * S;
   }
   if (wgs <= 0) return hipSuccess;
+  if (cfg.kind != SG_KIND_MFMA_WAVESPLIT && (segs[0].gamma != nullptr || (nseg == 2 && segs[1].gamma != nullptr)))
+    return hipErrorInvalidValue;
 
   if (cfg.kind == SG_KIND_MFMA_TILE) {
     const int NW = cfg.waves, C = cfg.k_unroll, XQ = cfg.m_tile / 4;
@@ -620,13 +713,13 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
     const int C = cfg.k_unroll, XQ = cfg.m_tile / 4;
     if (cfg.rows != 16 || cfg.waves != kSplitWaves || (cfg.m_tile % 4) != 0 || C != 3)
       return hipErrorInvalidValue;
-    switch (XQ) {
-      case 1: return launch_wsplit_inst<1, 3>(L, wgs, s);
-      case 2: return launch_wsplit_inst<2, 3>(L, wgs, s);
-      case 3: return launch_wsplit_inst<3, 3>(L, wgs, s);
-      case 4: return launch_wsplit_inst<4, 3>(L, wgs, s);
-      default: return hipErrorInvalidValue;
+    if (segs[0].gamma != nullptr) {
+      // The RMSNorm fold: one segment whose whole rows fit the prologue.
+      if (nseg != 1 || !wsplit_fold_fits(segs[0].K, cfg.k_split)) return hipErrorInvalidValue;
+      return launch_wsplit_xq<true>(L, XQ, wgs, s);
     }
+    if (nseg == 2 && segs[1].gamma != nullptr) return hipErrorInvalidValue;
+    return launch_wsplit_xq<false>(L, XQ, wgs, s);
   }
   if (cfg.kind == SG_KIND_MFMA_BLOCK) {
     if (cfg.rows != kBlkRows || cfg.waves != kBlkWaves || cfg.m_tile % kBlkM != 0) return hipErrorInvalidValue;

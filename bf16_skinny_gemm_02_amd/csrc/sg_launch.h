@@ -63,7 +63,9 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
 // The configuration table keeps both within kMfmaMaxLds.
 constexpr size_t kMfmaMaxLds = 160 * 1024;
 size_t tile_lds_bytes(int nw, int c, int xq);
-size_t wsplit_lds_bytes(int c, int xq);
+size_t wsplit_lds_bytes(int c, int xq, bool norm);
+// Whether the wave-split kernel can fold the RMSNorm for this K and K split.
+bool wsplit_fold_fits(int K, int k_split);
 size_t block_lds_bytes(int c);
 
 // out[m,n] = bf16( sum_{s<S} partial[s][m][n] + res[m,n] ).  The sum runs

@@ -310,10 +310,13 @@ def test_latent_tail_zero_weights_is_shared(device, M):
 
 
 @pytest.mark.parametrize("M,d,D", [(5, 264, 900), (24, 520, 100), (2, 128, 64),
-                                   (3, 1000, 5200), (11, 4104, 6000), (16, 2048, 5136)])
+                                   (3, 1000, 5200), (11, 4104, 6000), (16, 2048, 5136),
+                                   (4, 2048, 1024), (7, 1032, 3000), (12, 2048, 2000),
+                                   (16, 1024, 4096)])
 def test_latent_tail_other_shapes(device, M, d, D):
-    """Shapes that take the split-K, small-latent and folded-RMSNorm (ragged
-    latent, wide output) paths of the tail."""
+    """Shapes that take the split-K, small-latent and folded-RMSNorm paths of
+    the tail: the GEMV fold (M = 1), the wave-split fold (ragged latent, a
+    K split, every activation-row group), and the separate norm kernel."""
     _say(f"latent_moe_tail M={M} d={d} D={D} cfg={sg.sg_select(M, D, d)}")
     L, gamma, w_up, S = synth.tail_inputs(M, seed=123 + M, d=d, D=D)
     out = nan_like((M, D), device)
