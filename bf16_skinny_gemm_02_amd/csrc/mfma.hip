@@ -118,9 +118,37 @@ __device__ __forceinline__ Res4 load_res4(const MfmaArgs& g, int m, int n0) {
 }
 
 // Stores the four outputs (m, n0 .. n0+3) a lane holds.
+// Four consecutive outputs go out as one 16-byte (partials) or 8-byte (bf16)
+// store when they lie in one row of one output and the address is aligned;
+// otherwise element by element.
 __device__ __forceinline__ void store4(const MfmaArgs& g, const f32x4& acc, int m, int n0, int split,
                                        const Res4& res) {
   if (m >= g.M) return;
+  const bool whole = n0 + 3 < g.N;
+  if (g.partial != nullptr) {
+    float* p = g.partial + (static_cast<int64_t>(split) * g.M + m) * g.N + n0;
+    if (whole && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+      *reinterpret_cast<f32x4*>(p) = acc;
+      return;
+    }
+  } else if (whole && !(g.n_split > 0 && n0 < g.n_split && n0 + 3 >= g.n_split)) {
+    uint16_t* p = (g.n_split > 0 && n0 >= g.n_split) ? g.out2 + m * g.ldc2 + (n0 - g.n_split)
+                                                       : g.out + m * g.ldc + n0;
+    if ((reinterpret_cast<uintptr_t>(p) & 7u) == 0) {
+      float v0 = acc[0], v1 = acc[1], v2 = acc[2], v3 = acc[3];
+      if (g.res != nullptr) {
+        v0 += bf16_to_f32(res.v[0]);
+        v1 += bf16_to_f32(res.v[1]);
+        v2 += bf16_to_f32(res.v[2]);
+        v3 += bf16_to_f32(res.v[3]);
+      }
+      uint2 packed;
+      packed.x = pack_bf16x2(v0, v1);
+      packed.y = pack_bf16x2(v2, v3);
+      *reinterpret_cast<uint2*>(p) = packed;
+      return;
+    }
+  }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int n = n0 + v;
