@@ -156,6 +156,23 @@ __device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
     for (int v = 0; v < 4; ++v)
       if (e0 + v < total) acc[v] = sum_splits(g.partial + e0 + v, total, g.S);
   }
+  // The four outputs in one row of one output: one 8-byte store if aligned.
+  if (g.N % 4 == 0 && e0 + 3 < total &&
+      !(g.n_split > 0 && nn[0] < g.n_split && nn[0] + 3 >= g.n_split)) {
+    uint16_t* dst = (g.n_split > 0 && nn[0] >= g.n_split)
+                        ? g.out2 + mm[0] * g.ldc2 + (nn[0] - g.n_split)
+                        : g.out + mm[0] * g.ldc + nn[0];
+    if ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0) {
+      float v4[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) v4[v] = g.res != nullptr ? acc[v] + r[v] : acc[v];
+      uint2 packed;
+      packed.x = pack_bf16x2(v4[0], v4[1]);
+      packed.y = pack_bf16x2(v4[2], v4[3]);
+      *reinterpret_cast<uint2*>(dst) = packed;
+      return;
+    }
+  }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     if (e0 + v >= total) break;
