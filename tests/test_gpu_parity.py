@@ -204,6 +204,58 @@ def test_overlap_graph_replay(device, M):
         del junk
 
 
+def _replay_check(device, capture_fn, outs, eager, reps=4):
+    """Capture capture_fn() on a side stream, replay it `reps` times with
+    eager work and synchronisations in between, and compare every replay
+    with the eager outputs bit for bit."""
+    side = torch.cuda.Stream(device)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            capture_fn()
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(reps):
+        for t in outs:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        junk = torch.ones(1024, device=device).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {rep}"
+        del junk
+
+
+@pytest.mark.parametrize("M", [1, 8, 17, 64, 100])
+def test_qkvg_graph_replay(device, M):
+    """The single-launch (M <= 16), split-K + reduction (M > 16) and block
+    (M > 64) Q/K/V/G paths inside a captured graph."""
+    _say(f"kda_qkvg_proj graph M={M}")
+    x, w = synth.qkvg_inputs(M)
+    xd, wd = dev(x, device), dev(w, device)
+    eager = sg.kda_qkvg_proj(xd, wd)
+    out = torch.empty_like(eager)
+    ws = torch.empty(max(sg.sg_workspace_bytes(sg.SG_OP_GEMM, M, synth.N_QKVG, synth.HIDDEN), 256),
+                     dtype=torch.uint8, device=device)
+    _replay_check(device, lambda: sg.kda_qkvg_proj(xd, wd, out=out, workspace=ws), [out], [eager])
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 64])
+def test_latent_tail_graph_replay(device, M):
+    """The tail's GEMV fold (M = 1), wave-split fold (M = 4) and norm kernel +
+    GEMM (+ reduction) paths inside a captured graph."""
+    _say(f"latent_moe_tail graph M={M}")
+    L, gamma, w_up, S = synth.tail_inputs(M)
+    args = [dev(a, device) for a in (L, gamma, w_up, S)]
+    eager = sg.latent_moe_tail(*args)
+    out = torch.empty_like(eager)
+    ws = torch.empty(max(sg.sg_workspace_bytes(sg.SG_OP_LATENT_TAIL, M, synth.D_HIDDEN,
+                                               synth.D_LATENT), 256),
+                     dtype=torch.uint8, device=device)
+    _replay_check(device, lambda: sg.latent_moe_tail(*args, out=out, workspace=ws), [out], [eager])
+
+
 @pytest.mark.parametrize("M", [1, 3, 8, 16, 17, 64])
 def test_sequential_projection_equals_separate_calls(device, M):
     """The sequential KDA projection (Q/K/V/G and F_A/beta as two segments of
