@@ -84,6 +84,11 @@ def tail_flops(M):
     return 2 * M * D_HID * D_LAT
 
 
+def roofline_time_us(nbytes, flops):
+    """Time at the binding roofline: the larger of the HBM and the MFMA bound."""
+    return max(nbytes / (HBM_PEAK_GBS * 1e3), flops / (MFMA_BF16_PEAK_TFLOPS * 1e6))
+
+
 # ---- graph construction -------------------------------------------------------------
 
 def copies_for(weight_bytes):
@@ -174,6 +179,7 @@ def time_graph(g, stream, reps, warm=3):
 # ---- dominant-kernel roofline leg ---------------------------------------------------
 
 BREAKDOWN_REPS = 20
+BREAKDOWN_REPEATS = 5   # per-M breakdown: median, and the lowest / highest repeat (p10 / p90 of 5)
 
 ROOFLINE_M = 8   # the wave-split MFMA tile serves M = 2..16, five of the nine sweep points
 
@@ -246,8 +252,47 @@ def counters_mode(device):
         for r in range(R):
             sg.kda_qkvg_proj(xd, ws[r], out=out)
     torch.cuda.synchronize()
+    del ws
+    # The MFMA tile paths, once each, for the matrix-core counters: the packed
+    # projection at M = 64 (128-row tiles) and the latent-MoE tail at M = 256
+    # (block tile).
+    pc = ProjectionCase(64, device, None, None, None)
+    pc.call(0, concurrent=False)
+    tc = TailCase(256, device)
+    tc.call(0)
+    torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": COPY_BYTES, "roofline_m": M, "launches": 2 * R,
-                      "algorithmic_bytes_per_launch": qkvg_bytes(M)}), flush=True)
+                      "algorithmic_bytes_per_launch": qkvg_bytes(M),
+                      "mfma_legs": {"projection_m64_flops": proj_flops(64),
+                                    "tail_m256_flops": tail_flops(256)}}), flush=True)
+
+
+# ---- context: launch floor and a plain device copy ---------------------------------
+
+def context_figures(device, stream):
+    """The floor of one graph kernel node (a one-element add, 100 per graph)
+    and the bandwidth of a plain 512 MiB device-to-device copy (bytes read +
+    bytes written), the scale against which the projections' GB/s read."""
+    t = torch.zeros(1, device=device)
+    g = capture(lambda r: t.add_(1.0), 100, stream)
+    floor = time_graph(g, stream, 20) * 1000.0 / 100
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device=device)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        dst.copy_(src)
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(5):
+            dst.copy_(src)
+        stop.record(stream)
+    stop.synchronize()
+    us = start.elapsed_time(stop) * 1000.0 / 5
+    del src, dst
+    return {"graph_kernel_node_floor_us": round(floor, 3),
+            "copy_512MiB_gbs_read_plus_write": round(2 * n / (us * 1e-6) / 1e9, 1)}
 
 
 # ---- CPU baseline -------------------------------------------------------------------
@@ -273,9 +318,17 @@ def cpu_baseline(budget_s=15.0):
         if time.perf_counter() - t0 >= budget_s or passes >= 50:
             break
     dt = time.perf_counter() - t0
+    cpu = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": dt / calls * 1e6, "unit": "us/call", "cores": cores, "kind": "oracle",
             "sample": f"{passes} pass(es) over the KDA projection M sweep {M_SWEEP} "
-                      f"({calls} calls, {dt:.1f} s, fp64 oracle, OpenMP {cores} threads)"}
+                      f"({calls} calls, {dt:.1f} s, fp64 oracle, OpenMP {cores} threads, {cpu})"}
 
 
 # ---- main -----------------------------------------------------------------------------
@@ -360,17 +413,26 @@ def main():
     # back, timed with events on the replay stream.
     breakdown = {}
     for M in M_SWEEP:
-        pu = time_graph(g_proj[M], main_stream, BREAKDOWN_REPS) * 1000.0 / proj[M].R
-        tu = time_graph(g_tail[M], main_stream, BREAKDOWN_REPS) * 1000.0 / tail[M].R
+        ps = sorted(time_graph(g_proj[M], main_stream, BREAKDOWN_REPS) * 1000.0 / proj[M].R
+                    for _ in range(BREAKDOWN_REPEATS))
+        ts = sorted(time_graph(g_tail[M], main_stream, BREAKDOWN_REPS) * 1000.0 / tail[M].R
+                    for _ in range(BREAKDOWN_REPEATS))
+        pu, tu = ps[len(ps) // 2], ts[len(ts) // 2]
         breakdown[str(M)] = {
             "proj_us": round(pu, 3),
+            "proj_us_p10_p90": [round(ps[0], 3), round(ps[-1], 3)],
             "proj_gbs": round(proj_bytes(M) / (pu * 1e-6) / 1e9, 1),
             "proj_hbm_frac": round(proj_bytes(M) / (pu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "proj_tflops": round(proj_flops(M) / (pu * 1e-6) / 1e12, 2),
+            "proj_mfma_frac": round(proj_flops(M) / (pu * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "proj_roofline_frac": round(roofline_time_us(proj_bytes(M), proj_flops(M)) / pu, 4),
             "tail_us": round(tu, 3),
+            "tail_us_p10_p90": [round(ts[0], 3), round(ts[-1], 3)],
             "tail_gbs": round(tail_bytes(M) / (tu * 1e-6) / 1e9, 1),
             "tail_hbm_frac": round(tail_bytes(M) / (tu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "tail_tflops": round(tail_flops(M) / (tu * 1e-6) / 1e12, 2),
+            "tail_mfma_frac": round(tail_flops(M) / (tu * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "tail_roofline_frac": round(roofline_time_us(tail_bytes(M), tail_flops(M)) / tu, 4),
             "weight_copies": [proj[M].R, tail[M].R],
             "schedule": "two_stream" if gate[M] else "one_stream",
         }
@@ -405,6 +467,7 @@ def main():
             b["packed_gemm_then_fb_us"] = round(s2, 3)
             b["two_stream_speedup_vs_one_stream"] = round(one / two, 3)
 
+    context = context_figures(device, main_stream)
     leg = qkvg_kernel_leg(device, ROOFLINE_M)
     roofline = {"bound": "hbm", "achieved": round(leg["gbs"], 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(leg["gbs"] / HBM_PEAK_GBS, 4),
@@ -442,6 +505,7 @@ def main():
         },
         "roofline": roofline,
         "tail_us_per_call": round(tail_value, 3),
+        "context": context,
         "breakdown": breakdown,
     }
     if not args.no_cpu_baseline:
