@@ -358,7 +358,7 @@ extern "C" int latent_moe_tail(const sg_bf16* latent, const sg_bf16* gamma, floa
                                  ((c.kind == SG_KIND_GEMV_ROW || c.kind == SG_KIND_GEMV_SPLITK) &&
                                   c.k_split == 1));
   // 2 <= M <= 16 on the wave-split MFMA tile: the kernel normalises in registers.
-  const bool mfma_fold = c.kind == SG_KIND_MFMA_WAVESPLIT && sg::wsplit_fold_fits(d_latent, c.k_split);
+  const bool mfma_fold = sg::tail_folds(c, d_latent);
   if (!fold && !mfma_fold && d_latent > sg::kNormMaxD) return SG_ERR_UNSUPPORTED;
   if (!fold && !spans_ok(kMaxTileRows, d_latent, d_latent)) return SG_ERR_UNSUPPORTED;
   const size_t need = sg_workspace_bytes(SG_OP_LATENT_TAIL, M, d_hidden, d_latent);

@@ -49,15 +49,6 @@ constexpr int kOverlapMaxTokens = 0;
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// The wave-split tile's RMSNorm fold (latent-MoE tail): whole latent rows of
-// at most 2048 (4 16-byte chunks per lane), and at most 16 k-steps per wave
-// so that one wave's gamma range is one 64-piece copy.
-bool tail_fold_fits(int K, int k_split) {
-  const int ks = ceil_div(K, 32);
-  const int S = k_split > 0 ? k_split : 1;
-  const int sps = ceil_div(ks, S);
-  return K > 0 && K <= 2048 && ceil_div(sps, 4) <= 16;
-}
 
 int pow2_ceil(int v) {
   int p = 1;
@@ -193,6 +184,19 @@ extern "C" int sg_overlap_gate(int M, int x_contiguous, int have_aux_stream, int
 
 namespace sg {
 
+// The one decision on the wave-split tile's RMSNorm fold (latent-MoE tail),
+// shared by the entry point and the workspace size: whole latent rows of at
+// most 2048 (4 16-byte chunks per lane), and at most 16 k-steps per wave so
+// that one wave's gamma range is one 64-piece copy.  The kernel launcher
+// checks the same limits again before it launches.
+bool tail_folds(const sg_config_t& c, int K) {
+  if (c.kind != SG_KIND_MFMA_WAVESPLIT) return false;
+  const int ks = ceil_div(K, 32);
+  const int S = c.k_split > 0 ? c.k_split : 1;
+  const int sps = ceil_div(ks, S);
+  return K > 0 && K <= 2048 && ceil_div(sps, 4) <= 16;
+}
+
 // Workspace regions start on 256-byte boundaries.
 size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 size_t ws_round(size_t b) { return round256(b); }
@@ -223,7 +227,7 @@ extern "C" size_t sg_workspace_bytes(int op, int M, int N, int K) {
       if (gemv1) return 0;
       const size_t part = (c.k_split > 1 && c.kind != SG_KIND_GEMV_SMALLK) ? sg::round256(S * plane) : 0;
       // The wave-split tile normalises in registers: no normalised copy.
-      if (c.kind == SG_KIND_MFMA_WAVESPLIT && tail_fold_fits(K, c.k_split)) return part;
+      if (sg::tail_folds(c, K)) return part;
       return sg::round256(static_cast<size_t>(M) * static_cast<size_t>(K) * 2) + part;
     }
     default:

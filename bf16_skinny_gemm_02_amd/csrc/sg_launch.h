@@ -64,8 +64,12 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
 constexpr size_t kMfmaMaxLds = 160 * 1024;
 size_t tile_lds_bytes(int nw, int c, int xq);
 size_t wsplit_lds_bytes(int c, int xq, bool norm);
-// Whether the wave-split kernel can fold the RMSNorm for this K and K split.
+// Whether the wave-split kernel can fold the RMSNorm for this K and K split
+// (the launcher's own guard).
 bool wsplit_fold_fits(int K, int k_split);
+// Whether latent_moe_tail folds the RMSNorm into the GEMM for configuration c
+// (the single decision the entry point and the workspace size both use).
+bool tail_folds(const sg_config_t& c, int K);
 size_t block_lds_bytes(int c);
 
 // out[m,n] = bf16( sum_{s<S} partial[s][m][n] + res[m,n] ).  The sum runs
