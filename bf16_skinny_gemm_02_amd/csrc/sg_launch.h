@@ -23,8 +23,9 @@ struct DotProblem {
   uint16_t* out;           // [M,N] bf16 output (unused when partial != NULL)
   int64_t ldc;
   int M, N, K;
-  // RMSNorm fold (latent-MoE tail, GEMV kernel only): the activation is
-  // replaced by bf16(a * r[m] * gamma) with r[m] = rsqrt(mean_k a[m,k]^2 + eps).
+  // RMSNorm fold (latent-MoE tail; the GEMV kernel at M = 1 and the
+  // wave-split MFMA tile): the activation is replaced by
+  // bf16((a * r[m]) * gamma) with r[m] = rsqrt(mean_k a[m,k]^2 + eps).
   const uint16_t* gamma;   // [K], non-NULL enables the fold
   float eps;
   // Split-K partials: when non-NULL the kernel writes fp32 partial sums
