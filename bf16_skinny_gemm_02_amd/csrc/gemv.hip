@@ -11,15 +11,18 @@
 // 64 lanes of a wave read 64 consecutive 16-byte chunks of one weight row,
 // one fully coalesced 1 KiB global_load_dwordx4.
 //
-//  1. Each wave issues every weight chunk of its R rows over the workgroup's
+//  1. The workgroup stages its activation rows for the K-range in LDS with
+//     direct global->LDS copies (no registers); the products read them back
+//     with ds_read_b128.  The copies go out first: a wave's vector memory
+//     operations complete in issue order, so the wait for them (and the
+//     RMSNorm fold below) does not wait for the weight stream.
+//  2. Each wave issues every weight chunk of its R rows over the workgroup's
 //     K-range at once (non-temporal loads: each weight byte is used once).
 //     The table keeps the K-range within D steps (a whole 7168-wide row for
 //     R <= 2), so the whole weight stream is requested before the first
-//     product and there is nothing to refill: no waits inside the loop.  On
-//     MI355X a plain streaming read of the same bytes is only ~5% faster.
-//  2. The workgroup stages its activation rows for the K-range in LDS with
-//     direct global->LDS loads (no registers); the products read them back
-//     with ds_read_b128.
+//     product and there is nothing to refill; each step's products start as
+//     soon as it lands.  On MI355X a plain streaming read of the same bytes
+//     is only ~5% faster.
 //  3. acc[m][r] accumulates in fp32 with v_dot2c_f32_bf16; a DPP / permlane
 //     butterfly sums the 64 lanes and lane (m*R + r) stores output (m, r).
 //
@@ -94,7 +97,31 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
   const int total = M * row_chunks;
   const int c_base = s_begin * kWave;
 
-  // 1. Every weight chunk of the workgroup's K-range, issued up front (the
+  // 1. Activation rows of the range into LDS, one 1 KiB step-block per wave
+  //    copy, straight from global memory (no registers; chunks past K read
+  //    zeros), and with the fold gamma over the same range behind them.
+  //    They go out before the weights: a wave's vector memory operations
+  //    complete in issue order, so staging issued after the weight stream
+  //    would land only after all of it, and the normalisation below would
+  //    wait for the whole stream.
+  const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(((M - 1) * g.lda + g.K) * 2));
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    for (int t = wave; t < nst; t += NW) {
+      const int c = c_base + t * kWave + lane;
+      copy16_to_lds(xres, xs + m * row_chunks + t * kWave,
+                    c < K8 ? static_cast<uint32_t>((m * g.lda + c * 8) * 2) : kOob);
+    }
+  }
+  if constexpr (FOLD) {
+    const rsrc_t gres = make_rsrc(g.gamma, static_cast<uint32_t>(g.K * 2));
+    for (int t = wave; t < nst; t += NW) {
+      const int c = c_base + t * kWave + lane;
+      copy16_to_lds(gres, xs + total + t * kWave, c < K8 ? static_cast<uint32_t>(c * 16) : kOob);
+    }
+  }
+
+  // 2. Every weight chunk of the workgroup's K-range, issued up front (the
   //    range is at most D steps, so nothing is reloaded later).  Buffer
   //    loads: rows past N, chunks past K and steps past the range read zero.
   const int wg_row0 = group * NW * R;
@@ -115,43 +142,11 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
     }
   }
 
-  // 2. Activation rows of the range into LDS, one 1 KiB step-block per wave
-  //    instruction, straight from global memory to LDS (no registers).  The
-  //    last, partial step of a ragged K goes through registers with zeros.
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const uint16_t* xrow = g.a + m * g.lda;
-    for (int t = wave; t < nst; t += NW) {
-      const int c0 = c_base + t * kWave;
-      u32x4* dst = xs + m * row_chunks + t * kWave;
-      if (c0 + kWave <= K8) {
-        // Address-space casts: global source, LDS destination.
-        __builtin_amdgcn_global_load_lds(
-            (const void __attribute__((address_space(1)))*)(xrow + static_cast<int64_t>(c0 + lane) * 8),
-            (void __attribute__((address_space(3)))*)(dst), 16, 0, 0);
-      } else {
-        const int c = c0 + lane;
-        dst[lane] = (c < K8) ? load_cached(xrow + static_cast<int64_t>(c) * 8) : zero4();
-      }
-    }
-  }
-  if constexpr (FOLD) {
-    // gamma over the same range, staged behind the activation rows in the
-    // same way, so the normalisation below waits for no second round trip.
-    for (int t = wave; t < nst; t += NW) {
-      const int c0 = c_base + t * kWave;
-      u32x4* dst = xs + total + t * kWave;
-      if (c0 + kWave <= K8) {
-        __builtin_amdgcn_global_load_lds(
-            (const void __attribute__((address_space(1)))*)(g.gamma + static_cast<int64_t>(c0 + lane) * 8),
-            (void __attribute__((address_space(3)))*)(dst), 16, 0, 0);
-      } else {
-        const int c = c0 + lane;
-        dst[lane] = (c < K8) ? load_cached(g.gamma + static_cast<int64_t>(c) * 8) : zero4();
-      }
-    }
-  }
-  __syncthreads();
+  // This wave's staging has landed once at most its D * R weight loads are
+  // outstanding; the barrier makes that so for every wave.  (A full
+  // __syncthreads would also wait for the weights.)
+  wait_vmcnt<D * R>();
+  __builtin_amdgcn_s_barrier();
 
   if constexpr (FOLD) {
     // RMSNorm over the whole row (the host runs the fold with one split).
@@ -170,7 +165,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
       }
       rs[m] = __frsqrt_rn(wave_allreduce(ss) / static_cast<float>(g.K) + g.eps);
     }
-    __syncthreads();  // every wave has read the raw latent
+    __builtin_amdgcn_s_barrier();  // every wave has read the raw latent
     for (int q = tid; q < total; q += kThreads) {
       const int m = q / row_chunks;
       const int c = q - m * row_chunks;
@@ -187,11 +182,13 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
         xs[q] = o;
       }
     }
-    __syncthreads();
+    wait_lgkmcnt0();  // the normalised latent is in LDS
+    __builtin_amdgcn_s_barrier();
   }
   if (!active) return;  // no barrier follows
 
-  // 3. Products: every weight step is already in flight.
+  // 3. Products: every weight step is already in flight; each is used as
+  //    soon as it lands.
   float acc[M][R];
 #pragma unroll
   for (int m = 0; m < M; ++m)
