@@ -21,10 +21,12 @@ the next two: ``value`` is the projection half's time over its calls,
 tail µs, GB/s, fraction of HBM peak) is measured after the timed region, each
 graph replayed back to back.  ``--comparators`` adds, per M, the forced
 two-stream schedule (fork/join events, F_A/beta -> F_B on an aux stream), the
-forced single-stream schedule, and a plain packed GEMM followed by a second
-GEMM for F_B.  The line also carries the roofline of the dominant kernel (the
-wave-split MFMA tile at M = 8, with the M = 1 GEMV beside it, each timed with
-HIP events on its own stream) and the CPU oracle timed on this host.
+forced single-stream schedule, a plain packed GEMM followed by a second GEMM
+for F_B, and the vendor library on the same work (torch.mm / addmm, i.e.
+hipBLASLt, with the RMSNorm in unfused torch ops).  The line also carries the
+roofline of the dominant kernel (the wave-split MFMA tile at M = 8, with the
+M = 1 GEMV beside it, each timed with HIP events on its own stream) and the
+CPU oracle timed on this host.
 """
 from __future__ import annotations
 
@@ -341,8 +343,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--comparators", action="store_true",
-                    help="also time the forced two-stream and one-stream schedules and a plain "
-                         "packed GEMM followed by F_B")
+                    help="also time the forced two-stream and one-stream schedules, a plain "
+                         "packed GEMM followed by F_B, and the same work through torch "
+                         "(hipBLASLt) with an unfused RMSNorm")
     ap.add_argument("--counters", action="store_true",
                     help="counter-collection mode for rocprofv3 --pmc: a plain device copy of "
                          "known size (calibration), then the roofline kernel launched eagerly "
@@ -461,11 +464,38 @@ def main():
 
             g_s2 = capture(s2_call, c.R, main_stream)
             s2 = time_graph(g_s2, main_stream, 10) * 1000.0 / c.R
+            # The vendor library on the same work: torch.mm (hipBLASLt) over the packed
+            # weight, then a second torch.mm for F_B on the bf16 f_a columns.
+            out_t = torch.empty((M, N_QKVG + N_AB), dtype=torch.bfloat16, device=device)
+            g1_t = torch.empty((M, N_B), dtype=torch.bfloat16, device=device)
+
+            def blas_proj(r, c=c, out_t=out_t, g1_t=g1_t, pw=pw):
+                torch.mm(c.x, pw[r].t(), out=out_t)
+                torch.mm(out_t[:, N_QKVG:N_QKVG + RANK], c.w_b[r].t(), out=g1_t)
+
+            g_bp = capture(blas_proj, c.R, main_stream)
+            bp = time_graph(g_bp, main_stream, 10) * 1000.0 / c.R
+            # ... and the unfused latent-MoE tail: RMSNorm in torch ops (fp32, bf16
+            # result), then torch.addmm with the shared-expert partial.
+            tc = tail[M]
+            out_tt = torch.empty((M, D_HID), dtype=torch.bfloat16, device=device)
+
+            def blas_tail(r, tc=tc, out_tt=out_tt):
+                lf = tc.L.float()
+                n = (lf * torch.rsqrt(lf.pow(2).mean(-1, keepdim=True) + 1e-6) *
+                     tc.gamma.float()).to(torch.bfloat16)
+                torch.addmm(tc.S, n, tc.w_up[r].t(), out=out_tt)
+
+            g_bt = capture(blas_tail, tc.R, main_stream)
+            bt = time_graph(g_bt, main_stream, 10) * 1000.0 / tc.R
             b = breakdown[str(M)]
             b["two_stream_us"] = round(two, 3)
             b["one_stream_us"] = round(one, 3)
             b["packed_gemm_then_fb_us"] = round(s2, 3)
             b["two_stream_speedup_vs_one_stream"] = round(one / two, 3)
+            b["torch_blas_projection_us"] = round(bp, 3)
+            b["torch_blas_tail_us"] = round(bt, 3)
+            del g_two, g_one, g_s2, g_bp, g_bt
 
     context = context_figures(device, main_stream)
     leg = qkvg_kernel_leg(device, ROOFLINE_M)

@@ -197,6 +197,10 @@ bool tail_folds(const sg_config_t& c, int K) {
   return K > 0 && K <= 2048 && ceil_div(sps, 4) <= 16;
 }
 
+// The packed projection's F_A/beta rows store bf16 P themselves (no fp32
+// partials) when they run whole on the row GEMV.
+bool kda_fab_direct(const sg_config_t& c) { return c.kind == SG_KIND_GEMV_ROW && c.k_split == 1; }
+
 // Workspace regions start on 256-byte boundaries.
 size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 size_t ws_round(size_t b) { return round256(b); }
@@ -282,6 +286,14 @@ extern "C" int sg_kda_select(int which, int M, int K, int n_qkvg, int n_ab, sg_c
     *out = f;
     return SG_OK;
   }
+  // M = 1 with the Q/K/V/G rows on the whole-row GEMV: the F_A/beta rows join
+  // them as a second segment of the same instance, whole rows too, and store
+  // bf16 P directly (no K split: the F_B stage then reads P instead of summing
+  // partials, and the launch has no extra split-K workgroups).
+  if (q.kind == SG_KIND_GEMV_ROW && q.k_split == 1) {
+    f = q;
+    f.grid = ceil_div(n_ab, q.waves * q.rows);
+  }
   // 2 <= M <= 64: the table's wave-split and 64-row tiles give the Q/K/V/G
   // rows alone 256 workgroups, one per CU, so the F_A/beta segment would start
   // a second round.  Both ranges move to 128-row tiles with one K split sized
@@ -319,7 +331,10 @@ extern "C" size_t sg_kda_workspace_bytes(int which, int M, int K, int n_qkvg, in
   if (sg_kda_select(which, M, K, n_qkvg, n_ab, &c) != SG_OK || c.kind == SG_KIND_NONE) return 0;
   const int N = (which == SG_KDA_QKVG) ? n_qkvg : n_ab;
   const size_t plane = static_cast<size_t>(M) * static_cast<size_t>(N) * sizeof(float);
-  // Q/K/V/G: split-K partials only when K is split.  F_A/beta: always partials.
+  // Q/K/V/G: split-K partials only when K is split.  F_A/beta: bf16 P when
+  // its rows run whole on the GEMV, else fp32 partials.
   if (which == SG_KDA_QKVG && c.k_split <= 1) return 0;
+  if (which == SG_KDA_FAB && sg::kda_fab_direct(c))
+    return sg::round256(static_cast<size_t>(M) * static_cast<size_t>(N) * sizeof(uint16_t));
   return sg::round256(static_cast<size_t>(c.k_split) * plane);
 }

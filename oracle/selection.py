@@ -47,14 +47,17 @@ packed projection, 2 F_A/beta alone):
     GEMV_SPLITK (M == 1: m_tile 1, rows 1, waves 4, k_unroll 16,
     grid ceil(n_ab / 4)) or MFMA_WAVESPLIT (M > 1: m_tile 4 ceil(M / 4),
     rows 16, waves 4, k_unroll 3, grid ceil(n_ab / 16)); k_split >= 1.
-  * which 2: f.  Otherwise q = select(M, n_qkvg, K), and if q and f are both
+  * which 2: f.  Otherwise q = select(M, n_qkvg, K).  If q is GEMV_ROW with
+    k_split 1, f becomes q's configuration with grid ceil(n_ab / (4 rows)).
+    Else, if q and f are both
     MFMA_WAVESPLIT or MFMA_TILE: with t_q = ceil(n_qkvg / 128), t_f =
     ceil(n_ab / 128), ksteps = ceil(K / 32), S = split(ksteps,
     min(256 // (t_q + t_f), max(1, ksteps // 8))), both become MFMA_TILE with
     m_tile 4 ceil(M / 4) (M <= 16) or 16 ceil(M / 16), rows 128, waves 8,
     k_unroll 3, k_split S, grid t * S.
   * workspace: Q/K/V/G k_split * M * n_qkvg * 4 (0 when k_split <= 1),
-    F_A/beta k_split * M * n_ab * 4, each rounded up to 256.
+    F_A/beta M * n_ab * 2 when it is GEMV_ROW with k_split 1 (bf16 P), else
+    k_split * M * n_ab * 4, each rounded up to 256.
 """
 from __future__ import annotations
 
@@ -165,6 +168,8 @@ def kda_select(which: int, M: int, K: int, n_qkvg: int, n_ab: int):
     f["k_split"] = max(f["k_split"], 1)
     if which == 2:
         return OK, f
+    if q["kind"] == GEMV_ROW and q["k_split"] == 1:
+        f = dict(q, grid=_cdiv(n_ab, q["waves"] * q["rows"]))
     small = (MFMA_WAVESPLIT, MFMA_TILE)
     if q["kind"] in small and f["kind"] in small:
         tq, tf = _cdiv(n_qkvg, 128), _cdiv(n_ab, 128)
@@ -185,5 +190,7 @@ def kda_workspace_bytes(which: int, M: int, K: int, n_qkvg: int, n_ab: int) -> i
         return 0
     if which == 0 and c["k_split"] <= 1:
         return 0
+    if which == 1 and c["kind"] == GEMV_ROW and c["k_split"] == 1:
+        return -(-(M * n_ab * 2) // 256) * 256
     n = n_qkvg if which == 0 else n_ab
     return -(-(c["k_split"] * M * n * 4) // 256) * 256
