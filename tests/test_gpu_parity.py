@@ -380,6 +380,29 @@ def test_latent_tail_other_shapes(device, M, d, D):
     assert_close(host(out), ex, f"tail {M}x{d}->{D}")
 
 
+@pytest.mark.parametrize("M,d,D", [(17, 2048, 7168), (32, 2048, 7168), (64, 2048, 7168),
+                                   (24, 4104, 640), (40, 520, 1000)])
+def test_latent_tail_split_k_reused_workspace(device, M, d, D):
+    """The tail's norm launch, split-K tile GEMM and fixed-order reduction
+    share one workspace (normalised latent, then partials).  One workspace,
+    first filled with 0xFF bytes, serves three calls on different inputs:
+    every call must match the oracle, so nothing of another call (or of the
+    fill) can leak into a result."""
+    cfg = sg.sg_select(M, D, d)
+    _say(f"latent_moe_tail split-K M={M} d={d} D={D} cfg={cfg}")
+    assert cfg["kind"] == sg.SG_KIND_MFMA_TILE and cfg["k_split"] > 1
+    ws = torch.full((sg.sg_workspace_bytes(sg.SG_OP_LATENT_TAIL, M, D, d),), 255,
+                    dtype=torch.uint8, device=device)
+    for seed in (7, 8, 9):
+        L, gamma, w_up, S = synth.tail_inputs(M, seed=seed * 1000 + M, d=d, D=D)
+        out = nan_like((M, D), device)
+        sg.latent_moe_tail(dev(L, device), dev(gamma, device), dev(w_up, device), dev(S, device),
+                           out=out, workspace=ws)
+        torch.cuda.synchronize()
+        ex, _ = oracle.latent_tail(L, gamma, 1e-6, w_up, S)
+        assert_close(host(out), ex, f"split-K tail {M}x{d}->{D} seed {seed}")
+
+
 def test_empty_problems_are_noops(device):
     x = torch.zeros((0, 7168), dtype=torch.bfloat16, device=device)
     w = torch.zeros((4096, 7168), dtype=torch.bfloat16, device=device)
