@@ -87,6 +87,7 @@ struct FbArgs {
 // s = 0, 1, ..., S-1.  Loads go out kSumBatch at a time, so a sum over S
 // partials costs ceil(S / kSumBatch) memory round trips, not S.
 constexpr int kSumBatch = 16;
+constexpr int kRedBatch = 4;  // f32x4 partial loads in flight per thread in the reduction
 
 __device__ __forceinline__ float sum_splits(const float* p, int64_t plane, int S) {
   float acc = 0.f;
@@ -117,7 +118,7 @@ struct ReduceArgs {
 // Four consecutive elements (flat index over [M][N]) per thread.  The
 // residual is requested before the partial sums so the two loads overlap;
 // the S partials are summed in the fixed order s = 0..S-1.
-template <bool VEC>
+template <bool VEC, bool RES, bool BATCHED>
 __device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
   const int64_t total = static_cast<int64_t>(g.M) * g.N;
   const int64_t e0 = (static_cast<int64_t>(block) * 256 + threadIdx.x) * 4;
@@ -126,27 +127,44 @@ __device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
   float r[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int64_t e = e0 + v;
+    // Past the end the index is clamped to the last element: it is loaded
+    // (a valid address) but neither added nor stored.  Loads outside
+    // branches go out together instead of one memory round trip each.
+    const int64_t e = min(e0 + v, total - 1);
     mm[v] = static_cast<int>(e / g.N);
     nn[v] = static_cast<int>(e - static_cast<int64_t>(mm[v]) * g.N);
-    if (g.res != nullptr && e < total) r[v] = bf16_to_f32(g.res[mm[v] * g.ldr + nn[v]]);
+  }
+  // RES (g.res != NULL): the residual is requested first, outside any
+  // branch, and widened only after the partials are summed, so its loads and
+  // the partials' share one memory round trip.
+  uint16_t rv[4] = {0, 0, 0, 0};
+  if constexpr (RES) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) rv[v] = g.res[mm[v] * g.ldr + nn[v]];
   }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   if constexpr (VEC) {
-    // total % 4 == 0: every plane starts 16-byte aligned.
+    // total % 4 == 0: every plane starts 16-byte aligned.  BATCHED: the
+    // partials go out four at a time before any of them is added (a sum over
+    // S <= 4 splits waits for one memory round trip); otherwise whole groups
+    // of four, then one at a time (fewer registers: measured faster for the
+    // reduction role of the F_B launch).  Either way they are added in the
+    // order s = 0, 1, ..., S-1.
     const f32x4* p = reinterpret_cast<const f32x4*>(g.partial + e0);
     const int64_t plane4 = total / 4;
-    int s = 0;
-    for (; s + 4 <= g.S; s += 4) {
-      f32x4 t[4];
+    const int s_batched = BATCHED ? g.S : (g.S / 4) * 4;
+    for (int s = 0; s < s_batched; s += kRedBatch) {
+      f32x4 t[kRedBatch];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) t[k] = p[(s + k) * plane4];
+      for (int k = 0; k < kRedBatch; ++k)
+        t[k] = (s + k < g.S) ? p[(s + k) * plane4] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < kRedBatch; ++k)
+        if (s + k < g.S)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[v] += t[k][v];
+          for (int v = 0; v < 4; ++v) acc[v] += t[k][v];
     }
-    for (; s < g.S; ++s) {
+    for (int s = s_batched; s < g.S; ++s) {
       const f32x4 t = p[s * plane4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[v] += t[v];
@@ -155,6 +173,10 @@ __device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
 #pragma unroll
     for (int v = 0; v < 4; ++v)
       if (e0 + v < total) acc[v] = sum_splits(g.partial + e0 + v, total, g.S);
+  }
+  if constexpr (RES) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) r[v] = (e0 + v < total) ? bf16_to_f32(rv[v]) : 0.f;
   }
   // The four outputs in one row of one output: one 8-byte store if aligned.
   if (g.N % 4 == 0 && e0 + 3 < total &&
@@ -165,7 +187,7 @@ __device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
     if ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0) {
       float v4[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) v4[v] = g.res != nullptr ? acc[v] + r[v] : acc[v];
+      for (int v = 0; v < 4; ++v) v4[v] = RES ? acc[v] + r[v] : acc[v];
       uint2 packed;
       packed.x = pack_bf16x2(v4[0], v4[1]);
       packed.y = pack_bf16x2(v4[2], v4[3]);
@@ -176,7 +198,7 @@ __device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     if (e0 + v >= total) break;
-    const float val = g.res != nullptr ? acc[v] + r[v] : acc[v];
+    const float val = RES ? acc[v] + r[v] : acc[v];
     if (g.n_split > 0 && nn[v] >= g.n_split)
       g.out2[mm[v] * g.ldc2 + (nn[v] - g.n_split)] = f32_to_bf16(val);
     else
@@ -184,9 +206,9 @@ __device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
   }
 }
 
-template <bool VEC>
+template <bool VEC, bool RES>
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs g) {
-  reduce_block<VEC>(g, static_cast<int>(blockIdx.x));
+  reduce_block<VEC, RES, true>(g, static_cast<int>(blockIdx.x));
 }
 
 // Rows of w_b one F_B workgroup covers: one row per group of G lanes, every
@@ -215,7 +237,7 @@ __global__ __launch_bounds__(kSmallkWaves * kWave) void fab_fb_tail_kernel(FbArg
   int b = static_cast<int>(blockIdx.x);
   if constexpr (RED != 0) {
     if (b < red_wgs) {
-      reduce_block<RED == 1>(red, b);
+      reduce_block<RED == 1, false, false>(red, b);  // the projection's rows: no residual
       return;
     }
     b -= red_wgs;
@@ -402,6 +424,7 @@ hipError_t launch_fab_fb_tail(const FbProblem& p, hipStream_t s) {
   FbArgs g{p.partial, p.p_bf16, p.S, p.M, p.n_ab, p.rank, p.n_b, p.w_b, p.f_a, p.beta, p.g1};
   ReduceArgs r{};
   int red_wgs = 0, red_mode = 0;
+  if (p.red != nullptr && p.red->res != nullptr) return hipErrorInvalidValue;  // no residual role
   if (p.red != nullptr && reduce_blocks(*p.red) > 0) {
     r = reduce_args(*p.red);
     red_wgs = reduce_blocks(*p.red);
@@ -423,10 +446,15 @@ hipError_t launch_reduce(const ReduceProblem& p, hipStream_t s) {
   const int blocks = reduce_blocks(p);
   if (blocks < 1) return hipSuccess;
   const ReduceArgs g = reduce_args(p);
-  if (reduce_vec(p))
-    hipLaunchKernelGGL(reduce_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, g);
-  else
-    hipLaunchKernelGGL(reduce_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, g);
+  const dim3 grid(static_cast<unsigned>(blocks));
+  const bool res = p.res != nullptr;
+  if (reduce_vec(p)) {
+    if (res) hipLaunchKernelGGL((reduce_kernel<true, true>), grid, dim3(256), 0, s, g);
+    else hipLaunchKernelGGL((reduce_kernel<true, false>), grid, dim3(256), 0, s, g);
+  } else {
+    if (res) hipLaunchKernelGGL((reduce_kernel<false, true>), grid, dim3(256), 0, s, g);
+    else hipLaunchKernelGGL((reduce_kernel<false, false>), grid, dim3(256), 0, s, g);
+  }
   return hipGetLastError();
 }
 
