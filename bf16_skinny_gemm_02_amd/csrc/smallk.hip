@@ -219,6 +219,8 @@ constexpr int fb_rows_per_wg() { return kSmallkWaves * (kWave / G); }
 // P elements one F_B thread forms per pass (4 rows x 136 columns = 544 fit in
 // one pass of 256 threads x 3).
 constexpr int kFbPer = 3;
+// Splits the F_B stage requests per batch when it sums the F_A/beta partials.
+constexpr int kFbBatch = 8;
 
 // Workgroup (x, y) computes g1 rows [x*R, (x+1)*R), R = fb_rows_per_wg<G>(),
 // for activation rows [y*kFbMGroup, (y+1)*kFbMGroup).  Its w_b chunk is
@@ -262,38 +264,86 @@ __global__ __launch_bounds__(kSmallkWaves * kWave) void fab_fb_tail_kernel(FbArg
 
   // 1. P = bf16(sum_s partial[s][m][j]) for this workgroup's rows; all n_ab
   //    columns in the first column of workgroups, the rank f_a columns
-  //    elsewhere.  kFbPer elements per thread per pass, their loads issued
-  //    together.
+  //    elsewhere.  kFbPer elements per thread per pass.  The first pass
+  //    (every element when mg * cols <= kFbPer * nthreads, the usual case)
+  //    is straight-line code: with at most kSumBatch splits all its loads go
+  //    out together, behind the w_b load, and nothing waits for them until
+  //    the sums (one memory round trip).  Past the end of the rows a thread
+  //    loads element 0 (in bounds) and discards it.
   const int cols = first ? g.n_ab : g.rank;
   const int count = mg * cols;
-  for (int base = 0; base < count; base += kFbPer * nthreads) {
+  auto place = [&](int idx, uint16_t b) {
+    if (idx >= count) return;
+    const int mm = idx / cols, jj = idx - mm * cols;
+    const int m = m0 + mm;
+    if (jj < g.rank) {
+      fa_lds[mm * g.rank + jj] = b;
+      if (first && g.f_a != nullptr) g.f_a[static_cast<int64_t>(m) * g.rank + jj] = b;
+    } else {
+      g.beta[static_cast<int64_t>(m) * (g.n_ab - g.rank) + (jj - g.rank)] = b;
+    }
+  };
+  auto element = [&](int idx) -> int64_t {
+    if (idx >= count) return 0;
+    const int mm = idx / cols, jj = idx - mm * cols;
+    return static_cast<int64_t>(m0 + mm) * g.n_ab + jj;
+  };
+  int base = 0;
+  if (!PARTIALS || g.S <= kSumBatch) {
+    int64_t off[kFbPer];
+#pragma unroll
+    for (int e = 0; e < kFbPer; ++e) off[e] = element(e * nthreads + tid);
+    uint16_t b[kFbPer];
+    if constexpr (PARTIALS) {
+      // Splits in two straight-line batches of kFbBatch (the second only
+      // when S > kFbBatch); a batch's loads are unconditional (split indices
+      // past S - 1 repeat the last one) and the scheduling barrier keeps
+      // every load of a batch ahead of its first addition.  The additions
+      // run in the order s = 0, 1, ..., S-1.
+      float acc[kFbPer] = {0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < kSumBatch / kFbBatch; ++h) {
+        if (h > 0 && g.S <= h * kFbBatch) break;
+        float v[kFbPer][kFbBatch];
+#pragma unroll
+        for (int i = 0; i < kFbBatch; ++i) {
+          const int64_t si = min(h * kFbBatch + i, g.S - 1);
+#pragma unroll
+          for (int e = 0; e < kFbPer; ++e) v[e][i] = g.partial[off[e] + si * plane];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = 0; e < kFbPer; ++e)
+#pragma unroll
+          for (int i = 0; i < kFbBatch; ++i)
+            if (h * kFbBatch + i < g.S) acc[e] += v[e][i];
+      }
+#pragma unroll
+      for (int e = 0; e < kFbPer; ++e) b[e] = f32_to_bf16(acc[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kFbPer; ++e) b[e] = g.p_bf16[off[e]];
+    }
+#pragma unroll
+    for (int e = 0; e < kFbPer; ++e) place(e * nthreads + tid, b[e]);
+    base = kFbPer * nthreads;
+  }
+  for (; base < count; base += kFbPer * nthreads) {
     uint16_t b[kFbPer];
 #pragma unroll
     for (int e = 0; e < kFbPer; ++e) {
       const int idx = base + e * nthreads + tid;
       b[e] = 0;
       if (idx < count) {
-        const int mm = idx / cols, jj = idx - mm * cols;
-        const int64_t off = static_cast<int64_t>(m0 + mm) * g.n_ab + jj;
+        const int64_t o = element(idx);
         if constexpr (PARTIALS)
-          b[e] = f32_to_bf16(sum_splits(g.partial + off, plane, g.S));
+          b[e] = f32_to_bf16(sum_splits(g.partial + o, plane, g.S));
         else
-          b[e] = g.p_bf16[off];
+          b[e] = g.p_bf16[o];
       }
     }
 #pragma unroll
-    for (int e = 0; e < kFbPer; ++e) {
-      const int idx = base + e * nthreads + tid;
-      if (idx >= count) continue;
-      const int mm = idx / cols, jj = idx - mm * cols;
-      const int m = m0 + mm;
-      if (jj < g.rank) {
-        fa_lds[mm * g.rank + jj] = b[e];
-        if (first && g.f_a != nullptr) g.f_a[static_cast<int64_t>(m) * g.rank + jj] = b[e];
-      } else {
-        g.beta[static_cast<int64_t>(m) * (g.n_ab - g.rank) + (jj - g.rank)] = b[e];
-      }
-    }
+    for (int e = 0; e < kFbPer; ++e) place(base + e * nthreads + tid, b[e]);
   }
   __syncthreads();
 
