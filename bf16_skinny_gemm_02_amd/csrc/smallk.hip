@@ -87,7 +87,11 @@ struct FbArgs {
 // s = 0, 1, ..., S-1.  Loads go out kSumBatch at a time, so a sum over S
 // partials costs ceil(S / kSumBatch) memory round trips, not S.
 constexpr int kSumBatch = 16;
-constexpr int kRedBatch = 4;  // f32x4 partial loads in flight per thread in the reduction
+constexpr int kRedBatch = 8;  // f32x4 partial loads per straight-line batch per thread
+// How reduce_block requests the partials (see there).
+constexpr int kRedGroups = 0, kRedPredicated = 1, kRedStraight = 2;
+// The F_B launch's reduction role takes kRedStraight up to this many workgroups.
+constexpr int kRedStraightMaxWgs = 64;
 
 __device__ __forceinline__ float sum_splits(const float* p, int64_t plane, int S) {
   float acc = 0.f;
@@ -118,7 +122,7 @@ struct ReduceArgs {
 // Four consecutive elements (flat index over [M][N]) per thread.  The
 // residual is requested before the partial sums so the two loads overlap;
 // the S partials are summed in the fixed order s = 0..S-1.
-template <bool VEC, bool RES, bool BATCHED>
+template <bool VEC, bool RES, int MODE>
 __device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
   const int64_t total = static_cast<int64_t>(g.M) * g.N;
   const int64_t e0 = (static_cast<int64_t>(block) * 256 + threadIdx.x) * 4;
@@ -144,30 +148,54 @@ __device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
   }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   if constexpr (VEC) {
-    // total % 4 == 0: every plane starts 16-byte aligned.  BATCHED: the
-    // partials go out four at a time before any of them is added (a sum over
-    // S <= 4 splits waits for one memory round trip); otherwise whole groups
-    // of four, then one at a time (fewer registers: measured faster for the
-    // reduction role of the F_B launch).  Either way they are added in the
-    // order s = 0, 1, ..., S-1.
+    // total % 4 == 0: every plane starts 16-byte aligned.  Three ways to
+    // request the S partials, each adding them in the order s = 0, 1, ...,
+    // S-1 (so all give the same bits), chosen by measurement:
+    //  * kRedGroups: groups of four requested together, then the remainder
+    //    one by one (fewest registers: the many-workgroup reduction role of
+    //    the F_B launch at larger M);
+    //  * kRedPredicated: predicated groups of four (the reduction launch);
+    //  * kRedStraight: straight-line batches of kRedBatch whose loads are
+    //    unconditional (indices past S - 1 repeat the last split) and kept
+    //    ahead of the first addition by a scheduling barrier, one memory
+    //    round trip per batch (the few-workgroup reduction role at small M,
+    //    where its latency is the launch's critical path).
     const f32x4* p = reinterpret_cast<const f32x4*>(g.partial + e0);
     const int64_t plane4 = total / 4;
-    const int s_batched = BATCHED ? g.S : (g.S / 4) * 4;
-    for (int s = 0; s < s_batched; s += kRedBatch) {
-      f32x4 t[kRedBatch];
+    if constexpr (MODE == kRedStraight) {
+      auto batch = [&](int s0) {
+        f32x4 t[kRedBatch];
 #pragma unroll
-      for (int k = 0; k < kRedBatch; ++k)
-        t[k] = (s + k < g.S) ? p[(s + k) * plane4] : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < kRedBatch; ++k)
+          t[k] = p[static_cast<int64_t>(min(s0 + k, g.S - 1)) * plane4];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int k = 0; k < kRedBatch; ++k)
-        if (s + k < g.S)
+        for (int k = 0; k < kRedBatch; ++k)
+          if (s0 + k < g.S)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) acc[v] += t[k][v];
-    }
-    for (int s = s_batched; s < g.S; ++s) {
-      const f32x4 t = p[s * plane4];
+            for (int v = 0; v < 4; ++v) acc[v] += t[k][v];
+      };
+      batch(0);
+      if (g.S > kRedBatch) batch(kRedBatch);
+      for (int s0 = 2 * kRedBatch; s0 < g.S; s0 += kRedBatch) batch(s0);
+    } else {
+      const int grouped = MODE == kRedPredicated ? g.S : (g.S / 4) * 4;
+      for (int s = 0; s < grouped; s += 4) {
+        f32x4 t[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] += t[v];
+        for (int k = 0; k < 4; ++k)
+          t[k] = (s + k < g.S) ? p[(s + k) * plane4] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (s + k < g.S)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] += t[k][v];
+      }
+      for (int s = grouped; s < g.S; ++s) {
+        const f32x4 t = p[s * plane4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] += t[v];
+      }
     }
   } else {
 #pragma unroll
@@ -208,7 +236,7 @@ __device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
 
 template <bool VEC, bool RES>
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs g) {
-  reduce_block<VEC, RES, true>(g, static_cast<int>(blockIdx.x));
+  reduce_block<VEC, RES, kRedPredicated>(g, static_cast<int>(blockIdx.x));
 }
 
 // Rows of w_b one F_B workgroup covers: one row per group of G lanes, every
@@ -229,7 +257,7 @@ constexpr int kFbBatch = 8;
 // agrees bit for bit, else the bf16 P as stored); f_a goes to LDS, and
 // workgroups with x == 0 also store beta (and f_a).
 //
-// RED (0 none, 1 vector, 2 scalar): the first red_wgs workgroups instead run
+// RED (0 none, 1 vector, 2 scalar, 3 vector straight-line): the first red_wgs workgroups instead run
 // the split-K reduction of another problem (the Q/K/V/G projection that ran
 // beside F_A/beta), so both epilogues take one launch.
 template <int G, bool PARTIALS, int RED>
@@ -239,7 +267,8 @@ __global__ __launch_bounds__(kSmallkWaves * kWave) void fab_fb_tail_kernel(FbArg
   int b = static_cast<int>(blockIdx.x);
   if constexpr (RED != 0) {
     if (b < red_wgs) {
-      reduce_block<RED == 1, false, false>(red, b);  // the projection's rows: no residual
+      // The projection's rows: no residual.
+      reduce_block<RED != 2, false, RED == 3 ? kRedStraight : kRedGroups>(red, b);
       return;
     }
     b -= red_wgs;
@@ -429,10 +458,12 @@ hipError_t launch_fb_g(const FbArgs& g, const ReduceArgs& r, int red_wgs, int re
   if (g.partial != nullptr) {
     if (red_mode == 1) SG_FB(true, 1);
     else if (red_mode == 2) SG_FB(true, 2);
+    else if (red_mode == 3) SG_FB(true, 3);
     else SG_FB(true, 0);
   } else {
     if (red_mode == 1) SG_FB(false, 1);
     else if (red_mode == 2) SG_FB(false, 2);
+    else if (red_mode == 3) SG_FB(false, 3);
     else SG_FB(false, 0);
   }
 #undef SG_FB
@@ -478,7 +509,7 @@ hipError_t launch_fab_fb_tail(const FbProblem& p, hipStream_t s) {
   if (p.red != nullptr && reduce_blocks(*p.red) > 0) {
     r = reduce_args(*p.red);
     red_wgs = reduce_blocks(*p.red);
-    red_mode = reduce_vec(*p.red) ? 1 : 2;
+    red_mode = reduce_vec(*p.red) ? (red_wgs <= kRedStraightMaxWgs ? 3 : 1) : 2;
   }
   switch (lanes_for(p.rank >> 3)) {
     case 1: return launch_fb_g<1>(g, r, red_wgs, red_mode, s);
