@@ -100,19 +100,28 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 // The residual values of the four outputs (m, n0 .. n0+3) a lane will store,
-// requested when the kernel starts so that the epilogue does not wait a
-// memory round trip for them (zeros when there is no residual or the kernel
-// stores split-K partials).
+// requested when the kernel starts (before the ring's first chunks: loads
+// complete in issue order, so no chunk wait waits for them) and widened only
+// in the epilogue.  RES (a kernel instance launched for a segment with a
+// residual and bf16 output): the loads are unconditional, with the index
+// clamped to the last row and column (and the first activation element when
+// a segment has no residual), because a load under a branch gets a wait for
+// every load in flight at the branch's end, which made these loads a chain
+// of round trips.  Without RES nothing is loaded (store4 adds no residual).
 struct Res4 {
   uint16_t v[4];
 };
 
+template <bool RES>
 __device__ __forceinline__ Res4 load_res4(const MfmaArgs& g, int m, int n0) {
-  Res4 r;
+  Res4 r = {{0, 0, 0, 0}};
+  if constexpr (RES) {
+    const bool use = g.res != nullptr && g.partial == nullptr;
+    const uint16_t* base = use ? g.res : g.a;
+    const int64_t row = use ? static_cast<int64_t>(min(m, g.M - 1)) * g.ldr : 0;
+    const int nmax = use ? g.N - 1 : 0;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int n = n0 + v;
-    r.v[v] = (g.res != nullptr && g.partial == nullptr && m < g.M && n < g.N) ? g.res[m * g.ldr + n] : 0;
+    for (int v = 0; v < 4; ++v) r.v[v] = base[row + min(n0 + v, nmax)];
   }
   return r;
 }
@@ -171,7 +180,7 @@ __device__ __forceinline__ void store4(const MfmaArgs& g, const f32x4& acc, int 
 // MB: 16-row activation blocks (m_tile = 16*MB); NW: waves = 16-row weight
 // blocks per workgroup; C: ring slots; XQ: activation rows copied per chunk,
 // in groups of 4 (XQ*4 >= M).
-template <int MB, int NW, int C, int XQ>
+template <int MB, int NW, int C, int XQ, bool RES>
 __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaLaunch L) {
   extern __shared__ u32x4 lds[];
   int tile, split;
@@ -231,13 +240,15 @@ __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaLaunch L) {
     }
   };
 
-#pragma unroll
-  for (int q = 0; q < C - 1; ++q) issue(q);
-
+  // The residual goes out before the ring's first chunks: loads complete in
+  // issue order, so the chunk waits below never wait for it.
   const int n0 = tile_row0 + 16 * wave + 4 * kg;
   Res4 res[MB];
 #pragma unroll
-  for (int a = 0; a < MB; ++a) res[a] = load_res4(g, 16 * a + rl, n0);
+  for (int a = 0; a < MB; ++a) res[a] = load_res4<RES>(g, 16 * a + rl, n0);
+
+#pragma unroll
+  for (int q = 0; q < C - 1; ++q) issue(q);
 
   f32x4 acc[MB];
 #pragma unroll
@@ -288,7 +299,7 @@ constexpr int kFoldMaxK = kFoldChunks * kWave * 8;
 // activation fragment is then normalised in registers, n = bf16((L * r) *
 // gamma), before its MFMA: the rounding of the bf16 normalised latent that a
 // separate RMSNorm kernel would store.
-template <int XQ, int C, bool NORM>
+template <int XQ, int C, bool NORM, bool RES>
 __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch L) {
   extern __shared__ u32x4 lds[];
   int tile, split;
@@ -353,12 +364,12 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
     }
   };
 
-#pragma unroll
-  for (int q = 0; q < C - 1; ++q) issue(q);
-
-  float rn = 0.f;  // NORM: r of this lane's activation row (0 past the rows)
+  // The residual and (NORM) the whole latent rows go out before the ring's
+  // first chunks: loads complete in issue order, so neither the RMSNorm
+  // below nor the chunk waits of the loop wait for the other's loads.
+  const Res4 res = load_res4<RES>(g, rl, row0 + 4 * kg);
+  u32x4 lv[NORM ? XQ : 1][kFoldChunks];
   if constexpr (NORM) {
-    u32x4 lv[XQ][kFoldChunks];
 #pragma unroll
     for (int j = 0; j < XQ; ++j) {
       const int m = wave + 4 * j;
@@ -370,6 +381,13 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
         lv[j][i] = buf_load(xres, off);
       }
     }
+  }
+
+#pragma unroll
+  for (int q = 0; q < C - 1; ++q) issue(q);
+
+  float rn = 0.f;  // NORM: r of this lane's activation row (0 past the rows)
+  if constexpr (NORM) {
 #pragma unroll
     for (int j = 0; j < XQ; ++j) {
       float ss = 0.f;
@@ -386,11 +404,14 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
       if (lane == 0)
         rsc[m] = m < g.M ? __frsqrt_rn(ss / static_cast<float>(g.K) + g.eps) : 0.f;
     }
-    __syncthreads();  // r of every row is in LDS
+    // r of every row is in LDS.  A plain barrier after the LDS writes: a
+    // __syncthreads would also wait for the ring's chunks in flight (the
+    // global->LDS copies count as memory loads), which no other wave reads.
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
     rn = rl < XROWS ? rsc[rl] : 0.f;
   }
 
-  const Res4 res = load_res4(g, rl, row0 + 4 * kg);
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   const int xr = rl < XROWS ? rl : XROWS - 1;
   for (int q = 0; q < nch; ++q) {
@@ -461,7 +482,7 @@ __device__ __forceinline__ void block_coords(int tile, int ntiles, int mblocks, 
   nt = grp * 8 + (r - mb * nrem);
 }
 
-template <int C>
+template <int C, bool RES>
 __global__ __launch_bounds__(kBlkWaves * kWave) void block_kernel(MfmaLaunch L) {
   extern __shared__ u32x4 lds[];
   int tile, split;
@@ -520,9 +541,7 @@ __global__ __launch_bounds__(kBlkWaves * kWave) void block_kernel(MfmaLaunch L) 
     }
   };
 
-#pragma unroll
-  for (int q = 0; q < C - 1; ++q) issue(q);
-
+  // The residual goes out before the ring's first chunks (see tile_kernel).
   const int wr0 = 32 * (wave & 1);   // this wave's first weight row in the block
   const int xr0 = 64 * (wave >> 1);  // and first activation row
   Res4 res[2][4];
@@ -530,7 +549,10 @@ __global__ __launch_bounds__(kBlkWaves * kWave) void block_kernel(MfmaLaunch L) 
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      res[i][j] = load_res4(g, m0 + xr0 + 16 * j + rl, row0 + wr0 + 16 * i + 4 * kg);
+      res[i][j] = load_res4<RES>(g, m0 + xr0 + 16 * j + rl, row0 + wr0 + 16 * i + 4 * kg);
+
+#pragma unroll
+  for (int q = 0; q < C - 1; ++q) issue(q);
 
   f32x4 acc[2][4];
 #pragma unroll
@@ -569,9 +591,9 @@ __global__ __launch_bounds__(kBlkWaves * kWave) void block_kernel(MfmaLaunch L) 
 
 // One attribute call per kernel instance (the ring can exceed the default
 // 64 KiB of dynamic LDS).
-template <int MB, int NW, int C, int XQ>
+template <int MB, int NW, int C, int XQ, bool RES>
 hipError_t launch_tile_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
-  auto kern = tile_kernel<MB, NW, C, XQ>;
+  auto kern = tile_kernel<MB, NW, C, XQ, RES>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       static_cast<int>(kMfmaMaxLds));
@@ -580,9 +602,9 @@ hipError_t launch_tile_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int XQ, int C, bool NORM>
+template <int XQ, int C, bool NORM, bool RES>
 hipError_t launch_wsplit_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
-  auto kern = wsplit_kernel<XQ, C, NORM>;
+  auto kern = wsplit_kernel<XQ, C, NORM, RES>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       static_cast<int>(kMfmaMaxLds));
@@ -591,20 +613,20 @@ hipError_t launch_wsplit_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool NORM>
+template <bool NORM, bool RES>
 hipError_t launch_wsplit_xq(const MfmaLaunch& L, int XQ, int wgs, hipStream_t s) {
   switch (XQ) {
-    case 1: return launch_wsplit_inst<1, 3, NORM>(L, wgs, s);
-    case 2: return launch_wsplit_inst<2, 3, NORM>(L, wgs, s);
-    case 3: return launch_wsplit_inst<3, 3, NORM>(L, wgs, s);
-    case 4: return launch_wsplit_inst<4, 3, NORM>(L, wgs, s);
+    case 1: return launch_wsplit_inst<1, 3, NORM, RES>(L, wgs, s);
+    case 2: return launch_wsplit_inst<2, 3, NORM, RES>(L, wgs, s);
+    case 3: return launch_wsplit_inst<3, 3, NORM, RES>(L, wgs, s);
+    case 4: return launch_wsplit_inst<4, 3, NORM, RES>(L, wgs, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int C>
+template <int C, bool RES>
 hipError_t launch_block_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
-  auto kern = block_kernel<C>;
+  auto kern = block_kernel<C, RES>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       static_cast<int>(kMfmaMaxLds));
@@ -702,36 +724,40 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
   if (cfg.kind != SG_KIND_MFMA_WAVESPLIT && (segs[0].gamma != nullptr || (nseg == 2 && segs[1].gamma != nullptr)))
     return hipErrorInvalidValue;
 
+  // Instances that load a residual (RES) only where a segment has one and
+  // stores bf16; the packed KDA projection (8-wave tiles) never does.
+  const bool res = (segs[0].res != nullptr && segs[0].partial == nullptr) ||
+                   (nseg == 2 && segs[1].res != nullptr && segs[1].partial == nullptr);
   if (cfg.kind == SG_KIND_MFMA_TILE) {
     const int NW = cfg.waves, C = cfg.k_unroll, XQ = cfg.m_tile / 4;
     if (cfg.rows != 16 * NW || (cfg.m_tile % 4) != 0) return hipErrorInvalidValue;
     // The instances the configuration table uses.
     if (NW == 2 && C == 4) {
       switch (XQ) {
-        case 1: return launch_tile_inst<1, 2, 4, 1>(L, wgs, s);
-        case 2: return launch_tile_inst<1, 2, 4, 2>(L, wgs, s);
-        case 3: return launch_tile_inst<1, 2, 4, 3>(L, wgs, s);
-        case 4: return launch_tile_inst<1, 2, 4, 4>(L, wgs, s);
+        case 1: return res ? launch_tile_inst<1, 2, 4, 1, true>(L, wgs, s) : launch_tile_inst<1, 2, 4, 1, false>(L, wgs, s);
+        case 2: return res ? launch_tile_inst<1, 2, 4, 2, true>(L, wgs, s) : launch_tile_inst<1, 2, 4, 2, false>(L, wgs, s);
+        case 3: return res ? launch_tile_inst<1, 2, 4, 3, true>(L, wgs, s) : launch_tile_inst<1, 2, 4, 3, false>(L, wgs, s);
+        case 4: return res ? launch_tile_inst<1, 2, 4, 4, true>(L, wgs, s) : launch_tile_inst<1, 2, 4, 4, false>(L, wgs, s);
         default: break;
       }
     }
     if (NW == 4 && C == 3) {
       switch (XQ) {
-        case 8: return launch_tile_inst<2, 4, 3, 8>(L, wgs, s);
-        case 12: return launch_tile_inst<3, 4, 3, 12>(L, wgs, s);
-        case 16: return launch_tile_inst<4, 4, 3, 16>(L, wgs, s);
+        case 8: return res ? launch_tile_inst<2, 4, 3, 8, true>(L, wgs, s) : launch_tile_inst<2, 4, 3, 8, false>(L, wgs, s);
+        case 12: return res ? launch_tile_inst<3, 4, 3, 12, true>(L, wgs, s) : launch_tile_inst<3, 4, 3, 12, false>(L, wgs, s);
+        case 16: return res ? launch_tile_inst<4, 4, 3, 16, true>(L, wgs, s) : launch_tile_inst<4, 4, 3, 16, false>(L, wgs, s);
         default: break;
       }
     }
-    if (NW == 8 && C == 3) {  // the packed KDA projection, 2 <= M <= 64
+    if (NW == 8 && C == 3 && !res) {  // the packed KDA projection, 2 <= M <= 64
       switch (XQ) {
-        case 1: return launch_tile_inst<1, 8, 3, 1>(L, wgs, s);
-        case 2: return launch_tile_inst<1, 8, 3, 2>(L, wgs, s);
-        case 3: return launch_tile_inst<1, 8, 3, 3>(L, wgs, s);
-        case 4: return launch_tile_inst<1, 8, 3, 4>(L, wgs, s);
-        case 8: return launch_tile_inst<2, 8, 3, 8>(L, wgs, s);
-        case 12: return launch_tile_inst<3, 8, 3, 12>(L, wgs, s);
-        case 16: return launch_tile_inst<4, 8, 3, 16>(L, wgs, s);
+        case 1: return launch_tile_inst<1, 8, 3, 1, false>(L, wgs, s);
+        case 2: return launch_tile_inst<1, 8, 3, 2, false>(L, wgs, s);
+        case 3: return launch_tile_inst<1, 8, 3, 3, false>(L, wgs, s);
+        case 4: return launch_tile_inst<1, 8, 3, 4, false>(L, wgs, s);
+        case 8: return launch_tile_inst<2, 8, 3, 8, false>(L, wgs, s);
+        case 12: return launch_tile_inst<3, 8, 3, 12, false>(L, wgs, s);
+        case 16: return launch_tile_inst<4, 8, 3, 16, false>(L, wgs, s);
         default: break;
       }
     }
@@ -744,14 +770,14 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
     if (segs[0].gamma != nullptr) {
       // The RMSNorm fold: one segment whose whole rows fit the prologue.
       if (nseg != 1 || !wsplit_fold_fits(segs[0].K, cfg.k_split)) return hipErrorInvalidValue;
-      return launch_wsplit_xq<true>(L, XQ, wgs, s);
+      return res ? launch_wsplit_xq<true, true>(L, XQ, wgs, s) : launch_wsplit_xq<true, false>(L, XQ, wgs, s);
     }
     if (nseg == 2 && segs[1].gamma != nullptr) return hipErrorInvalidValue;
-    return launch_wsplit_xq<false>(L, XQ, wgs, s);
+    return res ? launch_wsplit_xq<false, true>(L, XQ, wgs, s) : launch_wsplit_xq<false, false>(L, XQ, wgs, s);
   }
   if (cfg.kind == SG_KIND_MFMA_BLOCK) {
     if (cfg.rows != kBlkRows || cfg.waves != kBlkWaves || cfg.m_tile % kBlkM != 0) return hipErrorInvalidValue;
-    if (cfg.k_unroll == 3) return launch_block_inst<3>(L, wgs, s);
+    if (cfg.k_unroll == 3) return res ? launch_block_inst<3, true>(L, wgs, s) : launch_block_inst<3, false>(L, wgs, s);
     return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
