@@ -278,9 +278,7 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
   red.out = qkvg;
   red.ldc = n_qkvg;
 
-  // F_A/beta rows: bf16 P [M, n_ab] in ws_aux when they run whole on the row
-  // GEMV, else fp32 partials in ws_aux summed by the F_B stage.
-  const bool fab_direct = sg::kda_fab_direct(cf);
+  // F_A/beta rows: always fp32 partials in ws_aux, summed by the F_B stage.
   DotProblem f{};
   f.a = x;
   f.lda = K;
@@ -289,16 +287,10 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
   f.M = M;
   f.N = n_ab;
   f.K = K;
-  if (fab_direct) {
-    f.out = static_cast<uint16_t*>(ws_aux);
-    f.ldc = n_ab;
-  } else {
-    f.partial = static_cast<float*>(ws_aux);
-  }
+  f.partial = static_cast<float*>(ws_aux);
 
   sg::FbProblem fb{};
   fb.partial = f.partial;
-  fb.p_bf16 = fab_direct ? static_cast<const uint16_t*>(ws_aux) : nullptr;
   fb.S = cf.k_split;
   fb.M = M;
   fb.n_ab = n_ab;

@@ -39,6 +39,9 @@ constexpr int kPairRows = 128;
 constexpr int kPairWaves = 8;
 constexpr int kPairRing = 3;
 constexpr int kPairWgs = 256;
+// K-ranges of the packed projection's F_A/beta rows beside the M = 1 GEMV (at
+// most the F_B stage's batch of 8 splits, one memory round trip).
+constexpr int kFabGemvSplit = 7;
 // Largest M for which the two-stream projection is worth its fork/join.  On
 // MI355X the concurrent schedule measured slower than the single-stream one
 // (two segments in one launch, then F_B) at every decode M from 1 to 64:
@@ -197,10 +200,6 @@ bool tail_folds(const sg_config_t& c, int K) {
   return K > 0 && K <= 2048 && ceil_div(sps, 4) <= 16;
 }
 
-// The packed projection's F_A/beta rows store bf16 P themselves (no fp32
-// partials) when they run whole on the row GEMV.
-bool kda_fab_direct(const sg_config_t& c) { return c.kind == SG_KIND_GEMV_ROW && c.k_split == 1; }
-
 // Workspace regions start on 256-byte boundaries.
 size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 size_t ws_round(size_t b) { return round256(b); }
@@ -287,12 +286,15 @@ extern "C" int sg_kda_select(int which, int M, int K, int n_qkvg, int n_ab, sg_c
     return SG_OK;
   }
   // M = 1 with the Q/K/V/G rows on the whole-row GEMV: the F_A/beta rows join
-  // them as a second segment of the same instance, whole rows too, and store
-  // bf16 P directly (no K split: the F_B stage then reads P instead of summing
-  // partials, and the launch has no extra split-K workgroups).
+  // them as a second segment of the same instance with kFabGemvSplit K-ranges:
+  // short workgroups that fill the CUs the Q/K/V/G rows leave idle at the end
+  // of the launch, and few enough partials for the F_B stage to sum in one
+  // batch.
   if (q.kind == SG_KIND_GEMV_ROW && q.k_split == 1) {
     f = q;
-    f.grid = ceil_div(n_ab, q.waves * q.rows);
+    f.kind = SG_KIND_GEMV_SPLITK;
+    f.k_split = effective_split(ceil_div(K / 8, 64), kFabGemvSplit);
+    f.grid = ceil_div(n_ab, q.waves * q.rows) * f.k_split;
   }
   // 2 <= M <= 64: the table's wave-split and 64-row tiles give the Q/K/V/G
   // rows alone 256 workgroups, one per CU, so the F_A/beta segment would start
@@ -331,10 +333,7 @@ extern "C" size_t sg_kda_workspace_bytes(int which, int M, int K, int n_qkvg, in
   if (sg_kda_select(which, M, K, n_qkvg, n_ab, &c) != SG_OK || c.kind == SG_KIND_NONE) return 0;
   const int N = (which == SG_KDA_QKVG) ? n_qkvg : n_ab;
   const size_t plane = static_cast<size_t>(M) * static_cast<size_t>(N) * sizeof(float);
-  // Q/K/V/G: split-K partials only when K is split.  F_A/beta: bf16 P when
-  // its rows run whole on the GEMV, else fp32 partials.
+  // Q/K/V/G: split-K partials only when K is split.  F_A/beta: always partials.
   if (which == SG_KDA_QKVG && c.k_split <= 1) return 0;
-  if (which == SG_KDA_FAB && sg::kda_fab_direct(c))
-    return sg::round256(static_cast<size_t>(M) * static_cast<size_t>(N) * sizeof(uint16_t));
   return sg::round256(static_cast<size_t>(c.k_split) * plane);
 }

@@ -71,8 +71,6 @@ bool wsplit_fold_fits(int K, int k_split);
 // Whether latent_moe_tail folds the RMSNorm into the GEMM for configuration c
 // (the single decision the entry point and the workspace size both use).
 bool tail_folds(const sg_config_t& c, int K);
-// The packed projection's F_A/beta configuration stores bf16 P directly.
-bool kda_fab_direct(const sg_config_t& c);
 size_t block_lds_bytes(int c);
 
 // out[m,n] = bf16( sum_{s<S} partial[s][m][n] + res[m,n] ).  The sum runs

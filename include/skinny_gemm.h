@@ -163,9 +163,9 @@ enum {
  *   SG_KDA_QKVG / SG_KDA_FAB: sg_select(M, n_qkvg, K, 0) and the
  *     SG_KDA_FAB_ALONE configuration, except that
  *     - where the Q/K/V/G rows run whole on GEMV_ROW (k_split 1, M == 1)
- *       the F_A/beta rows take that same configuration (grid ceil(n_ab /
- *       (waves * rows))) and store bf16 P [M, n_ab] into ws_aux, which the
- *       F_B stage reads directly;
+ *       the F_A/beta rows take that configuration as GEMV_SPLITK with
+ *       k_split = split(ceil((K/8)/64), 7), grid ceil(n_ab / (waves * rows))
+ *       * k_split;
  *     - where both are MFMA_WAVESPLIT or MFMA_TILE (2 <= M <= 64) both
  *       ranges use MFMA_TILE with 128-row tiles of 8 waves (m_tile M rounded
  *       up to 4 for M <= 16, to 16 above) and one K split S =
@@ -179,9 +179,8 @@ int sg_kda_select(int which, int M, int K, int n_qkvg, int n_ab, sg_config_t *ou
 /* Bytes of device workspace kda_projection_overlap needs: which =
  * SG_KDA_QKVG for ws_main (the Q/K/V/G split-K partials, k_split * M *
  * n_qkvg * 4 rounded up to 256, 0 when unsplit), SG_KDA_FAB for ws_aux (the
- * F_A/beta partials, k_split * M * n_ab * 4 rounded up to 256, or bf16 P,
- * M * n_ab * 2 rounded up to 256, when that range is GEMV_ROW with k_split 1),
- * with the configurations of sg_kda_select().  0 for any other which. */
+ * F_A/beta partials, k_split * M * n_ab * 4 rounded up to 256), with the
+ * configurations of sg_kda_select().  0 for any other which. */
 size_t sg_kda_workspace_bytes(int which, int M, int K, int n_qkvg, int n_ab);
 
 /* Human-readable name of a status code (static string, never NULL). */

@@ -48,7 +48,8 @@ packed projection, 2 F_A/beta alone):
     grid ceil(n_ab / 4)) or MFMA_WAVESPLIT (M > 1: m_tile 4 ceil(M / 4),
     rows 16, waves 4, k_unroll 3, grid ceil(n_ab / 16)); k_split >= 1.
   * which 2: f.  Otherwise q = select(M, n_qkvg, K).  If q is GEMV_ROW with
-    k_split 1, f becomes q's configuration with grid ceil(n_ab / (4 rows)).
+    k_split 1, f becomes q's configuration with kind GEMV_SPLITK, k_split =
+    split(ceil((K/8) / 64), 7) and grid ceil(n_ab / (4 rows)) * k_split.
     Else, if q and f are both
     MFMA_WAVESPLIT or MFMA_TILE: with t_q = ceil(n_qkvg / 128), t_f =
     ceil(n_ab / 128), ksteps = ceil(K / 32), S = split(ksteps,
@@ -56,8 +57,7 @@ packed projection, 2 F_A/beta alone):
     m_tile 4 ceil(M / 4) (M <= 16) or 16 ceil(M / 16), rows 128, waves 8,
     k_unroll 3, k_split S, grid t * S.
   * workspace: Q/K/V/G k_split * M * n_qkvg * 4 (0 when k_split <= 1),
-    F_A/beta M * n_ab * 2 when it is GEMV_ROW with k_split 1 (bf16 P), else
-    k_split * M * n_ab * 4, each rounded up to 256.
+    F_A/beta k_split * M * n_ab * 4, each rounded up to 256.
 """
 from __future__ import annotations
 
@@ -169,7 +169,8 @@ def kda_select(which: int, M: int, K: int, n_qkvg: int, n_ab: int):
     if which == 2:
         return OK, f
     if q["kind"] == GEMV_ROW and q["k_split"] == 1:
-        f = dict(q, grid=_cdiv(n_ab, q["waves"] * q["rows"]))
+        ks = _split(_cdiv(K // 8, 64), 7)
+        f = dict(q, kind=GEMV_SPLITK, k_split=ks, grid=_cdiv(n_ab, q["waves"] * q["rows"]) * ks)
     small = (MFMA_WAVESPLIT, MFMA_TILE)
     if q["kind"] in small and f["kind"] in small:
         tq, tf = _cdiv(n_qkvg, 128), _cdiv(n_ab, 128)
@@ -190,7 +191,5 @@ def kda_workspace_bytes(which: int, M: int, K: int, n_qkvg: int, n_ab: int) -> i
         return 0
     if which == 0 and c["k_split"] <= 1:
         return 0
-    if which == 1 and c["kind"] == GEMV_ROW and c["k_split"] == 1:
-        return -(-(M * n_ab * 2) // 256) * 256
     n = n_qkvg if which == 0 else n_ab
     return -(-(c["k_split"] * M * n * 4) // 256) * 256

@@ -262,8 +262,8 @@ def test_sequential_projection_equals_separate_calls(device, M):
     one launch, then F_B with the Q/K/V/G split-K reduction) against
     kda_qkvg_proj + kda_fab_fb_proj: bit for bit the same outputs wherever
     sg_kda_select gives the same configurations as the standalone calls
-    (64 < M); at M = 1 the projection's F_A/beta rows run whole on the Q/K/V/G
-    rows' GEMV (bf16 P, no K split) and at 2 <= M <= 64 it pairs its ranges in
+    (64 < M); at M = 1 the projection's F_A/beta rows run on the Q/K/V/G rows'
+    GEMV in 7 K-ranges and at 2 <= M <= 64 it pairs its ranges in
     128-row tiles with another K split, so the sums round in another order and
     both must meet the oracle's tolerance instead."""
     _say(f"sequential projection vs separate calls M={M}")

@@ -273,11 +273,11 @@ def test_fab_fb_validation(lib):
 
 def test_overlap_validation(lib):
     E = _lib
-    # M = 1: the Q/K/V/G rows need no workspace and the F_A/beta rows run whole
-    # on the same GEMV, storing bf16 P; M = 2: the paired tiles split K, so
-    # both ranges leave partials.
+    # M = 1: the Q/K/V/G rows need no workspace and the F_A/beta rows run on
+    # the same GEMV in 7 K-ranges; M = 2: the paired tiles split K, so both
+    # ranges leave partials.
     need_aux = lib.sg_kda_workspace_bytes(1, 1, 7168, 4096, 136)
-    assert need_aux == 512  # 136 bf16 rounded up to 256 bytes
+    assert need_aux == 3840  # 7 x 1 x 136 fp32, rounded up to 256 bytes
     assert lib.sg_kda_workspace_bytes(1, 2, 7168, 4096, 136) == 7680  # 7 x 2 x 136 fp32, rounded
     assert lib.sg_kda_workspace_bytes(0, 1, 7168, 4096, 136) == 0
     assert lib.sg_kda_workspace_bytes(0, 2, 7168, 4096, 136) == 7 * 2 * 4096 * 4
