@@ -148,6 +148,49 @@ def test_fab_fb_lattice_bitwise(device, M):
     assert np.array_equal(host(g1), o["g1_bits"])
 
 
+@pytest.mark.parametrize("M,K", [(2, 16384), (3, 12288)])
+def test_fab_fb_many_splits(device, M, K):
+    """More F_A/beta K splits than the F_B stage sums in its straight-line
+    batches (25 and 24 splits here): the remaining splits take its loop."""
+    cfg = sg.sg_kda_select(sg.SG_KDA_FAB_ALONE, M, K, 4096, 136)
+    _say(f"kda_fab_fb_proj many splits M={M} K={K} cfg={cfg}")
+    assert cfg["k_split"] > 16
+    x, w_ab, w_b = synth.fab_fb_inputs(M, seed=77 + M, K=K)
+    g1, beta, f_a = sg.kda_fab_fb_proj(dev(x, device), dev(w_ab, device), dev(w_b, device),
+                                       want_f_a=True)
+    torch.cuda.synchronize()
+    o = oracle.fab_fb(x, w_ab, w_b)
+    assert_close(host(f_a), o["p_exact"][:, :128], "f_a")
+    assert_close(host(beta), o["beta_exact"], "beta")
+    assert_close(host(g1), o["g1_exact"], "g1")
+
+
+@pytest.mark.parametrize("M", [3, 12])
+def test_projection_many_splits(device, M):
+    """A small Q/K/V/G range (256 rows): the paired tiles split K 28 ways, so
+    the F_B launch sums 28 F_A/beta partials (batches, then its loop) and its
+    reduction role 28 Q/K/V/G partials (straight-line batches, then a loop);
+    both schedules against each other and the oracle."""
+    K, nq = synth.HIDDEN, 256
+    cq = sg.sg_kda_select(sg.SG_KDA_QKVG, M, K, nq, 136)
+    _say(f"kda_projection_overlap many splits M={M} n_qkvg={nq} cfg={cq}")
+    assert cq["k_split"] > 16
+    x, packed, w_b = synth.overlap_inputs(M, seed=88 + M, n_qkvg=nq)
+    xd, pd, wbd = dev(x, device), dev(packed, device), dev(w_b, device)
+    aux = torch.cuda.Stream(device)
+    fork, join = sg.HipEvent(), sg.HipEvent()
+    q_s, g1_s, b_s = sg.kda_projection_overlap(xd, pd, wbd, n_qkvg=nq)
+    q_c, g1_c, b_c = sg.kda_projection_overlap(xd, pd, wbd, n_qkvg=nq, aux_stream=aux, fork=fork,
+                                               join=join)
+    torch.cuda.synchronize()
+    for a, b in ((q_c, q_s), (g1_c, g1_s), (b_c, b_s)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    o = oracle.projection_overlap(x, packed, w_b, n_qkvg=nq)
+    assert_close(host(q_s), o["qkvg_exact"], "qkvg")
+    assert_close(host(g1_s), o["g1_exact"], "g1")
+    assert_close(host(b_s), o["beta_exact"], "beta")
+
+
 # ---- the concurrent projection ------------------------------------------------------------
 
 @pytest.mark.parametrize("M", [1, 4, 16, 17, 32, 48, 64])
