@@ -295,10 +295,11 @@ __global__ __launch_bounds__(kSmallkWaves * kWave) void fab_fb_tail_kernel(FbArg
   //    columns in the first column of workgroups, the rank f_a columns
   //    elsewhere.  kFbPer elements per thread per pass.  The first pass
   //    (every element when mg * cols <= kFbPer * nthreads, the usual case)
-  //    is straight-line code: with at most kSumBatch splits all its loads go
-  //    out together, behind the w_b load, and nothing waits for them until
-  //    the sums (one memory round trip).  Past the end of the rows a thread
-  //    loads element 0 (in bounds) and discards it.
+  //    is straight-line code for up to kSumBatch splits: batches of kFbBatch
+  //    splits whose loads go out together (the first behind the w_b load),
+  //    one memory round trip per batch.  Past the end of the rows a thread
+  //    loads element 0 (in bounds) and discards it.  More splits, or a
+  //    second pass, take the loop below.
   const int cols = first ? g.n_ab : g.rank;
   const int count = mg * cols;
   auto place = [&](int idx, uint16_t b) {
