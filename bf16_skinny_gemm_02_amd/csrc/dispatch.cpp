@@ -27,6 +27,7 @@ constexpr int kNoSplitTiles = 192;   // this many tiles fill the chip without a 
 constexpr int kSplitMaxTiles = 320;  // WAVESPLIT up to this many 16-row tiles
 constexpr int kSplitPairTiles = 512; // ... or this many when two workgroups fit a CU (M <= 8)
 constexpr int kSplitRing = 3;        // WAVESPLIT ring slots
+constexpr int kSplitRing2 = 2;       // ... for 9 <= M <= 16 with two workgroups per CU
 constexpr int kWideRing = 4;         // TILE ring slots for M <= 16 (2 waves, 32 rows)
 constexpr int kTileRing = 3;         // TILE ring slots for 16 < M <= 64 (4 waves, 64 rows)
 constexpr int kBlockRows = 64;       // BLOCK (M > 64): weight rows per workgroup
@@ -140,6 +141,15 @@ extern "C" int sg_select(int M, int N, int K, int has_residual, sg_config_t* out
       c.rows = 16;
       c.waves = 4;
       c.k_unroll = kSplitRing;
+      c.k_split = mfma_split(tiles16, ksteps, 16);
+      c.grid = tiles16 * c.k_split;
+    } else if (tiles16 <= kSplitPairTiles) {
+      // 9 <= M <= 16: 2-slot rings, so that two workgroups again fit one CU
+      // and up to 512 tiles run in one round.
+      c.kind = SG_KIND_MFMA_WAVESPLIT;
+      c.rows = 16;
+      c.waves = 4;
+      c.k_unroll = kSplitRing2;
       c.k_split = mfma_split(tiles16, ksteps, 16);
       c.grid = tiles16 * c.k_split;
     } else {

@@ -614,7 +614,15 @@ hipError_t launch_wsplit_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
 }
 
 template <bool NORM, bool RES>
-hipError_t launch_wsplit_xq(const MfmaLaunch& L, int XQ, int wgs, hipStream_t s) {
+hipError_t launch_wsplit_xq(const MfmaLaunch& L, int XQ, int C, int wgs, hipStream_t s) {
+  if (C == 2) {  // 9 <= M <= 16, two workgroups per CU
+    switch (XQ) {
+      case 3: return launch_wsplit_inst<3, 2, NORM, RES>(L, wgs, s);
+      case 4: return launch_wsplit_inst<4, 2, NORM, RES>(L, wgs, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (C != 3) return hipErrorInvalidValue;
   switch (XQ) {
     case 1: return launch_wsplit_inst<1, 3, NORM, RES>(L, wgs, s);
     case 2: return launch_wsplit_inst<2, 3, NORM, RES>(L, wgs, s);
@@ -765,15 +773,17 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
   }
   if (cfg.kind == SG_KIND_MFMA_WAVESPLIT) {
     const int C = cfg.k_unroll, XQ = cfg.m_tile / 4;
-    if (cfg.rows != 16 || cfg.waves != kSplitWaves || (cfg.m_tile % 4) != 0 || C != 3)
+    if (cfg.rows != 16 || cfg.waves != kSplitWaves || (cfg.m_tile % 4) != 0 || (C != 2 && C != 3))
       return hipErrorInvalidValue;
     if (segs[0].gamma != nullptr) {
       // The RMSNorm fold: one segment whose whole rows fit the prologue.
       if (nseg != 1 || !wsplit_fold_fits(segs[0].K, cfg.k_split)) return hipErrorInvalidValue;
-      return res ? launch_wsplit_xq<true, true>(L, XQ, wgs, s) : launch_wsplit_xq<true, false>(L, XQ, wgs, s);
+      return res ? launch_wsplit_xq<true, true>(L, XQ, C, wgs, s)
+                 : launch_wsplit_xq<true, false>(L, XQ, C, wgs, s);
     }
     if (nseg == 2 && segs[1].gamma != nullptr) return hipErrorInvalidValue;
-    return res ? launch_wsplit_xq<false, true>(L, XQ, wgs, s) : launch_wsplit_xq<false, false>(L, XQ, wgs, s);
+    return res ? launch_wsplit_xq<false, true>(L, XQ, C, wgs, s)
+               : launch_wsplit_xq<false, false>(L, XQ, C, wgs, s);
   }
   if (cfg.kind == SG_KIND_MFMA_BLOCK) {
     if (cfg.rows != kBlkRows || cfg.waves != kBlkWaves || cfg.m_tile % kBlkM != 0) return hipErrorInvalidValue;

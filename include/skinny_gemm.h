@@ -265,7 +265,7 @@ int kda_projection_overlap(const sg_bf16 *x, const sg_bf16 *packed_w, const sg_b
  * must be finite and > 0, d_latent > 0.  out may alias shared exactly.
  * For M == 1 (when one workgroup covers the whole latent row) one GEMV
  * kernel normalises on the fly, and so does the wave-split MFMA tile (2 <= M
- * <= 16) when d_latent <= 2048; otherwise the normalised latent is written
+ * <= 16, d_hidden / 16 <= 512 tiles) when d_latent <= 2048; otherwise the normalised latent is written
  * to the workspace by a norm kernel and consumed by the GEMM, which needs
  * d_latent <= 8192 (SG_ERR_UNSUPPORTED otherwise).  Workspace:
  * sg_workspace_bytes(SG_OP_LATENT_TAIL, M, d_hidden, d_latent), 0 unless

@@ -25,6 +25,7 @@ Rule, for C[M,N] = A[M,K] W[N,K]^T:
       - tiles16 <= 320, or m_tile <= 8 and tiles16 <= 512: MFMA_WAVESPLIT,
         rows = 16, waves = 4, k_unroll = 3, k_split = msplit(tiles16, 16),
         grid = tiles16 * k_split.
+      - else tiles16 <= 512: the same with k_unroll = 2.
       - else MFMA_TILE, rows = 32, waves = 2, k_unroll = 4,
         tiles = ceil(N / 32), k_split = msplit(tiles, 8), grid = tiles * k_split.
   * 17 <= M <= 64: MFMA_TILE, m_tile = 16 * ceil(M / 16), rows = 64, waves = 4,
@@ -123,6 +124,10 @@ def select(M: int, N: int, K: int, has_residual: bool = False):
         if tiles16 <= 320 or (cfg["m_tile"] <= 8 and tiles16 <= 512):
             ks = msplit(tiles16, 16)
             cfg.update(kind=MFMA_WAVESPLIT, rows=16, waves=4, k_unroll=3, k_split=ks,
+                       grid=tiles16 * ks)
+        elif tiles16 <= 512:
+            ks = msplit(tiles16, 16)
+            cfg.update(kind=MFMA_WAVESPLIT, rows=16, waves=4, k_unroll=2, k_split=ks,
                        grid=tiles16 * ks)
         else:
             tiles = _cdiv(N, 32)

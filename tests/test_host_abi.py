@@ -111,12 +111,16 @@ def test_kind_follows_m_boundaries():
         st, cfg = selection.select(M, 4096, 7168)
         assert st == selection.OK
         assert cfg["kind"] == _kind_for(M), M
-    # A wide N moves M <= 16 to the shared-activation tile (32 rows per
-    # workgroup), except up to M = 8 while two wave-split workgroups fit a CU.
-    assert selection.select(12, 7168, 2048)[1]["kind"] == selection.MFMA_TILE
-    assert selection.select(12, 7168, 2048)[1]["rows"] == 32
+    # A wide N keeps M <= 16 on the wave-split tile while two of its
+    # workgroups fit a CU (3-slot rings up to M = 8, 2-slot rings above), up
+    # to 512 tiles; wider N moves to the shared-activation tile (32 rows).
+    assert selection.select(12, 7168, 2048)[1]["kind"] == selection.MFMA_WAVESPLIT
+    assert selection.select(12, 7168, 2048)[1]["k_unroll"] == 2
     assert selection.select(8, 7168, 2048)[1]["kind"] == selection.MFMA_WAVESPLIT
+    assert selection.select(8, 7168, 2048)[1]["k_unroll"] == 3
     assert selection.select(8, 9000, 2048)[1]["kind"] == selection.MFMA_TILE
+    assert selection.select(12, 9000, 2048)[1]["kind"] == selection.MFMA_TILE
+    assert selection.select(12, 9000, 2048)[1]["rows"] == 32
     # M = 1 takes four rows per wave when a whole row fits seven 512-wide steps.
     assert selection.select(1, 7168, 2048)[1]["rows"] == 4
     assert selection.select(1, 7168, 2048)[1]["grid"] == 448
