@@ -264,12 +264,13 @@ int kda_projection_overlap(const sg_bf16 *x, const sg_bf16 *packed_w, const sg_b
  * [M,d_hidden] (nullable: no add), out [M,d_hidden]; all contiguous.  eps
  * must be finite and > 0, d_latent > 0.  out may alias shared exactly.
  * For M == 1 (when one workgroup covers the whole latent row) one GEMV
- * kernel normalises on the fly, and so does the wave-split MFMA tile (2 <= M
- * <= 16, d_hidden / 16 <= 512 tiles) when d_latent <= 2048; otherwise the normalised latent is written
- * to the workspace by a norm kernel and consumed by the GEMM, which needs
- * d_latent <= 8192 (SG_ERR_UNSUPPORTED otherwise).  Workspace:
- * sg_workspace_bytes(SG_OP_LATENT_TAIL, M, d_hidden, d_latent), 0 unless
- * the GEMM splits K or the norm kernel runs. */
+ * kernel normalises on the fly, and so does the wave-split MFMA tile
+ * (2 <= M <= 16, at most 512 tiles of 16 rows of w_up) when d_latent <=
+ * 2048; otherwise the normalised latent is written to the workspace by a
+ * norm kernel and consumed by the GEMM, which needs d_latent <= 8192
+ * (SG_ERR_UNSUPPORTED otherwise).  Workspace: sg_workspace_bytes(
+ * SG_OP_LATENT_TAIL, M, d_hidden, d_latent), 0 unless the GEMM splits K or
+ * the norm kernel runs. */
 int latent_moe_tail(const sg_bf16 *latent, const sg_bf16 *gamma, float eps,
                     const sg_bf16 *w_up, const sg_bf16 *shared, sg_bf16 *out,
                     int M, int d_latent, int d_hidden,
