@@ -36,6 +36,7 @@ GEMM_CASES = [
     (16, 1, 7168, False), (20, 1, 64, True), (3, 7, 0, True),
     (6, 5200, 1000, True), (13, 7170, 2056, False), (20, 9000, 512, True), (2, 4100, 7176, False),
     (130, 1000, 2056, True), (200, 4100, 520, False), (65, 7168, 2048, True), (129, 64, 1032, False),
+    (12, 6000, 1032, True), (9, 8190, 264, False),
 ]
 
 
