@@ -90,12 +90,11 @@ struct ReduceProblem {
 hipError_t launch_reduce(const ReduceProblem& p, hipStream_t s);
 
 // F_B stage of the KDA F_A/beta -> F_B branch.  The F_A/beta projection
-// P [M, n_ab] arrives either as fp32 split-K partials (partial != NULL,
-// summed in fixed order) or as bf16 (p_bf16).  The stage stores beta = P[:,
-// rank:] (and f_a = P[:, :rank] when requested) and g1 = bf16(f_a @ w_b^T).
+// P [M, n_ab] arrives as fp32 split-K partials, summed in fixed order.  The
+// stage stores beta = P[:, rank:] (and f_a = P[:, :rank] when requested) and
+// g1 = bf16(f_a @ w_b^T).
 struct FbProblem {
-  const float* partial;     // [S][M][n_ab], or NULL
-  const uint16_t* p_bf16;   // [M][n_ab] when partial == NULL
+  const float* partial;     // [S][M][n_ab]
   int S, M, n_ab, rank, n_b;
   const uint16_t* w_b;      // [n_b, rank]
   uint16_t* f_a;            // [M, rank], nullable

@@ -75,7 +75,6 @@ __global__ __launch_bounds__(kSmallkWaves * kWave) void smallk_kernel(SmallkArgs
 
 struct FbArgs {
   const float* partial;
-  const uint16_t* p_bf16;
   int S, M, n_ab, rank, n_b;
   const uint16_t* w_b;
   uint16_t* f_a;
@@ -253,14 +252,14 @@ constexpr int kFbBatch = 8;
 // Workgroup (x, y) computes g1 rows [x*R, (x+1)*R), R = fb_rows_per_wg<G>(),
 // for activation rows [y*kFbMGroup, (y+1)*kFbMGroup).  Its w_b chunk is
 // requested first, so that load overlaps forming P: the rows' bf16 P (the
-// F_A/beta partials summed in fixed order when PARTIALS, so every workgroup
-// agrees bit for bit, else the bf16 P as stored); f_a goes to LDS, and
-// workgroups with x == 0 also store beta (and f_a).
+// F_A/beta partials summed in fixed order, so every workgroup agrees bit for
+// bit); f_a goes to LDS, and workgroups with x == 0 also store beta (and
+// f_a).
 //
 // RED (0 none, 1 vector, 2 scalar, 3 vector straight-line): the first red_wgs workgroups instead run
 // the split-K reduction of another problem (the Q/K/V/G projection that ran
 // beside F_A/beta), so both epilogues take one launch.
-template <int G, bool PARTIALS, int RED>
+template <int G, int RED>
 __global__ __launch_bounds__(kSmallkWaves * kWave) void fab_fb_tail_kernel(FbArgs g, ReduceArgs red,
                                                                            int red_wgs, int fbx) {
   __shared__ __attribute__((aligned(16))) uint16_t fa_lds[kFbMGroup * kFbMaxRank];
@@ -319,12 +318,12 @@ __global__ __launch_bounds__(kSmallkWaves * kWave) void fab_fb_tail_kernel(FbArg
     return static_cast<int64_t>(m0 + mm) * g.n_ab + jj;
   };
   int base = 0;
-  if (!PARTIALS || g.S <= kSumBatch) {
+  if (g.S <= kSumBatch) {
     int64_t off[kFbPer];
 #pragma unroll
     for (int e = 0; e < kFbPer; ++e) off[e] = element(e * nthreads + tid);
     uint16_t b[kFbPer];
-    if constexpr (PARTIALS) {
+    {
       // Splits in two straight-line batches of kFbBatch (the second only
       // when S > kFbBatch); a batch's loads are unconditional (split indices
       // past S - 1 repeat the last one) and the scheduling barrier keeps
@@ -350,9 +349,6 @@ __global__ __launch_bounds__(kSmallkWaves * kWave) void fab_fb_tail_kernel(FbArg
       }
 #pragma unroll
       for (int e = 0; e < kFbPer; ++e) b[e] = f32_to_bf16(acc[e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < kFbPer; ++e) b[e] = g.p_bf16[off[e]];
     }
 #pragma unroll
     for (int e = 0; e < kFbPer; ++e) place(e * nthreads + tid, b[e]);
@@ -364,13 +360,7 @@ __global__ __launch_bounds__(kSmallkWaves * kWave) void fab_fb_tail_kernel(FbArg
     for (int e = 0; e < kFbPer; ++e) {
       const int idx = base + e * nthreads + tid;
       b[e] = 0;
-      if (idx < count) {
-        const int64_t o = element(idx);
-        if constexpr (PARTIALS)
-          b[e] = f32_to_bf16(sum_splits(g.partial + o, plane, g.S));
-        else
-          b[e] = g.p_bf16[o];
-      }
+      if (idx < count) b[e] = f32_to_bf16(sum_splits(g.partial + element(idx), plane, g.S));
     }
 #pragma unroll
     for (int e = 0; e < kFbPer; ++e) place(base + e * nthreads + tid, b[e]);
@@ -455,18 +445,11 @@ hipError_t launch_fb_g(const FbArgs& g, const ReduceArgs& r, int red_wgs, int re
   const int fby = (g.M + kFbMGroup - 1) / kFbMGroup;
   const dim3 grid(red_wgs + fbx * fby);
   const dim3 block(kSmallkWaves * kWave);
-#define SG_FB(P, RM) hipLaunchKernelGGL((fab_fb_tail_kernel<G, P, RM>), grid, block, 0, s, g, r, red_wgs, fbx)
-  if (g.partial != nullptr) {
-    if (red_mode == 1) SG_FB(true, 1);
-    else if (red_mode == 2) SG_FB(true, 2);
-    else if (red_mode == 3) SG_FB(true, 3);
-    else SG_FB(true, 0);
-  } else {
-    if (red_mode == 1) SG_FB(false, 1);
-    else if (red_mode == 2) SG_FB(false, 2);
-    else if (red_mode == 3) SG_FB(false, 3);
-    else SG_FB(false, 0);
-  }
+#define SG_FB(RM) hipLaunchKernelGGL((fab_fb_tail_kernel<G, RM>), grid, block, 0, s, g, r, red_wgs, fbx)
+  if (red_mode == 1) SG_FB(1);
+  else if (red_mode == 2) SG_FB(2);
+  else if (red_mode == 3) SG_FB(3);
+  else SG_FB(0);
 #undef SG_FB
   return hipGetLastError();
 }
@@ -503,7 +486,8 @@ hipError_t launch_smallk(const DotProblem& p, const sg_config_t& cfg, hipStream_
 }
 
 hipError_t launch_fab_fb_tail(const FbProblem& p, hipStream_t s) {
-  FbArgs g{p.partial, p.p_bf16, p.S, p.M, p.n_ab, p.rank, p.n_b, p.w_b, p.f_a, p.beta, p.g1};
+  if (p.partial == nullptr || p.S < 1) return hipErrorInvalidValue;
+  FbArgs g{p.partial, p.S, p.M, p.n_ab, p.rank, p.n_b, p.w_b, p.f_a, p.beta, p.g1};
   ReduceArgs r{};
   int red_wgs = 0, red_mode = 0;
   if (p.red != nullptr && p.red->res != nullptr) return hipErrorInvalidValue;  // no residual role
