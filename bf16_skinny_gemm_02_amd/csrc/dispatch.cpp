@@ -43,6 +43,8 @@ constexpr int kPairWgs = 256;
 // K-ranges of the packed projection's F_A/beta rows beside the M = 1 GEMV (at
 // most the F_B stage's batch of 8 splits, one memory round trip).
 constexpr int kFabGemvSplit = 7;
+// Most K-ranges of the standalone F_A/beta rows (the F_B stage's batch).
+constexpr int kFabMaxSplit = 8;
 // Largest M for which the two-stream projection is worth its fork/join.  On
 // MI355X the concurrent schedule measured slower than the single-stream one
 // (two segments in one launch, then F_B) at every decode M from 1 to 64:
@@ -226,9 +228,11 @@ extern "C" size_t sg_workspace_bytes(int op, int M, int N, int K) {
     case SG_OP_GEMM:
       return c.k_split > 1 ? sg::round256(S * plane) : 0;
     case SG_OP_FAB_FB: {
-      // The F_A/beta stage always leaves partials for the F_B stage to sum.
-      const size_t s = (c.kind == SG_KIND_GEMV_SMALLK) ? 1 : S;
-      return sg::round256(s * plane);
+      // The F_A/beta stage always leaves partials for the F_B stage to sum,
+      // with the configuration sg_kda_select gives it alone.
+      sg_config_t f;
+      if (sg_kda_select(SG_KDA_FAB_ALONE, M, K, 0, N, &f) != SG_OK) return 0;
+      return sg::round256(static_cast<size_t>(f.k_split > 0 ? f.k_split : 1) * plane);
     }
     case SG_OP_LATENT_TAIL: {
       // M = 1 with the whole row in one workgroup: the GEMV normalises the
@@ -291,6 +295,17 @@ extern "C" int sg_kda_select(int which, int M, int K, int n_qkvg, int n_ab, sg_c
     f.k_split = 1;
   }
   if (f.k_split < 1) f.k_split = 1;
+  // At most one batch of partials for the F_B stage (kFabMaxSplit, one memory
+  // round trip): longer F_A/beta workgroups cost less than a second round
+  // trip.  A GEMV range still fits the steps a wave holds.
+  if (f.k_split > kFabMaxSplit) {
+    const bool gemv = f.kind == SG_KIND_GEMV_SPLITK || f.kind == SG_KIND_GEMV_ROW;
+    const int steps = gemv ? ceil_div(K / 8, 64) : ceil_div(K, 32);
+    const int need = gemv ? ceil_div(steps, kGemvDepth) : 1;
+    const int tiles = f.grid / f.k_split;
+    f.k_split = effective_split(steps, need > kFabMaxSplit ? need : kFabMaxSplit);
+    f.grid = tiles * f.k_split;
+  }
   if (which == SG_KDA_FAB_ALONE) {
     *out = f;
     return SG_OK;

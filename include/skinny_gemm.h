@@ -159,7 +159,10 @@ enum {
  *   SG_KDA_FAB_ALONE: sg_select(M, n_ab, K, 0), except that the small-K
  *     kind, which has no partial output, becomes GEMV_SPLITK (M == 1) or
  *     MFMA_WAVESPLIT (M > 1) over one K-range: the F_B stage always sums
- *     fp32 partials.
+ *     fp32 partials.  More than 8 K-ranges become split(steps, max(need,
+ *     8)) with the grid scaled to match (steps = ceil((K/8)/64), need =
+ *     ceil(steps/16) for the GEMV kinds; steps = ceil(K/32), need = 1
+ *     otherwise): the F_B stage then sums them in one batch of loads.
  *   SG_KDA_QKVG / SG_KDA_FAB: sg_select(M, n_qkvg, K, 0) and the
  *     SG_KDA_FAB_ALONE configuration, except that
  *     - where the Q/K/V/G rows run whole on GEMV_ROW (k_split 1, M == 1)

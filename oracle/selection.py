@@ -47,7 +47,10 @@ packed projection, 2 F_A/beta alone):
   * f = select(M, n_ab, K); a GEMV_SMALLK f becomes, with k_split = 1,
     GEMV_SPLITK (M == 1: m_tile 1, rows 1, waves 4, k_unroll 16,
     grid ceil(n_ab / 4)) or MFMA_WAVESPLIT (M > 1: m_tile 4 ceil(M / 4),
-    rows 16, waves 4, k_unroll 3, grid ceil(n_ab / 16)); k_split >= 1.
+    rows 16, waves 4, k_unroll 3, grid ceil(n_ab / 16)); k_split >= 1;
+    more than 8 K-ranges are cut to split(steps, max(need, 8)), steps =
+    ceil((K/8) / 64) and need = ceil(steps / 16) for the GEMV kinds, steps =
+    ceil(K / 32) and need = 1 otherwise, grid scaled to match.
   * which 2: f.  Otherwise q = select(M, n_qkvg, K).  If q is GEMV_ROW with
     k_split 1, f becomes q's configuration with kind GEMV_SPLITK, k_split =
     split(ceil((K/8) / 64), 7) and grid ceil(n_ab / (4 rows)) * k_split.
@@ -171,6 +174,13 @@ def kda_select(which: int, M: int, K: int, n_qkvg: int, n_ab: int):
                      grid=_cdiv(n_ab, 16))
         f["k_split"] = 1
     f["k_split"] = max(f["k_split"], 1)
+    if f["k_split"] > 8:
+        gemv = f["kind"] in (GEMV_SPLITK, GEMV_ROW)
+        steps = _cdiv(K // 8, 64) if gemv else _cdiv(K, 32)
+        need = _cdiv(steps, 16) if gemv else 1
+        tiles = f["grid"] // f["k_split"]
+        f["k_split"] = _split(steps, max(need, 8))
+        f["grid"] = tiles * f["k_split"]
     if which == 2:
         return OK, f
     if q["kind"] == GEMV_ROW and q["k_split"] == 1:

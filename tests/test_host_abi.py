@@ -188,11 +188,14 @@ def test_workspace_bytes(lib):
     assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, 1, 4096, 7168) == 0
     assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, 8, 4096, 7168) == 0
     assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, 64, 4096, 7168) == 4 * 64 * 4096 * 4
-    for M in (1, 2, 4, 8, 16, 32):
-        st, cfg = selection.select(M, 136, 7168)
+    # The standalone F_A/beta -> F_B call sizes its partials for the F_A/beta
+    # configuration it runs alone, at most 8 K-ranges at the projection shape.
+    for M in (1, 2, 4, 8, 16, 32, 64, 65, 200):
+        st, cfg = selection.kda_select(2, M, 7168, 0, 136)
+        assert st == selection.OK
+        assert 1 <= cfg["k_split"] <= 8
         need = lib.sg_workspace_bytes(_lib.SG_OP_FAB_FB, M, 136, 7168)
-        assert need >= cfg["k_split"] * M * 136 * 4
-        assert need % 256 == 0
+        assert need == (cfg["k_split"] * M * 136 * 4 + 255) // 256 * 256
     assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, -1, 4, 8) == 0
     assert lib.sg_workspace_bytes(99, 4, 4, 8) == 0
 
