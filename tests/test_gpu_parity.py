@@ -118,10 +118,11 @@ def test_qkvg_repeat_is_deterministic(device):
 
 # ---- F_A/beta -> F_B ------------------------------------------------------------------
 
-@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 32])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 32, 64, 128])
 @pytest.mark.parametrize("n_ab", [136, 140, 144])
 def test_fab_fb_matches_oracle(device, M, n_ab):
-    _say(f"kda_fab_fb_proj M={M} n_ab={n_ab} cfg={sg.sg_select(M, n_ab, synth.HIDDEN)}")
+    cfg = sg.sg_kda_select(sg.SG_KDA_FAB_ALONE, M, synth.HIDDEN, 0, n_ab)
+    _say(f"kda_fab_fb_proj M={M} n_ab={n_ab} cfg={cfg}")
     x, w_ab, w_b = synth.fab_fb_inputs(M, n_ab=n_ab)
     beta = nan_like((M, n_ab - 128), device)
     g1 = nan_like((M, synth.N_B), device)
@@ -302,7 +303,7 @@ def test_latent_tail_graph_replay(device, M):
     _replay_check(device, lambda: sg.latent_moe_tail(*args, out=out, workspace=ws), [out], [eager])
 
 
-@pytest.mark.parametrize("M", [1, 3, 8, 16, 17, 64])
+@pytest.mark.parametrize("M", [1, 3, 8, 16, 17, 64, 100])
 def test_sequential_projection_equals_separate_calls(device, M):
     """The sequential KDA projection (Q/K/V/G and F_A/beta as two segments of
     one launch, then F_B with the Q/K/V/G split-K reduction) against
