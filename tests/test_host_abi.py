@@ -131,7 +131,8 @@ def test_kind_follows_m_boundaries():
 
 KDA_SHAPES = [(7168, 4096, 136), (7168, 4096, 140), (7168, 4096, 144), (2048, 1024, 136),
               (128, 512, 136), (7168, 0, 136), (264, 64, 16), (7168, 4096, 0), (1000, 300, 40),
-              (7168, 40000, 136), (8, 8, 8), (520, 4096, 260)]
+              (7168, 40000, 136), (8, 8, 8), (520, 4096, 260), (131072, 4096, 136),
+              (16384, 256, 136)]
 
 
 def _c_kda_select(lib, which, M, K, nq, nab):
@@ -155,6 +156,23 @@ def test_kda_select_matches_oracle(lib):
                     selection.kda_workspace_bytes(w, M, K, nq, nab), (w, M, K, nq, nab)
     assert checked > 10000
     assert lib.sg_kda_select(0, 1, 8, 8, 8, None) == _lib.SG_ERR_INVALID_ARG
+
+
+def test_fab_k_ranges_fit_one_batch():
+    """The F_A/beta rows keep at most 8 K-ranges (one batch of partials for the
+    F_B stage) unless a GEMV wave could not hold its range: then as few as fit
+    16 of its 512-wide steps."""
+    for K in (2048, 7168, 16384, 65536, 131072, 262144):
+        for M in (1, 2, 16, 64, 65, 256):
+            st, f = selection.kda_select(2, M, K, 0, 136)
+            assert st == selection.OK
+            if f["kind"] in (selection.GEMV_SPLITK, selection.GEMV_ROW):
+                steps = -(-(K // 8) // 64)
+                per = -(-steps // f["k_split"])
+                assert per <= 16 and (f["k_split"] <= 8 or per == 16), (M, K, f)
+            else:
+                assert f["k_split"] <= 8, (M, K, f)
+            assert f["grid"] % f["k_split"] == 0
 
 
 def test_kda_select_pairs_the_projection_tiles():
