@@ -192,8 +192,8 @@ ROOFLINE_M = 8   # the wave-split MFMA tile serves M = 2..16, five of the nine s
 # counters are taken again.
 TRAFFIC_SOURCES = ("bf16_skinny_gemm_02_amd/csrc/mfma.hip", "bf16_skinny_gemm_02_amd/csrc/sg_device.h",
                    "bf16_skinny_gemm_02_amd/csrc/dispatch.cpp")
-TRAFFIC_PMC = {"sources_sha256": "c4951ecaaa5cec02209c996060cc0a5448eb3385ba7ce5f06d7cc37a778c1302",
-               "bytes_per_launch": 59784044}
+TRAFFIC_PMC = {"sources_sha256": "ff8c56fa576d1e4e66bc76e381eda24c5571d6f976ddabb910e38533ef6e01b4",
+               "bytes_per_launch": 59784527}
 
 
 def measured_traffic():

@@ -243,9 +243,8 @@ template <int M, int R, int NW, bool FOLD>
 hipError_t launch_inst(const GemvLaunch& g, dim3 grid, size_t lds, hipStream_t s) {
   constexpr int D = gemv_depth(R);
   auto kern = gemv_kernel<M, R, NW, D, FOLD>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-      static_cast<int>(kGemvMaxLds));
+  static std::atomic<bool> lds_set[kLdsAttrDevices];
+  const hipError_t attr = ensure_lds_limit(reinterpret_cast<const void*>(kern), kGemvMaxLds, lds_set);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, grid, dim3(NW * kWave), lds, s, g);
   return hipGetLastError();

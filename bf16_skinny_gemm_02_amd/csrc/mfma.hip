@@ -589,14 +589,13 @@ __global__ __launch_bounds__(kBlkWaves * kWave) void block_kernel(MfmaLaunch L) 
 
 // ---- launchers -------------------------------------------------------------------
 
-// One attribute call per kernel instance (the ring can exceed the default
+// One attribute call per kernel instance and device (the ring can exceed the default
 // 64 KiB of dynamic LDS).
 template <int MB, int NW, int C, int XQ, bool RES>
 hipError_t launch_tile_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
   auto kern = tile_kernel<MB, NW, C, XQ, RES>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-      static_cast<int>(kMfmaMaxLds));
+  static std::atomic<bool> lds_set[kLdsAttrDevices];
+  const hipError_t attr = ensure_lds_limit(reinterpret_cast<const void*>(kern), kMfmaMaxLds, lds_set);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(wgs), dim3(NW * kWave), tile_lds_bytes(NW, C, XQ), s, L);
   return hipGetLastError();
@@ -605,9 +604,8 @@ hipError_t launch_tile_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
 template <int XQ, int C, bool NORM, bool RES>
 hipError_t launch_wsplit_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
   auto kern = wsplit_kernel<XQ, C, NORM, RES>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-      static_cast<int>(kMfmaMaxLds));
+  static std::atomic<bool> lds_set[kLdsAttrDevices];
+  const hipError_t attr = ensure_lds_limit(reinterpret_cast<const void*>(kern), kMfmaMaxLds, lds_set);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(wgs), dim3(kSplitWaves * kWave), wsplit_lds_bytes(C, XQ, NORM), s, L);
   return hipGetLastError();
@@ -635,9 +633,8 @@ hipError_t launch_wsplit_xq(const MfmaLaunch& L, int XQ, int C, int wgs, hipStre
 template <int C, bool RES>
 hipError_t launch_block_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
   auto kern = block_kernel<C, RES>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-      static_cast<int>(kMfmaMaxLds));
+  static std::atomic<bool> lds_set[kLdsAttrDevices];
+  const hipError_t attr = ensure_lds_limit(reinterpret_cast<const void*>(kern), kMfmaMaxLds, lds_set);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(wgs), dim3(kBlkWaves * kWave), block_lds_bytes(C), s, L);
   return hipGetLastError();

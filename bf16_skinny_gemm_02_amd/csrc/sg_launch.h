@@ -7,9 +7,27 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "skinny_gemm.h"
 
 namespace sg {
+
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once
+// per device: `done` is the kernel instance's own table of devices already
+// set (static storage, so it starts all false).  Devices past the table are
+// set on every call.
+constexpr int kLdsAttrDevices = 64;
+inline hipError_t ensure_lds_limit(const void* kernel, size_t bytes, std::atomic<bool>* done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool tracked = dev >= 0 && dev < kLdsAttrDevices;
+  if (tracked && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+  if (e == hipSuccess && tracked) done[dev].store(true, std::memory_order_release);
+  return e;
+}
 
 // One dot-product problem out[m,n] = sum_k a[m,k] * w[n,k] with one of the
 // epilogues below.
