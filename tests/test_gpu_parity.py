@@ -41,6 +41,8 @@ GEMM_CASES = [
     # block splits (the reduction's loop over many partials)
     (1, 300, 65536, False), (8, 500, 32768, True), (64, 256, 16384, True), (200, 128, 16392, False),
     (16, 2000, 40000, True),
+    # 17 <= M <= 32 with wide N (64-row tiles, K split, reduction)
+    (24, 7168, 2048, True), (32, 8000, 1000, False), (17, 6200, 4104, True),
 ]
 
 
@@ -374,7 +376,7 @@ def test_packed_projection_equals_split(device):
 
 # ---- latent-MoE tail ----------------------------------------------------------------------
 
-@pytest.mark.parametrize("M", [1, 2, 8, 13, 16, 17, 64, 130, 256])
+@pytest.mark.parametrize("M", [1, 2, 8, 13, 16, 17, 24, 32, 33, 64, 130, 256])
 def test_latent_tail_full_size(device, M):
     cfg = sg.sg_select(M, synth.D_HIDDEN, synth.D_LATENT)
     _say(f"latent_moe_tail M={M} cfg={cfg}")
@@ -416,7 +418,7 @@ def test_latent_tail_zero_weights_is_shared(device, M):
 @pytest.mark.parametrize("M,d,D", [(5, 264, 900), (24, 520, 100), (2, 128, 64),
                                    (3, 1000, 5200), (11, 4104, 6000), (16, 2048, 5136),
                                    (4, 2048, 1024), (7, 1032, 3000), (12, 2048, 2000),
-                                   (16, 1024, 4096)])
+                                   (16, 1024, 4096), (20, 2048, 6400), (29, 1032, 8192)])
 def test_latent_tail_other_shapes(device, M, d, D):
     """Shapes that take the split-K, small-latent and folded-RMSNorm paths of
     the tail: the GEMV fold (M = 1), the wave-split fold (ragged latent, a
