@@ -85,17 +85,28 @@ def sg_version() -> str:
 
 # ---- marshalling helpers ----------------------------------------------------
 
-def _check_tensor(t: torch.Tensor, name: str, ndim: int) -> None:
+def _check_tensor(t: torch.Tensor, name: str, ndim: int, contiguous: bool = False,
+                  on_gpu: bool = True) -> None:
+    """Type, dtype, rank and layout first, the device last, so that layout
+    errors are reported the same way on any host."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype not in _16BIT:
         raise TypeError(f"{name} must be bfloat16 (or a 16-bit bit-pattern view), got {t.dtype}")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
     if t.dim() != ndim:
         raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
     if t.numel() and t.stride(-1) != 1:
         raise ValueError(f"{name} must have unit stride in its last dimension")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (the C ABI takes no row stride for it)")
+    if on_gpu and not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _same_device(*tensors) -> None:
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"all tensors of one call must be on one device, got {sorted(map(str, devs))}")
 
 
 def _ld(t: torch.Tensor) -> int:
@@ -113,19 +124,32 @@ def _stream(stream, device) -> ctypes.c_void_p:
 
 
 def _workspace(ws, nbytes: int, device):
+    """A caller's workspace must be a contiguous tensor on the call's device;
+    without one, a zero-filled one of the required size is allocated."""
+    if ws is not None:
+        if not isinstance(ws, torch.Tensor):
+            raise TypeError("workspace must be a torch.Tensor")
+        if not ws.is_cuda or (device is not None and ws.device != torch.device(device)):
+            raise ValueError(f"workspace must be on {device}, got {ws.device}")
+        if not ws.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        return ws, ws.numel() * ws.element_size()
     if nbytes == 0:
-        return ws, 0 if ws is None else ws.numel() * ws.element_size()
-    if ws is None:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    return ws, ws.numel() * ws.element_size()
+        return None, 0
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
-def _out(out, shape, like: torch.Tensor, name: str):
+def _out(out, shape, like: torch.Tensor, name: str, contiguous: bool = True):
+    """An output given by the caller must have the right shape, lie on the
+    same device as `like` and, unless the C ABI takes its row stride
+    (contiguous=False), be contiguous."""
     if out is None:
         return torch.empty(shape, dtype=torch.bfloat16, device=like.device)
-    _check_tensor(out, name, len(shape))
+    _check_tensor(out, name, len(shape), contiguous=contiguous, on_gpu=False)
     if tuple(out.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    if out.device != like.device:
+        raise ValueError(f"{name} is on {out.device}, expected {like.device}")
     return out
 
 
@@ -166,7 +190,8 @@ def skinny_gemm(A: torch.Tensor, W: torch.Tensor, residual: torch.Tensor | None 
         _check_tensor(residual, "residual", 2)
         if tuple(residual.shape) != (M, N):
             raise ValueError("residual must be [M, N]")
-    out = _out(out, (M, N), A, "out")
+    _same_device(A, W, residual)
+    out = _out(out, (M, N), A, "out", contiguous=False)
     ws, ws_bytes = _workspace(workspace, sg_workspace_bytes(SG_OP_GEMM, M, N, K), A.device)
     c = None
     if cfg is not None:
@@ -188,6 +213,7 @@ def kda_qkvg_proj(x: torch.Tensor, w_qkvg: torch.Tensor, *, out: torch.Tensor | 
     N = w_qkvg.shape[0]
     if w_qkvg.shape[1] != K or not x.is_contiguous() or not w_qkvg.is_contiguous():
         raise ValueError("x [M,K] and w_qkvg [N,K] must be contiguous with matching K")
+    _same_device(x, w_qkvg)
     out = _out(out, (M, N), x, "out")
     ws, ws_bytes = _workspace(workspace, sg_workspace_bytes(SG_OP_GEMM, M, N, K), x.device)
     st = _lib.load().kda_qkvg_proj(_ptr(x), _ptr(w_qkvg), _ptr(out), M, N, K, _ptr(ws), ws_bytes,
@@ -210,9 +236,12 @@ def kda_fab_fb_proj(x: torch.Tensor, w_ab: torch.Tensor, w_b: torch.Tensor, rank
     n_b = w_b.shape[0]
     if w_ab.shape[1] != K or w_b.shape[1] != rank:
         raise ValueError("w_ab must be [n_ab, K] and w_b [n_b, rank]")
+    _same_device(x, w_ab, w_b)
     beta = _out(beta, (M, n_ab - rank), x, "beta")
     g1 = _out(g1, (M, n_b), x, "g1")
-    if want_f_a and f_a is None:
+    if f_a is not None:
+        f_a = _out(f_a, (M, rank), x, "f_a")
+    elif want_f_a:
         f_a = torch.empty((M, rank), dtype=torch.bfloat16, device=x.device)
     ws, ws_bytes = _workspace(workspace, sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K), x.device)
     st = _lib.load().kda_fab_fb_proj(_ptr(x), _ptr(w_ab), _ptr(w_b), _ptr(f_a), _ptr(beta),
@@ -240,6 +269,7 @@ def kda_projection_overlap(x: torch.Tensor, packed_w: torch.Tensor, w_b: torch.T
     n_b = w_b.shape[0]
     if packed_w.shape != (n_qkvg + n_ab, K) or w_b.shape[1] != rank:
         raise ValueError("packed_w must be [n_qkvg + n_ab, K] and w_b [n_b, rank]")
+    _same_device(x, packed_w, w_b)
     qkvg = _out(qkvg, (M, n_qkvg), x, "qkvg")
     beta = _out(beta, (M, n_ab - rank), x, "beta")
     g1 = _out(g1, (M, n_b), x, "g1")
@@ -274,6 +304,7 @@ def latent_moe_tail(latent: torch.Tensor, gamma: torch.Tensor, w_up: torch.Tenso
         _check_tensor(shared, "shared", 2)
         if tuple(shared.shape) != (M, D) or not shared.is_contiguous():
             raise ValueError("shared must be a contiguous [M, d_hidden] tensor")
+    _same_device(latent, gamma, w_up, shared)
     out = _out(out, (M, D), latent, "out")
     ws, ws_bytes = _workspace(workspace, sg_workspace_bytes(SG_OP_LATENT_TAIL, M, D, d),
                               latent.device)

@@ -40,6 +40,7 @@ int check_output2(const void* p, int64_t ld, int64_t min_ld) {
 // through 32-bit buffer offsets: both spans must stay below 2^31 bytes.
 constexpr int64_t kMaxTileRows = 128;
 bool spans_ok(int64_t rows, int64_t ld, int64_t K) {
+  if (ld < 0 || K < 0) return false;
   if (rows <= 0) return true;
   return ((rows - 1) * ld + K) * 2 < (int64_t(1) << 31);
 }
@@ -107,6 +108,9 @@ int validate_gemm(const sg_bf16* A, int64_t lda, const sg_bf16* W, int64_t ldw, 
     *empty = true;
     return SG_OK;
   }
+  // Row strides are at least K (so never negative) whatever K is: the MFMA
+  // kernels build 32-bit buffer bounds from them even when K == 0.
+  if (lda < K || ldw < K) return SG_ERR_INVALID_ARG;
   if (K > 0) {  // with K == 0 the operands are never read
     if ((st = check_operand16(A, lda, K)) != SG_OK) return st;
     if ((st = check_operand16(W, ldw, K)) != SG_OK) return st;

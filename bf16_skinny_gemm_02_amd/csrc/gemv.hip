@@ -246,8 +246,7 @@ hipError_t launch_inst(const GemvLaunch& g, dim3 grid, size_t lds, hipStream_t s
   static std::atomic<bool> lds_set[kLdsAttrDevices];
   const hipError_t attr = ensure_lds_limit(reinterpret_cast<const void*>(kern), kGemvMaxLds, lds_set);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, grid, dim3(NW * kWave), lds, s, g);
-  return hipGetLastError();
+  return launch_kernel(kern, grid, dim3(NW * kWave), lds, s, g);
 }
 
 // The table sends only M = 1 here (4 waves; one weight row per wave, or four

@@ -597,8 +597,7 @@ hipError_t launch_tile_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
   static std::atomic<bool> lds_set[kLdsAttrDevices];
   const hipError_t attr = ensure_lds_limit(reinterpret_cast<const void*>(kern), kMfmaMaxLds, lds_set);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(wgs), dim3(NW * kWave), tile_lds_bytes(NW, C, XQ), s, L);
-  return hipGetLastError();
+  return launch_kernel(kern, dim3(wgs), dim3(NW * kWave), tile_lds_bytes(NW, C, XQ), s, L);
 }
 
 template <int XQ, int C, bool NORM, bool RES>
@@ -607,8 +606,7 @@ hipError_t launch_wsplit_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
   static std::atomic<bool> lds_set[kLdsAttrDevices];
   const hipError_t attr = ensure_lds_limit(reinterpret_cast<const void*>(kern), kMfmaMaxLds, lds_set);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(wgs), dim3(kSplitWaves * kWave), wsplit_lds_bytes(C, XQ, NORM), s, L);
-  return hipGetLastError();
+  return launch_kernel(kern, dim3(wgs), dim3(kSplitWaves * kWave), wsplit_lds_bytes(C, XQ, NORM), s, L);
 }
 
 template <bool NORM, bool RES>
@@ -636,8 +634,7 @@ hipError_t launch_block_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
   static std::atomic<bool> lds_set[kLdsAttrDevices];
   const hipError_t attr = ensure_lds_limit(reinterpret_cast<const void*>(kern), kMfmaMaxLds, lds_set);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3(wgs), dim3(kBlkWaves * kWave), block_lds_bytes(C), s, L);
-  return hipGetLastError();
+  return launch_kernel(kern, dim3(wgs), dim3(kBlkWaves * kWave), block_lds_bytes(C), s, L);
 }
 
 int ksteps_of(int K) { return (K + kKStep - 1) / kKStep; }

@@ -29,6 +29,21 @@ inline hipError_t ensure_lds_limit(const void* kernel, size_t bytes, std::atomic
   return e;
 }
 
+// Enqueues kern<<<grid, block, lds, s>>>(args...) through hipLaunchKernel
+// and returns that call's own status.  (Reading the runtime's last-error
+// slot after a launch would also report an error some earlier, unrelated
+// call of the caller left there.)
+template <typename T>
+struct arg_ident {
+  using type = T;
+};
+template <typename... P>
+inline hipError_t launch_kernel(void (*kern)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                                typename arg_ident<P>::type... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, argv, lds, s);
+}
+
 // One dot-product problem out[m,n] = sum_k a[m,k] * w[n,k] with one of the
 // epilogues below.
 struct DotProblem {

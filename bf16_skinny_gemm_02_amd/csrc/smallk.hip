@@ -432,8 +432,7 @@ template <int G>
 hipError_t launch_smallk_g(const SmallkArgs& g, hipStream_t s) {
   const int rows_per_wg = kSmallkWaves * (kWave / G);
   const dim3 grid((g.N + rows_per_wg - 1) / rows_per_wg);
-  hipLaunchKernelGGL((smallk_kernel<G>), grid, dim3(kSmallkWaves * kWave), 0, s, g);
-  return hipGetLastError();
+  return launch_kernel(smallk_kernel<G>, grid, dim3(kSmallkWaves * kWave), 0, s, g);
 }
 
 template <int G>
@@ -445,13 +444,12 @@ hipError_t launch_fb_g(const FbArgs& g, const ReduceArgs& r, int red_wgs, int re
   const int fby = (g.M + kFbMGroup - 1) / kFbMGroup;
   const dim3 grid(red_wgs + fbx * fby);
   const dim3 block(kSmallkWaves * kWave);
-#define SG_FB(RM) hipLaunchKernelGGL((fab_fb_tail_kernel<G, RM>), grid, block, 0, s, g, r, red_wgs, fbx)
-  if (red_mode == 1) SG_FB(1);
-  else if (red_mode == 2) SG_FB(2);
-  else if (red_mode == 3) SG_FB(3);
-  else SG_FB(0);
-#undef SG_FB
-  return hipGetLastError();
+  switch (red_mode) {
+    case 1: return launch_kernel(fab_fb_tail_kernel<G, 1>, grid, block, 0, s, g, r, red_wgs, fbx);
+    case 2: return launch_kernel(fab_fb_tail_kernel<G, 2>, grid, block, 0, s, g, r, red_wgs, fbx);
+    case 3: return launch_kernel(fab_fb_tail_kernel<G, 3>, grid, block, 0, s, g, r, red_wgs, fbx);
+    default: return launch_kernel(fab_fb_tail_kernel<G, 0>, grid, block, 0, s, g, r, red_wgs, fbx);
+  }
 }
 
 int reduce_blocks(const ReduceProblem& p) {
@@ -514,20 +512,16 @@ hipError_t launch_reduce(const ReduceProblem& p, hipStream_t s) {
   const ReduceArgs g = reduce_args(p);
   const dim3 grid(static_cast<unsigned>(blocks));
   const bool res = p.res != nullptr;
-  if (reduce_vec(p)) {
-    if (res) hipLaunchKernelGGL((reduce_kernel<true, true>), grid, dim3(256), 0, s, g);
-    else hipLaunchKernelGGL((reduce_kernel<true, false>), grid, dim3(256), 0, s, g);
-  } else {
-    if (res) hipLaunchKernelGGL((reduce_kernel<false, true>), grid, dim3(256), 0, s, g);
-    else hipLaunchKernelGGL((reduce_kernel<false, false>), grid, dim3(256), 0, s, g);
-  }
-  return hipGetLastError();
+  if (reduce_vec(p))
+    return res ? launch_kernel(reduce_kernel<true, true>, grid, dim3(256), 0, s, g)
+               : launch_kernel(reduce_kernel<true, false>, grid, dim3(256), 0, s, g);
+  return res ? launch_kernel(reduce_kernel<false, true>, grid, dim3(256), 0, s, g)
+             : launch_kernel(reduce_kernel<false, false>, grid, dim3(256), 0, s, g);
 }
 
 hipError_t launch_rmsnorm(const NormProblem& p, hipStream_t s) {
   if ((p.d >> 3) > 256 * kNormChunks) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(static_cast<unsigned>(p.M)), dim3(256), 0, s, p);
-  return hipGetLastError();
+  return launch_kernel(rmsnorm_kernel, dim3(static_cast<unsigned>(p.M)), dim3(256), 0, s, p);
 }
 
 }  // namespace sg

@@ -36,12 +36,20 @@
  *    kernels and return without synchronising.  All calls are capturable
  *    into a hipGraph (no allocation, no memset, no host synchronisation).
  *  - Errors: every argument is validated before anything is enqueued, so an
- *    error return means no work was enqueued.  Launch failures reported by
- *    the runtime are returned as SG_ERR_HIP.  M == 0 (or an empty N) is a
- *    valid no-op that returns SG_OK.
- *  - Every output element is written on every successful path.
- *  - State: the library allocates nothing and keeps no mutable global state;
- *    the entry points are thread-safe.
+ *    error return means no work was enqueued.  A launch the runtime refuses
+ *    is returned as SG_ERR_HIP; each launch's own status is read, so an error
+ *    some earlier, unrelated call left pending in the runtime is neither
+ *    reported as this call's nor cleared.  (If a later launch of a
+ *    multi-launch call fails, the earlier ones stay enqueued.)  M == 0 (or an
+ *    empty N) is a valid no-op that returns SG_OK.
+ *  - Every output element is written on every successful path, and nothing
+ *    outside the outputs and the workspace is written.
+ *  - State: the library allocates nothing.  Its only process state is, per
+ *    kernel instance and per device, a flag that the kernel's dynamic-LDS
+ *    limit has been raised (hipFuncSetAttribute, on first use).  The flag is
+ *    kept for the device current at the call, so a call must be made with
+ *    its stream's device current (as torch does).  The entry points are
+ *    thread-safe.
  */
 #ifndef SKINNY_GEMM_H
 #define SKINNY_GEMM_H

@@ -139,11 +139,6 @@ def qkvg(x: np.ndarray, w_qkvg: np.ndarray):
     return gemm(x, w_qkvg)
 
 
-def split_qkvg(qkvg_out: np.ndarray, head_block: int = 1024):
-    """Columns [0,1024) q, [1024,2048) k, [2048,3072) v, [3072,4096) g."""
-    return tuple(qkvg_out[:, i * head_block:(i + 1) * head_block] for i in range(4))
-
-
 def fab_fb(x: np.ndarray, w_ab: np.ndarray, w_b: np.ndarray, rank: int = 128):
     """O3: returns dict with p (exact, bits), f_a, beta, g1 (exact, bits)."""
     p_exact, p_bits = gemm(x, w_ab)

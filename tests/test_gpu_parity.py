@@ -221,29 +221,34 @@ def test_overlap_matches_sequential_and_oracle(device, M):
     assert_close(host(b_c), o["beta_exact"], "beta")
 
 
-@pytest.mark.parametrize("M", [1, 16, 32])
-def test_overlap_graph_replay(device, M):
-    """Capture the concurrent call in a graph, replay it several times with
-    eager work in between, and compare every replay with the eager result."""
+@pytest.mark.parametrize("concurrent", [True, False])
+@pytest.mark.parametrize("M", [1, 4, 16, 32])
+def test_overlap_graph_replay(device, M, concurrent):
+    """Capture the KDA projection (the two-stream fork/join schedule, or the
+    single-stream one the closed gate picks) in a graph, replay it several
+    times with eager work in between, and compare every replay bit for bit
+    with the eager single-stream result."""
+    _say(f"kda_projection_overlap graph M={M} concurrent={concurrent}")
     x, packed, w_b = synth.overlap_inputs(M)
     xd, pd, wbd = dev(x, device), dev(packed, device), dev(w_b, device)
     aux = torch.cuda.Stream(device)
     fork, join = sg.HipEvent(), sg.HipEvent()
-    q_e, g1_e, b_e = sg.kda_projection_overlap(xd, pd, wbd, aux_stream=aux, fork=fork, join=join)
+    q_e, g1_e, b_e = sg.kda_projection_overlap(xd, pd, wbd)
     q = torch.empty_like(q_e)
     g1 = torch.empty_like(g1_e)
     beta = torch.empty_like(b_e)
-    ws_aux = torch.empty(sg.sg_kda_workspace_bytes(1, M, synth.HIDDEN, 4096, 136),
+    ws_aux = torch.zeros(max(sg.sg_kda_workspace_bytes(1, M, synth.HIDDEN, 4096, 136), 256),
                          dtype=torch.uint8, device=device)
-    ws_main = torch.empty(max(sg.sg_kda_workspace_bytes(0, M, synth.HIDDEN, 4096, 136), 256),
+    ws_main = torch.zeros(max(sg.sg_kda_workspace_bytes(0, M, synth.HIDDEN, 4096, 136), 256),
                           dtype=torch.uint8, device=device)
+    kw = dict(aux_stream=aux, fork=fork, join=join) if concurrent else {}
     side = torch.cuda.Stream(device)
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=side):
             sg.kda_projection_overlap(xd, pd, wbd, qkvg=q, g1=g1, beta=beta, ws_aux=ws_aux,
-                                      ws_main=ws_main, aux_stream=aux, fork=fork, join=join)
+                                      ws_main=ws_main, **kw)
     torch.cuda.current_stream().wait_stream(side)
     for rep in range(4):
         for t in (q, g1, beta):

@@ -260,6 +260,12 @@ def test_skinny_gemm_validation(lib):
                  ws_bytes=need - 1) == E.SG_ERR_WORKSPACE
     assert _gemm(lib, lda=4096, ldw=4096, K=4096, ws=ctypes.c_void_p(0x50004),
                  ws_bytes=need) == E.SG_ERR_MISALIGNED
+    # row strides below K (negative ones included) are refused whatever K is,
+    # K == 0 too: the MFMA kernels build 32-bit buffer bounds from them
+    assert _gemm(lib, M=17, N=8, K=0, lda=-1, ldw=0) == E.SG_ERR_INVALID_ARG
+    assert _gemm(lib, M=17, N=8, K=0, lda=0, ldw=-8) == E.SG_ERR_INVALID_ARG
+    assert _gemm(lib, M=100, N=8, K=0, lda=-(1 << 40), ldw=0) == E.SG_ERR_INVALID_ARG
+    assert _gemm(lib, M=2, N=8, K=0, lda=-1, ldw=0, A=NUL, W=NUL) == E.SG_ERR_INVALID_ARG
     # empty problems are no-ops
     assert _gemm(lib, M=0) == E.SG_OK
     assert _gemm(lib, N=0) == E.SG_OK

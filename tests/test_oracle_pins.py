@@ -225,8 +225,6 @@ def test_projection_overlap_matches_packed_gemm():
     assert np.array_equal(o["qkvg_bits"], packed_bits[:, :64])
     assert np.array_equal(o["p_bits"], packed_bits[:, 64:84])
     assert np.array_equal(o["beta"], packed_bits[:, 80:84])
-    q, k, v, g = oracle.split_qkvg(np.zeros((1, 4096)))
-    assert q.shape == k.shape == v.shape == g.shape == (1, 1024)
 
 
 # ---- O5 latent-MoE tail -----------------------------------------------------------------
@@ -299,10 +297,26 @@ def test_latent_tail_scale_invariance_and_variants():
     assert np.allclose(ex4, ex, rtol=0, atol=1e-5 * np.abs(ex).max())
     # Rounding the normalised latent to bf16 perturbs each product by <= 2^-9
     # relative; over 2048 terms of unit-variance products the output moves by
-    # ~1.2e-3 (one sigma), up to ~9e-3 over a 256 x 7168 output.
+    # ~1e-3 (one sigma).
     ex1, _ = oracle.latent_tail(L, gamma, 1e-6, w_up, S, variant=1)
     assert np.all(np.abs(ex1 - ex) <= 5e-3 * np.maximum(1.0, np.abs(ex)))
     assert np.abs(ex1 - ex).max() > 1e-4  # the two readings do differ
+
+
+def test_latent_tail_variant_drift_at_full_size():
+    """The drift between the two readings of the RMSNorm output on the tail
+    workload at its largest batch (M = 256, d = 2048, D = 7168, the inputs
+    the GPU tests use): one sigma ~1.0e-3 and a maximum of 7.9e-3 scaled by
+    max(1, |out|), below the 1e-2 budget but close to it, which is why the
+    GPU is held to one reading (the bf16 normalised latent) rather than
+    either."""
+    L, gamma, w_up, S = synth.tail_inputs(256)
+    ex0, _ = oracle.latent_tail(L, gamma, 1e-6, w_up, S, variant=0)
+    ex1, _ = oracle.latent_tail(L, gamma, 1e-6, w_up, S, variant=1)
+    diff = np.abs(ex1 - ex0)
+    scaled = diff / np.maximum(1.0, np.abs(ex0))
+    assert 7.0e-3 < scaled.max() < 8.5e-3, scaled.max()
+    assert 0.8e-3 < diff.std() < 1.3e-3, diff.std()
 
 
 # ---- planted mistakes: the pins above must reject each ------------------------------------
