@@ -29,7 +29,7 @@ __all__ = [
     "sg_select", "sg_overlap_gate", "sg_overlap_max_tokens", "sg_workspace_bytes",
     "sg_kda_select", "sg_kda_workspace_bytes", "sg_version",
     "skinny_gemm", "kda_qkvg_proj", "kda_fab_fb_proj", "kda_projection_overlap",
-    "latent_moe_tail", "HipEvent", "library_path",
+    "latent_moe_tail", "kda_projection_noalloc", "HipEvent", "library_path",
 ]
 
 _16BIT = (torch.bfloat16, torch.int16, torch.uint16)
@@ -281,6 +281,35 @@ def kda_projection_overlap(x: torch.Tensor, packed_w: torch.Tensor, w_b: torch.T
         ctypes.c_void_p(aux_stream.cuda_stream) if aux_stream is not None else None,
         fork.handle if fork is not None else None, join.handle if join is not None else None)
     _lib.check(st, "kda_projection_overlap")
+    return qkvg, g1, beta
+
+
+def kda_projection_noalloc(x: torch.Tensor, packed_w: torch.Tensor, w_b: torch.Tensor, *,
+                           n_qkvg: int = 4096, n_ab: int = 136, rank: int = 128,
+                           qkvg: torch.Tensor, beta: torch.Tensor, g1: torch.Tensor,
+                           main_stream=None, aux_stream=None, fork: HipEvent | None = None,
+                           join: HipEvent | None = None):
+    """kda_projection_overlap with its workspaces in the library's own
+    per-GPU device array: no allocation anywhere, so the outputs must be
+    given.  Calls that may overlap on one GPU must not be issued."""
+    for t, n in ((x, "x"), (packed_w, "packed_w"), (w_b, "w_b")):
+        _check_tensor(t, n, 2, contiguous=True)
+    M, K = x.shape
+    n_b = w_b.shape[0]
+    if packed_w.shape != (n_qkvg + n_ab, K) or w_b.shape[1] != rank:
+        raise ValueError("packed_w must be [n_qkvg + n_ab, K] and w_b [n_b, rank]")
+    _same_device(x, packed_w, w_b)
+    if qkvg is None or beta is None or g1 is None:
+        raise ValueError("kda_projection_noalloc allocates nothing: pass qkvg, beta and g1")
+    qkvg = _out(qkvg, (M, n_qkvg), x, "qkvg")
+    beta = _out(beta, (M, n_ab - rank), x, "beta")
+    g1 = _out(g1, (M, n_b), x, "g1")
+    st = _lib.load().kda_projection_noalloc(
+        _ptr(x), _ptr(packed_w), _ptr(w_b), _ptr(qkvg), _ptr(beta), _ptr(g1), M, K, n_qkvg, n_ab,
+        rank, n_b, _stream(main_stream, x.device),
+        ctypes.c_void_p(aux_stream.cuda_stream) if aux_stream is not None else None,
+        fork.handle if fork is not None else None, join.handle if join is not None else None)
+    _lib.check(st, "kda_projection_noalloc")
     return qkvg, g1, beta
 
 

@@ -23,7 +23,7 @@ BUILD = ROOT / "_build"
 LIB = PKG / "libskinny_gemm.so"
 ARCH = "gfx950"
 
-SOURCES = ["gemv.hip", "smallk.hip", "mfma.hip", "abi.cpp", "dispatch.cpp"]
+SOURCES = ["gemv.hip", "smallk.hip", "mfma.hip", "noalloc.hip", "abi.cpp", "dispatch.cpp"]
 
 
 def _hipcc() -> str:

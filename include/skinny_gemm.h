@@ -287,6 +287,28 @@ int latent_moe_tail(const sg_bf16 *latent, const sg_bf16 *gamma, float eps,
                     int M, int d_latent, int d_hidden,
                     void *ws, size_t ws_bytes, sg_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under hipGraph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * projection of kda_projection_overlap, same arguments and results, with
+ * both workspaces taken from a device array the library owns instead of the
+ * caller's ws_main / ws_aux.
+ * The array holds SG_NOALLOC_SCRATCH_BYTES per GPU, zero-filled when the
+ * library is loaded and kept until the process ends.  A call whose two
+ * workspaces (sg_kda_workspace_bytes(SG_KDA_FAB, ...) and
+ * sg_kda_workspace_bytes(SG_KDA_QKVG, ...), each rounded up to 256 bytes)
+ * need more returns SG_ERR_WORKSPACE before anything is enqueued (at the
+ * Kimi-K3 shapes, M <= 256 needs less than 10 MiB).  It calls no allocating
+ * routine; its first call on a device looks up that device's array address
+ * (hipGetSymbolAddress).  All calls on one GPU share the array: calls that
+ * may overlap on one GPU (two streams, two host threads) race on it and
+ * must not be issued.  Returns the statuses of kda_projection_overlap. */
+#define SG_NOALLOC_SCRATCH_BYTES (16u << 20)
+int kda_projection_noalloc(const sg_bf16 *x, const sg_bf16 *packed_w, const sg_bf16 *w_b,
+                           sg_bf16 *qkvg, sg_bf16 *beta, sg_bf16 *g1,
+                           int M, int K, int n_qkvg, int n_ab, int rank, int n_b,
+                           sg_stream_t main_stream, sg_stream_t aux_stream,
+                           sg_event_t fork, sg_event_t join);
+
 #ifdef __cplusplus
 }
 #endif

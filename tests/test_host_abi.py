@@ -354,3 +354,21 @@ def test_latent_tail_validation(lib):
     assert tail(S=ctypes.c_void_p(0x90001)) == E.SG_ERR_MISALIGNED
     assert tail(M=0) == E.SG_OK
     assert tail(D=0) == E.SG_OK
+
+
+def test_noalloc_rejects_beyond_its_array_before_any_gpu_call(lib):
+    """kda_projection_noalloc checks its array's size before it touches the
+    GPU: a projection whose workspaces exceed SG_NOALLOC_SCRATCH_BYTES returns
+    SG_ERR_WORKSPACE (fake pointers: nothing is dereferenced); M = 0 is a
+    no-op."""
+    M, K, nq, nab = 256, 7168, 4096, 2304
+    need = lib.sg_kda_workspace_bytes(0, M, K, nq, nab) + lib.sg_kda_workspace_bytes(1, M, K, nq, nab)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    args = (A16, B16, C16, ctypes.c_void_p(0x80000), ctypes.c_void_p(0x60000),
+            ctypes.c_void_p(0x70000))
+    assert lib.kda_projection_noalloc(*args, M, K, nq, nab, 128, 1024, None, None, None,
+                                      None) == _lib.SG_ERR_WORKSPACE
+    assert lib.kda_projection_noalloc(*args, 0, K, 4096, nab, 128, 1024, None, None, None,
+                                      None) == _lib.SG_OK
+    assert lib.kda_projection_noalloc(*args, -1, K, 4096, nab, 128, 1024, None, None, None,
+                                      None) == _lib.SG_ERR_INVALID_ARG
