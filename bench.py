@@ -112,9 +112,9 @@ class ProjectionCase:
         self.qkvg = torch.empty((M, N_QKVG), dtype=torch.bfloat16, device=device)
         self.g1 = torch.empty((M, N_B), dtype=torch.bfloat16, device=device)
         self.beta = torch.empty((M, N_AB - RANK), dtype=torch.bfloat16, device=device)
-        self.ws_aux = torch.empty(max(sg.sg_kda_workspace_bytes(1, M, K, N_QKVG, N_AB), 256),
+        self.ws_aux = torch.zeros(max(sg.sg_kda_workspace_bytes(1, M, K, N_QKVG, N_AB), 256),
                                   dtype=torch.uint8, device=device)
-        self.ws_main = torch.empty(max(sg.sg_kda_workspace_bytes(0, M, K, N_QKVG, N_AB), 256),
+        self.ws_main = torch.zeros(max(sg.sg_kda_workspace_bytes(0, M, K, N_QKVG, N_AB), 256),
                                    dtype=torch.uint8, device=device)
         self.aux, self.fork, self.join = aux, fork, join
 

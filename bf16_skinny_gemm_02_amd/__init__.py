@@ -29,7 +29,8 @@ __all__ = [
     "sg_select", "sg_overlap_gate", "sg_overlap_max_tokens", "sg_workspace_bytes",
     "sg_kda_select", "sg_kda_workspace_bytes", "sg_version",
     "skinny_gemm", "kda_qkvg_proj", "kda_fab_fb_proj", "kda_projection_overlap",
-    "latent_moe_tail", "kda_projection_noalloc", "HipEvent", "library_path",
+    "latent_moe_tail", "kda_projection_noalloc", "kda_fab_fb_proj_fused", "HipEvent",
+    "library_path",
 ]
 
 _16BIT = (torch.bfloat16, torch.int16, torch.uint16)
@@ -222,10 +223,18 @@ def kda_qkvg_proj(x: torch.Tensor, w_qkvg: torch.Tensor, *, out: torch.Tensor | 
     return out
 
 
+def kda_fab_fb_proj_fused(*args, **kwargs):
+    """kda_fab_fb_proj as one launch (the in-launch F_A/beta -> F_B hand-off):
+    same arguments and results.  A workspace given by the caller must have
+    been zero-filled once before its first use by this call."""
+    return kda_fab_fb_proj(*args, _entry="kda_fab_fb_proj_fused", **kwargs)
+
+
 def kda_fab_fb_proj(x: torch.Tensor, w_ab: torch.Tensor, w_b: torch.Tensor, rank: int = 128, *,
                     want_f_a: bool = False, f_a: torch.Tensor | None = None,
                     beta: torch.Tensor | None = None, g1: torch.Tensor | None = None,
-                    workspace: torch.Tensor | None = None, stream=None):
+                    workspace: torch.Tensor | None = None, stream=None,
+                    _entry: str = "kda_fab_fb_proj"):
     """F_A/beta -> F_B branch.  Returns (g1, beta) or (g1, beta, f_a) if want_f_a."""
     for t, n in ((x, "x"), (w_ab, "w_ab"), (w_b, "w_b")):
         _check_tensor(t, n, 2)
@@ -244,10 +253,10 @@ def kda_fab_fb_proj(x: torch.Tensor, w_ab: torch.Tensor, w_b: torch.Tensor, rank
     elif want_f_a:
         f_a = torch.empty((M, rank), dtype=torch.bfloat16, device=x.device)
     ws, ws_bytes = _workspace(workspace, sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K), x.device)
-    st = _lib.load().kda_fab_fb_proj(_ptr(x), _ptr(w_ab), _ptr(w_b), _ptr(f_a), _ptr(beta),
-                                     _ptr(g1), M, K, n_ab, rank, n_b, _ptr(ws), ws_bytes,
-                                     _stream(stream, x.device))
-    _lib.check(st, "kda_fab_fb_proj")
+    st = getattr(_lib.load(), _entry)(_ptr(x), _ptr(w_ab), _ptr(w_b), _ptr(f_a), _ptr(beta),
+                                      _ptr(g1), M, K, n_ab, rank, n_b, _ptr(ws), ws_bytes,
+                                      _stream(stream, x.device))
+    _lib.check(st, _entry)
     return (g1, beta, f_a) if f_a is not None else (g1, beta)
 
 

@@ -39,7 +39,7 @@ EXPORTED_SYMBOLS = (
     "sg_select", "sg_overlap_gate", "sg_overlap_max_tokens", "sg_workspace_bytes",
     "sg_kda_select", "sg_kda_workspace_bytes",
     "sg_strerror", "sg_version", "skinny_gemm", "kda_qkvg_proj", "kda_fab_fb_proj",
-    "kda_projection_overlap", "latent_moe_tail", "kda_projection_noalloc",
+    "kda_projection_overlap", "latent_moe_tail", "kda_projection_noalloc", "kda_fab_fb_proj_fused",
 )
 
 
@@ -76,6 +76,8 @@ _PROTOS = {
                                _vp, _sz, _vp]),
     "kda_projection_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                       _i32, _i32, _vp, _vp, _vp, _vp]),
+    "kda_fab_fb_proj_fused": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                     _vp, _sz, _vp]),
 }
 
 # Per-GPU scratch of kda_projection_noalloc (SG_NOALLOC_SCRATCH_BYTES).

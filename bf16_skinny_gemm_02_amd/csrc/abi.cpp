@@ -8,6 +8,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include "sg_fused.h"
 #include "sg_launch.h"
 #include "skinny_gemm.h"
 
@@ -59,6 +60,24 @@ bool same_config(const sg_config_t& a, const sg_config_t& b) {
 
 bool is_mfma(int kind) {
   return kind == SG_KIND_MFMA_TILE || kind == SG_KIND_MFMA_WAVESPLIT || kind == SG_KIND_MFMA_BLOCK;
+}
+
+// Whether the F_A/beta rows of configuration f can hand their partials to an
+// F_B role in the same launch: the kernels that host the role (the 4-wave
+// GEMV, M = 1, and the wave-split MFMA tile, M <= 16), with a flag for every
+// producer (each GEMV wave, each wave-split workgroup) and a cursor for every
+// F_B workgroup in the workspace header.
+bool hosts_fb(const sg_config_t& f, int rank, int n_b) {
+  int64_t producers;
+  if (f.kind == SG_KIND_GEMV_ROW || f.kind == SG_KIND_GEMV_SPLITK) {
+    if (f.waves != 4 || f.m_tile != 1) return false;
+    producers = static_cast<int64_t>(f.grid) * f.waves;
+  } else if (f.kind == SG_KIND_MFMA_WAVESPLIT) {
+    producers = f.grid;
+  } else {
+    return false;
+  }
+  return producers <= sg::kFbMaxProducers && sg::fused_fb_wgs(rank, n_b) <= sg::kFbMaxConsumers;
 }
 
 // The main kernel of configuration c, with the problem's epilogue as given
@@ -153,10 +172,14 @@ int validate_fab_fb(const sg_bf16* x, const sg_bf16* w_ab, const sg_bf16* w_b, s
   return check_workspace(ws, ws_bytes, sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K));
 }
 
+// The F_A/beta -> F_B branch.  Its workspace: the hand-off header
+// (kSyncBytes), then the F_A/beta partials.  one_launch: the F_B role runs in
+// the F_A/beta launch where a kernel hosts it (else F_B is a second launch).
 int enqueue_fab_fb(const sg_bf16* x, const sg_bf16* w_ab, const sg_bf16* w_b, sg_bf16* f_a,
                    sg_bf16* beta, sg_bf16* g1, int M, int K, int n_ab, int rank, int n_b, void* ws,
-                   hipStream_t s) {
+                   bool one_launch, hipStream_t s) {
   const sg_config_t c = fab_config(M, n_ab, K);
+  unsigned* sync = static_cast<unsigned*>(ws);
   DotProblem p{};
   p.a = x;
   p.lda = K;
@@ -165,7 +188,17 @@ int enqueue_fab_fb(const sg_bf16* x, const sg_bf16* w_ab, const sg_bf16* w_b, sg
   p.M = M;
   p.N = n_ab;
   p.K = K;
-  p.partial = static_cast<float*>(ws);
+  p.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + sg::kSyncBytes);
+  if (one_launch && hosts_fb(c, rank, n_b)) {
+    // One grid: the F_A/beta workgroups, then the F_B role.
+    p.arrive = sync;
+    const sg::FusedFb ff{p.partial, sync, c.k_split, M, n_ab, rank, n_b, w_b, f_a, beta, g1};
+    const DotProblem segs[1] = {p};
+    const sg_config_t cfgs[1] = {c};
+    const bool gemv = c.kind != SG_KIND_MFMA_WAVESPLIT;
+    return hip_status(gemv ? sg::launch_gemv_fused(segs, cfgs, 1, ff, 1, s)
+                           : sg::launch_mfma_fused(segs, cfgs, 1, ff, 1, s));
+  }
   if (launch_main(p, c, s) != hipSuccess) return SG_ERR_HIP;
   sg::FbProblem fb{};
   fb.partial = p.partial;
@@ -217,7 +250,18 @@ extern "C" int kda_fab_fb_proj(const sg_bf16* x, const sg_bf16* w_ab, const sg_b
   bool empty = false;
   int st = validate_fab_fb(x, w_ab, w_b, beta, g1, f_a, M, K, n_ab, rank, n_b, ws, ws_bytes, &empty);
   if (st != SG_OK || empty) return st;
-  return enqueue_fab_fb(x, w_ab, w_b, f_a, beta, g1, M, K, n_ab, rank, n_b, ws,
+  return enqueue_fab_fb(x, w_ab, w_b, f_a, beta, g1, M, K, n_ab, rank, n_b, ws, false,
+                        static_cast<hipStream_t>(stream));
+}
+
+extern "C" int kda_fab_fb_proj_fused(const sg_bf16* x, const sg_bf16* w_ab, const sg_bf16* w_b,
+                                     sg_bf16* f_a, sg_bf16* beta, sg_bf16* g1, int M, int K,
+                                     int n_ab, int rank, int n_b, void* ws, size_t ws_bytes,
+                                     sg_stream_t stream) {
+  bool empty = false;
+  int st = validate_fab_fb(x, w_ab, w_b, beta, g1, f_a, M, K, n_ab, rank, n_b, ws, ws_bytes, &empty);
+  if (st != SG_OK || empty) return st;
+  return enqueue_fab_fb(x, w_ab, w_b, f_a, beta, g1, M, K, n_ab, rank, n_b, ws, true,
                         static_cast<hipStream_t>(stream));
 }
 

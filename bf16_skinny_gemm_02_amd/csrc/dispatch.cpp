@@ -52,6 +52,10 @@ constexpr int kFabMaxSplit = 8;
 // main kernel leaves no room beside it for the aux branch's workgroups.  The
 // gate therefore stays closed; the concurrent path remains available.
 constexpr int kOverlapMaxTokens = 0;
+// Bytes at the start of a kda_fab_fb_proj(_fused) workspace: the hand-off
+// header of the one-launch F_A/beta -> F_B path (4096 producer flags and 512
+// consumer cursors, uint32), then the partials.
+constexpr size_t kFabHeaderBytes = 18432;
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -229,10 +233,11 @@ extern "C" size_t sg_workspace_bytes(int op, int M, int N, int K) {
       return c.k_split > 1 ? sg::round256(S * plane) : 0;
     case SG_OP_FAB_FB: {
       // The F_A/beta stage always leaves partials for the F_B stage to sum,
-      // with the configuration sg_kda_select gives it alone.
+      // with the configuration sg_kda_select gives it alone, behind the
+      // hand-off header of the one-launch path (kFabHeaderBytes).
       sg_config_t f;
       if (sg_kda_select(SG_KDA_FAB_ALONE, M, K, 0, N, &f) != SG_OK) return 0;
-      return sg::round256(static_cast<size_t>(f.k_split > 0 ? f.k_split : 1) * plane);
+      return kFabHeaderBytes + sg::round256(static_cast<size_t>(f.k_split > 0 ? f.k_split : 1) * plane);
     }
     case SG_OP_LATENT_TAIL: {
       // M = 1 with the whole row in one workgroup: the GEMV normalises the

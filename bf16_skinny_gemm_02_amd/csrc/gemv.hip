@@ -36,9 +36,14 @@
 // place with n = bf16(L * r * gamma), the bf16 normalised latent the
 // up-projection consumes.  One launch, no workspace.
 #include "sg_device.h"
+#include "sg_fused.h"
 #include "sg_launch.h"
 
 namespace sg {
+
+static_assert(kSyncBytes == static_cast<size_t>(kFbMaxProducers + kFbMaxConsumers) * sizeof(unsigned),
+              "hand-off header size");
+
 namespace {
 
 struct GemvArgs {
@@ -55,38 +60,58 @@ struct GemvArgs {
   uint16_t* out2;
   int64_t ldc2;
   int n_split;
+  unsigned* arrive;  // in-launch hand-off (FB instances, sg_fused.h): the flag header
+  int nslots;        // producer slots of the launch (every wave of the F_A/beta segment)
   int N, K;
   int sps;  // steps per split
   float eps;
 };
 
 // One launch covers one or two segments (independent problems sharing a
-// flat grid, segment 1's workgroups after segment 0's).  Within a segment,
-// workgroup `local` takes row group local % groups of K-range local / groups.
+// flat grid), and optionally the F_B role of a fused launch.  Within a
+// segment, workgroup `local` takes row group local % groups of K-range
+// local / groups.
 struct GemvSeg {
   GemvArgs g;
   int groups;
-  int wg_begin;  // first workgroup of the segment (INT_MAX: unused)
+  int wg_begin, wg_end;  // the segment's workgroups (empty range: unused)
 };
 struct GemvLaunch {
   GemvSeg seg[2];
+  FbFuse fb;
 };
 
-template <int M, int R, int NW, int D, bool FOLD>
+// FB (instances of the one-launch F_A/beta -> F_B branch only): workgroups
+// in L.fb's range run the F_B role, and a segment with `arrive` set hands
+// its partials over (sg_fused.h).  Other instances carry none of that code.
+template <int M, int R, int NW, int D, bool FOLD, bool FB>
 __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
+  extern __shared__ u32x4 xs[];  // [M][row_chunks] 16-byte chunks of the activation
   const int b = static_cast<int>(blockIdx.x);
-  const GemvSeg sgm = (b >= L.seg[1].wg_begin) ? L.seg[1] : L.seg[0];  // into registers once
+  if constexpr (FB) {
+    static_assert(NW * kWave == kFbThreads && !FOLD, "F_B role instances");
+    if (b >= L.fb.wg_begin && b < L.fb.wg_end) {
+      fb_role(L.fb, b, xs);
+      return;
+    }
+  }
+  const GemvSeg sgm = (b >= L.seg[1].wg_begin && b < L.seg[1].wg_end) ? L.seg[1] : L.seg[0];
   const GemvArgs g = sgm.g;
   const int local = b - sgm.wg_begin;
   const int split = local / sgm.groups;
   const int group = local - split * sgm.groups;
-  extern __shared__ u32x4 xs[];  // [M][row_chunks] 16-byte chunks of the activation
   constexpr int kThreads = NW * kWave;
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & (kWave - 1);
   const int wave = wave_id();
   const int n0 = (group * NW + wave) * R;
   const bool active = n0 < g.N;
+
+  // Hand-off: this wave's producer flag, read before anything else is in
+  // flight (so the counted waits below are unchanged).
+  const int slot = local * NW + wave;
+  unsigned prev = 0u;
+  if constexpr (FB) prev = g.arrive != nullptr ? load_flag(g.arrive + slot) : 0u;
 
   const int K8 = g.K >> 3;
   const int nsteps = (K8 + kWave - 1) / kWave;
@@ -185,7 +210,12 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
     wait_lgkmcnt0();  // the normalised latent is in LDS
     __builtin_amdgcn_s_barrier();
   }
-  if (!active) return;  // no barrier follows
+  if (!active) {  // no barrier follows; in a hand-off every wave is a producer
+    if constexpr (FB) {
+      if (g.arrive != nullptr) produce(g.arrive, slot, g.nslots, prev);
+    }
+    return;
+  }
 
   // 3. Products: every weight step is already in flight; each is used as
   //    soon as it lands.
@@ -222,7 +252,13 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
     const int n = n0 + r;
     if (n < g.N) {
       if (g.partial != nullptr) {
-        g.partial[(static_cast<int64_t>(split) * M + m) * g.N + n] = v;
+        float* dst = g.partial + (static_cast<int64_t>(split) * M + m) * g.N + n;
+        if constexpr (FB) {
+          if (g.arrive != nullptr) store_coherent(dst, v);
+          else *dst = v;
+        } else {
+          *dst = v;
+        }
       } else {
         if (g.res != nullptr) v += bf16_to_f32(g.res[m * g.ldr + n]);
         if (g.n_split > 0 && n >= g.n_split)
@@ -232,6 +268,9 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
       }
     }
   }
+  if constexpr (FB) {
+    if (g.arrive != nullptr) produce(g.arrive, slot, g.nslots, prev);
+  }
 }
 
 // Weight steps a wave holds (the largest K-range, in 512-wide steps, the
@@ -239,10 +278,10 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
 // most 112 VGPRs of weights, and a whole 7168-wide row for R <= 2.
 constexpr int gemv_depth(int R) { return R == 1 ? 16 : (R == 2 ? 14 : 7); }
 
-template <int M, int R, int NW, bool FOLD>
+template <int M, int R, int NW, bool FOLD, bool FB>
 hipError_t launch_inst(const GemvLaunch& g, dim3 grid, size_t lds, hipStream_t s) {
   constexpr int D = gemv_depth(R);
-  auto kern = gemv_kernel<M, R, NW, D, FOLD>;
+  auto kern = gemv_kernel<M, R, NW, D, FOLD, FB>;
   static std::atomic<bool> lds_set[kLdsAttrDevices];
   const hipError_t attr = ensure_lds_limit(reinterpret_cast<const void*>(kern), kGemvMaxLds, lds_set);
   if (attr != hipSuccess) return attr;
@@ -254,8 +293,16 @@ hipError_t launch_inst(const GemvLaunch& g, dim3 grid, size_t lds, hipStream_t s
 template <bool FOLD>
 hipError_t launch_fold(const GemvLaunch& g, int M, int R, int NW, dim3 grid, size_t lds,
                        hipStream_t s) {
-  if (M == 1 && R == 1 && NW == 4) return launch_inst<1, 1, 4, FOLD>(g, grid, lds, s);
-  if (M == 1 && R == 4 && NW == 4) return launch_inst<1, 4, 4, FOLD>(g, grid, lds, s);
+  if (M == 1 && R == 1 && NW == 4) return launch_inst<1, 1, 4, FOLD, false>(g, grid, lds, s);
+  if (M == 1 && R == 4 && NW == 4) return launch_inst<1, 4, 4, FOLD, false>(g, grid, lds, s);
+  return hipErrorInvalidValue;
+}
+
+// The one-launch F_A/beta -> F_B instances (M = 1, 4 waves, no fold).
+hipError_t launch_fb(const GemvLaunch& g, int M, int R, int NW, dim3 grid, size_t lds,
+                     hipStream_t s) {
+  if (M == 1 && R == 1 && NW == 4) return launch_inst<1, 1, 4, false, true>(g, grid, lds, s);
+  if (M == 1 && R == 4 && NW == 4) return launch_inst<1, 4, 4, false, true>(g, grid, lds, s);
   return hipErrorInvalidValue;
 }
 
@@ -284,20 +331,34 @@ bool gemv_same_instance(const sg_config_t& a, const sg_config_t& b) {
          a.waves == b.waves && a.m_tile == b.m_tile;
 }
 
-hipError_t launch_gemv(const DotProblem* segs, const sg_config_t* cfgs, int nseg, hipStream_t s) {
+namespace {
+
+// Segments in grid order, and the F_B role (fb != NULL) after the first
+// fb_after of them.
+hipError_t launch_gemv_impl(const DotProblem* segs, const sg_config_t* cfgs, int nseg,
+                            const FusedFb* fb, int fb_after, hipStream_t s) {
   if (nseg < 1 || nseg > 2) return hipErrorInvalidValue;
   if (nseg == 2 && (!gemv_same_instance(cfgs[0], cfgs[1]) || segs[0].M != segs[1].M ||
                     (segs[0].gamma == nullptr) != (segs[1].gamma == nullptr)))
     return hipErrorInvalidValue;
+  if (fb != nullptr && (fb_after < 0 || fb_after > nseg || cfgs[0].waves * kWave != kFbThreads ||
+                        segs[0].gamma != nullptr))
+    return hipErrorInvalidValue;
   GemvLaunch L;
-  int wgs = 0;
+  L.fb = no_fb_fuse();
+  const int nfb = fb != nullptr ? fused_fb_wgs(fb->rank, fb->n_b) : 0;
+  int wgs = 0, arrivals = 0, arriving = 0;
   size_t lds = 0;
   for (int i = 0; i < 2; ++i) {
     GemvSeg& sgm = L.seg[i];
     if (i >= nseg) {
       sgm = L.seg[0];
-      sgm.wg_begin = INT32_MAX;
+      sgm.wg_begin = sgm.wg_end = 0;
       continue;
+    }
+    if (fb != nullptr && i == fb_after) {
+      L.fb = make_fb_fuse(*fb, wgs, wgs + nfb, 0);
+      wgs += nfb;
     }
     const DotProblem& p = segs[i];
     const sg_config_t& cfg = cfgs[i];
@@ -315,6 +376,8 @@ hipError_t launch_gemv(const DotProblem* segs, const sg_config_t* cfgs, int nseg
     g.out2 = p.out2;
     g.ldc2 = p.ldc2;
     g.n_split = p.n_split;
+    g.arrive = fb != nullptr ? p.arrive : nullptr;
+    g.nslots = 0;
     g.N = p.N;
     g.K = p.K;
     g.eps = p.eps;
@@ -331,11 +394,42 @@ hipError_t launch_gemv(const DotProblem* segs, const sg_config_t* cfgs, int nseg
     if (sgm.groups <= 0) return hipErrorInvalidValue;
     sgm.wg_begin = wgs;
     wgs += sgm.groups * S;
+    sgm.wg_end = wgs;
+    if (g.arrive != nullptr) {
+      if (p.partial == nullptr || p.partial != fb->partial || S != fb->S || p.arrive != fb->sync)
+        return hipErrorInvalidValue;
+      arrivals += sgm.groups * S * cfg.waves;  // every wave of the segment is a producer
+      ++arriving;
+    }
+  }
+  if (fb != nullptr) {
+    if (fb_after == nseg) {
+      L.fb = make_fb_fuse(*fb, wgs, wgs + nfb, 0);
+      wgs += nfb;
+    }
+    if (arriving != 1 || arrivals > kFbMaxProducers || nfb > kFbMaxConsumers) return hipErrorInvalidValue;
+    L.fb.arrivals = arrivals;
+    for (int i = 0; i < nseg; ++i) L.seg[i].g.nslots = arrivals;
+    const size_t fa_bytes = fb_lds_bytes(fb->M, fb->rank);
+    if (fa_bytes > lds) lds = fa_bytes;
+    if (lds > kGemvMaxLds) return hipErrorInvalidValue;
   }
   if (wgs <= 0) return hipSuccess;
   const dim3 grid(wgs);
+  if (fb != nullptr) return launch_fb(L, segs[0].M, cfgs[0].rows, cfgs[0].waves, grid, lds, s);
   if (segs[0].gamma != nullptr) return launch_fold<true>(L, segs[0].M, cfgs[0].rows, cfgs[0].waves, grid, lds, s);
   return launch_fold<false>(L, segs[0].M, cfgs[0].rows, cfgs[0].waves, grid, lds, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const DotProblem* segs, const sg_config_t* cfgs, int nseg, hipStream_t s) {
+  return launch_gemv_impl(segs, cfgs, nseg, nullptr, 0, s);
+}
+
+hipError_t launch_gemv_fused(const DotProblem* segs, const sg_config_t* cfgs, int nseg,
+                             const FusedFb& fb, int fb_after, hipStream_t s) {
+  return launch_gemv_impl(segs, cfgs, nseg, &fb, fb_after, s);
 }
 
 hipError_t launch_gemv(const DotProblem& p, const sg_config_t& cfg, hipStream_t s) {

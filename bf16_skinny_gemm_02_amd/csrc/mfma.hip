@@ -42,6 +42,7 @@
 // formed in an order that depends only on K and the configuration, never on
 // timing or on which tile holds the row.
 #include "sg_device.h"
+#include "sg_fused.h"
 #include "sg_launch.h"
 
 namespace sg {
@@ -64,30 +65,38 @@ struct MfmaArgs {
   int sps;  // k-steps (32 k) per split
   const uint16_t* gamma;  // RMSNorm fold (wave-split kernel): gamma[K], else unused
   float eps;
+  unsigned* arrive;  // in-launch hand-off (FB wave-split instances, sg_fused.h): the flag header
+  int nslots;        // producer slots of the launch (one per workgroup of the F_A/beta segment)
 };
 
-// One launch covers one or two segments: independent problems whose
-// workgroups share a flat grid, segment 1's after segment 0's.  Within a
-// segment, workgroup `local` takes tile local % tiles of K-range
-// local / tiles.
+// One launch covers one or two segments (independent problems whose
+// workgroups share a flat grid) and, for the wave-split tile, optionally the
+// F_B role of a fused launch.  Within a segment, workgroup `local` takes tile
+// local % tiles of K-range local / tiles.
 struct MfmaSeg {
   MfmaArgs g;
   int tiles;
-  int wg_begin;  // first workgroup of the segment (INT_MAX: unused)
+  int wg_begin, wg_end;  // the segment's workgroups (empty range: unused)
 };
 struct MfmaLaunch {
   MfmaSeg seg[2];
+  FbFuse fb;
 };
 
 // The segment's arguments are copied into registers once (uniform values in
 // SGPRs), so nothing re-reads the kernel arguments inside the loops.
-__device__ __forceinline__ MfmaArgs pick_segment(const MfmaLaunch& L, int& tile, int& split) {
+__device__ __forceinline__ MfmaArgs pick_segment(const MfmaLaunch& L, int& tile, int& split,
+                                                 int& local) {
   const int b = static_cast<int>(blockIdx.x);
-  const MfmaSeg sg = (b >= L.seg[1].wg_begin) ? L.seg[1] : L.seg[0];
-  const int local = b - sg.wg_begin;
+  const MfmaSeg sg = (b >= L.seg[1].wg_begin && b < L.seg[1].wg_end) ? L.seg[1] : L.seg[0];
+  local = b - sg.wg_begin;
   split = local / sg.tiles;
   tile = local - split * sg.tiles;
   return sg.g;
+}
+__device__ __forceinline__ MfmaArgs pick_segment(const MfmaLaunch& L, int& tile, int& split) {
+  int local;
+  return pick_segment(L, tile, split, local);
 }
 
 constexpr int kKStep = 32;       // k per MFMA
@@ -130,12 +139,21 @@ __device__ __forceinline__ Res4 load_res4(const MfmaArgs& g, int m, int n0) {
 // Four consecutive outputs go out as one 16-byte (partials) or 8-byte (bf16)
 // store when they lie in one row of one output and the address is aligned;
 // otherwise element by element.
+// COHERENT (the F_A/beta segment of a one-launch F_A/beta -> F_B call): the
+// partials go out as device-coherent stores for the F_B role to read.
+template <bool COHERENT = false>
 __device__ __forceinline__ void store4(const MfmaArgs& g, const f32x4& acc, int m, int n0, int split,
                                        const Res4& res) {
   if (m >= g.M) return;
   const bool whole = n0 + 3 < g.N;
   if (g.partial != nullptr) {
     float* p = g.partial + (static_cast<int64_t>(split) * g.M + m) * g.N + n0;
+    if constexpr (COHERENT) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (n0 + v < g.N) store_coherent(p + v, acc[v]);
+      return;
+    }
     if (whole && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
       *reinterpret_cast<f32x4*>(p) = acc;
       return;
@@ -299,11 +317,27 @@ constexpr int kFoldMaxK = kFoldChunks * kWave * 8;
 // activation fragment is then normalised in registers, n = bf16((L * r) *
 // gamma), before its MFMA: the rounding of the bf16 normalised latent that a
 // separate RMSNorm kernel would store.
-template <int XQ, int C, bool NORM, bool RES>
+//
+// FB (instances of the one-launch F_A/beta -> F_B branch only): workgroups in
+// L.fb's range run the F_B role, and the segment with `arrive` set hands its
+// partials over (sg_fused.h).  Other instances carry none of that code.
+template <int XQ, int C, bool NORM, bool RES, bool FB>
 __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch L) {
   extern __shared__ u32x4 lds[];
-  int tile, split;
-  const MfmaArgs g = pick_segment(L, tile, split);
+  if constexpr (FB) {
+    static_assert(kSplitWaves * kWave == kFbThreads && !NORM && !RES, "F_B role instances");
+    const int b = static_cast<int>(blockIdx.x);
+    if (b >= L.fb.wg_begin && b < L.fb.wg_end) {
+      fb_role(L.fb, b, lds);
+      return;
+    }
+  }
+  int tile, split, slot;
+  const MfmaArgs g = pick_segment(L, tile, split, slot);
+  // Hand-off: this workgroup's producer flag (slot = its index in the
+  // segment), read before anything else is in flight.
+  unsigned prev = 0u;
+  if constexpr (FB) prev = g.arrive != nullptr ? load_flag(g.arrive + slot) : 0u;
   constexpr int XROWS = 4 * XQ;
   constexpr int SLOT = (16 + XROWS) * kPieces;
   constexpr int P = 4 + XQ;
@@ -454,6 +488,13 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
   for (int w = 0; w < kSplitWaves - 1; ++w)
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[v] += red[(w * 4 + v) * kWave + lane];
+  if constexpr (FB) {
+    if (g.arrive != nullptr) {  // wave 0 alone stores: one producer slot per workgroup
+      store4<true>(g, acc, rl, row0 + 4 * kg, split, res);
+      produce(g.arrive, slot, g.nslots, prev);
+      return;
+    }
+  }
   store4(g, acc, rl, row0 + 4 * kg, split, res);
 }
 
@@ -600,9 +641,9 @@ hipError_t launch_tile_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
   return launch_kernel(kern, dim3(wgs), dim3(NW * kWave), tile_lds_bytes(NW, C, XQ), s, L);
 }
 
-template <int XQ, int C, bool NORM, bool RES>
+template <int XQ, int C, bool NORM, bool RES, bool FB = false>
 hipError_t launch_wsplit_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
-  auto kern = wsplit_kernel<XQ, C, NORM, RES>;
+  auto kern = wsplit_kernel<XQ, C, NORM, RES, FB>;
   static std::atomic<bool> lds_set[kLdsAttrDevices];
   const hipError_t attr = ensure_lds_limit(reinterpret_cast<const void*>(kern), kMfmaMaxLds, lds_set);
   if (attr != hipSuccess) return attr;
@@ -624,6 +665,25 @@ hipError_t launch_wsplit_xq(const MfmaLaunch& L, int XQ, int C, int wgs, hipStre
     case 2: return launch_wsplit_inst<2, 3, NORM, RES>(L, wgs, s);
     case 3: return launch_wsplit_inst<3, 3, NORM, RES>(L, wgs, s);
     case 4: return launch_wsplit_inst<4, 3, NORM, RES>(L, wgs, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The one-launch F_A/beta -> F_B instances (no fold, no residual).
+hipError_t launch_wsplit_fb(const MfmaLaunch& L, int XQ, int C, int wgs, hipStream_t s) {
+  if (C == 2) {
+    switch (XQ) {
+      case 3: return launch_wsplit_inst<3, 2, false, false, true>(L, wgs, s);
+      case 4: return launch_wsplit_inst<4, 2, false, false, true>(L, wgs, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (C != 3) return hipErrorInvalidValue;
+  switch (XQ) {
+    case 1: return launch_wsplit_inst<1, 3, false, false, true>(L, wgs, s);
+    case 2: return launch_wsplit_inst<2, 3, false, false, true>(L, wgs, s);
+    case 3: return launch_wsplit_inst<3, 3, false, false, true>(L, wgs, s);
+    case 4: return launch_wsplit_inst<4, 3, false, false, true>(L, wgs, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -677,19 +737,32 @@ bool mfma_same_instance(const sg_config_t& a, const sg_config_t& b) {
          a.k_unroll == b.k_unroll;
 }
 
-hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg, hipStream_t s) {
+namespace {
+
+// Segments in grid order, and the F_B role (fb != NULL, wave-split tile
+// only) after the first fb_after of them.
+hipError_t launch_mfma_impl(const DotProblem* segs, const sg_config_t* cfgs, int nseg,
+                            const FusedFb* fb, int fb_after, hipStream_t s) {
   if (nseg < 1 || nseg > 2) return hipErrorInvalidValue;
   const sg_config_t& cfg = cfgs[0];
   if (nseg == 2 && !mfma_same_instance(cfgs[0], cfgs[1])) return hipErrorInvalidValue;
+  if (fb != nullptr && (fb_after < 0 || fb_after > nseg || cfg.kind != SG_KIND_MFMA_WAVESPLIT))
+    return hipErrorInvalidValue;
   MfmaLaunch L;
-  int wgs = 0;
+  L.fb = no_fb_fuse();
+  const int nfb = fb != nullptr ? fused_fb_wgs(fb->rank, fb->n_b) : 0;
+  int wgs = 0, arrivals = 0, arriving = 0;
   int max_sps = 0;
   for (int i = 0; i < 2; ++i) {
     MfmaSeg& sgm = L.seg[i];
     if (i >= nseg) {
       sgm = L.seg[0];
-      sgm.wg_begin = INT32_MAX;
+      sgm.wg_begin = sgm.wg_end = 0;
       continue;
+    }
+    if (fb != nullptr && i == fb_after) {
+      L.fb = make_fb_fuse(*fb, wgs, wgs + nfb, 0);
+      wgs += nfb;
     }
     const DotProblem& p = segs[i];
     const sg_config_t& c = cfgs[i];
@@ -712,6 +785,8 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
     g.K = p.K;
     g.gamma = p.gamma;
     g.eps = p.eps;
+    g.arrive = fb != nullptr ? p.arrive : nullptr;
+    g.nslots = 0;
     const int KS = ksteps_of(p.K);
     const int S = c.k_split > 0 ? c.k_split : 1;
     g.sps = (KS + S - 1) / S;
@@ -721,6 +796,27 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
     sgm.wg_begin = wgs;
     if (sgm.tiles <= 0) return hipErrorInvalidValue;
     wgs += sgm.tiles * S;
+    sgm.wg_end = wgs;
+    if (g.arrive != nullptr) {
+      if (p.partial == nullptr || p.partial != fb->partial || S != fb->S || p.gamma != nullptr ||
+          p.res != nullptr || p.arrive != fb->sync)
+        return hipErrorInvalidValue;
+      arrivals += sgm.tiles * S;  // one producer slot per workgroup
+      ++arriving;
+    }
+  }
+  if (fb != nullptr) {
+    if (fb_after == nseg) {
+      L.fb = make_fb_fuse(*fb, wgs, wgs + nfb, 0);
+      wgs += nfb;
+    }
+    if (arriving != 1 || arrivals > kFbMaxProducers || nfb > kFbMaxConsumers) return hipErrorInvalidValue;
+    L.fb.arrivals = arrivals;
+    for (int i = 0; i < nseg; ++i) L.seg[i].g.nslots = arrivals;
+    if (fb_lds_bytes(fb->M, fb->rank) > wsplit_lds_bytes(cfg.k_unroll, cfg.m_tile / 4, false))
+      return hipErrorInvalidValue;
+    for (int i = 0; i < nseg; ++i)
+      if (segs[i].gamma != nullptr || segs[i].res != nullptr) return hipErrorInvalidValue;
   }
   if (wgs <= 0) return hipSuccess;
   if (cfg.kind != SG_KIND_MFMA_WAVESPLIT && (segs[0].gamma != nullptr || (nseg == 2 && segs[1].gamma != nullptr)))
@@ -769,6 +865,7 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
     const int C = cfg.k_unroll, XQ = cfg.m_tile / 4;
     if (cfg.rows != 16 || cfg.waves != kSplitWaves || (cfg.m_tile % 4) != 0 || (C != 2 && C != 3))
       return hipErrorInvalidValue;
+    if (fb != nullptr) return launch_wsplit_fb(L, XQ, C, wgs, s);
     if (segs[0].gamma != nullptr) {
       // The RMSNorm fold: one segment whose whole rows fit the prologue.
       if (nseg != 1 || !wsplit_fold_fits(segs[0].K, cfg.k_split)) return hipErrorInvalidValue;
@@ -785,6 +882,17 @@ hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg
     return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg, hipStream_t s) {
+  return launch_mfma_impl(segs, cfgs, nseg, nullptr, 0, s);
+}
+
+hipError_t launch_mfma_fused(const DotProblem* segs, const sg_config_t* cfgs, int nseg,
+                             const FusedFb& fb, int fb_after, hipStream_t s) {
+  return launch_mfma_impl(segs, cfgs, nseg, &fb, fb_after, s);
 }
 
 hipError_t launch_mfma(const DotProblem& p, const sg_config_t& cfg, hipStream_t s) {

@@ -70,6 +70,24 @@ struct DotProblem {
   uint16_t* out2;
   int64_t ldc2;
   int n_split;
+  // In-launch hand-off (with `partial`, in a fused launch): the workspace's
+  // flag header.  The partials are stored device-coherently and each wave
+  // (GEMV) or workgroup (wave-split) then advances its flag, for an F_B role
+  // later in the same grid (sg_fused.h).
+  unsigned* arrive;
+};
+
+// The F_B role of a fused launch (see sg_fused.h): workgroups that wait for
+// the arrivals of the segment whose `arrive` is set, then sum its partials
+// (S of them, [S][M][n_ab]) into bf16 P and compute g1 = bf16(f_a W_b^T).
+struct FusedFb {
+  const float* partial;     // the arriving segment's partials
+  unsigned* sync;           // the workspace's flag header, zero before the first call
+  int S, M, n_ab, rank, n_b;
+  const uint16_t* w_b;      // [n_b, rank]
+  uint16_t* f_a;            // [M, rank], nullable
+  uint16_t* beta;           // [M, n_ab - rank]
+  uint16_t* g1;             // [M, n_b]
 };
 
 // Workspace regions start on 256-byte boundaries.
@@ -91,6 +109,20 @@ bool gemv_same_instance(const sg_config_t& a, const sg_config_t& b);
 bool mfma_same_instance(const sg_config_t& a, const sg_config_t& b);
 hipError_t launch_gemv(const DotProblem* segs, const sg_config_t* cfgs, int nseg, hipStream_t s);
 hipError_t launch_mfma(const DotProblem* segs, const sg_config_t* cfgs, int nseg, hipStream_t s);
+
+// Fused launches: the segments in grid order, plus the F_B role's
+// workgroups placed after the first `fb_after` segments (0 <= fb_after <=
+// nseg).  Exactly one segment has `arrive` and `partial` set (the F_A/beta
+// rows); GEMV instances with 4 waves (M == 1) and the wave-split MFMA tile
+// host the role.
+hipError_t launch_gemv_fused(const DotProblem* segs, const sg_config_t* cfgs, int nseg,
+                             const FusedFb& fb, int fb_after, hipStream_t s);
+hipError_t launch_mfma_fused(const DotProblem* segs, const sg_config_t* cfgs, int nseg,
+                             const FusedFb& fb, int fb_after, hipStream_t s);
+// Bytes at the start of a kda_fab_fb_proj(_fused) workspace that hold the
+// hand-off header (4096 producer flags and 512 consumer cursors, uint32);
+// the fp32 partials follow.
+constexpr size_t kSyncBytes = 18432;
 
 // LDS of the MFMA ring kernels: the shared-activation tile (nw waves, c ring
 // slots, 4*xq activation rows) and the wave-split tile (4 private rings).

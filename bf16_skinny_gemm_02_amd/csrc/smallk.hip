@@ -105,7 +105,6 @@ __device__ __forceinline__ float sum_splits(const float* p, int64_t plane, int S
   return acc;
 }
 
-
 struct ReduceArgs {
   const float* partial;
   int S, M, N;

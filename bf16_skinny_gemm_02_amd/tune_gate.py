@@ -74,9 +74,9 @@ def measure(ms, reps, device):
         qkvg = torch.empty(M, N_QKVG, dtype=torch.bfloat16, device=device)
         g1 = torch.empty(M, N_B, dtype=torch.bfloat16, device=device)
         beta = torch.empty(M, N_AB - RANK, dtype=torch.bfloat16, device=device)
-        ws_main = torch.empty(max(sg_kda_workspace_bytes(0, M, HIDDEN, N_QKVG, N_AB), 256),
+        ws_main = torch.zeros(max(sg_kda_workspace_bytes(0, M, HIDDEN, N_QKVG, N_AB), 256),
                               dtype=torch.uint8, device=device)
-        ws_aux = torch.empty(max(sg_kda_workspace_bytes(1, M, HIDDEN, N_QKVG, N_AB), 256),
+        ws_aux = torch.zeros(max(sg_kda_workspace_bytes(1, M, HIDDEN, N_QKVG, N_AB), 256),
                              dtype=torch.uint8, device=device)
 
         def call(r, concurrent):

@@ -28,8 +28,9 @@
  *    ld % 8 == 0 is not required for them.
  *  - Workspace: some paths keep fp32 split-K partial sums in a caller-owned
  *    device workspace; query its size with sg_workspace_bytes().  Its contents
- *    need no initialisation and are dead after the call.  Two calls that may
- *    run concurrently must not share one workspace.
+ *    need no initialisation and are dead after the call, except for the
+ *    hand-off header of kda_fab_fb_proj(_fused) workspaces (see there).  Two
+ *    calls that may run concurrently must not share one workspace.
  *  - Streams/events: sg_stream_t is a hipStream_t (NULL = the legacy default
  *    stream); sg_event_t is a hipEvent_t.  Both are owned by the caller.
  *  - Asynchrony: calls validate every argument on the host, then enqueue
@@ -231,11 +232,39 @@ int kda_qkvg_proj(const sg_bf16 *x, const sg_bf16 *w_qkvg, sg_bf16 *qkvg,
  * x [M,K], w_ab [n_ab,K], w_b [n_b,rank], f_a [M,rank] (nullable: not
  * stored), beta [M,n_ab-rank], g1 [M,n_b]; all contiguous.  Requires
  * 0 < rank < n_ab, rank % 8 == 0, rank <= 512.  Needs workspace
- * sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K). */
+ * sg_workspace_bytes(SG_OP_FAB_FB, M, n_ab, K): SG_FAB_HEADER_BYTES of
+ * hand-off header (used by kda_fab_fb_proj_fused only; this call neither
+ * reads nor writes it), then the F_A/beta partials.  Two launches: F_A/beta
+ * (split-K partials), then the F_B stage. */
+#define SG_FAB_HEADER_BYTES 18432
 int kda_fab_fb_proj(const sg_bf16 *x, const sg_bf16 *w_ab, const sg_bf16 *w_b,
                     sg_bf16 *f_a, sg_bf16 *beta, sg_bf16 *g1,
                     int M, int K, int n_ab, int rank, int n_b,
                     void *ws, size_t ws_bytes, sg_stream_t stream);
+
+/* The F_A/beta -> F_B branch of kda_fab_fb_proj as ONE launch [P3
+ * low_latency_gemm.py run_fab_fb, which chains its two GEMMs with
+ * programmatic dependent launch]: same arguments, same workspace size and
+ * bit-for-bit the same results.  Where the F_A/beta configuration runs on a
+ * kernel that hosts the in-launch hand-off (the 4-wave GEMV at M == 1, the
+ * wave-split MFMA tile at M <= 16 for these shapes) and the header has room
+ * (at most 4096 producers and 512 F_B workgroups), the F_A/beta workgroups
+ * store their partials device-coherently and each advances a flag in the
+ * workspace header; F_B workgroups later in the same grid wait for every
+ * flag (a bounded wait: on a time-out they write NaN to g1, beta and f_a),
+ * sum the partials in fixed order and compute g1.  Elsewhere it is
+ * kda_fab_fb_proj.  The header (the first SG_FAB_HEADER_BYTES of ws) must
+ * be zero before the first call on a workspace; each call then keeps it
+ * consistent by itself (it is not zero afterwards and must not be
+ * altered), so zero-filling a workspace once when it is allocated
+ * suffices, whatever the shapes of later calls.
+ * On MI355X under graph replay the single launch is slower than
+ * kda_fab_fb_proj's two (the in-launch hand-off costs more than a launch
+ * boundary); it is for callers that count launches. */
+int kda_fab_fb_proj_fused(const sg_bf16 *x, const sg_bf16 *w_ab, const sg_bf16 *w_b,
+                          sg_bf16 *f_a, sg_bf16 *beta, sg_bf16 *g1,
+                          int M, int K, int n_ab, int rank, int n_b,
+                          void *ws, size_t ws_bytes, sg_stream_t stream);
 
 /* Concurrent KDA projection [P3 low_latency_gemm.py
  * run_kda_projection_overlap; kda.py forward fallback]:

@@ -213,7 +213,8 @@ def test_workspace_bytes(lib):
         assert st == selection.OK
         assert 1 <= cfg["k_split"] <= 8
         need = lib.sg_workspace_bytes(_lib.SG_OP_FAB_FB, M, 136, 7168)
-        assert need == (cfg["k_split"] * M * 136 * 4 + 255) // 256 * 256
+        # the hand-off header of the one-launch entry point, then the partials
+        assert need == 18432 + (cfg["k_split"] * M * 136 * 4 + 255) // 256 * 256
     assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, -1, 4, 8) == 0
     assert lib.sg_workspace_bytes(99, 4, 4, 8) == 0
 
@@ -372,3 +373,20 @@ def test_noalloc_rejects_beyond_its_array_before_any_gpu_call(lib):
                                       None) == _lib.SG_OK
     assert lib.kda_projection_noalloc(*args, -1, K, 4096, nab, 128, 1024, None, None, None,
                                       None) == _lib.SG_ERR_INVALID_ARG
+
+
+def test_fab_fb_fused_validates_like_fab_fb(lib):
+    """kda_fab_fb_proj_fused takes kda_fab_fb_proj's arguments and checks
+    them the same way, before anything is enqueued."""
+    def fused(**kw):
+        args = dict(x=A16, w_ab=B16, w_b=C16, f_a=NUL, beta=ctypes.c_void_p(0x60000),
+                    g1=ctypes.c_void_p(0x70000), M=2, K=7168, n_ab=136, rank=128, n_b=1024,
+                    ws=NUL, ws_bytes=0)
+        args.update(kw)
+        return lib.kda_fab_fb_proj_fused(*args.values(), None)
+
+    E = _lib
+    for kw in ({"rank": 0}, {"n_ab": 128}, {"rank": 124}, {"M": 300}, {"x": NUL}, {"g1": NUL},
+               {"w_b": ODD}, {}, {"M": 0}, {"ws": ctypes.c_void_p(0x90000), "ws_bytes": 100}):
+        assert fused(**kw) == _fab(lib, **kw), kw
+    assert fused() == E.SG_ERR_WORKSPACE
