@@ -17,16 +17,23 @@ Reported ``value``: mean microseconds per KDA projection call over the M sweep
 (the metric's unit).  Within each timed step the projection graphs of the
 whole sweep run back to back between two events, then the tail graphs between
 the next two: ``value`` is the projection half's time over its calls,
-``tail_us_per_call`` the tail half's.  The per-M ``breakdown`` (projection and
-tail µs, GB/s, fraction of HBM peak) is measured after the timed region, each
-graph replayed back to back.  ``--comparators`` adds, per M, the forced
-two-stream schedule (fork/join events, F_A/beta -> F_B on an aux stream), the
-forced single-stream schedule, a plain packed GEMM followed by a second GEMM
-for F_B, and the vendor library on the same work (torch.mm / addmm, i.e.
-hipBLASLt, with the RMSNorm in unfused torch ops).  The line also carries the
-roofline of the dominant kernel (the wave-split MFMA tile at M = 8, with the
-M = 1 GEMV beside it, each timed with HIP events on its own stream) and the
-CPU oracle timed on this host.
+``tail_us_per_call`` the tail half's.
+
+``roofline`` is the headline path's own unit of work: one projection call at
+M = 8 (its two launches), that M's graph replayed back to back right after the
+timed region between HIP events on its stream; ``traffic`` is that call's HBM
+bytes from rocprofv3 counters; ``sweep_gbs`` the timed region's own rate.
+
+After the timed region: the per-M ``breakdown`` (projection and tail µs, GB/s,
+fractions of the HBM and MFMA peaks), and ``configs``, one entry per workload
+of the benchmark's definition: the single GEMV (M = 1), the F_A/beta -> F_B
+branch alone (two launches, and the one-launch entry point, under graph
+replay and launched eagerly), the Q/K/V/G projection alone over the sweep,
+the two projection schedules against a packed GEMM followed by F_B, and the
+latent-MoE tail up to M = 256.  ``--comparators`` adds the vendor library on
+the same work (torch.mm / addmm, i.e. hipBLASLt, with the RMSNorm in unfused
+torch ops).  ``cpu_baseline``: the CPU oracle on this host, on all its threads
+and on one.
 """
 from __future__ import annotations
 
@@ -178,95 +185,212 @@ def time_graph(g, stream, reps, warm=3):
     return start.elapsed_time(stop) / reps
 
 
-# ---- dominant-kernel roofline leg ---------------------------------------------------
+# ---- roofline leg and counters -------------------------------------------------------
 
 BREAKDOWN_REPS = 20
 BREAKDOWN_REPEATS = 5   # per-M breakdown: median, and the lowest / highest repeat (p10 / p90 of 5)
 
-ROOFLINE_M = 8   # the wave-split MFMA tile serves M = 2..16, five of the nine sweep points
+ROOFLINE_M = 8   # the projection call the roofline leg times (two launches at 2 <= M <= 64)
 
-# HBM traffic of the roofline kernel from two rocprofv3 --pmc runs of `bench.py --counters`
-# (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 KiB per dispatch; factors from a 256 MiB device copy),
-# summarised with the commands in profiles/qkvg_wsplit_m8_pmc_traffic.md.  Valid only for the
-# kernel sources it was measured on: any change to them reports traffic as null until the
-# counters are taken again.
-TRAFFIC_SOURCES = ("bf16_skinny_gemm_02_amd/csrc/mfma.hip", "bf16_skinny_gemm_02_amd/csrc/sg_device.h",
-                   "bf16_skinny_gemm_02_amd/csrc/dispatch.cpp")
-TRAFFIC_PMC = {"sources_sha256": "ff8c56fa576d1e4e66bc76e381eda24c5571d6f976ddabb910e38533ef6e01b4",
-               "bytes_per_launch": 59784527}
+# HBM traffic of one projection call at M = ROOFLINE_M (both of its launches) from two rocprofv3
+# --pmc runs of `bench.py --counters` (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 KiB per dispatch;
+# factors from a 256 MiB device copy), summarised with the commands in
+# profiles/kda_projection_m8_m64_pmc_traffic.md.  Valid only for the sources it was measured on:
+# any change to them reports traffic as null until the counters are taken again.
+TRAFFIC_SOURCES = ("bf16_skinny_gemm_02_amd/csrc/mfma.hip", "bf16_skinny_gemm_02_amd/csrc/gemv.hip",
+                   "bf16_skinny_gemm_02_amd/csrc/smallk.hip", "bf16_skinny_gemm_02_amd/csrc/sg_device.h",
+                   "bf16_skinny_gemm_02_amd/csrc/dispatch.cpp", "bf16_skinny_gemm_02_amd/csrc/abi.cpp")
+TRAFFIC_PMC = {"sources_sha256": None, "bytes_per_call": None}
 
 
-def measured_traffic():
+def sources_sha256():
     h = hashlib.sha256()
     for rel in TRAFFIC_SOURCES:
         h.update((ROOT / rel).read_bytes())
-    return TRAFFIC_PMC["bytes_per_launch"] if h.hexdigest() == TRAFFIC_PMC["sources_sha256"] else None
+    return h.hexdigest()
 
 
-def qkvg_kernel_leg(device, M, reps=200):
-    """Average duration of the Q/K/V/G projection kernel at batch M
-    (x[M,7168] x W[4096,7168]^T, one launch per call for M <= 16), back-to-back
-    launches on one stream cycling cold weight copies, timed with HIP events
-    recorded on that stream."""
-    x, w = synth.qkvg_inputs(M, seed=1000 * synth.WL_QKVG_SWEEP + M)
-    R = copies_for(2 * N_QKVG * K)
-    xd = bf16_dev(x, device)
-    w0 = bf16_dev(w, device)
-    ws = [w0] + [w0.clone() for _ in range(R - 1)]
-    out = torch.empty((M, N_QKVG), dtype=torch.bfloat16, device=device)
-    stream = torch.cuda.Stream(device)
-    g = capture(lambda r: sg.kda_qkvg_proj(xd, ws[r], out=out), R, stream)
-    for _ in range(5):
-        g.replay()
-    torch.cuda.synchronize()
-    ms = time_graph(g, stream, reps)
-    us = ms * 1000.0 / R
-    gbs = qkvg_bytes(M) / (us * 1e-6) / 1e9
-    cfg = sg.sg_select(M, N_QKVG, K)
-    kinds = {sg.SG_KIND_GEMV_ROW: "gemv_kernel", sg.SG_KIND_MFMA_WAVESPLIT: "wsplit_kernel",
-             sg.SG_KIND_MFMA_TILE: "tile_kernel", sg.SG_KIND_MFMA_BLOCK: "block_kernel"}
-    name = f"{kinds.get(cfg['kind'], '?')} (kda_qkvg_proj M={M}, {cfg['grid']} workgroups)"
-    return {"kernel": name, "us_per_launch": us, "launches_timed": reps * R, "gbs": gbs,
-            "bytes": qkvg_bytes(M)}
+def measured_traffic():
+    if TRAFFIC_PMC["sources_sha256"] != sources_sha256():
+        return None
+    return TRAFFIC_PMC["bytes_per_call"]
 
 
 COPY_BYTES = 256 << 20   # calibration copy: reads and writes exactly this many bytes
+COUNTER_PROJ_M = (8, 64)
+COUNTER_TAIL_M = (1, 8, 64, 256)
 
 
 def counters_mode(device):
     """One eager pass for the PMC runs: three device-to-device copies of
     COPY_BYTES (their FETCH_SIZE / WRITE_SIZE per dispatch calibrate the
-    counters against known traffic), then the roofline kernel once per cold
-    weight copy, twice over."""
+    counters against known traffic), then the projection call at M = 8 and
+    64 and the latent-MoE tail at M = 1, 8, 64, 256, once per cold weight
+    copy, twice over.  Prints what was launched and exits."""
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=device)
     src.fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
-    M = ROOFLINE_M
-    x, w = synth.qkvg_inputs(M, seed=1000 * synth.WL_QKVG_SWEEP + M)
-    R = copies_for(2 * N_QKVG * K)
-    xd = bf16_dev(x, device)
-    w0 = bf16_dev(w, device)
-    ws = [w0] + [w0.clone() for _ in range(R - 1)]
-    out = torch.empty((M, N_QKVG), dtype=torch.bfloat16, device=device)
-    for _ in range(2):
+    torch.cuda.synchronize()
+    del src, dst
+    launched = {}
+    for M in COUNTER_PROJ_M:
+        c = ProjectionCase(M, device, None, None, None)
+        for _ in range(2):
+            for r in range(c.R):
+                c.call(r, concurrent=False)
+        torch.cuda.synchronize()
+        launched[f"projection_m{M}"] = {"calls": 2 * c.R, "bytes_per_call": proj_bytes(M),
+                                        "flops_per_call": proj_flops(M),
+                                        "q": sg.sg_kda_select(sg.SG_KDA_QKVG, M, K, N_QKVG, N_AB),
+                                        "f": sg.sg_kda_select(sg.SG_KDA_FAB, M, K, N_QKVG, N_AB)}
+        del c
+    for M in COUNTER_TAIL_M:
+        c = TailCase(M, device)
+        for _ in range(2):
+            for r in range(c.R):
+                c.call(r)
+        torch.cuda.synchronize()
+        launched[f"tail_m{M}"] = {"calls": 2 * c.R, "bytes_per_call": tail_bytes(M),
+                                  "flops_per_call": tail_flops(M),
+                                  "cfg": sg.sg_select(M, D_HID, D_LAT, True)}
+        del c
+    print(json.dumps({"copy_bytes": COPY_BYTES, "sources_sha256": sources_sha256(),
+                      "launched": launched}), flush=True)
+
+
+# ---- the benchmark's other workloads ---------------------------------------------------
+
+def graph_us(fn, R, stream, reps=10, repeats=3):
+    """Median over `repeats` of the mean µs per call of a graph of fn(0..R-1)."""
+    g = capture(fn, R, stream)
+    ts = sorted(time_graph(g, stream, reps) * 1000.0 / R for _ in range(repeats))
+    del g
+    return ts[len(ts) // 2]
+
+
+def eager_us(fn, R, stream, reps=5, repeats=3):
+    """Median over `repeats` of the mean µs per call of fn(0..R-1) launched one
+    by one from the host (no graph), timed with events on `stream`."""
+    ts = []
+    with torch.cuda.stream(stream):
         for r in range(R):
-            sg.kda_qkvg_proj(xd, ws[r], out=out)
-    torch.cuda.synchronize()
-    del ws
-    # The MFMA tile paths, once each, for the matrix-core counters: the packed
-    # projection at M = 64 (128-row tiles) and the latent-MoE tail at M = 256
-    # (block tile).
-    pc = ProjectionCase(64, device, None, None, None)
-    pc.call(0, concurrent=False)
-    tc = TailCase(256, device)
-    tc.call(0)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": COPY_BYTES, "roofline_m": M, "launches": 2 * R,
-                      "algorithmic_bytes_per_launch": qkvg_bytes(M),
-                      "mfma_legs": {"projection_m64_flops": proj_flops(64),
-                                    "tail_m256_flops": tail_flops(256)}}), flush=True)
+            fn(r)
+        for _ in range(repeats):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                for r in range(R):
+                    fn(r)
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1000.0 / (reps * R))
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def fab_bytes(M):
+    return 2 * (N_AB * K + N_B * RANK + M * K + M * ((N_AB - RANK) + N_B))
+
+
+def config_fab_fb(device, stream, Ms=(1, 2, 4, 8)):
+    """The F_A/beta -> F_B branch alone: kda_fab_fb_proj (two launches) and
+    kda_fab_fb_proj_fused (one launch), as graphs over cold weight copies and
+    launched eagerly from the host."""
+    out = {}
+    for M in Ms:
+        x, w_ab, w_b = synth.fab_fb_inputs(M)
+        R = copies_for(2 * (N_AB * K + N_B * RANK))
+        xd = bf16_dev(x, device)
+        a0, b0 = bf16_dev(w_ab, device), bf16_dev(w_b, device)
+        was = [a0] + [a0.clone() for _ in range(R - 1)]
+        wbs = [b0] + [b0.clone() for _ in range(R - 1)]
+        g1 = torch.empty((M, N_B), dtype=torch.bfloat16, device=device)
+        beta = torch.empty((M, N_AB - RANK), dtype=torch.bfloat16, device=device)
+        ws = torch.zeros(sg.sg_workspace_bytes(sg.SG_OP_FAB_FB, M, N_AB, K), dtype=torch.uint8,
+                         device=device)
+        row = {}
+        for name, fn in (("two_launch", sg.kda_fab_fb_proj), ("one_launch", sg.kda_fab_fb_proj_fused)):
+            call = (lambda r, fn=fn: fn(xd, was[r], wbs[r], g1=g1, beta=beta, workspace=ws))
+            row[f"{name}_graph_us"] = round(graph_us(call, R, stream), 3)
+            row[f"{name}_eager_us"] = round(eager_us(call, min(R, 64), stream), 3)
+        row["bytes"] = fab_bytes(M)
+        row["two_launch_graph_gbs"] = round(fab_bytes(M) / (row["two_launch_graph_us"] * 1e-6) / 1e9, 1)
+        out[str(M)] = row
+        del was, wbs
+    return out
+
+
+def config_qkvg(device, stream, Ms=M_SWEEP):
+    """The packed Q/K/V/G projection alone (kda_qkvg_proj) over the sweep."""
+    out = {}
+    for M in Ms:
+        x, w = synth.qkvg_inputs(M)
+        R = copies_for(2 * N_QKVG * K)
+        xd = bf16_dev(x, device)
+        w0 = bf16_dev(w, device)
+        ws = [w0] + [w0.clone() for _ in range(R - 1)]
+        o = torch.empty((M, N_QKVG), dtype=torch.bfloat16, device=device)
+        wsp = torch.empty(max(sg.sg_workspace_bytes(sg.SG_OP_GEMM, M, N_QKVG, K), 256),
+                          dtype=torch.uint8, device=device)
+        us = graph_us(lambda r: sg.kda_qkvg_proj(xd, ws[r], out=o, workspace=wsp), R, stream,
+                      reps=BREAKDOWN_REPS)
+        cfg = sg.sg_select(M, N_QKVG, K)
+        out[str(M)] = {"us": round(us, 3), "gbs": round(qkvg_bytes(M) / (us * 1e-6) / 1e9, 1),
+                       "hbm_frac": round(qkvg_bytes(M) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                       "mfma_frac": round(2 * M * N_QKVG * K / (us * 1e-6) / 1e12 /
+                                          MFMA_BF16_PEAK_TFLOPS, 4),
+                       "kind": cfg["kind"], "grid": cfg["grid"], "k_split": cfg["k_split"]}
+        del ws
+    return out
+
+
+def config_schedules(proj, device, stream, Ms=(1, 4, 16, 32)):
+    """The projection's two schedules (one stream; fork/join onto an aux
+    stream) and a plain packed GEMM over [W_qkvg; W_ab] followed by a second
+    GEMM for F_B, all as graphs over the same cold weight copies."""
+    out = {}
+    for M in Ms:
+        c = proj[M]
+        one = graph_us(lambda r, c=c: c.call(r, concurrent=False), c.R, stream)
+        two = graph_us(lambda r, c=c: c.call(r, concurrent=True), c.R, stream)
+        out_packed = torch.empty((M, N_QKVG + N_AB), dtype=torch.bfloat16, device=device)
+        g1_s2 = torch.empty((M, N_B), dtype=torch.bfloat16, device=device)
+        ws2 = torch.empty(max(sg.sg_workspace_bytes(sg.SG_OP_GEMM, M, N_QKVG + N_AB, K), 256),
+                          dtype=torch.uint8, device=device)
+
+        def s2_call(r, c=c):
+            sg.skinny_gemm(c.x, c.packed[r], out=out_packed, workspace=ws2)
+            sg.skinny_gemm(out_packed[:, N_QKVG:N_QKVG + RANK], c.w_b[r], out=g1_s2)
+
+        s2 = graph_us(s2_call, c.R, stream)
+        out[str(M)] = {"one_stream_us": round(one, 3), "two_stream_us": round(two, 3),
+                       "packed_gemm_then_fb_us": round(s2, 3),
+                       "two_stream_speedup_vs_one_stream": round(one / two, 3),
+                       "two_stream_speedup_vs_packed": round(s2 / two, 3),
+                       "gate_picks": "two_stream" if sg.sg_overlap_gate(M, True, True, True, True)
+                       else "one_stream"}
+    return out
+
+
+def config_tail(tail, device, stream, extra_Ms=(256,)):
+    """The latent-MoE tail at the benchmark's batch sizes M = 1, 8, 64, 256
+    (the sweep's cases plus the larger ones)."""
+    out = {}
+    for M in (1, 8, 64) + tuple(extra_Ms):
+        c = tail[M] if M in tail else TailCase(M, device)
+        us = graph_us(c.call, c.R, stream, reps=BREAKDOWN_REPS)
+        cfg = sg.sg_select(M, D_HID, D_LAT, True)
+        out[str(M)] = {"us": round(us, 3), "gbs": round(tail_bytes(M) / (us * 1e-6) / 1e9, 1),
+                       "hbm_frac": round(tail_bytes(M) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                       "mfma_frac": round(tail_flops(M) / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "roofline_frac": round(roofline_time_us(tail_bytes(M), tail_flops(M)) / us, 4),
+                       "kind": cfg["kind"], "grid": cfg["grid"], "k_split": cfg["k_split"]}
+        if M not in tail:
+            del c
+    return out
 
 
 # ---- context: launch floor and a plain device copy ---------------------------------
@@ -299,18 +423,24 @@ def context_figures(device, stream):
 
 # ---- CPU baseline -------------------------------------------------------------------
 
-def cpu_baseline(budget_s=15.0):
-    """The oracle (fp64, OpenMP over outputs) on this host's cores, on a bounded
-    sample: whole passes over the M sweep of the KDA projection, as many as fit
-    in the budget (at least one)."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def _oracle_rate(threads, budget_s):
+    """Whole passes over the projection M sweep with the oracle on `threads`
+    OpenMP threads, as many as fit in budget_s (at least one)."""
     import oracle
-    cores = len(os.sched_getaffinity(0))
-    cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
-    oracle.set_threads(cores)
+    oracle.set_threads(threads)
     inputs = {M: synth.overlap_inputs(M) for M in M_SWEEP}
-    calls = 0
+    calls = passes = 0
     t0 = time.perf_counter()
-    passes = 0
     while True:
         for M in M_SWEEP:
             x, packed, w_b = inputs[M]
@@ -320,20 +450,39 @@ def cpu_baseline(budget_s=15.0):
         if time.perf_counter() - t0 >= budget_s or passes >= 50:
             break
     dt = time.perf_counter() - t0
-    cpu = "unknown CPU"
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    return {"value": dt / calls * 1e6, "unit": "us/call", "cores": cores, "kind": "oracle",
+    return dt / calls * 1e6, calls, passes, dt
+
+
+def cpu_baseline(budget_s=15.0):
+    """The oracle (fp64, OpenMP over outputs) on this host, on a bounded
+    sample: whole passes over the M sweep of the KDA projection, on all the
+    host's threads, then on one."""
+    cores = len(os.sched_getaffinity(0))
+    cores = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+    cpu = _cpu_model()
+    us, calls, passes, dt = _oracle_rate(cores, budget_s)
+    us1, calls1, passes1, dt1 = _oracle_rate(1, budget_s)
+    return {"value": us, "unit": "us/call", "cores": cores, "kind": "oracle",
             "sample": f"{passes} pass(es) over the KDA projection M sweep {M_SWEEP} "
-                      f"({calls} calls, {dt:.1f} s, fp64 oracle, OpenMP {cores} threads, {cpu})"}
+                      f"({calls} calls, {dt:.1f} s, fp64 oracle, OpenMP {cores} threads, {cpu})",
+            "single_thread": {"value": us1, "unit": "us/call", "cores": 1,
+                              "sample": f"{passes1} pass(es), {calls1} calls, {dt1:.1f} s"}}
 
 
 # ---- main -----------------------------------------------------------------------------
+
+KINDS = {sg.SG_KIND_GEMV_ROW: "gemv_kernel", sg.SG_KIND_GEMV_SPLITK: "gemv_kernel",
+         sg.SG_KIND_MFMA_WAVESPLIT: "wsplit_kernel", sg.SG_KIND_MFMA_TILE: "tile_kernel",
+         sg.SG_KIND_MFMA_BLOCK: "block_kernel"}
+
+
+def projection_kernels(M):
+    q = sg.sg_kda_select(sg.SG_KDA_QKVG, M, K, N_QKVG, N_AB)
+    f = sg.sg_kda_select(sg.SG_KDA_FAB, M, K, N_QKVG, N_AB)
+    return (f"{KINDS.get(q['kind'], '?')} with the Q/K/V/G and F_A/beta rows as two segments "
+            f"({q['grid'] + f['grid']} workgroups), then fab_fb_tail_kernel (F_B"
+            f"{' and the Q/K/V/G split-K reduction' if q['k_split'] > 1 else ''})")
+
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
@@ -341,15 +490,15 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload configs (the timed sweep and breakdown only)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--comparators", action="store_true",
-                    help="also time the forced two-stream and one-stream schedules, a plain "
-                         "packed GEMM followed by F_B, and the same work through torch "
-                         "(hipBLASLt) with an unfused RMSNorm")
+                    help="also time the same work through torch (hipBLASLt) with an unfused RMSNorm")
     ap.add_argument("--counters", action="store_true",
                     help="counter-collection mode for rocprofv3 --pmc: a plain device copy of "
-                         "known size (calibration), then the roofline kernel launched eagerly "
-                         "over its cold weight copies; prints the byte counts and exits")
+                         "known size (calibration), then the projection and the tail launched "
+                         "eagerly over their cold weight copies; prints what ran and exits")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the hot path has no cross-GPU step (each TP8 rank's "
@@ -445,38 +594,43 @@ def main():
     tail_value = t_tail_all * 1000.0 / calls_tail
     ms_per_step = wall * 1000.0 / args.steps
 
+    # Roofline leg: the same M = ROOFLINE_M projection graph replayed back to
+    # back right after the timed region, between two events on its stream.
+    roof_reps = 100
+    us_call = time_graph(g_proj[ROOFLINE_M], main_stream, roof_reps) * 1000.0 / proj[ROOFLINE_M].R
+    achieved = proj_bytes(ROOFLINE_M) / (us_call * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                "kernel": f"KDA projection call at M = {ROOFLINE_M}: {projection_kernels(ROOFLINE_M)}",
+                "unit_of_work": "one call of the headline path (both launches)",
+                "us_per_call": round(us_call, 3),
+                "algorithmic_bytes_per_call": proj_bytes(ROOFLINE_M),
+                "calls_timed": roof_reps * proj[ROOFLINE_M].R,
+                "sweep_gbs": round(sum(proj_bytes(M) for M in M_SWEEP) * args.steps * proj[1].R /
+                                   (t_proj_all * 1e-3) / 1e9, 1)}
+    roofline["sweep_frac"] = round(roofline["sweep_gbs"] / HBM_PEAK_GBS, 4)
+
+    configs = {}
+    if not args.no_configs:
+        print("[bench] per-workload configs", file=sys.stderr, flush=True)
+        q1 = config_qkvg(device, main_stream)
+        configs["qkvg_gemv_m1"] = {"workload": "single bf16 GEMV x[1,7168] W[4096,7168]",
+                                   **q1["1"]}
+        configs["fab_fb"] = config_fab_fb(device, main_stream)
+        configs["qkvg_sweep"] = q1
+        configs["projection_schedules"] = config_schedules(proj, device, main_stream)
+        configs["latent_tail"] = config_tail(tail, device, main_stream)
+
     if args.comparators:
         for M in M_SWEEP:
             c = proj[M]
-            g_two = capture(lambda r, c=c: c.call(r, concurrent=True), c.R, main_stream)
-            two = time_graph(g_two, main_stream, 10) * 1000.0 / c.R
-            g_one = capture(lambda r, c=c: c.call(r, concurrent=False), c.R, main_stream)
-            one = time_graph(g_one, main_stream, 10) * 1000.0 / c.R
-            pw = c.packed
-            out_packed = torch.empty((M, N_QKVG + N_AB), dtype=torch.bfloat16, device=device)
-            g1_s2 = torch.empty((M, N_B), dtype=torch.bfloat16, device=device)
-            ws2 = torch.empty(max(sg.sg_workspace_bytes(sg.SG_OP_GEMM, M, N_QKVG + N_AB, K), 256),
-                              dtype=torch.uint8, device=device)
-
-            def s2_call(r, c=c, out_packed=out_packed, g1_s2=g1_s2, ws2=ws2, pw=pw):
-                sg.skinny_gemm(c.x, pw[r], out=out_packed, workspace=ws2)
-                sg.skinny_gemm(out_packed[:, N_QKVG:N_QKVG + RANK], c.w_b[r], out=g1_s2)
-
-            g_s2 = capture(s2_call, c.R, main_stream)
-            s2 = time_graph(g_s2, main_stream, 10) * 1000.0 / c.R
-            # The vendor library on the same work: torch.mm (hipBLASLt) over the packed
-            # weight, then a second torch.mm for F_B on the bf16 f_a columns.
             out_t = torch.empty((M, N_QKVG + N_AB), dtype=torch.bfloat16, device=device)
             g1_t = torch.empty((M, N_B), dtype=torch.bfloat16, device=device)
 
-            def blas_proj(r, c=c, out_t=out_t, g1_t=g1_t, pw=pw):
-                torch.mm(c.x, pw[r].t(), out=out_t)
+            def blas_proj(r, c=c, out_t=out_t, g1_t=g1_t):
+                torch.mm(c.x, c.packed[r].t(), out=out_t)
                 torch.mm(out_t[:, N_QKVG:N_QKVG + RANK], c.w_b[r].t(), out=g1_t)
 
-            g_bp = capture(blas_proj, c.R, main_stream)
-            bp = time_graph(g_bp, main_stream, 10) * 1000.0 / c.R
-            # ... and the unfused latent-MoE tail: RMSNorm in torch ops (fp32, bf16
-            # result), then torch.addmm with the shared-expert partial.
             tc = tail[M]
             out_tt = torch.empty((M, D_HID), dtype=torch.bfloat16, device=device)
 
@@ -486,29 +640,11 @@ def main():
                      tc.gamma.float()).to(torch.bfloat16)
                 torch.addmm(tc.S, n, tc.w_up[r].t(), out=out_tt)
 
-            g_bt = capture(blas_tail, tc.R, main_stream)
-            bt = time_graph(g_bt, main_stream, 10) * 1000.0 / tc.R
             b = breakdown[str(M)]
-            b["two_stream_us"] = round(two, 3)
-            b["one_stream_us"] = round(one, 3)
-            b["packed_gemm_then_fb_us"] = round(s2, 3)
-            b["two_stream_speedup_vs_one_stream"] = round(one / two, 3)
-            b["torch_blas_projection_us"] = round(bp, 3)
-            b["torch_blas_tail_us"] = round(bt, 3)
-            del g_two, g_one, g_s2, g_bp, g_bt
+            b["torch_blas_projection_us"] = round(graph_us(blas_proj, c.R, main_stream), 3)
+            b["torch_blas_tail_us"] = round(graph_us(blas_tail, tc.R, main_stream), 3)
 
     context = context_figures(device, main_stream)
-    leg = qkvg_kernel_leg(device, ROOFLINE_M)
-    roofline = {"bound": "hbm", "achieved": round(leg["gbs"], 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(leg["gbs"] / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(),
-                "kernel": leg["kernel"], "us_per_launch": round(leg["us_per_launch"], 3),
-                "algorithmic_bytes_per_launch": leg["bytes"]}
-    gemv = qkvg_kernel_leg(device, 1)
-    roofline["gemv_m1"] = {"kernel": gemv["kernel"], "us_per_launch": round(gemv["us_per_launch"], 3),
-                           "achieved": round(gemv["gbs"], 1),
-                           "frac": round(gemv["gbs"] / HBM_PEAK_GBS, 4),
-                           "algorithmic_bytes_per_launch": gemv["bytes"]}
 
     result = {
         "metric": METRIC,
@@ -537,6 +673,7 @@ def main():
         "tail_us_per_call": round(tail_value, 3),
         "context": context,
         "breakdown": breakdown,
+        "configs": configs,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
