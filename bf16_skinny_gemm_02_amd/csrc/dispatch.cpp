@@ -21,6 +21,7 @@ constexpr int kGemvWaveTarget = 2048;  // waves the split-K GEMV aims for
 constexpr int kSmallK = 256;         // K at or below this: small-K GEMV
 constexpr int kGemvDepth = 16;       // 512-wide weight steps an M = 1 GEMV wave holds
 constexpr int kGemvDepth4 = 7;       // the same with four weight rows per wave
+constexpr int kGemvDepth7 = 4;       // ... and with seven
 // MFMA ring kernels.  A chunk is 4 k-steps of 32 (128 k).
 constexpr int kWgTarget = 224;       // workgroups a launch aims for (256 CUs, one each)
 constexpr int kNoSplitTiles = 192;   // this many tiles fill the chip without a K split
@@ -28,6 +29,8 @@ constexpr int kSplitMaxTiles = 320;  // WAVESPLIT up to this many 16-row tiles
 constexpr int kSplitPairTiles = 512; // ... or this many when two workgroups fit a CU (M <= 8)
 constexpr int kSplitRing = 3;        // WAVESPLIT ring slots
 constexpr int kSplitRing2 = 2;       // ... for 9 <= M <= 16 with two workgroups per CU
+constexpr int kCus = 256;            // compute units (8 XCDs of 32)
+constexpr int kSplitWideRows = 32;   // WAVESPLIT: most weight rows per workgroup (two fragments)
 constexpr int kWideRing = 4;         // TILE ring slots for M <= 16 (2 waves, 32 rows)
 constexpr int kTileRing = 3;         // TILE ring slots for 16 < M <= 64 (4 waves, 64 rows)
 constexpr int kBlockRows = 64;       // BLOCK (M > 64): weight rows per workgroup
@@ -129,9 +132,14 @@ extern "C" int sg_select(int M, int N, int K, int has_residual, sg_config_t* out
       want = ceil_div(kGemvWaveTarget, N);
     }
     c.m_tile = 1;
-    // Four rows per wave when a whole short row fits in the shallower
-    // register ring: fewer, longer workgroups (each stages the activation once).
-    c.rows = (c.kind == SG_KIND_GEMV_ROW && steps <= kGemvDepth4) ? 4 : 1;
+    // Several rows per wave when a whole short row fits in a shallower
+    // register ring: fewer, longer workgroups (each stages the activation
+    // once).  Seven rows of up to four steps (28 rows per workgroup: 7168
+    // rows, the latent-MoE up-projection, are exactly 256 workgroups), else
+    // four rows of up to seven.
+    c.rows = 1;
+    if (c.kind == SG_KIND_GEMV_ROW && steps <= kGemvDepth7) c.rows = 7;
+    else if (c.kind == SG_KIND_GEMV_ROW && steps <= kGemvDepth4) c.rows = 4;
     const int need = ceil_div(steps, kGemvDepth);
     c.k_split = effective_split(steps, want > need ? want : need);
     c.k_unroll = kGemvDepth;
@@ -139,7 +147,19 @@ extern "C" int sg_select(int M, int N, int K, int has_residual, sg_config_t* out
   } else if (M <= 16) {
     c.m_tile = 4 * ceil_div(M, 4);
     const int tiles16 = ceil_div(N, 16);
-    if (tiles16 <= kSplitMaxTiles || (c.m_tile <= 8 && tiles16 <= kSplitPairTiles)) {
+    // Past kSplitMaxTiles 16-row tiles, one workgroup per CU with 17..32 rows
+    // (two fragments, a multiple of 4) while that covers N in one round:
+    // e.g. 7168 rows are 256 workgroups of 28.
+    const int wide_rows = 4 * ceil_div(ceil_div(N, kCus), 4);
+    if (tiles16 > kSplitMaxTiles && wide_rows <= kSplitWideRows) {
+      c.kind = SG_KIND_MFMA_WAVESPLIT;
+      c.rows = wide_rows;
+      c.waves = 4;
+      c.k_unroll = kSplitRing;
+      const int tiles = ceil_div(N, c.rows);
+      c.k_split = mfma_split(tiles, ksteps, 16);
+      c.grid = tiles * c.k_split;
+    } else if (tiles16 <= kSplitMaxTiles || (c.m_tile <= 8 && tiles16 <= kSplitPairTiles)) {
       // Each wave walks a quarter of the workgroup's K-range: at least one
       // chunk (4 k-steps) per wave.  Up to M = 8 the 3-slot rings of two
       // workgroups fit one CU's LDS, so up to 512 tiles run in one round.

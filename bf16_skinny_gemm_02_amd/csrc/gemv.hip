@@ -84,7 +84,10 @@ struct GemvLaunch {
 // FB (instances of the one-launch F_A/beta -> F_B branch only): workgroups
 // in L.fb's range run the F_B role, and a segment with `arrive` set hands
 // its partials over (sg_fused.h).  Other instances carry none of that code.
-template <int M, int R, int NW, int D, bool FOLD, bool FB>
+//
+// RES (instances launched for a problem with a residual and bf16 output):
+// the residual is requested first; other instances load none.
+template <int M, int R, int NW, int D, bool FOLD, bool FB, bool RES>
 __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
   extern __shared__ u32x4 xs[];  // [M][row_chunks] 16-byte chunks of the activation
   const int b = static_cast<int>(blockIdx.x);
@@ -121,6 +124,19 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
   const int row_chunks = nst * kWave;
   const int total = M * row_chunks;
   const int c_base = s_begin * kWave;
+
+  // 0. The residual this lane adds in the epilogue (lane m * R + r adds
+  //    res[m, n0 + r]), requested before anything else: it lands with the
+  //    first round trip instead of costing one of its own at the end.  The
+  //    load is unconditional (index clamped; the activation stands in when
+  //    there is no residual) so that no wait is attached to it.
+  uint16_t res_bits = 0;
+  if constexpr (RES) {
+    const bool use = g.res != nullptr && g.partial == nullptr;
+    const int mr = min(lane / R, M - 1);
+    const int nr = min(n0 + lane % R, g.N - 1);
+    res_bits = use ? g.res[static_cast<int64_t>(mr) * g.ldr + nr] : g.a[0];
+  }
 
   // 1. Activation rows of the range into LDS, one 1 KiB step-block per wave
   //    copy, straight from global memory (no registers; chunks past K read
@@ -260,7 +276,9 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
           *dst = v;
         }
       } else {
-        if (g.res != nullptr) v += bf16_to_f32(g.res[m * g.ldr + n]);
+        if constexpr (RES) {
+          if (g.res != nullptr) v += bf16_to_f32(res_bits);
+        }
         if (g.n_split > 0 && n >= g.n_split)
           g.out2[m * g.ldc2 + (n - g.n_split)] = f32_to_bf16(v);
         else
@@ -274,14 +292,15 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
 }
 
 // Weight steps a wave holds (the largest K-range, in 512-wide steps, the
-// table gives one workgroup): 16, 14, 7 steps for R = 1, 2, 4 rows, i.e. at
-// most 112 VGPRs of weights, and a whole 7168-wide row for R <= 2.
-constexpr int gemv_depth(int R) { return R == 1 ? 16 : (R == 2 ? 14 : 7); }
+// table gives one workgroup): 16, 14, 7, 4 steps for R = 1, 2, 4, 7 rows,
+// i.e. at most 112 VGPRs of weights; a whole 7168-wide row for R <= 2, a
+// whole 2048-wide one for R = 7.
+constexpr int gemv_depth(int R) { return R == 1 ? 16 : (R == 2 ? 14 : (R == 4 ? 7 : 4)); }
 
-template <int M, int R, int NW, bool FOLD, bool FB>
+template <int M, int R, int NW, bool FOLD, bool FB, bool RES>
 hipError_t launch_inst(const GemvLaunch& g, dim3 grid, size_t lds, hipStream_t s) {
   constexpr int D = gemv_depth(R);
-  auto kern = gemv_kernel<M, R, NW, D, FOLD, FB>;
+  auto kern = gemv_kernel<M, R, NW, D, FOLD, FB, RES>;
   static std::atomic<bool> lds_set[kLdsAttrDevices];
   const hipError_t attr = ensure_lds_limit(reinterpret_cast<const void*>(kern), kGemvMaxLds, lds_set);
   if (attr != hipSuccess) return attr;
@@ -290,19 +309,21 @@ hipError_t launch_inst(const GemvLaunch& g, dim3 grid, size_t lds, hipStream_t s
 
 // The table sends only M = 1 here (4 waves; one weight row per wave, or four
 // when a whole row fits in 7 steps); wider M goes to the MFMA kernels.
-template <bool FOLD>
+template <bool FOLD, bool RES>
 hipError_t launch_fold(const GemvLaunch& g, int M, int R, int NW, dim3 grid, size_t lds,
                        hipStream_t s) {
-  if (M == 1 && R == 1 && NW == 4) return launch_inst<1, 1, 4, FOLD, false>(g, grid, lds, s);
-  if (M == 1 && R == 4 && NW == 4) return launch_inst<1, 4, 4, FOLD, false>(g, grid, lds, s);
+  if (M == 1 && R == 1 && NW == 4) return launch_inst<1, 1, 4, FOLD, false, RES>(g, grid, lds, s);
+  if (M == 1 && R == 4 && NW == 4) return launch_inst<1, 4, 4, FOLD, false, RES>(g, grid, lds, s);
+  if (M == 1 && R == 7 && NW == 4) return launch_inst<1, 7, 4, FOLD, false, RES>(g, grid, lds, s);
   return hipErrorInvalidValue;
 }
 
 // The one-launch F_A/beta -> F_B instances (M = 1, 4 waves, no fold).
 hipError_t launch_fb(const GemvLaunch& g, int M, int R, int NW, dim3 grid, size_t lds,
                      hipStream_t s) {
-  if (M == 1 && R == 1 && NW == 4) return launch_inst<1, 1, 4, false, true>(g, grid, lds, s);
-  if (M == 1 && R == 4 && NW == 4) return launch_inst<1, 4, 4, false, true>(g, grid, lds, s);
+  if (M == 1 && R == 1 && NW == 4) return launch_inst<1, 1, 4, false, true, false>(g, grid, lds, s);
+  if (M == 1 && R == 4 && NW == 4) return launch_inst<1, 4, 4, false, true, false>(g, grid, lds, s);
+  if (M == 1 && R == 7 && NW == 4) return launch_inst<1, 7, 4, false, true, false>(g, grid, lds, s);
   return hipErrorInvalidValue;
 }
 
@@ -417,8 +438,13 @@ hipError_t launch_gemv_impl(const DotProblem* segs, const sg_config_t* cfgs, int
   if (wgs <= 0) return hipSuccess;
   const dim3 grid(wgs);
   if (fb != nullptr) return launch_fb(L, segs[0].M, cfgs[0].rows, cfgs[0].waves, grid, lds, s);
-  if (segs[0].gamma != nullptr) return launch_fold<true>(L, segs[0].M, cfgs[0].rows, cfgs[0].waves, grid, lds, s);
-  return launch_fold<false>(L, segs[0].M, cfgs[0].rows, cfgs[0].waves, grid, lds, s);
+  // Instances that load a residual only where a segment has one and stores bf16.
+  bool res = false;
+  for (int i = 0; i < nseg; ++i) res = res || (segs[i].res != nullptr && segs[i].partial == nullptr);
+  const int M = segs[0].M, R = cfgs[0].rows, NW = cfgs[0].waves;
+  if (segs[0].gamma != nullptr)
+    return res ? launch_fold<true, true>(L, M, R, NW, grid, lds, s) : launch_fold<true, false>(L, M, R, NW, grid, lds, s);
+  return res ? launch_fold<false, true>(L, M, R, NW, grid, lds, s) : launch_fold<false, false>(L, M, R, NW, grid, lds, s);
 }
 
 }  // namespace

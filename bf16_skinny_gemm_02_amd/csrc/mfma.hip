@@ -67,6 +67,7 @@ struct MfmaArgs {
   float eps;
   unsigned* arrive;  // in-launch hand-off (FB wave-split instances, sg_fused.h): the flag header
   int nslots;        // producer slots of the launch (one per workgroup of the F_A/beta segment)
+  int tile_rows;     // wave-split kernel: weight rows per workgroup (16, or 17..32 with NT = 2)
 };
 
 // One launch covers one or two segments (independent problems whose
@@ -141,17 +142,19 @@ __device__ __forceinline__ Res4 load_res4(const MfmaArgs& g, int m, int n0) {
 // otherwise element by element.
 // COHERENT (the F_A/beta segment of a one-launch F_A/beta -> F_B call): the
 // partials go out as device-coherent stores for the F_B role to read.
+// Rows n >= nlim (the next workgroup's, or past N) are not stored.
 template <bool COHERENT = false>
 __device__ __forceinline__ void store4(const MfmaArgs& g, const f32x4& acc, int m, int n0, int split,
-                                       const Res4& res) {
+                                       const Res4& res, int nlim = INT32_MAX) {
   if (m >= g.M) return;
-  const bool whole = n0 + 3 < g.N;
+  nlim = min(nlim, g.N);
+  const bool whole = n0 + 3 < nlim;
   if (g.partial != nullptr) {
     float* p = g.partial + (static_cast<int64_t>(split) * g.M + m) * g.N + n0;
     if constexpr (COHERENT) {
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        if (n0 + v < g.N) store_coherent(p + v, acc[v]);
+        if (n0 + v < nlim) store_coherent(p + v, acc[v]);
       return;
     }
     if (whole && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
@@ -179,7 +182,7 @@ __device__ __forceinline__ void store4(const MfmaArgs& g, const f32x4& acc, int 
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int n = n0 + v;
-    if (n >= g.N) continue;
+    if (n >= nlim) continue;
     if (g.partial != nullptr) {
       g.partial[(static_cast<int64_t>(split) * g.M + m) * g.N + n] = acc[v];
     } else {
@@ -321,7 +324,11 @@ constexpr int kFoldMaxK = kFoldChunks * kWave * 8;
 // FB (instances of the one-launch F_A/beta -> F_B branch only): workgroups in
 // L.fb's range run the F_B role, and the segment with `arrive` set hands its
 // partials over (sg_fused.h).  Other instances carry none of that code.
-template <int XQ, int C, bool NORM, bool RES, bool FB>
+//
+// NT: 16-row weight fragments per workgroup (1, or 2 for a workgroup of
+// 17..32 rows: the second fragment's rows past g.tile_rows read zeros and are
+// not stored), so that e.g. 7168 rows make exactly 256 workgroups of 28.
+template <int XQ, int C, bool NORM, bool RES, bool FB, int NT>
 __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch L) {
   extern __shared__ u32x4 lds[];
   if constexpr (FB) {
@@ -339,10 +346,11 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
   unsigned prev = 0u;
   if constexpr (FB) prev = g.arrive != nullptr ? load_flag(g.arrive + slot) : 0u;
   constexpr int XROWS = 4 * XQ;
-  constexpr int SLOT = (16 + XROWS) * kPieces;
-  constexpr int P = 4 + XQ;
+  constexpr int WROWS = 16 * NT;
+  constexpr int SLOT = (WROWS + XROWS) * kPieces;
+  constexpr int P = 4 * NT + XQ;
   constexpr int kInFlight = (C - 2) * P;
-  static_assert(XQ >= 1 && XQ <= 4 && C >= 2, "configuration");
+  static_assert(XQ >= 1 && XQ <= 4 && C >= 2 && (NT == 1 || NT == 2), "configuration");
 
   const int lane = lane_id();
   const int wave = wave_id();
@@ -358,8 +366,8 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
   const int npieces = nk * 4;
   const int nch = (nk + kChunkSteps - 1) / kChunkSteps;
   const int c0 = w_begin * 4;
-  const int row0 = tile * 16;
-  const int rows = min(16, g.N - row0);
+  const int row0 = tile * g.tile_rows;
+  const int rows = min(g.tile_rows, g.N - row0);
   u32x4* ring = lds + wave * C * SLOT;
 
   const rsrc_t wres = make_rsrc(g.w + static_cast<int64_t>(row0) * g.ldw,
@@ -379,9 +387,9 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
   auto issue = [&](int q) {
     u32x4* slot = ring + (q % C) * SLOT;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4 * NT; ++i) {
       const int r = 4 * i + dr;
-      const int pc = kPieces * q + (dp ^ r);
+      const int pc = kPieces * q + (dp ^ (r & 15));
       const uint32_t off = (r < rows && pc < npieces && c0 + pc < K8)
                                ? static_cast<uint32_t>((r * g.ldw + (c0 + pc) * 8) * 2)
                                : kOob;
@@ -394,14 +402,16 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
       const uint32_t off = (m < g.M && pc < npieces && c0 + pc < K8)
                                ? static_cast<uint32_t>((m * g.lda + (c0 + pc) * 8) * 2)
                                : kOob;
-      copy16_to_lds(xres, slot + (16 + 4 * j) * kPieces, off);
+      copy16_to_lds(xres, slot + (WROWS + 4 * j) * kPieces, off);
     }
   };
 
   // The residual and (NORM) the whole latent rows go out before the ring's
   // first chunks: loads complete in issue order, so neither the RMSNorm
   // below nor the chunk waits of the loop wait for the other's loads.
-  const Res4 res = load_res4<RES>(g, rl, row0 + 4 * kg);
+  Res4 res[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) res[nt] = load_res4<RES>(g, rl, row0 + 16 * nt + 4 * kg);
   u32x4 lv[NORM ? XQ : 1][kFoldChunks];
   if constexpr (NORM) {
 #pragma unroll
@@ -446,16 +456,19 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
     rn = rl < XROWS ? rsc[rl] : 0.f;
   }
 
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int xr = rl < XROWS ? rl : XROWS - 1;
   for (int q = 0; q < nch; ++q) {
     wait_vmcnt<kInFlight>();  // this wave's chunk q has landed (its own ring)
     const u32x4* slot = ring + (q % C) * SLOT;
-    u32x4 wf[kChunkSteps], xf[kChunkSteps];
+    u32x4 wf[kChunkSteps][NT], xf[kChunkSteps];
 #pragma unroll
     for (int t = 0; t < kChunkSteps; ++t) {
-      wf[t] = slot[rl * kPieces + ((4 * t + kg) ^ rl)];
-      xf[t] = slot[(16 + xr) * kPieces + ((4 * t + kg) ^ xr)];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) wf[t][nt] = slot[(16 * nt + rl) * kPieces + ((4 * t + kg) ^ rl)];
+      xf[t] = slot[(WROWS + xr) * kPieces + ((4 * t + kg) ^ xr)];
     }
     if constexpr (NORM) {
 #pragma unroll
@@ -472,7 +485,9 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
     wait_lgkmcnt0();  // the slot is in registers before the copy below refills the ring
     issue(q + C - 1);
 #pragma unroll
-    for (int t = 0; t < kChunkSteps; ++t) acc = mfma16(wf[t], xf[t], acc);
+    for (int t = 0; t < kChunkSteps; ++t)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16(wf[t][nt], xf[t], acc[nt]);
   }
   wait_vmcnt<0>();
   __syncthreads();  // every ring is drained: LDS is reused for the wave sums
@@ -480,22 +495,30 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
   float* red = reinterpret_cast<float*>(lds);
   if (wave > 0) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[((wave - 1) * 4 + v) * kWave + lane] = acc[v];
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[(((wave - 1) * NT + nt) * 4 + v) * kWave + lane] = acc[nt][v];
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
   for (int w = 0; w < kSplitWaves - 1; ++w)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] += red[(w * 4 + v) * kWave + lane];
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[nt][v] += red[((w * NT + nt) * 4 + v) * kWave + lane];
+  const int nlim = row0 + rows;
   if constexpr (FB) {
     if (g.arrive != nullptr) {  // wave 0 alone stores: one producer slot per workgroup
-      store4<true>(g, acc, rl, row0 + 4 * kg, split, res);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        store4<true>(g, acc[nt], rl, row0 + 16 * nt + 4 * kg, split, res[nt], nlim);
       produce(g.arrive, slot, g.nslots, prev);
       return;
     }
   }
-  store4(g, acc, rl, row0 + 4 * kg, split, res);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) store4(g, acc[nt], rl, row0 + 16 * nt + 4 * kg, split, res[nt], nlim);
 }
 
 // ---- two-dimensional LDS block tile (M > 64) ----------------------------------------
@@ -641,17 +664,29 @@ hipError_t launch_tile_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
   return launch_kernel(kern, dim3(wgs), dim3(NW * kWave), tile_lds_bytes(NW, C, XQ), s, L);
 }
 
-template <int XQ, int C, bool NORM, bool RES, bool FB = false>
+template <int XQ, int C, bool NORM, bool RES, bool FB = false, int NT = 1>
 hipError_t launch_wsplit_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
-  auto kern = wsplit_kernel<XQ, C, NORM, RES, FB>;
+  auto kern = wsplit_kernel<XQ, C, NORM, RES, FB, NT>;
   static std::atomic<bool> lds_set[kLdsAttrDevices];
   const hipError_t attr = ensure_lds_limit(reinterpret_cast<const void*>(kern), kMfmaMaxLds, lds_set);
   if (attr != hipSuccess) return attr;
-  return launch_kernel(kern, dim3(wgs), dim3(kSplitWaves * kWave), wsplit_lds_bytes(C, XQ, NORM), s, L);
+  return launch_kernel(kern, dim3(wgs), dim3(kSplitWaves * kWave), wsplit_lds_bytes(C, XQ, NORM, NT), s,
+                       L);
 }
 
 template <bool NORM, bool RES>
-hipError_t launch_wsplit_xq(const MfmaLaunch& L, int XQ, int C, int wgs, hipStream_t s) {
+hipError_t launch_wsplit_xq(const MfmaLaunch& L, int XQ, int C, int NT, int wgs, hipStream_t s) {
+  if (NT == 2) {  // 17..32 rows per workgroup, one workgroup per CU
+    if (C != 3) return hipErrorInvalidValue;
+    switch (XQ) {
+      case 1: return launch_wsplit_inst<1, 3, NORM, RES, false, 2>(L, wgs, s);
+      case 2: return launch_wsplit_inst<2, 3, NORM, RES, false, 2>(L, wgs, s);
+      case 3: return launch_wsplit_inst<3, 3, NORM, RES, false, 2>(L, wgs, s);
+      case 4: return launch_wsplit_inst<4, 3, NORM, RES, false, 2>(L, wgs, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (NT != 1) return hipErrorInvalidValue;
   if (C == 2) {  // 9 <= M <= 16, two workgroups per CU
     switch (XQ) {
       case 3: return launch_wsplit_inst<3, 2, NORM, RES>(L, wgs, s);
@@ -699,13 +734,13 @@ hipError_t launch_block_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
 
 int ksteps_of(int K) { return (K + kKStep - 1) / kKStep; }
 
-// Workgroup tiles of one K-range: 16 * NW (TILE) or 16 (WAVESPLIT) weight
-// rows each, or (BLOCK) 64 weight rows x 128 activation rows.
+// Workgroup tiles of one K-range: c.rows weight rows each (16 * NW for
+// TILE, 16 or 17..32 for WAVESPLIT), or (BLOCK) 64 weight rows x 128
+// activation rows.
 int tiles_of(const sg_config_t& c, int M, int N) {
   if (c.kind == SG_KIND_MFMA_BLOCK)
     return ((N + kBlkRows - 1) / kBlkRows) * ((M + kBlkM - 1) / kBlkM);
-  const int rows = c.kind == SG_KIND_MFMA_TILE ? c.rows : 16;
-  return (N + rows - 1) / rows;
+  return (N + c.rows - 1) / c.rows;
 }
 
 }  // namespace
@@ -718,8 +753,8 @@ size_t block_lds_bytes(int c) {
   return static_cast<size_t>(c) * (kBlkRows + kBlkM) * kPieces * 16;
 }
 
-size_t wsplit_lds_bytes(int c, int xq, bool norm) {
-  const size_t rings = static_cast<size_t>(kSplitWaves) * c * (16 + 4 * xq) * kPieces * 16;
+size_t wsplit_lds_bytes(int c, int xq, bool norm, int nt) {
+  const size_t rings = static_cast<size_t>(kSplitWaves) * c * (16 * nt + 4 * xq) * kPieces * 16;
   return rings + (norm ? kSplitWaves * kWave * 16 + 16 * sizeof(float) : 0);
 }
 
@@ -787,6 +822,7 @@ hipError_t launch_mfma_impl(const DotProblem* segs, const sg_config_t* cfgs, int
     g.eps = p.eps;
     g.arrive = fb != nullptr ? p.arrive : nullptr;
     g.nslots = 0;
+    g.tile_rows = c.rows;
     const int KS = ksteps_of(p.K);
     const int S = c.k_split > 0 ? c.k_split : 1;
     g.sps = (KS + S - 1) / S;
@@ -813,7 +849,7 @@ hipError_t launch_mfma_impl(const DotProblem* segs, const sg_config_t* cfgs, int
     if (arriving != 1 || arrivals > kFbMaxProducers || nfb > kFbMaxConsumers) return hipErrorInvalidValue;
     L.fb.arrivals = arrivals;
     for (int i = 0; i < nseg; ++i) L.seg[i].g.nslots = arrivals;
-    if (fb_lds_bytes(fb->M, fb->rank) > wsplit_lds_bytes(cfg.k_unroll, cfg.m_tile / 4, false))
+    if (fb_lds_bytes(fb->M, fb->rank) > wsplit_lds_bytes(cfg.k_unroll, cfg.m_tile / 4, false, 1))
       return hipErrorInvalidValue;
     for (int i = 0; i < nseg; ++i)
       if (segs[i].gamma != nullptr || segs[i].res != nullptr) return hipErrorInvalidValue;
@@ -863,18 +899,24 @@ hipError_t launch_mfma_impl(const DotProblem* segs, const sg_config_t* cfgs, int
   }
   if (cfg.kind == SG_KIND_MFMA_WAVESPLIT) {
     const int C = cfg.k_unroll, XQ = cfg.m_tile / 4;
-    if (cfg.rows != 16 || cfg.waves != kSplitWaves || (cfg.m_tile % 4) != 0 || (C != 2 && C != 3))
+    // 16 rows per workgroup (one fragment), or 17..32 in steps of 4 (two).
+    const int NT = cfg.rows == 16 ? 1 : 2;
+    if (cfg.rows < 16 || cfg.rows > 32 || cfg.rows % 4 != 0 || cfg.waves != kSplitWaves ||
+        (cfg.m_tile % 4) != 0 || (C != 2 && C != 3))
       return hipErrorInvalidValue;
-    if (fb != nullptr) return launch_wsplit_fb(L, XQ, C, wgs, s);
+    if (fb != nullptr) {
+      if (NT != 1) return hipErrorInvalidValue;
+      return launch_wsplit_fb(L, XQ, C, wgs, s);
+    }
     if (segs[0].gamma != nullptr) {
       // The RMSNorm fold: one segment whose whole rows fit the prologue.
       if (nseg != 1 || !wsplit_fold_fits(segs[0].K, cfg.k_split)) return hipErrorInvalidValue;
-      return res ? launch_wsplit_xq<true, true>(L, XQ, C, wgs, s)
-                 : launch_wsplit_xq<true, false>(L, XQ, C, wgs, s);
+      return res ? launch_wsplit_xq<true, true>(L, XQ, C, NT, wgs, s)
+                 : launch_wsplit_xq<true, false>(L, XQ, C, NT, wgs, s);
     }
     if (nseg == 2 && segs[1].gamma != nullptr) return hipErrorInvalidValue;
-    return res ? launch_wsplit_xq<false, true>(L, XQ, C, wgs, s)
-               : launch_wsplit_xq<false, false>(L, XQ, C, wgs, s);
+    return res ? launch_wsplit_xq<false, true>(L, XQ, C, NT, wgs, s)
+               : launch_wsplit_xq<false, false>(L, XQ, C, NT, wgs, s);
   }
   if (cfg.kind == SG_KIND_MFMA_BLOCK) {
     if (cfg.rows != kBlkRows || cfg.waves != kBlkWaves || cfg.m_tile % kBlkM != 0) return hipErrorInvalidValue;

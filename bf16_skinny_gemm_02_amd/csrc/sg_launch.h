@@ -129,7 +129,7 @@ constexpr size_t kSyncBytes = 18432;
 // The configuration table keeps both within kMfmaMaxLds.
 constexpr size_t kMfmaMaxLds = 160 * 1024;
 size_t tile_lds_bytes(int nw, int c, int xq);
-size_t wsplit_lds_bytes(int c, int xq, bool norm);
+size_t wsplit_lds_bytes(int c, int xq, bool norm, int nt);
 // Whether the wave-split kernel can fold the RMSNorm for this K and K split
 // (the launcher's own guard).
 bool wsplit_fold_fits(int K, int k_split);

@@ -19,9 +19,14 @@ Rule, for C[M,N] = A[M,K] W[N,K]^T:
       - N >= 1024: GEMV_ROW, want = 1.
       - N < 1024: GEMV_SPLITK, want = ceil(2048 / N).
       need = ceil(steps / 16), k_split = split(steps, max(want, need)),
-      m_tile = 1, rows = 4 if GEMV_ROW and steps <= 7 else 1, k_unroll = 16,
+      m_tile = 1, rows = 7 if GEMV_ROW and steps <= 4, else 4 if GEMV_ROW and
+      steps <= 7, else 1, k_unroll = 16,
       grid = ceil(N / (4 * rows)) * k_split.
-  * 2 <= M <= 16: m_tile = 4 * ceil(M / 4), tiles16 = ceil(N / 16).
+  * 2 <= M <= 16: m_tile = 4 * ceil(M / 4), tiles16 = ceil(N / 16),
+    wide = 4 * ceil(ceil(N / 256) / 4).
+      - tiles16 > 320 and wide <= 32: MFMA_WAVESPLIT, rows = wide, waves = 4,
+        k_unroll = 3, k_split = msplit(ceil(N / wide), 16), grid =
+        ceil(N / wide) * k_split.
       - tiles16 <= 320, or m_tile <= 8 and tiles16 <= 512: MFMA_WAVESPLIT,
         rows = 16, waves = 4, k_unroll = 3, k_split = msplit(tiles16, 16),
         grid = tiles16 * k_split.
@@ -118,13 +123,19 @@ def select(M: int, N: int, K: int, has_residual: bool = False):
         else:
             kind, want = GEMV_SPLITK, _cdiv(2048, N)
         ks = _split(steps, max(want, _cdiv(steps, 16)))
-        rows = 4 if (kind == GEMV_ROW and steps <= 7) else 1
+        rows = 7 if (kind == GEMV_ROW and steps <= 4) else (4 if (kind == GEMV_ROW and steps <= 7) else 1)
         cfg.update(kind=kind, m_tile=1, rows=rows, k_split=ks, k_unroll=16,
                    grid=_cdiv(N, 4 * rows) * ks)
     elif M <= 16:
         cfg["m_tile"] = 4 * _cdiv(M, 4)
         tiles16 = _cdiv(N, 16)
-        if tiles16 <= 320 or (cfg["m_tile"] <= 8 and tiles16 <= 512):
+        wide = 4 * _cdiv(_cdiv(N, 256), 4)
+        if tiles16 > 320 and wide <= 32:
+            tiles = _cdiv(N, wide)
+            ks = msplit(tiles, 16)
+            cfg.update(kind=MFMA_WAVESPLIT, rows=wide, waves=4, k_unroll=3, k_split=ks,
+                       grid=tiles * ks)
+        elif tiles16 <= 320 or (cfg["m_tile"] <= 8 and tiles16 <= 512):
             ks = msplit(tiles16, 16)
             cfg.update(kind=MFMA_WAVESPLIT, rows=16, waves=4, k_unroll=3, k_split=ks,
                        grid=tiles16 * ks)

@@ -37,6 +37,9 @@ GEMM_CASES = [
     (6, 5200, 1000, True), (13, 7170, 2056, False), (20, 9000, 512, True), (2, 4100, 7176, False),
     (130, 1000, 2056, True), (200, 4100, 520, False), (65, 7168, 2048, True), (129, 64, 1032, False),
     (12, 6000, 1032, True), (9, 8190, 264, False),
+    # one workgroup per CU of 17..32 rows (two 16-row fragments): a ragged
+    # first fragment in the last tile, and whole 32-row tiles
+    (3, 5124, 2048, True), (16, 8192, 1032, False),
     # long K: GEMV ranges at their full depth, split wave-split partials, 52-way tile and
     # block splits (the reduction's loop over many partials)
     (1, 300, 65536, False), (8, 500, 32768, True), (64, 256, 16384, True), (200, 128, 16392, False),

@@ -111,19 +111,26 @@ def test_kind_follows_m_boundaries():
         st, cfg = selection.select(M, 4096, 7168)
         assert st == selection.OK
         assert cfg["kind"] == _kind_for(M), M
-    # A wide N keeps M <= 16 on the wave-split tile while two of its
-    # workgroups fit a CU (3-slot rings up to M = 8, 2-slot rings above), up
-    # to 512 tiles; wider N moves to the shared-activation tile (32 rows).
-    assert selection.select(12, 7168, 2048)[1]["kind"] == selection.MFMA_WAVESPLIT
-    assert selection.select(12, 7168, 2048)[1]["k_unroll"] == 2
-    assert selection.select(8, 7168, 2048)[1]["kind"] == selection.MFMA_WAVESPLIT
-    assert selection.select(8, 7168, 2048)[1]["k_unroll"] == 3
+    # Past 320 tiles of 16 rows, M <= 16 stays on the wave-split tile with
+    # one workgroup per CU of up to 32 rows (two fragments): the tail's 7168
+    # rows are 256 workgroups of 28.  Wider N moves to the shared-activation
+    # tile (32 rows).
+    for M in (2, 8, 12, 16):
+        cfg = selection.select(M, 7168, 2048)[1]
+        assert cfg["kind"] == selection.MFMA_WAVESPLIT
+        assert (cfg["rows"], cfg["k_unroll"], cfg["grid"]) == (28, 3, 256)
+    assert selection.select(8, 5200, 2048)[1]["rows"] == 24
+    assert selection.select(8, 5120, 2048)[1]["rows"] == 16
+    assert selection.select(8, 8192, 2048)[1]["rows"] == 32
     assert selection.select(8, 9000, 2048)[1]["kind"] == selection.MFMA_TILE
     assert selection.select(12, 9000, 2048)[1]["kind"] == selection.MFMA_TILE
     assert selection.select(12, 9000, 2048)[1]["rows"] == 32
-    # M = 1 takes four rows per wave when a whole row fits seven 512-wide steps.
-    assert selection.select(1, 7168, 2048)[1]["rows"] == 4
-    assert selection.select(1, 7168, 2048)[1]["grid"] == 448
+    # M = 1 takes seven rows per wave when a whole row fits four 512-wide
+    # steps (the tail's 7168 x 2048: exactly 256 workgroups), four rows when
+    # it fits seven.
+    assert selection.select(1, 7168, 2048)[1]["rows"] == 7
+    assert selection.select(1, 7168, 2048)[1]["grid"] == 256
+    assert selection.select(1, 7168, 3584)[1]["rows"] == 4
     assert selection.select(1, 4096, 7168)[1]["rows"] == 1
     assert selection.select(257, 4096, 7168)[0] == selection.UNSUPPORTED
     assert selection.select(0, 4096, 7168)[1]["kind"] == selection.NONE
