@@ -23,11 +23,12 @@ from . import _lib
 from ._lib import (SG_KIND_MFMA_BLOCK, SG_KIND_GEMV_ROW, SG_KIND_GEMV_SMALLK, SG_KIND_GEMV_SPLITK,  # noqa: F401
                    SG_KIND_MFMA_TILE, SG_KIND_MFMA_WAVESPLIT, SG_KIND_NONE,
                    SG_KDA_FAB, SG_KDA_FAB_ALONE, SG_KDA_QKVG, SG_OP_FAB_FB, SG_OP_GEMM,
-                   SG_OP_LATENT_TAIL, SgConfig)
+                   SG_OP_LATENT_TAIL, SgConfig, SgTableEntry)
 
 __all__ = [
     "sg_select", "sg_overlap_gate", "sg_overlap_max_tokens", "sg_workspace_bytes",
-    "sg_kda_select", "sg_kda_workspace_bytes", "sg_version",
+    "sg_kda_select", "sg_kda_workspace_bytes", "sg_version", "sg_config_supported",
+    "sg_config_workspace_bytes", "sg_tuned_table", "sg_set_table_override",
     "skinny_gemm", "kda_qkvg_proj", "kda_fab_fb_proj", "kda_projection_overlap",
     "latent_moe_tail", "kda_projection_noalloc", "kda_fab_fb_proj_fused", "HipEvent",
     "library_path",
@@ -78,6 +79,45 @@ def sg_kda_select(which: int, M: int, K: int, n_qkvg: int, n_ab: int) -> dict:
 def sg_kda_workspace_bytes(which: int, M: int, K: int, n_qkvg: int, n_ab: int) -> int:
     return int(_lib.load().sg_kda_workspace_bytes(int(which), int(M), int(K), int(n_qkvg),
                                                   int(n_ab)))
+
+
+def _config(cfg: dict) -> SgConfig:
+    c = SgConfig()
+    for name, _ in SgConfig._fields_:
+        setattr(c, name, int(cfg.get(name, 1 if name == "nt_weights" else 0)))
+    return c
+
+
+def sg_config_supported(cfg: dict, M: int, N: int, K: int) -> bool:
+    """Whether the kernels can run configuration `cfg` (a dict of sg_config_t
+    fields) on an M x N x K problem."""
+    st = _lib.load().sg_config_supported(ctypes.byref(_config(cfg)), int(M), int(N), int(K))
+    if st == _lib.SG_ERR_INVALID_ARG:
+        _lib.check(st, "sg_config_supported")
+    return st == _lib.SG_OK
+
+
+def sg_config_workspace_bytes(cfg: dict, M: int, N: int) -> int:
+    return int(_lib.load().sg_config_workspace_bytes(ctypes.byref(_config(cfg)), int(M), int(N)))
+
+
+def sg_tuned_table() -> list:
+    """The compiled measured table, as a list of dicts (N, K, m_lo, m_hi,
+    kind, rows, waves, k_unroll, k_split)."""
+    ptr = ctypes.POINTER(SgTableEntry)()
+    n = int(_lib.load().sg_tuned_table(ctypes.byref(ptr)))
+    return [ptr[i].as_dict() for i in range(n)]
+
+
+def sg_set_table_override(entries: list) -> None:
+    """Replace the process-wide override table that sg_select consults first
+    (an empty list clears it).  Not to be called while other calls are in
+    flight or being captured."""
+    arr = (SgTableEntry * max(1, len(entries)))()
+    for i, e in enumerate(entries):
+        for name in _lib.TABLE_FIELDS:
+            setattr(arr[i], name, int(e[name]))
+    _lib.check(_lib.load().sg_set_table_override(arr, len(entries)), "sg_set_table_override")
 
 
 def sg_version() -> str:
@@ -170,8 +210,11 @@ class HipEvent:
         self.handle = h
 
     def __del__(self):
-        if getattr(self, "handle", None) and HipEvent._hip is not None:
-            HipEvent._hip.hipEventDestroy(self.handle)
+        # type(self), not the module global: at interpreter exit the module's
+        # globals may already be gone.
+        hip = type(self)._hip
+        if getattr(self, "handle", None) and hip is not None:
+            hip.hipEventDestroy(self.handle)
             self.handle = None
 
 
@@ -193,10 +236,10 @@ def skinny_gemm(A: torch.Tensor, W: torch.Tensor, residual: torch.Tensor | None 
             raise ValueError("residual must be [M, N]")
     _same_device(A, W, residual)
     out = _out(out, (M, N), A, "out", contiguous=False)
-    ws, ws_bytes = _workspace(workspace, sg_workspace_bytes(SG_OP_GEMM, M, N, K), A.device)
-    c = None
-    if cfg is not None:
-        c = SgConfig(**{k: int(v) for k, v in cfg.items()})
+    c = _config(cfg) if cfg is not None else None
+    need = (sg_config_workspace_bytes(cfg, M, N) if cfg is not None
+            else sg_workspace_bytes(SG_OP_GEMM, M, N, K))
+    ws, ws_bytes = _workspace(workspace, need, A.device)
     st = _lib.load().skinny_gemm(
         _ptr(A), _ld(A), _ptr(W), _ld(W), _ptr(residual),
         _ld(residual) if residual is not None else N, _ptr(out), _ld(out), M, N, K,

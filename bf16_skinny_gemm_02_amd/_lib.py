@@ -40,12 +40,23 @@ EXPORTED_SYMBOLS = (
     "sg_kda_select", "sg_kda_workspace_bytes",
     "sg_strerror", "sg_version", "skinny_gemm", "kda_qkvg_proj", "kda_fab_fb_proj",
     "kda_projection_overlap", "latent_moe_tail", "kda_projection_noalloc", "kda_fab_fb_proj_fused",
+    "sg_config_supported", "sg_config_workspace_bytes", "sg_tuned_table", "sg_set_table_override",
 )
 
 
 class SgConfig(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in
                 ("kind", "m_tile", "rows", "waves", "k_split", "k_unroll", "grid", "nt_weights")]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+TABLE_FIELDS = ("N", "K", "m_lo", "m_hi", "kind", "rows", "waves", "k_unroll", "k_split")
+
+
+class SgTableEntry(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in TABLE_FIELDS]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -78,6 +89,10 @@ _PROTOS = {
                                       _i32, _i32, _vp, _vp, _vp, _vp]),
     "kda_fab_fb_proj_fused": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                      _vp, _sz, _vp]),
+    "sg_config_supported": (_i32, [ctypes.POINTER(SgConfig), _i32, _i32, _i32]),
+    "sg_config_workspace_bytes": (_sz, [ctypes.POINTER(SgConfig), _i32, _i32]),
+    "sg_tuned_table": (_i32, [ctypes.POINTER(ctypes.POINTER(SgTableEntry))]),
+    "sg_set_table_override": (_i32, [ctypes.POINTER(SgTableEntry), _i32]),
 }
 
 # Per-GPU scratch of kda_projection_noalloc (SG_NOALLOC_SCRATCH_BYTES).

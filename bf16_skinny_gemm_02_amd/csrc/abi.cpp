@@ -53,11 +53,6 @@ int check_workspace(void* ws, size_t ws_bytes, size_t need) {
   return SG_OK;
 }
 
-bool same_config(const sg_config_t& a, const sg_config_t& b) {
-  return a.kind == b.kind && a.m_tile == b.m_tile && a.rows == b.rows && a.waves == b.waves &&
-         a.k_split == b.k_split && a.grid == b.grid;
-}
-
 bool is_mfma(int kind) {
   return kind == SG_KIND_MFMA_TILE || kind == SG_KIND_MFMA_WAVESPLIT || kind == SG_KIND_MFMA_BLOCK;
 }
@@ -72,7 +67,7 @@ bool hosts_fb(const sg_config_t& f, int rank, int n_b) {
   if (f.kind == SG_KIND_GEMV_ROW || f.kind == SG_KIND_GEMV_SPLITK) {
     if (f.waves != 4 || f.m_tile != 1) return false;
     producers = static_cast<int64_t>(f.grid) * f.waves;
-  } else if (f.kind == SG_KIND_MFMA_WAVESPLIT) {
+  } else if (f.kind == SG_KIND_MFMA_WAVESPLIT && f.rows == 16) {  // one-fragment instances
     producers = f.grid;
   } else {
     return false;
@@ -136,9 +131,13 @@ int validate_gemm(const sg_bf16* A, int64_t lda, const sg_bf16* W, int64_t ldw, 
   }
   if ((st = check_output2(C, ldc, N)) != SG_OK) return st;
   if (R != nullptr && (st = check_output2(R, ldr, N)) != SG_OK) return st;
-  if (user_cfg != nullptr && !same_config(*user_cfg, *cfg)) return SG_ERR_UNSUPPORTED;
+  if (user_cfg != nullptr) {
+    if (sg_config_supported(user_cfg, M, N, K) != SG_OK) return SG_ERR_UNSUPPORTED;
+    *cfg = *user_cfg;
+  }
   if (!spans_ok(M, lda, K) || !spans_ok(kMaxTileRows, ldw, K)) return SG_ERR_UNSUPPORTED;
-  return check_workspace(ws, ws_bytes, sg_workspace_bytes(SG_OP_GEMM, M, N, K));
+  return check_workspace(ws, ws_bytes, user_cfg != nullptr ? sg_config_workspace_bytes(cfg, M, N)
+                                                           : sg_workspace_bytes(SG_OP_GEMM, M, N, K));
 }
 
 // The F_A/beta stage configuration of kda_fab_fb_proj (the table's choice,

@@ -11,6 +11,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "skinny_gemm.h"
 
 namespace {
@@ -48,13 +50,20 @@ constexpr int kPairWgs = 256;
 constexpr int kFabGemvSplit = 7;
 // Most K-ranges of the standalone F_A/beta rows (the F_B stage's batch).
 constexpr int kFabMaxSplit = 8;
-// Largest M for which the two-stream projection is worth its fork/join.  On
-// MI355X the concurrent schedule measured slower than the single-stream one
-// (two segments in one launch, then F_B) at every decode M from 1 to 64:
-// the event pair costs more than the overlap recovers, and the LDS-resident
-// main kernel leaves no room beside it for the aux branch's workgroups.  The
-// gate therefore stays closed; the concurrent path remains available.
-constexpr int kOverlapMaxTokens = 0;
+// The measured table (tuned_table.inc, written by the tuner from its measured
+// table, tuned_table.json): per (N, K) and range of M, the configuration that
+// measured fastest on MI355X among the candidates the kernels support, and
+// the overlap gate derived from timing both projection schedules.
+#include "tuned_table.inc"
+// Largest M for which the two-stream projection is worth its fork/join: the
+// largest M up to which the fork/join schedule measured faster than the
+// single-stream one at every M (0: it never did on MI355X).
+constexpr int kOverlapMaxTokens = kTunedOverlapMaxTokens;
+constexpr int kTunedCount = static_cast<int>(sizeof(kTunedTable) / sizeof(kTunedTable[0]));
+// Process-wide override (sg_set_table_override), consulted before the table.
+constexpr int kMaxOverride = 64;
+sg_table_entry_t g_override[kMaxOverride];
+std::atomic<int> g_override_n{0};
 // Bytes at the start of a kda_fab_fb_proj(_fused) workspace: the hand-off
 // header of the one-launch F_A/beta -> F_B path (4096 producer flags and 512
 // consumer cursors, uint32), then the partials.
@@ -91,11 +100,156 @@ int mfma_split(int tiles, int ksteps, int min_steps) {
 }
 
 
+// m_tile and grid of a configuration with the given kind, rows, waves and
+// k_split for an M x N problem (the table entries leave them implicit).
+int m_tile_for(int kind, int waves, int M) {
+  switch (kind) {
+    case SG_KIND_MFMA_WAVESPLIT: return 4 * ceil_div(M, 4);
+    case SG_KIND_MFMA_TILE: return waves == 2 ? 4 * ceil_div(M, 4) : 16 * ceil_div(M, 16);
+    case SG_KIND_MFMA_BLOCK: return kBlockM * ceil_div(M, kBlockM);
+    default: return M;
+  }
+}
+
+int grid_for(const sg_config_t& c, int M, int N) {
+  const int S = c.k_split > 0 ? c.k_split : 1;
+  switch (c.kind) {
+    case SG_KIND_GEMV_ROW:
+    case SG_KIND_GEMV_SPLITK: return ceil_div(N, c.waves * c.rows) * S;
+    case SG_KIND_GEMV_SMALLK: return ceil_div(N, c.waves * c.rows);
+    case SG_KIND_MFMA_BLOCK: return ceil_div(N, kBlockRows) * ceil_div(M, kBlockM) * S;
+    default: return ceil_div(N, c.rows) * S;
+  }
+}
+
+sg_config_t from_entry(const sg_table_entry_t& e, int M, int N) {
+  sg_config_t c;
+  memset(&c, 0, sizeof c);
+  c.kind = e.kind;
+  c.rows = e.rows;
+  c.waves = e.waves;
+  c.k_unroll = e.k_unroll;
+  c.k_split = e.k_split;
+  c.nt_weights = 1;
+  c.m_tile = m_tile_for(c.kind, c.waves, M);
+  c.grid = grid_for(c, M, N);
+  return c;
+}
+
+int rule_select(int M, int N, int K, sg_config_t* out);
+
+// Whether the kernels can run configuration c on an M x N x K problem (an
+// instance exists for its kind, waves, rows, ring and activation tile; a
+// GEMV K-range fits the steps a wave holds).  The small-K GEMV has no free
+// parameter: only the rule's own configuration.
+bool supported(const sg_config_t& c, int M, int N, int K) {
+  if (M < 1 || M > 256 || N < 1 || K < 8 || K % 8 != 0) return false;
+  if (c.nt_weights != 1 || c.k_split < 1) return false;
+  if (c.m_tile != m_tile_for(c.kind, c.waves, M) || c.grid != grid_for(c, M, N)) return false;
+  const int ksteps = ceil_div(K, 32);
+  switch (c.kind) {
+    case SG_KIND_GEMV_ROW:
+    case SG_KIND_GEMV_SPLITK: {
+      const int steps = ceil_div(K / 8, 64);
+      const int depth = c.rows == 1 ? kGemvDepth : (c.rows == 4 ? kGemvDepth4 : kGemvDepth7);
+      return M == 1 && c.waves == kWaves && (c.rows == 1 || c.rows == 4 || c.rows == 7) &&
+             c.k_unroll == kGemvDepth && c.k_split <= steps &&
+             effective_split(steps, c.k_split) == c.k_split && ceil_div(steps, c.k_split) <= depth;
+    }
+    case SG_KIND_GEMV_SMALLK: {
+      sg_config_t r;
+      if (rule_select(M, N, K, &r) != SG_OK) return false;
+      return memcmp(&r, &c, sizeof r) == 0;
+    }
+    case SG_KIND_MFMA_WAVESPLIT:
+      if (M > 16 || c.waves != 4) return false;
+      // 2-slot rings are built for 9 <= M <= 16 only; two fragments with 3.
+      if (!((c.rows == 16 && (c.k_unroll == kSplitRing || (c.k_unroll == kSplitRing2 && M > 8))) ||
+            (c.rows > 16 && c.rows <= kSplitWideRows && c.rows % 4 == 0 && c.k_unroll == kSplitRing)))
+        return false;
+      break;
+    case SG_KIND_MFMA_TILE:
+      if (!((c.waves == 2 && c.rows == 32 && c.k_unroll == kWideRing && M <= 16) ||
+            (c.waves == 4 && c.rows == 64 && c.k_unroll == kTileRing && M >= 17 && M <= 64)))
+        return false;
+      break;
+    case SG_KIND_MFMA_BLOCK:
+      if (c.waves != 4 || c.rows != kBlockRows || c.k_unroll != kBlockRing || M < 17) return false;
+      break;
+    default:
+      return false;
+  }
+  return c.k_split <= ksteps && effective_split(ksteps, c.k_split) == c.k_split;
+}
+
+// The first entry of `t` that covers (M, N, K) and whose configuration the
+// kernels support there.
+bool lookup(const sg_table_entry_t* t, int n, int M, int N, int K, sg_config_t* out) {
+  for (int i = 0; i < n; ++i) {
+    const sg_table_entry_t& e = t[i];
+    if (e.N != N || e.K != K || M < e.m_lo || M > e.m_hi) continue;
+    const sg_config_t c = from_entry(e, M, N);
+    if (!supported(c, M, N, K)) continue;
+    *out = c;
+    return true;
+  }
+  return false;
+}
+
 }  // namespace
 
 extern "C" int sg_select(int M, int N, int K, int has_residual, sg_config_t* out) {
   (void)has_residual;
   if (out == nullptr) return SG_ERR_INVALID_ARG;
+  const int st = rule_select(M, N, K, out);
+  if (st != SG_OK || out->kind == SG_KIND_NONE) return st;
+  // The override, then the measured table, replace the rule's choice where
+  // they cover the shape.
+  const int n_over = g_override_n.load(std::memory_order_acquire);
+  if (n_over > 0 && lookup(g_override, n_over, M, N, K, out)) return SG_OK;
+  lookup(kTunedTable, kTunedCount, M, N, K, out);
+  return SG_OK;
+}
+
+extern "C" int sg_config_supported(const sg_config_t* cfg, int M, int N, int K) {
+  if (cfg == nullptr || M < 0 || N < 0 || K < 0) return SG_ERR_INVALID_ARG;
+  return supported(*cfg, M, N, K) ? SG_OK : SG_ERR_UNSUPPORTED;
+}
+
+extern "C" size_t sg_config_workspace_bytes(const sg_config_t* cfg, int M, int N) {
+  if (cfg == nullptr || M <= 0 || N <= 0) return 0;
+  if (cfg->k_split <= 1 || cfg->kind == SG_KIND_GEMV_SMALLK) return 0;
+  const size_t plane = static_cast<size_t>(M) * static_cast<size_t>(N) * sizeof(float);
+  return (static_cast<size_t>(cfg->k_split) * plane + 255) & ~static_cast<size_t>(255);
+}
+
+extern "C" int sg_tuned_table(const sg_table_entry_t** entries) {
+  // A table with no entries is compiled as one sentinel entry of N = 0
+  // (which no problem matches).
+  const int n = (kTunedCount == 1 && kTunedTable[0].N == 0) ? 0 : kTunedCount;
+  if (entries != nullptr) *entries = kTunedTable;
+  return n;
+}
+
+extern "C" int sg_set_table_override(const sg_table_entry_t* entries, int n) {
+  if (n < 0 || n > kMaxOverride || (n > 0 && entries == nullptr)) return SG_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i) {
+    const sg_table_entry_t& e = entries[i];
+    if (e.N < 1 || e.K < 8 || e.K % 8 != 0 || e.m_lo < 1 || e.m_hi < e.m_lo || e.m_hi > 256)
+      return SG_ERR_INVALID_ARG;
+    for (int M = e.m_lo; M <= e.m_hi; ++M)
+      if (!supported(from_entry(e, M, e.N), M, e.N, e.K)) return SG_ERR_UNSUPPORTED;
+  }
+  g_override_n.store(0, std::memory_order_release);
+  for (int i = 0; i < n; ++i) g_override[i] = entries[i];
+  g_override_n.store(n, std::memory_order_release);
+  return SG_OK;
+}
+
+namespace {
+
+// The rule: the configuration by shape alone.
+int rule_select(int M, int N, int K, sg_config_t* out) {
   if (M < 0 || N < 0 || K < 0) return SG_ERR_INVALID_ARG;
   if (K % 8 != 0) return SG_ERR_UNSUPPORTED;
   if (M > 256) return SG_ERR_UNSUPPORTED;
@@ -210,6 +364,8 @@ extern "C" int sg_select(int M, int N, int K, int has_residual, sg_config_t* out
   *out = c;
   return SG_OK;
 }
+
+}  // namespace
 
 extern "C" int sg_overlap_max_tokens(void) { return kOverlapMaxTokens; }
 

@@ -125,15 +125,54 @@ enum {
     SG_OP_LATENT_TAIL = 2   /* latent_moe_tail:   N = d_hidden, K = d_latent  */
 };
 
-/* Host-only, pure: the configuration the library uses for C[M,N] = A[M,K] *
+/* Host-only: the configuration the library uses for C[M,N] = A[M,K] *
  * W[N,K]^T.  Plays the role of ShapeDynamicSkinnyGemm._config(m, n, k)
  * [P1 skinny_gemm.py] with a table of this library's own (the reference's
- * values were tuned for other hardware).  has_residual does not change the
- * choice today; it is part of the key so that it may.
+ * values were tuned for other hardware): a rule by shape, replaced where a
+ * measured table entry covers (N, K, M) (sg_tuned_table; the analogue of the
+ * autotuned KDA_QKVG_CONFIGS [P3 low_latency_gemm.py autotune_kda_qkvg]),
+ * and before that where an entry of the caller's override covers it
+ * (sg_set_table_override).  has_residual does not change the choice today;
+ * it is part of the key so that it may.
  * Returns SG_OK and fills *out, SG_ERR_INVALID_ARG for negative sizes or a
  * NULL out, SG_ERR_UNSUPPORTED for K % 8 != 0 or M > 256.  An empty problem
  * (M == 0 or N == 0) returns SG_OK with kind SG_KIND_NONE. */
 int sg_select(int M, int N, int K, int has_residual, sg_config_t *out);
+
+/* One entry of the measured configuration table: problems with this N and K
+ * and m_lo <= M <= m_hi take this kind, rows, waves, k_unroll and k_split
+ * (m_tile and grid follow from them and M). */
+typedef struct {
+    int32_t N, K, m_lo, m_hi;
+    int32_t kind, rows, waves, k_unroll, k_split;
+} sg_table_entry_t;
+
+/* Host-only, pure: SG_OK if the kernels can run *cfg on an M x N x K
+ * problem (an instance exists for its kind, waves, rows, ring slots and
+ * activation tile, m_tile and grid are the ones that follow from it, the K
+ * split has no empty range, a GEMV K-range fits the steps a wave holds; the
+ * small-K kind only as sg_select gives it), SG_ERR_UNSUPPORTED if not,
+ * SG_ERR_INVALID_ARG for a NULL cfg or negative sizes. */
+int sg_config_supported(const sg_config_t *cfg, int M, int N, int K);
+
+/* Host-only, pure: workspace bytes skinny_gemm needs with configuration *cfg
+ * at M x N (fp32 split-K partials, 0 without a K split or for a NULL cfg). */
+size_t sg_config_workspace_bytes(const sg_config_t *cfg, int M, int N);
+
+/* Host-only, pure: the compiled measured table.  Returns its number of
+ * entries and, if entries != NULL, points *entries at them (static storage,
+ * owned by the library). */
+int sg_tuned_table(const sg_table_entry_t **entries);
+
+/* Host-only: replaces the process-wide override table (n = 0 clears it),
+ * which sg_select consults before the measured table; for a tuner that
+ * times candidate configurations through the entry points.  Every entry must
+ * satisfy sg_config_supported for every M of its range (else
+ * SG_ERR_UNSUPPORTED, and the override is unchanged); n <= 64
+ * (SG_ERR_INVALID_ARG otherwise).  This is the library's one piece of
+ * mutable configuration: it must not change while other calls are in flight
+ * or being captured, and workspaces sized before a change may no longer fit. */
+int sg_set_table_override(const sg_table_entry_t *entries, int n);
 
 /* Host-only, pure: whether the two-stream KDA projection should be used, the
  * analogue of the gate in KimiK3DeltaAttention.forward [P3 kda.py]:
@@ -144,9 +183,10 @@ int sg_select(int M, int N, int K, int has_residual, sg_config_t *out);
 int sg_overlap_gate(int M, int x_contiguous, int have_aux_stream, int have_events, int enabled);
 
 /* The largest M for which sg_overlap_gate() opens (the analogue of
- * KDA_PROJECTION_OVERLAP_MAX_TOKENS [P3 low_latency_gemm.py]).  Set from
- * measurement on MI355X: 0, the single-stream schedule was faster at every
- * M tried (1..64), so the gate stays closed. */
+ * KDA_PROJECTION_OVERLAP_MAX_TOKENS [P3 low_latency_gemm.py]), compiled with
+ * the measured table: the largest M up to which the two-stream schedule
+ * measured faster at every M on MI355X (0: it never did, the gate stays
+ * closed). */
 int sg_overlap_max_tokens(void);
 
 /* Bytes of device workspace the operation needs at this shape (0 if none).
@@ -206,11 +246,12 @@ const char *sg_version(void);
 /* Generic skinny GEMM [P1 _skinny_gemm.py CuteSkinnyGemm]:
  *   C[m,n] = bf16( sum_k A[m,k] * W[n,k] + R[m,n] )   (R omitted when NULL)
  * A [M,K] lda, W [N,K] ldw, R [M,N] ldr (nullable), C [M,N] ldc.
- * cfg: NULL = sg_select(M, N, K, R != NULL); a caller-supplied config must
- * equal the one sg_select returns for that shape in every field except
- * k_unroll / nt_weights, which are ignored (kernels are compiled per table
- * entry), else SG_ERR_UNSUPPORTED.  C may alias R exactly (in-place add);
- * any other overlap of C with an input is undefined. */
+ * cfg: NULL = sg_select(M, N, K, R != NULL); otherwise any configuration
+ * that sg_config_supported accepts for this shape (else SG_ERR_UNSUPPORTED),
+ * with ws of at least sg_config_workspace_bytes(cfg, M, N) bytes (the
+ * analogue of passing a config to shape_dynamic_skinny_gemm [P1]).  C may
+ * alias R exactly (in-place add); any other overlap of C with an input is
+ * undefined. */
 int skinny_gemm(const sg_bf16 *A, int64_t lda, const sg_bf16 *W, int64_t ldw,
                 const sg_bf16 *R, int64_t ldr, sg_bf16 *C, int64_t ldc,
                 int M, int N, int K, const sg_config_t *cfg,

@@ -7,6 +7,16 @@ own: the reference's ShapeDynamicSkinnyGemm._config in "Kimi K3 support, phase
 "Overlap low-M TP8 KDA projections", were tuned for other hardware).  The C++
 dispatcher must agree with it field by field.
 
+The measured table: bf16_skinny_gemm_02_amd/tuned_table.json (written by the
+tuner from its own measurements; data, not code).  Where one of its chosen
+entries has this N and K and m_lo <= M <= m_hi, the entry's kind, rows,
+waves, k_unroll and k_split replace the rule's, with m_tile 4 ceil(M / 4)
+(MFMA_WAVESPLIT; MFMA_TILE with 2 waves), 16 ceil(M / 16) (MFMA_TILE with 4
+waves), 128 ceil(M / 128) (MFMA_BLOCK) or M (the GEMV kinds), and grid
+ceil(N / (waves rows)) k_split (GEMV), ceil(N / 64) ceil(M / 128) k_split
+(BLOCK) or ceil(N / rows) k_split; the gate's OVERLAP_MAX_TOKENS is the
+table's overlap.max_tokens (0 without a table).
+
 Rule, for C[M,N] = A[M,K] W[N,K]^T:
   * M, N or K negative -> INVALID_ARG.  K not a multiple of 8 -> UNSUPPORTED.
     M > 256 -> UNSUPPORTED.  M == 0 or N == 0 -> kind NONE, every field 0.
@@ -72,7 +82,23 @@ from __future__ import annotations
 
 OK, INVALID_ARG, UNSUPPORTED = 0, -1, -2
 NONE, GEMV_ROW, GEMV_SPLITK, GEMV_SMALLK, MFMA_TILE, MFMA_WAVESPLIT, MFMA_BLOCK = 0, 1, 2, 3, 4, 5, 6
-OVERLAP_MAX_TOKENS = 0
+
+def _load_table():
+    import json
+    from pathlib import Path
+    path = Path(__file__).resolve().parent.parent / "bf16_skinny_gemm_02_amd" / "tuned_table.json"
+    if not path.exists():
+        return [], 0
+    t = json.loads(path.read_text())
+    entries = []
+    for b in t["buckets"]:
+        e = {"N": b["N"], "K": b["K"], "m_lo": b["m_lo"], "m_hi": b["m_hi"]}
+        e.update({f: int(b["chosen"][f]) for f in ("kind", "rows", "waves", "k_unroll", "k_split")})
+        entries.append(e)
+    return entries, int(t["overlap"]["max_tokens"])
+
+
+TABLE, OVERLAP_MAX_TOKENS = _load_table()
 
 FIELDS = ("kind", "m_tile", "rows", "waves", "k_split", "k_unroll", "grid", "nt_weights")
 
@@ -158,7 +184,32 @@ def select(M: int, N: int, K: int, has_residual: bool = False):
         ks = msplit(tiles, 8)
         cfg.update(kind=MFMA_BLOCK, m_tile=128 * _cdiv(M, 128), rows=64, k_unroll=3, k_split=ks,
                    grid=tiles * ks)
+    for e in TABLE:
+        if e["N"] == N and e["K"] == K and e["m_lo"] <= M <= e["m_hi"]:
+            return OK, _from_entry(e, M, N)
     return OK, cfg
+
+
+def _from_entry(e: dict, M: int, N: int) -> dict:
+    kind, rows, waves, S = e["kind"], e["rows"], e["waves"], e["k_split"]
+    if kind == MFMA_WAVESPLIT or (kind == MFMA_TILE and waves == 2):
+        m_tile = 4 * _cdiv(M, 4)
+    elif kind == MFMA_TILE:
+        m_tile = 16 * _cdiv(M, 16)
+    elif kind == MFMA_BLOCK:
+        m_tile = 128 * _cdiv(M, 128)
+    else:
+        m_tile = M
+    if kind in (GEMV_ROW, GEMV_SPLITK):
+        grid = _cdiv(N, waves * rows) * S
+    elif kind == GEMV_SMALLK:
+        grid = _cdiv(N, waves * rows)
+    elif kind == MFMA_BLOCK:
+        grid = _cdiv(N, 64) * _cdiv(M, 128) * S
+    else:
+        grid = _cdiv(N, rows) * S
+    return dict(kind=kind, m_tile=m_tile, rows=rows, waves=waves, k_split=S, k_unroll=e["k_unroll"],
+                grid=grid, nt_weights=1)
 
 
 def overlap_gate(M: int, x_contiguous: bool, have_aux: bool, have_events: bool,

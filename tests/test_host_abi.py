@@ -256,9 +256,18 @@ def test_skinny_gemm_validation(lib):
     assert _gemm(lib, lda=68) == E.SG_ERR_MISALIGNED
     assert _gemm(lib, C=ctypes.c_void_p(0x30001)) == E.SG_ERR_MISALIGNED
     assert _gemm(lib, R=ctypes.c_void_p(0x40001)) == E.SG_ERR_MISALIGNED
-    # a config that is not the table's choice
+    # a config the kernels cannot run (no 1-row MFMA tile), and one they can
+    # whose K split needs a workspace
     bad = _lib.SgConfig(kind=4, m_tile=16, rows=1, waves=4, k_split=1, k_unroll=8, grid=2)
     assert _gemm(lib, cfg=ctypes.byref(bad)) == E.SG_ERR_UNSUPPORTED
+    alt = _lib.SgConfig(kind=5, m_tile=4, rows=16, waves=4, k_split=2, k_unroll=3, grid=4,
+                        nt_weights=1)
+    assert lib.sg_config_supported(ctypes.byref(alt), 4, 32, 64) == E.SG_OK
+    assert _gemm(lib, cfg=ctypes.byref(alt)) == E.SG_ERR_WORKSPACE
+    need = lib.sg_config_workspace_bytes(ctypes.byref(alt), 4, 32)
+    assert need == 2 * 4 * 32 * 4 + 0  # one 256-byte rounded plane pair: 1024 bytes
+    assert _gemm(lib, cfg=ctypes.byref(alt), ws=ctypes.c_void_p(0x50000), ws_bytes=need - 1) == \
+        E.SG_ERR_WORKSPACE
     # a split-K shape without workspace
     st, cfg = selection.select(4, 32, 4096)
     assert cfg["k_split"] > 1
