@@ -288,6 +288,9 @@ def measure_bucket(shape, lo, hi, stream, reps, log):
         eff = tuple(_effective(shape, entry, M) for M in points)
         if eff in seen:  # the serving entry point runs an already measured configuration
             sg_set_table_override([])
+            same = seen[eff]
+            results.append({"cfg": c, "same_as": same["cfg"], "us": same["us"],
+                            "total_us": same["total_us"]})
             continue
         us = []
         try:
@@ -299,8 +302,8 @@ def measure_bucket(shape, lo, hi, stream, reps, log):
             log(f"[tune] {shape.name} M={lo}..{hi} {c}: {e}")
         finally:
             sg_set_table_override([])
-        seen[eff] = c
         results.append({"cfg": c, "us": us, "total_us": total})
+        seen[eff] = results[-1]
     chosen = choose(results, incumbent)
     return {"shape": shape.name, "N": shape.N, "K": shape.K, "m_lo": lo, "m_hi": hi,
             "measured_at": list(points), "incumbent": incumbent, "chosen": chosen,
@@ -370,7 +373,8 @@ def main():
     sg_set_table_override([])
     table = {
         "generated_by": "python -m bf16_skinny_gemm_02_amd.tune",
-        "device": torch.cuda.get_device_name(device),
+        "device": f"{torch.cuda.get_device_name(device)} "
+                  f"({torch.cuda.get_device_properties(device).gcnArchName})",
         "date": time.strftime("%Y-%m-%d"),
         "margin": MARGIN,
         "timing": f"hipGraph of R calls over R weight copies (>= 512 MiB, at most {MAX_COPIES}), "
