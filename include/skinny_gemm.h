@@ -45,12 +45,15 @@
  *    empty N) is a valid no-op that returns SG_OK.
  *  - Every output element is written on every successful path, and nothing
  *    outside the outputs and the workspace is written.
- *  - State: the library allocates nothing.  Its only process state is, per
+ *  - State: the library allocates nothing.  Its process state is, per
  *    kernel instance and per device, a flag that the kernel's dynamic-LDS
- *    limit has been raised (hipFuncSetAttribute, on first use).  The flag is
- *    kept for the device current at the call, so a call must be made with
- *    its stream's device current (as torch does).  The entry points are
- *    thread-safe.
+ *    limit has been raised (hipFuncSetAttribute, on first use; kept for the
+ *    device current at the call, so a call must be made with its stream's
+ *    device current, as torch does), the per-device address of the
+ *    no-allocation scratch array (kda_projection_noalloc), and the
+ *    configuration override a tuner may install (sg_set_table_override;
+ *    empty unless set).  The entry points are thread-safe as long as the
+ *    override does not change during calls.
  */
 #ifndef SKINNY_GEMM_H
 #define SKINNY_GEMM_H
