@@ -195,12 +195,13 @@ ROOFLINE_M = 8   # the projection call the roofline leg times (two launches at 2
 # HBM traffic of one projection call at M = ROOFLINE_M (both of its launches) from two rocprofv3
 # --pmc runs of `bench.py --counters` (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 KiB per dispatch;
 # factors from a 256 MiB device copy), summarised with the commands in
-# profiles/kda_projection_m8_m64_pmc_traffic.md.  Valid only for the sources it was measured on:
+# profiles/kda_projection_and_tail_pmc_traffic.md.  Valid only for the sources it was measured on:
 # any change to them reports traffic as null until the counters are taken again.
 TRAFFIC_SOURCES = ("bf16_skinny_gemm_02_amd/csrc/mfma.hip", "bf16_skinny_gemm_02_amd/csrc/gemv.hip",
                    "bf16_skinny_gemm_02_amd/csrc/smallk.hip", "bf16_skinny_gemm_02_amd/csrc/sg_device.h",
-                   "bf16_skinny_gemm_02_amd/csrc/dispatch.cpp", "bf16_skinny_gemm_02_amd/csrc/abi.cpp")
-TRAFFIC_PMC = {"sources_sha256": None, "bytes_per_call": None}
+                   "bf16_skinny_gemm_02_amd/csrc/dispatch.cpp", "bf16_skinny_gemm_02_amd/csrc/abi.cpp",
+                   "bf16_skinny_gemm_02_amd/csrc/tuned_table.inc")
+TRAFFIC_PMC = {"sources_sha256": "6006cd95f4ce89c48c263bca92d8583f2b98d3090e662de84202c7492b5fd75d", "bytes_per_call": 64309372}
 
 
 def sources_sha256():
