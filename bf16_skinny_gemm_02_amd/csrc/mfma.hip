@@ -160,7 +160,8 @@ __device__ __forceinline__ Res4 load_res4(const MfmaArgs& g, int m, int n0, bool
 // Stores the four outputs (m, n0 .. n0+3) a lane holds.
 // Four consecutive outputs go out as one 16-byte (partials) or 8-byte (bf16)
 // store when they lie in one row of one output and the address is aligned;
-// otherwise element by element.
+// otherwise element by element.  Partials are stored non-temporally: every
+// workgroup writes them at its very end and the next launch reads them once.
 // COHERENT (the F_A/beta segment of a one-launch F_A/beta -> F_B call): the
 // partials go out as device-coherent stores for the F_B role to read.
 // Rows n >= nlim (the next workgroup's, or past N) are not stored.
@@ -179,7 +180,7 @@ __device__ __forceinline__ void store4(const MfmaArgs& g, const f32x4& acc, int 
       return;
     }
     if (whole && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
-      *reinterpret_cast<f32x4*>(p) = acc;
+      __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(p));
       return;
     }
   } else if (whole && !(g.n_split > 0 && n0 < g.n_split && n0 + 3 >= g.n_split)) {
