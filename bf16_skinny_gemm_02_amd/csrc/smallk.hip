@@ -152,7 +152,9 @@ __device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
     //  * kRedGroups: groups of four requested together, then the remainder
     //    one by one (fewest registers: the many-workgroup reduction role of
     //    the F_B launch at larger M);
-    //  * kRedPredicated: predicated groups of four (the reduction launch);
+    //  * kRedPredicated: predicated groups of four, non-temporal (the
+    //    reduction launch: each partial is read once; in the F_B launch's
+    //    roles non-temporal loads measured slower);
     //  * kRedStraight: straight-line batches of kRedBatch whose loads are
     //    unconditional (indices past S - 1 repeat the last split) and kept
     //    ahead of the first addition by a scheduling barrier, one memory
@@ -182,7 +184,9 @@ __device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
         f32x4 t[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          t[k] = (s + k < g.S) ? p[(s + k) * plane4] : f32x4{0.f, 0.f, 0.f, 0.f};
+          t[k] = (s + k < g.S) ? (MODE == kRedPredicated ? __builtin_nontemporal_load(p + (s + k) * plane4)
+                                                         : p[(s + k) * plane4])
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           if (s + k < g.S)
