@@ -115,7 +115,8 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 // in the epilogue.  RES (a kernel instance launched for a segment with a
 // residual and bf16 output): two 8-byte buffer loads of the 8-byte-aligned
 // blocks that hold the four values (n0 is a multiple of 4, so they span at
-// most two), then a funnel shift, whatever the residual's 2-byte alignment.
+// most two; when they fill one, both loads read it), then a funnel shift,
+// whatever the residual's 2-byte alignment.
 // The buffer runs from the 8-byte boundary at or below the residual to its
 // end rounded up to 8 bytes: an aligned 8-byte block never crosses a page,
 // and every block lies wholly inside or outside the buffer.  Rows past M, a
@@ -139,7 +140,8 @@ __device__ __forceinline__ Res4 load_res4(const MfmaArgs& g, int m, int n0, bool
     const rsrc_t rr = make_rsrc(reinterpret_cast<const void*>(rb), bytes);
     const uint32_t a = static_cast<uint32_t>(res - rb + (static_cast<int64_t>(m) * g.ldr + n0) * 2);
     const uint32_t s0 = m < g.M ? (a & ~7u) : kOob;
-    const uint32_t s1 = m < g.M ? (a & ~7u) + 8u : kOob;
+    // the second block only when the values straddle two (else the first again: no extra line)
+    const uint32_t s1 = m < g.M ? (a & ~7u) + ((a & 7u) != 0u ? 8u : 0u) : kOob;
     const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, static_cast<int>(s0), 0, 0));
     const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, static_cast<int>(s1), 0, 0));
     const bool k = ((a >> 2) & 1u) != 0;  // the first value's word: 0 or 1 of the four
