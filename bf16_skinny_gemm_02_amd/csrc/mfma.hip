@@ -668,6 +668,46 @@ __global__ __launch_bounds__(kBlkWaves * kWave) void block_kernel(MfmaLaunch L) 
   }
   wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
 
+  // bf16 output with 16-byte aligned rows: the block goes through LDS in row
+  // order, so each output row leaves as whole 16-byte pieces (8 lanes per
+  // 128-byte row segment) instead of 8-byte pieces of 16 rows per store.
+  const bool rows16 = g.partial == nullptr && g.n_split <= 0 &&
+                      (reinterpret_cast<uintptr_t>(g.out) & 15u) == 0 && (g.ldc & 7) == 0;
+  if (rows16) {
+    constexpr int LD = kBlkRows + 8;  // bf16 per LDS row (padded against bank conflicts)
+    uint16_t* tl = reinterpret_cast<uint16_t*>(lds);
+    __syncthreads();  // every wave has finished reading the ring
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ml = xr0 + 16 * j + rl, nl = wr0 + 16 * i + 4 * kg;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = acc[i][j][e] + ((RES && g.res != nullptr) ? bf16_to_f32(res[i][j].v[e]) : 0.f);
+        uint2 pk;
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(tl + ml * LD + nl) = pk;
+      }
+    __syncthreads();
+    constexpr int kPer = kBlkRows / 8;  // 16-byte pieces per row
+    for (int c = static_cast<int>(threadIdx.x); c < kBlkM * kPer; c += kBlkWaves * kWave) {
+      const int ml = c / kPer, nl = (c - ml * kPer) * 8;
+      const int m = m0 + ml, n = row0 + nl;
+      if (m >= g.M || n >= g.N) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(tl + ml * LD + nl);
+      uint16_t* dst = g.out + static_cast<int64_t>(m) * g.ldc + n;
+      if (n + 7 < g.N) {
+        *reinterpret_cast<u32x4*>(dst) = v;
+      } else {
+        const uint16_t* sv = tl + ml * LD + nl;
+        for (int e = 0; e < g.N - n; ++e) dst[e] = sv[e];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
