@@ -570,7 +570,11 @@ __device__ __forceinline__ void block_coords(int tile, int ntiles, int mblocks, 
   nt = grp * 8 + (r - mb * nrem);
 }
 
-template <int C, bool RES>
+// RES: 0 no residual; 1 the residual in the MFMA layout (load_res4); 2 a
+// residual with 16-byte aligned rows, read in row order (16-byte pieces of
+// whole rows, the pieces each thread stores) and added in the row-order
+// epilogue.
+template <int C, int RES>
 __global__ __launch_bounds__(kBlkWaves * kWave) void block_kernel(MfmaLaunch L) {
   extern __shared__ u32x4 lds[];
   int tile, split;
@@ -637,7 +641,25 @@ __global__ __launch_bounds__(kBlkWaves * kWave) void block_kernel(MfmaLaunch L) 
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      res[i][j] = load_res4<RES>(g, m0 + xr0 + 16 * j + rl, row0 + wr0 + 16 * i + 4 * kg);
+      res[i][j] = load_res4<RES == 1>(g, m0 + xr0 + 16 * j + rl, row0 + wr0 + 16 * i + 4 * kg);
+  constexpr int kPer = kBlkRows / 8;                       // 16-byte pieces per block row
+  constexpr int kRowPieces = kBlkM * kPer / (kBlkWaves * kWave);  // per thread
+  u32x4 rrow[RES == 2 ? kRowPieces : 1];
+  if constexpr (RES == 2) {
+    // Buffer from the residual to its end rounded up to 16 bytes: every
+    // piece lies wholly inside or outside it, and none crosses a page.
+    const int64_t span = (static_cast<int64_t>(g.M - 1) * g.ldr + g.N) * 2;
+    const rsrc_t rres = make_rsrc(g.res, static_cast<uint32_t>((span + 15) & ~static_cast<int64_t>(15)));
+#pragma unroll
+    for (int q = 0; q < kRowPieces; ++q) {
+      const int c = static_cast<int>(threadIdx.x) + q * kBlkWaves * kWave;
+      const int ml = c / kPer, nl = (c - ml * kPer) * 8;
+      const int m = m0 + ml, n = row0 + nl;
+      rrow[q] = buf_load(rres, (m < g.M && n < g.N)
+                                   ? static_cast<uint32_t>((static_cast<int64_t>(m) * g.ldr + n) * 2)
+                                   : kOob);
+    }
+  }
 
 #pragma unroll
   for (int q = 0; q < C - 1; ++q) issue(q);
@@ -673,6 +695,40 @@ __global__ __launch_bounds__(kBlkWaves * kWave) void block_kernel(MfmaLaunch L) 
   // 128-byte row segment) instead of 8-byte pieces of 16 rows per store.
   const bool rows16 = g.partial == nullptr && g.n_split <= 0 &&
                       (reinterpret_cast<uintptr_t>(g.out) & 15u) == 0 && (g.ldc & 7) == 0;
+  if constexpr (RES == 2) {
+    // (the launcher picks RES 2 only for 16-byte aligned output rows)
+    constexpr int LDF = kBlkRows + 4;  // fp32 per LDS row (padded against bank conflicts)
+    float* tf = reinterpret_cast<float*>(lds);
+    __syncthreads();  // every wave has finished reading the ring
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(tf + (xr0 + 16 * j + rl) * LDF + wr0 + 16 * i + 4 * kg) = acc[i][j];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kRowPieces; ++q) {
+      const int c = static_cast<int>(threadIdx.x) + q * kBlkWaves * kWave;
+      const int ml = c / kPer, nl = (c - ml * kPer) * 8;
+      const int m = m0 + ml, n = row0 + nl;
+      if (m >= g.M || n >= g.N) continue;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(tf + ml * LDF + nl);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(tf + ml * LDF + nl + 4);
+      const u32x4 r = rrow[q];
+      u32x4 o;
+      o[0] = pack_bf16x2(a0[0] + bf16_lo(r[0]), a0[1] + bf16_hi(r[0]));
+      o[1] = pack_bf16x2(a0[2] + bf16_lo(r[1]), a0[3] + bf16_hi(r[1]));
+      o[2] = pack_bf16x2(a1[0] + bf16_lo(r[2]), a1[1] + bf16_hi(r[2]));
+      o[3] = pack_bf16x2(a1[2] + bf16_lo(r[3]), a1[3] + bf16_hi(r[3]));
+      uint16_t* dst = g.out + static_cast<int64_t>(m) * g.ldc + n;
+      if (n + 7 < g.N) {
+        *reinterpret_cast<u32x4*>(dst) = o;
+      } else {
+        for (int e = 0; e < g.N - n; ++e) dst[e] = static_cast<uint16_t>(o[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+    return;
+  }
   if (rows16) {
     constexpr int LD = kBlkRows + 8;  // bf16 per LDS row (padded against bank conflicts)
     uint16_t* tl = reinterpret_cast<uint16_t*>(lds);
@@ -685,7 +741,7 @@ __global__ __launch_bounds__(kBlkWaves * kWave) void block_kernel(MfmaLaunch L) 
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          v[e] = acc[i][j][e] + ((RES && g.res != nullptr) ? bf16_to_f32(res[i][j].v[e]) : 0.f);
+          v[e] = acc[i][j][e] + ((RES == 1 && g.res != nullptr) ? bf16_to_f32(res[i][j].v[e]) : 0.f);
         uint2 pk;
         pk.x = pack_bf16x2(v[0], v[1]);
         pk.y = pack_bf16x2(v[2], v[3]);
@@ -787,7 +843,7 @@ hipError_t launch_wsplit_fb(const MfmaLaunch& L, int XQ, int C, int wgs, hipStre
   }
 }
 
-template <int C, bool RES>
+template <int C, int RES>
 hipError_t launch_block_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
   auto kern = block_kernel<C, RES>;
   static std::atomic<bool> lds_set[kLdsAttrDevices];
@@ -984,8 +1040,15 @@ hipError_t launch_mfma_impl(const DotProblem* segs, const sg_config_t* cfgs, int
   }
   if (cfg.kind == SG_KIND_MFMA_BLOCK) {
     if (cfg.rows != kBlkRows || cfg.waves != kBlkWaves || cfg.m_tile % kBlkM != 0) return hipErrorInvalidValue;
-    if (cfg.k_unroll == 3) return res ? launch_block_inst<3, true>(L, wgs, s) : launch_block_inst<3, false>(L, wgs, s);
-    return hipErrorInvalidValue;
+    if (cfg.k_unroll != 3) return hipErrorInvalidValue;
+    // One segment with a residual, bf16 output and 16-byte aligned output and
+    // residual rows: the residual in row order.
+    const DotProblem& p0 = segs[0];
+    const bool rows16 = nseg == 1 && res && p0.n_split <= 0 &&
+                        (reinterpret_cast<uintptr_t>(p0.out) & 15u) == 0 && (p0.ldc & 7) == 0 &&
+                        (reinterpret_cast<uintptr_t>(p0.res) & 15u) == 0 && (p0.ldr & 7) == 0;
+    if (rows16) return launch_block_inst<3, 2>(L, wgs, s);
+    return res ? launch_block_inst<3, 1>(L, wgs, s) : launch_block_inst<3, 0>(L, wgs, s);
   }
   return hipErrorInvalidValue;
 }
