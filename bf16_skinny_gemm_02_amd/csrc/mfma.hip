@@ -113,15 +113,9 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 // requested when the kernel starts (before the ring's first chunks: loads
 // complete in issue order, so no chunk wait waits for them) and widened only
 // in the epilogue.  RES (a kernel instance launched for a segment with a
-// residual and bf16 output): two 8-byte buffer loads of the 8-byte-aligned
-// blocks that hold the four values (n0 is a multiple of 4, so they span at
-// most two; when they fill one, both loads read it), then a funnel shift,
-// whatever the residual's 2-byte alignment.
-// The buffer runs from the 8-byte boundary at or below the residual to its
-// end rounded up to 8 bytes: an aligned 8-byte block never crosses a page,
-// and every block lies wholly inside or outside the buffer.  Rows past M, a
-// lane that stores nothing (`active` false, uniform per wave) and a segment
-// without a residual read zeros and fetch nothing.  The loads are
+// residual and bf16 output): load4_bf16 (n0 is a multiple of 4).  Rows past
+// M, a lane that stores nothing (`active` false, uniform per wave) and a
+// segment without a residual read zeros and fetch nothing.  The loads are
 // unconditional: a load under a branch would get a wait for every load in
 // flight at the branch's end.  Without RES nothing is loaded.
 struct Res4 {
@@ -133,28 +127,8 @@ __device__ __forceinline__ Res4 load_res4(const MfmaArgs& g, int m, int n0, bool
   Res4 r = {{0, 0, 0, 0}};
   if constexpr (RES) {
     const bool use = g.res != nullptr && g.partial == nullptr && active;
-    const uintptr_t res = reinterpret_cast<uintptr_t>(g.res);
-    const uintptr_t rb = res & ~static_cast<uintptr_t>(7);
-    const int64_t span = static_cast<int64_t>(res - rb) + (static_cast<int64_t>(g.M - 1) * g.ldr + g.N) * 2;
-    const uint32_t bytes = use ? static_cast<uint32_t>((span + 7) & ~static_cast<int64_t>(7)) : 0u;
-    const rsrc_t rr = make_rsrc(reinterpret_cast<const void*>(rb), bytes);
-    const uint32_t a = static_cast<uint32_t>(res - rb + (static_cast<int64_t>(m) * g.ldr + n0) * 2);
-    const uint32_t s0 = m < g.M ? (a & ~7u) : kOob;
-    // the second block only when the values straddle two (else the first again: no extra line)
-    const uint32_t s1 = m < g.M ? (a & ~7u) + ((a & 7u) != 0u ? 8u : 0u) : kOob;
-    const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, static_cast<int>(s0), 0, 0));
-    const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, static_cast<int>(s1), 0, 0));
-    const bool k = ((a >> 2) & 1u) != 0;  // the first value's word: 0 or 1 of the four
-    const uint32_t bb = a & 3u;           // and its byte within it: 0 or 2
-    const uint32_t w0 = k ? lo[1] : lo[0];
-    const uint32_t w1 = k ? hi[0] : lo[1];
-    const uint32_t w2 = k ? hi[1] : hi[0];
-    const uint32_t v01 = __builtin_amdgcn_alignbyte(w1, w0, bb);
-    const uint32_t v23 = __builtin_amdgcn_alignbyte(w2, w1, bb);
-    r.v[0] = static_cast<uint16_t>(v01 & 0xFFFFu);
-    r.v[1] = static_cast<uint16_t>(v01 >> 16);
-    r.v[2] = static_cast<uint16_t>(v23 & 0xFFFFu);
-    r.v[3] = static_cast<uint16_t>(v23 >> 16);
+    load4_bf16(g.res, static_cast<int64_t>(g.M - 1) * g.ldr + g.N, static_cast<int64_t>(m) * g.ldr + n0,
+               use, m < g.M, r.v);
   }
   return r;
 }

@@ -59,6 +59,39 @@ __device__ __forceinline__ u32x4 buf_load(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
 }
 
+// Four consecutive bf16 values base[idx .. idx+3] of a buffer of `elems`
+// elements with any 2-byte alignment, as two 8-byte buffer loads of the
+// 8-byte-aligned blocks that hold them (the second only when they straddle
+// two): the buffer runs from the 8-byte boundary at or below `base` to its
+// end rounded up to 8 bytes, so every block lies wholly inside or outside it
+// and none crosses a page.  `use` false (uniform across the wave: it sizes
+// the buffer, which must stay in scalar registers) or `lane` false reads
+// zeros and fetches nothing.  Values past the end read zeros or are unused.
+__device__ __forceinline__ void load4_bf16(const uint16_t* base, int64_t elems, int64_t idx, bool use,
+                                           bool lane, uint16_t (&out)[4]) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(base);
+  const uintptr_t rb = b & ~static_cast<uintptr_t>(7);
+  const int64_t span = static_cast<int64_t>(b - rb) + elems * 2;
+  const rsrc_t rr = make_rsrc(reinterpret_cast<const void*>(rb),
+                              use ? static_cast<uint32_t>((span + 7) & ~static_cast<int64_t>(7)) : 0u);
+  const uint32_t a = static_cast<uint32_t>(static_cast<int64_t>(b - rb) + idx * 2);
+  const uint32_t s0 = lane ? (a & ~7u) : kOob;
+  const uint32_t s1 = lane ? (a & ~7u) + ((a & 7u) != 0u ? 8u : 0u) : kOob;
+  const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, static_cast<int>(s0), 0, 0));
+  const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rr, static_cast<int>(s1), 0, 0));
+  const bool k = ((a >> 2) & 1u) != 0;  // the first value's word in the first block: 0 or 1
+  const uint32_t bb = a & 3u;           // and its byte within it: 0 or 2
+  const uint32_t w0 = k ? lo[1] : lo[0];
+  const uint32_t w1 = k ? hi[0] : lo[1];
+  const uint32_t w2 = k ? hi[1] : hi[0];
+  const uint32_t v01 = __builtin_amdgcn_alignbyte(w1, w0, bb);
+  const uint32_t v23 = __builtin_amdgcn_alignbyte(w2, w1, bb);
+  out[0] = static_cast<uint16_t>(v01 & 0xFFFFu);
+  out[1] = static_cast<uint16_t>(v01 >> 16);
+  out[2] = static_cast<uint16_t>(v23 & 0xFFFFu);
+  out[3] = static_cast<uint16_t>(v23 >> 16);
+}
+
 // ---- bf16 <-> fp32 ---------------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }

@@ -120,7 +120,9 @@ struct ReduceArgs {
 // Four consecutive elements (flat index over [M][N]) per thread.  The
 // residual is requested before the partial sums so the two loads overlap;
 // the S partials are summed in the fixed order s = 0..S-1.
-template <bool VEC, bool RES, int MODE>
+// RV (N % 4 == 0): the four elements lie in one row, so their residual
+// comes as one aligned-block load (load4_bf16).
+template <bool VEC, bool RES, int MODE, bool RV = false>
 __device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
   const int64_t total = static_cast<int64_t>(g.M) * g.N;
   const int64_t e0 = (static_cast<int64_t>(block) * 256 + threadIdx.x) * 4;
@@ -141,8 +143,13 @@ __device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
   // the partials' share one memory round trip.
   uint16_t rv[4] = {0, 0, 0, 0};
   if constexpr (RES) {
+    if constexpr (RV) {
+      load4_bf16(g.res, static_cast<int64_t>(g.M - 1) * g.ldr + g.N,
+                 static_cast<int64_t>(mm[0]) * g.ldr + nn[0], true, true, rv);
+    } else {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) rv[v] = g.res[mm[v] * g.ldr + nn[v]];
+      for (int v = 0; v < 4; ++v) rv[v] = g.res[mm[v] * g.ldr + nn[v]];
+    }
   }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   if constexpr (VEC) {
@@ -236,9 +243,9 @@ __device__ __forceinline__ void reduce_block(const ReduceArgs& g, int block) {
   }
 }
 
-template <bool VEC, bool RES>
+template <bool VEC, bool RES, bool RV = false>
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs g) {
-  reduce_block<VEC, RES, kRedPredicated>(g, static_cast<int>(blockIdx.x));
+  reduce_block<VEC, RES, kRedPredicated, RV>(g, static_cast<int>(blockIdx.x));
 }
 
 // Rows of w_b one F_B workgroup covers: one row per group of G lanes, every
@@ -515,6 +522,9 @@ hipError_t launch_reduce(const ReduceProblem& p, hipStream_t s) {
   const ReduceArgs g = reduce_args(p);
   const dim3 grid(static_cast<unsigned>(blocks));
   const bool res = p.res != nullptr;
+  if (res && p.N % 4 == 0)
+    return reduce_vec(p) ? launch_kernel(reduce_kernel<true, true, true>, grid, dim3(256), 0, s, g)
+                         : launch_kernel(reduce_kernel<false, true, true>, grid, dim3(256), 0, s, g);
   if (reduce_vec(p))
     return res ? launch_kernel(reduce_kernel<true, true>, grid, dim3(256), 0, s, g)
                : launch_kernel(reduce_kernel<true, false>, grid, dim3(256), 0, s, g);
