@@ -201,7 +201,7 @@ TRAFFIC_SOURCES = ("bf16_skinny_gemm_02_amd/csrc/mfma.hip", "bf16_skinny_gemm_02
                    "bf16_skinny_gemm_02_amd/csrc/smallk.hip", "bf16_skinny_gemm_02_amd/csrc/sg_device.h",
                    "bf16_skinny_gemm_02_amd/csrc/dispatch.cpp", "bf16_skinny_gemm_02_amd/csrc/abi.cpp",
                    "bf16_skinny_gemm_02_amd/csrc/tuned_table.inc")
-TRAFFIC_PMC = {"sources_sha256": "6006cd95f4ce89c48c263bca92d8583f2b98d3090e662de84202c7492b5fd75d", "bytes_per_call": 64309372}
+TRAFFIC_PMC = {"sources_sha256": "c3c0d2555acd66ad15e2be4c73c18a990cfe8f9def45ecf78ff6e21e7ed26ab6", "bytes_per_call": 64478247}
 
 
 def sources_sha256():
