@@ -4,10 +4,12 @@
 
 One step is one pass of the whole hot path over the decode batch sizes
 M in {1, 2, 3, 4, 8, 16, 17, 32, 64}: for every M, the KDA projection (Q/K/V/G
-and F_A/beta -> F_B) in the schedule the overlap gate picks for that M, and the
-latent-MoE tail (RMSNorm -> up-projection -> shared add).  With the gate
-closed (its measured setting on MI355X) the projection runs on one stream: the
-Q/K/V/G and F_A/beta rows as two segments of one launch, then F_B.
+and F_A/beta -> F_B) through kda_projection_fused, and the latent-MoE tail
+(RMSNorm -> up-projection -> shared add).  At 2 <= M <= 8 the projection is one
+launch (the wave-split Q/K/V/G tile with a helper wave per workgroup that runs
+the F_A/beta -> F_B chain); elsewhere it is the one-stream schedule of
+kda_projection_overlap (the overlap gate is closed, its measured setting on
+MI355X): the Q/K/V/G and F_A/beta rows as two segments of one launch, then F_B.
 Each (op, M) is a hipGraph of R back-to-back calls that cycle through R copies
 of the weights, with R chosen so that the copies span >= 512 MiB: the 256 MiB
 Infinity Cache cannot hold them, so the weights stream from HBM on every call.
@@ -20,7 +22,7 @@ the next two: ``value`` is the projection half's time over its calls,
 ``tail_us_per_call`` the tail half's.
 
 ``roofline`` is the headline path's own unit of work: one projection call at
-M = 8 (its two launches), that M's graph replayed back to back right after the
+M = 8 (its one launch), that M's graph replayed back to back right after the
 timed region between HIP events on its stream; ``traffic`` is that call's HBM
 bytes from rocprofv3 counters; ``sweep_gbs`` the timed region's own rate.
 
@@ -29,7 +31,8 @@ fractions of the HBM and MFMA peaks), and ``configs``, one entry per workload
 of the benchmark's definition: the single GEMV (M = 1), the F_A/beta -> F_B
 branch alone (two launches, and the one-launch entry point, under graph
 replay and launched eagerly), the Q/K/V/G projection alone over the sweep,
-the two projection schedules against a packed GEMM followed by F_B, and the
+the projection's schedules (one launch, one stream, two streams) against a
+packed GEMM followed by F_B, and the
 latent-MoE tail up to M = 256.  ``--comparators`` adds the vendor library on
 the same work (torch.mm / addmm, i.e. hipBLASLt, with the RMSNorm in unfused
 torch ops).  ``cpu_baseline``: the CPU oracle on this host, on all its threads
@@ -123,12 +126,22 @@ class ProjectionCase:
                                   dtype=torch.uint8, device=device)
         self.ws_main = torch.zeros(max(sg.sg_kda_workspace_bytes(0, M, K, N_QKVG, N_AB), 256),
                                    dtype=torch.uint8, device=device)
+        # kda_projection_fused's workspace: zero-filled once (its header), then reused.
+        self.ws_one = torch.zeros(sg.sg_kda_workspace_bytes(sg.SG_KDA_ONE_LAUNCH, M, K, N_QKVG, N_AB),
+                                  dtype=torch.uint8, device=device)
         self.aux, self.fork, self.join = aux, fork, join
 
-    def call(self, r, concurrent=True):
+    def call(self, r, schedule="fused"):
+        """schedule: "fused" (kda_projection_fused: one launch where it fits,
+        else the one-stream schedule), "one_stream" or "two_stream"
+        (kda_projection_overlap)."""
+        if schedule == "fused":
+            sg.kda_projection_fused(self.x, self.packed[r], self.w_b[r], qkvg=self.qkvg, g1=self.g1,
+                                    beta=self.beta, workspace=self.ws_one)
+            return
         sg.kda_projection_overlap(self.x, self.packed[r], self.w_b[r], qkvg=self.qkvg, g1=self.g1,
                                   beta=self.beta, ws_main=self.ws_main, ws_aux=self.ws_aux,
-                                  aux_stream=self.aux if concurrent else None,
+                                  aux_stream=self.aux if schedule == "two_stream" else None,
                                   fork=self.fork, join=self.join)
 
 
@@ -190,18 +203,19 @@ def time_graph(g, stream, reps, warm=3):
 BREAKDOWN_REPS = 20
 BREAKDOWN_REPEATS = 5   # per-M breakdown: median, and the lowest / highest repeat (p10 / p90 of 5)
 
-ROOFLINE_M = 8   # the projection call the roofline leg times (two launches at 2 <= M <= 64)
+ROOFLINE_M = 8   # the projection call the roofline leg times (one launch at 2 <= M <= 8)
 
-# HBM traffic of one projection call at M = ROOFLINE_M (both of its launches) from two rocprofv3
+# HBM traffic of one projection call at M = ROOFLINE_M (its one launch) from two rocprofv3
 # --pmc runs of `bench.py --counters` (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 KiB per dispatch;
 # factors from a 256 MiB device copy), summarised with the commands in
 # profiles/kda_projection_and_tail_pmc_traffic.md.  Valid only for the sources it was measured on:
 # any change to them reports traffic as null until the counters are taken again.
 TRAFFIC_SOURCES = ("bf16_skinny_gemm_02_amd/csrc/mfma.hip", "bf16_skinny_gemm_02_amd/csrc/gemv.hip",
                    "bf16_skinny_gemm_02_amd/csrc/smallk.hip", "bf16_skinny_gemm_02_amd/csrc/sg_device.h",
+                   "bf16_skinny_gemm_02_amd/csrc/sg_help.h", "bf16_skinny_gemm_02_amd/csrc/sg_fused.h",
                    "bf16_skinny_gemm_02_amd/csrc/dispatch.cpp", "bf16_skinny_gemm_02_amd/csrc/abi.cpp",
                    "bf16_skinny_gemm_02_amd/csrc/tuned_table.inc")
-TRAFFIC_PMC = {"sources_sha256": "c3c0d2555acd66ad15e2be4c73c18a990cfe8f9def45ecf78ff6e21e7ed26ab6", "bytes_per_call": 64478247}
+TRAFFIC_PMC = {"sources_sha256": "657c35009b092beba29462def63ae3426972e3cb481e57717280afe072c5a5e8", "bytes_per_call": 63196628}
 
 
 def sources_sha256():
@@ -240,9 +254,10 @@ def counters_mode(device):
         c = ProjectionCase(M, device, None, None, None)
         for _ in range(2):
             for r in range(c.R):
-                c.call(r, concurrent=False)
+                c.call(r)
         torch.cuda.synchronize()
         launched[f"projection_m{M}"] = {"calls": 2 * c.R, "bytes_per_call": proj_bytes(M),
+                                        "one_launch": bool(sg.sg_kda_one_launch_fits(M, K, N_QKVG, N_AB, RANK, N_B)),
                                         "flops_per_call": proj_flops(M),
                                         "q": sg.sg_kda_select(sg.SG_KDA_QKVG, M, K, N_QKVG, N_AB),
                                         "f": sg.sg_kda_select(sg.SG_KDA_FAB, M, K, N_QKVG, N_AB)}
@@ -348,15 +363,17 @@ def config_qkvg(device, stream, Ms=M_SWEEP):
     return out
 
 
-def config_schedules(proj, device, stream, Ms=(1, 4, 16, 32)):
-    """The projection's two schedules (one stream; fork/join onto an aux
-    stream) and a plain packed GEMM over [W_qkvg; W_ab] followed by a second
-    GEMM for F_B, all as graphs over the same cold weight copies."""
+def config_schedules(proj, device, stream, Ms=(1, 4, 8, 16, 32)):
+    """The projection's schedules (one launch where it fits; one stream;
+    fork/join onto an aux stream) and a plain packed GEMM over [W_qkvg; W_ab]
+    followed by a second GEMM for F_B, all as graphs over the same cold weight
+    copies."""
     out = {}
     for M in Ms:
         c = proj[M]
-        one = graph_us(lambda r, c=c: c.call(r, concurrent=False), c.R, stream)
-        two = graph_us(lambda r, c=c: c.call(r, concurrent=True), c.R, stream)
+        fused = graph_us(lambda r, c=c: c.call(r, "fused"), c.R, stream)
+        one = graph_us(lambda r, c=c: c.call(r, "one_stream"), c.R, stream)
+        two = graph_us(lambda r, c=c: c.call(r, "two_stream"), c.R, stream)
         out_packed = torch.empty((M, N_QKVG + N_AB), dtype=torch.bfloat16, device=device)
         g1_s2 = torch.empty((M, N_B), dtype=torch.bfloat16, device=device)
         ws2 = torch.empty(max(sg.sg_workspace_bytes(sg.SG_OP_GEMM, M, N_QKVG + N_AB, K), 256),
@@ -367,8 +384,11 @@ def config_schedules(proj, device, stream, Ms=(1, 4, 16, 32)):
             sg.skinny_gemm(out_packed[:, N_QKVG:N_QKVG + RANK], c.w_b[r], out=g1_s2)
 
         s2 = graph_us(s2_call, c.R, stream)
-        out[str(M)] = {"one_stream_us": round(one, 3), "two_stream_us": round(two, 3),
+        out[str(M)] = {"fused_us": round(fused, 3),
+                       "fused_is_one_launch": bool(sg.sg_kda_one_launch_fits(M, K, N_QKVG, N_AB, RANK, N_B)),
+                       "one_stream_us": round(one, 3), "two_stream_us": round(two, 3),
                        "packed_gemm_then_fb_us": round(s2, 3),
+                       "one_launch_speedup_vs_one_stream": round(one / fused, 3),
                        "two_stream_speedup_vs_one_stream": round(one / two, 3),
                        "two_stream_speedup_vs_packed": round(s2 / two, 3),
                        "gate_picks": "two_stream" if sg.sg_overlap_gate(M, True, True, True, True)
@@ -478,6 +498,9 @@ KINDS = {sg.SG_KIND_GEMV_ROW: "gemv_kernel", sg.SG_KIND_GEMV_SPLITK: "gemv_kerne
 
 
 def projection_kernels(M):
+    if sg.sg_kda_one_launch_fits(M, K, N_QKVG, N_AB, RANK, N_B):
+        return (f"wsplit_help_kernel, one launch: {N_QKVG // 16} wave-split workgroups of 16 "
+                f"Q/K/V/G rows, each with a helper wave (F_A/beta producer units, then F_B hosts)")
     q = sg.sg_kda_select(sg.SG_KDA_QKVG, M, K, N_QKVG, N_AB)
     f = sg.sg_kda_select(sg.SG_KDA_FAB, M, K, N_QKVG, N_AB)
     return (f"{KINDS.get(q['kind'], '?')} with the Q/K/V/G and F_A/beta rows as two segments "
@@ -521,7 +544,8 @@ def main():
     proj = {M: ProjectionCase(M, device, aux, fork, join) for M in M_SWEEP}
     tail = {M: TailCase(M, device) for M in M_SWEEP}
     gate = {M: sg.sg_overlap_gate(M, True, True, True, True) for M in M_SWEEP}
-    g_proj = {M: capture(lambda r, c=proj[M], conc=gate[M]: c.call(r, concurrent=conc), proj[M].R,
+    sched = {M: "two_stream" if gate[M] else "fused" for M in M_SWEEP}
+    g_proj = {M: capture(lambda r, c=proj[M], s=sched[M]: c.call(r, s), proj[M].R,
                          main_stream) for M in M_SWEEP}
     g_tail = {M: capture(lambda r, c=tail[M]: c.call(r), tail[M].R, main_stream) for M in M_SWEEP}
     print("[bench] graphs captured", file=sys.stderr, flush=True)
@@ -587,7 +611,9 @@ def main():
             "tail_mfma_frac": round(tail_flops(M) / (tu * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "tail_roofline_frac": round(roofline_time_us(tail_bytes(M), tail_flops(M)) / tu, 4),
             "weight_copies": [proj[M].R, tail[M].R],
-            "schedule": "two_stream" if gate[M] else "one_stream",
+            "schedule": ("two_stream" if gate[M] else
+                         "one_launch" if sg.sg_kda_one_launch_fits(M, K, N_QKVG, N_AB, RANK, N_B)
+                         else "one_stream"),
         }
     # Every projection graph holds the same number of calls, so this is also
     # the mean over the sweep of the per-M time per call.
@@ -603,7 +629,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                 "kernel": f"KDA projection call at M = {ROOFLINE_M}: {projection_kernels(ROOFLINE_M)}",
-                "unit_of_work": "one call of the headline path (both launches)",
+                "unit_of_work": "one call of the headline path",
                 "us_per_call": round(us_call, 3),
                 "algorithmic_bytes_per_call": proj_bytes(ROOFLINE_M),
                 "calls_timed": roof_reps * proj[ROOFLINE_M].R,
@@ -662,7 +688,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "kda_decode_projection_sweep",
-            "description": "KDA projection per M in the schedule the overlap gate picks (QKVG "
+            "description": "KDA projection per M through kda_projection_fused (one launch at "
+                           "2 <= M <= 8, else the one-stream schedule the closed overlap gate picks; QKVG "
                            "[4096,7168] and F_A/beta [136,7168] -> F_B [1024,128], hipGraph), "
                            "plus the latent-MoE tail (RMSNorm 2048 -> up-proj [7168,2048] + "
                            "shared add) per M; value = mean us per projection call over the "

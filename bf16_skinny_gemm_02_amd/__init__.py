@@ -22,15 +22,17 @@ import torch
 from . import _lib
 from ._lib import (SG_KIND_MFMA_BLOCK, SG_KIND_GEMV_ROW, SG_KIND_GEMV_SMALLK, SG_KIND_GEMV_SPLITK,  # noqa: F401
                    SG_KIND_MFMA_TILE, SG_KIND_MFMA_WAVESPLIT, SG_KIND_NONE,
-                   SG_KDA_FAB, SG_KDA_FAB_ALONE, SG_KDA_QKVG, SG_OP_FAB_FB, SG_OP_GEMM,
+                   SG_KDA_FAB, SG_KDA_FAB_ALONE, SG_KDA_ONE_LAUNCH, SG_KDA_QKVG, SG_OP_FAB_FB, SG_OP_GEMM,
                    SG_OP_LATENT_TAIL, SgConfig, SgTableEntry)
 
 __all__ = [
     "sg_select", "sg_overlap_gate", "sg_overlap_max_tokens", "sg_workspace_bytes",
-    "sg_kda_select", "sg_kda_workspace_bytes", "sg_version", "sg_config_supported",
+    "sg_kda_select", "sg_kda_workspace_bytes", "sg_kda_one_launch_fits", "sg_version",
+    "sg_config_supported",
     "sg_config_workspace_bytes", "sg_tuned_table", "sg_set_table_override",
     "skinny_gemm", "kda_qkvg_proj", "kda_fab_fb_proj", "kda_projection_overlap",
-    "latent_moe_tail", "kda_projection_noalloc", "kda_fab_fb_proj_fused", "HipEvent",
+    "latent_moe_tail", "kda_projection_noalloc", "kda_fab_fb_proj_fused", "kda_projection_fused",
+    "HipEvent",
     "library_path",
 ]
 
@@ -79,6 +81,12 @@ def sg_kda_select(which: int, M: int, K: int, n_qkvg: int, n_ab: int) -> dict:
 def sg_kda_workspace_bytes(which: int, M: int, K: int, n_qkvg: int, n_ab: int) -> int:
     return int(_lib.load().sg_kda_workspace_bytes(int(which), int(M), int(K), int(n_qkvg),
                                                   int(n_ab)))
+
+
+def sg_kda_one_launch_fits(M: int, K: int, n_qkvg: int, n_ab: int, rank: int, n_b: int) -> bool:
+    """Whether kda_projection_fused runs these shapes as one launch."""
+    return bool(_lib.load().sg_kda_one_launch_fits(int(M), int(K), int(n_qkvg), int(n_ab), int(rank),
+                                                   int(n_b)))
 
 
 def _config(cfg: dict) -> SgConfig:
@@ -333,6 +341,34 @@ def kda_projection_overlap(x: torch.Tensor, packed_w: torch.Tensor, w_b: torch.T
         ctypes.c_void_p(aux_stream.cuda_stream) if aux_stream is not None else None,
         fork.handle if fork is not None else None, join.handle if join is not None else None)
     _lib.check(st, "kda_projection_overlap")
+    return qkvg, g1, beta
+
+
+def kda_projection_fused(x: torch.Tensor, packed_w: torch.Tensor, w_b: torch.Tensor, *,
+                         n_qkvg: int = 4096, n_ab: int = 136, rank: int = 128,
+                         qkvg: torch.Tensor | None = None, beta: torch.Tensor | None = None,
+                         g1: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                         stream=None):
+    """The KDA projection as one launch (a helper wave per Q/K/V/G workgroup
+    runs the F_A/beta -> F_B chain).  Returns (qkvg, g1, beta).  A workspace
+    given by the caller must have been zero-filled once before its first use
+    by this call and not altered since."""
+    for t, n in ((x, "x"), (packed_w, "packed_w"), (w_b, "w_b")):
+        _check_tensor(t, n, 2, contiguous=True)
+    M, K = x.shape
+    n_b = w_b.shape[0]
+    if packed_w.shape != (n_qkvg + n_ab, K) or w_b.shape[1] != rank:
+        raise ValueError("packed_w must be [n_qkvg + n_ab, K] and w_b [n_b, rank]")
+    _same_device(x, packed_w, w_b)
+    qkvg = _out(qkvg, (M, n_qkvg), x, "qkvg")
+    beta = _out(beta, (M, n_ab - rank), x, "beta")
+    g1 = _out(g1, (M, n_b), x, "g1")
+    ws, ws_bytes = _workspace(workspace, sg_kda_workspace_bytes(SG_KDA_ONE_LAUNCH, M, K, n_qkvg, n_ab),
+                              x.device)
+    st = _lib.load().kda_projection_fused(
+        _ptr(x), _ptr(packed_w), _ptr(w_b), _ptr(qkvg), _ptr(beta), _ptr(g1), M, K, n_qkvg, n_ab,
+        rank, n_b, _ptr(ws), ws_bytes, _stream(stream, x.device))
+    _lib.check(st, "kda_projection_fused")
     return qkvg, g1, beta
 
 

@@ -33,6 +33,7 @@ SG_OP_LATENT_TAIL = 2
 SG_KDA_QKVG = 0
 SG_KDA_FAB = 1
 SG_KDA_FAB_ALONE = 2
+SG_KDA_ONE_LAUNCH = 3
 
 # Every extern "C" symbol declared in include/skinny_gemm.h.
 EXPORTED_SYMBOLS = (
@@ -40,6 +41,7 @@ EXPORTED_SYMBOLS = (
     "sg_kda_select", "sg_kda_workspace_bytes",
     "sg_strerror", "sg_version", "skinny_gemm", "kda_qkvg_proj", "kda_fab_fb_proj",
     "kda_projection_overlap", "latent_moe_tail", "kda_projection_noalloc", "kda_fab_fb_proj_fused",
+    "kda_projection_fused", "sg_kda_one_launch_fits",
     "sg_config_supported", "sg_config_workspace_bytes", "sg_tuned_table", "sg_set_table_override",
 )
 
@@ -89,11 +91,17 @@ _PROTOS = {
                                       _i32, _i32, _vp, _vp, _vp, _vp]),
     "kda_fab_fb_proj_fused": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                      _vp, _sz, _vp]),
+    "kda_projection_fused": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                    _i32, _i32, _vp, _sz, _vp]),
+    "sg_kda_one_launch_fits": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "sg_config_supported": (_i32, [ctypes.POINTER(SgConfig), _i32, _i32, _i32]),
     "sg_config_workspace_bytes": (_sz, [ctypes.POINTER(SgConfig), _i32, _i32]),
     "sg_tuned_table": (_i32, [ctypes.POINTER(ctypes.POINTER(SgTableEntry))]),
     "sg_set_table_override": (_i32, [ctypes.POINTER(SgTableEntry), _i32]),
 }
+
+# Hand-off header at the start of the one-launch workspaces (SG_FAB_HEADER_BYTES).
+SG_FAB_HEADER_BYTES = 18432
 
 # Per-GPU scratch of kda_projection_noalloc (SG_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 16 << 20

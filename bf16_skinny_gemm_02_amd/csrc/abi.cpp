@@ -385,6 +385,68 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
   return SG_OK;
 }
 
+// The workspace query (dispatch.cpp, host-only code) restates these.
+static_assert(sg::kSyncBytes == SG_FAB_HEADER_BYTES, "hand-off header size");
+static_assert(sg::kHelpSteps == 4, "one-launch K-ranges: four 512-k steps per unit");
+
+extern "C" int sg_kda_one_launch_fits(int M, int K, int n_qkvg, int n_ab, int rank, int n_b) {
+  sg::HelpPlan plan;
+  return sg::help_plan(M, K, n_qkvg, n_ab, rank, n_b, &plan) ? 1 : 0;
+}
+
+extern "C" int kda_projection_fused(const sg_bf16* x, const sg_bf16* packed_w, const sg_bf16* w_b,
+                                    sg_bf16* qkvg, sg_bf16* beta, sg_bf16* g1, int M, int K,
+                                    int n_qkvg, int n_ab, int rank, int n_b, void* ws,
+                                    size_t ws_bytes, sg_stream_t stream) {
+  if (M < 0 || K < 0 || n_qkvg < 0 || n_b < 0 || rank <= 0 || n_ab <= rank)
+    return SG_ERR_INVALID_ARG;
+  if (rank % 8 != 0 || rank > sg::kFbMaxRank) return SG_ERR_UNSUPPORTED;
+  sg_config_t cq;  // the one-stream schedule's shape checks, for either path
+  int st = sg_kda_select(SG_KDA_QKVG, M, K, n_qkvg, n_ab, &cq);
+  if (st != SG_OK) return st;
+  if (M == 0) return SG_OK;
+  if ((st = check_operand16(x, K, K)) != SG_OK) return st;
+  if ((st = check_operand16(packed_w, K, K)) != SG_OK) return st;
+  if ((st = check_operand16(w_b, rank, rank)) != SG_OK) return st;
+  if (n_qkvg > 0 && (st = check_output2(qkvg, n_qkvg, n_qkvg)) != SG_OK) return st;
+  if ((st = check_output2(beta, n_ab - rank, n_ab - rank)) != SG_OK) return st;
+  if (n_b > 0 && (st = check_output2(g1, n_b, n_b)) != SG_OK) return st;
+  if (!spans_ok(M, K, K) || !spans_ok(kMaxTileRows, K, K)) return SG_ERR_UNSUPPORTED;
+  if ((st = check_workspace(ws, ws_bytes, sg_kda_workspace_bytes(SG_KDA_ONE_LAUNCH, M, K, n_qkvg, n_ab))) != SG_OK)
+    return st;
+  sg::HelpPlan plan;
+  if (!sg::help_plan(M, K, n_qkvg, n_ab, rank, n_b, &plan)) {
+    // The one-stream schedule, its two workspaces behind the header.
+    const size_t need_main = sg_kda_workspace_bytes(SG_KDA_QKVG, M, K, n_qkvg, n_ab);
+    const size_t need_aux = sg_kda_workspace_bytes(SG_KDA_FAB, M, K, n_qkvg, n_ab);
+    char* base = static_cast<char*>(ws) + sg::kSyncBytes;
+    return kda_projection_overlap(x, packed_w, w_b, qkvg, beta, g1, M, K, n_qkvg, n_ab, rank, n_b,
+                                  need_main > 0 ? base : nullptr, need_main,
+                                  need_aux > 0 ? base + need_main : nullptr, need_aux, stream,
+                                  nullptr, nullptr, nullptr);
+  }
+  sg::OneLaunchProj p{};
+  p.q.a = x;
+  p.q.lda = K;
+  p.q.w = packed_w;
+  p.q.ldw = K;
+  p.q.out = qkvg;
+  p.q.ldc = n_qkvg;
+  p.q.M = M;
+  p.q.N = n_qkvg;
+  p.q.K = K;
+  p.w_ab = packed_w + static_cast<int64_t>(n_qkvg) * K;
+  p.n_ab = n_ab;
+  p.rank = rank;
+  p.n_b = n_b;
+  p.w_b = w_b;
+  p.beta = beta;
+  p.g1 = g1;
+  p.sync = static_cast<unsigned*>(ws);
+  p.pairs = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sg::kSyncBytes);
+  return hip_status(sg::launch_proj_one(p, plan, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int latent_moe_tail(const sg_bf16* latent, const sg_bf16* gamma, float eps,
                                const sg_bf16* w_up, const sg_bf16* shared, sg_bf16* out, int M,
                                int d_latent, int d_hidden, void* ws, size_t ws_bytes,

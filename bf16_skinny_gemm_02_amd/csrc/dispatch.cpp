@@ -534,6 +534,19 @@ extern "C" int sg_kda_select(int which, int M, int K, int n_qkvg, int n_ab, sg_c
 
 extern "C" size_t sg_kda_workspace_bytes(int which, int M, int K, int n_qkvg, int n_ab) {
   if (M <= 0 || K < 0 || n_qkvg < 0 || n_ab <= 0) return 0;
+  if (which == SG_KDA_ONE_LAUNCH) {
+    // The hand-off header, then the larger of the one-launch F_A/beta
+    // partials and the two workspaces of the one-stream schedule it falls
+    // back to.
+    // Its K-ranges: ceil(ceil(K/512) / 4), a unit covering four 512-k
+    // steps; each partial is 8 bytes (fp32 and a generation tag).
+    const int ranges = ((K / 8 + 63) / 64 + 3) / 4;
+    const size_t one = sg::round256(static_cast<size_t>(ranges) * static_cast<size_t>(M) *
+                                    static_cast<size_t>(n_ab) * 8);
+    const size_t two = sg_kda_workspace_bytes(SG_KDA_QKVG, M, K, n_qkvg, n_ab) +
+                       sg_kda_workspace_bytes(SG_KDA_FAB, M, K, n_qkvg, n_ab);
+    return kFabHeaderBytes + (one > two ? one : two);
+  }
   if (which != SG_KDA_QKVG && which != SG_KDA_FAB) return 0;
   sg_config_t c;
   if (sg_kda_select(which, M, K, n_qkvg, n_ab, &c) != SG_OK || c.kind == SG_KIND_NONE) return 0;

@@ -43,6 +43,7 @@
 // timing or on which tile holds the row.
 #include "sg_device.h"
 #include "sg_fused.h"
+#include "sg_help.h"
 #include "sg_launch.h"
 
 namespace sg {
@@ -306,6 +307,7 @@ __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaLaunch L) {
 // ---- wave-split LDS tile (M <= 16) ------------------------------------------------
 
 constexpr int kSplitWaves = 4;
+constexpr int kHelpRing = 3;  // ring slots of the one-launch projection's tile
 // RMSNorm fold: the latent row is read in at most this many 16-byte chunks
 // per lane (d_latent <= 2048), and one wave's K-range of gamma fits one copy.
 constexpr int kFoldChunks = 4;
@@ -327,8 +329,7 @@ constexpr int kFoldMaxK = kFoldChunks * kWave * 8;
 // 17..32 rows: the second fragment's rows past g.tile_rows read zeros and are
 // not stored), so that e.g. 7168 rows make exactly 256 workgroups of 28.
 template <int XQ, int C, bool NORM, bool RES, bool FB, int NT>
-__global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch L) {
-  extern __shared__ u32x4 lds[];
+__device__ __forceinline__ void wsplit_body(const MfmaLaunch& L, u32x4* lds) {
   if constexpr (FB) {
     static_assert(kSplitWaves * kWave == kFbThreads && !NORM && !RES, "F_B role instances");
     const int b = static_cast<int>(blockIdx.x);
@@ -517,6 +518,33 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch 
   }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) store4(g, acc[nt], rl, row0 + 16 * nt + 4 * kg, split, res[nt], nlim);
+}
+
+template <int XQ, int C, bool NORM, bool RES, bool FB, int NT>
+__global__ __launch_bounds__(kSplitWaves * kWave) void wsplit_kernel(MfmaLaunch L) {
+  extern __shared__ u32x4 lds[];
+  wsplit_body<XQ, C, NORM, RES, FB, NT>(L, lds);
+}
+
+// The one-launch KDA projection (sg_help.h): the four waves of the wave-split
+// tile stream the Q/K/V/G rows (16 per workgroup, all of K, bf16 out); a
+// fifth wave runs the F_A/beta -> F_B chain in LDS behind the four rings, at
+// the highest issue priority among the workgroup's waves, so that its few
+// loads go out ahead of the rings' copies (the chain, not the stream, ends
+// the launch).  The helper meets the tile's two epilogue barriers once its
+// own work is done.
+template <int XQ>
+__global__ __launch_bounds__((kSplitWaves + 1) * kWave) void wsplit_help_kernel(MfmaLaunch L, HelpArgs H) {
+  extern __shared__ u32x4 lds[];
+  if (wave_id() == kSplitWaves) {
+    __builtin_amdgcn_s_setprio(3);
+    constexpr int kRing = kSplitWaves * kHelpRing * (16 + 4 * XQ) * kPieces;
+    help_wave<XQ>(H, static_cast<int>(blockIdx.x), lds + kRing);
+    __syncthreads();
+    __syncthreads();
+    return;
+  }
+  wsplit_body<XQ, kHelpRing, false, false, false, 1>(L, lds);
 }
 
 // ---- two-dimensional LDS block tile (M > 64) ----------------------------------------
@@ -1040,6 +1068,100 @@ hipError_t launch_mfma_fused(const DotProblem* segs, const sg_config_t* cfgs, in
 
 hipError_t launch_mfma(const DotProblem& p, const sg_config_t& cfg, hipStream_t s) {
   return launch_mfma(&p, &cfg, 1, s);
+}
+
+// ---- the one-launch KDA projection -------------------------------------------------
+
+bool help_plan(int M, int K, int n_qkvg, int n_ab, int rank, int n_b, HelpPlan* out) {
+  if (M < 1 || M > kHelpMaxM || K <= 0 || K % 8 != 0 || n_qkvg <= 0 || rank <= 0 || n_ab <= rank ||
+      n_ab % 4 != 0 || rank % 8 != 0 || rank > kHelpMaxRank || n_b <= 0)
+    return false;
+  HelpPlan p;
+  p.wgs = (n_qkvg + 15) / 16;
+  const int wsteps = (K / 8 + kWave - 1) / kWave;
+  p.S = help_ranges(K);
+  if (p.S > kHelpMaxS) return false;
+  p.per = (wsteps + p.S - 1) / p.S;
+  p.groups = (n_ab + kHelpRows - 1) / kHelpRows;
+  p.units = p.groups * p.S;
+  // As few hosts as the rows allow: every host reads all the partials.
+  p.hosts = (n_b + kHelpHostRows - 1) / kHelpHostRows;
+  p.host_rows = ((n_b + p.hosts - 1) / p.hosts + 3) / 4 * 4;
+  if (p.units > kFbMaxProducers || p.hosts > kFbMaxConsumers || p.units + p.hosts > p.wgs) return false;
+  // Each lane of a host polls at most kHelpPollItems 16-byte loads per K-range.
+  if (M * (n_ab / 2) > kHelpPollItems * kWave) return false;
+  const int XQ = (M + 3) / 4;
+  if (wsplit_lds_bytes(kHelpRing, XQ, false, 1) + help_lds_bytes(M, rank) > kMfmaMaxLds) return false;
+  *out = p;
+  return true;
+}
+
+namespace {
+
+template <int XQ>
+hipError_t launch_help_inst(const MfmaLaunch& L, const HelpArgs& H, int wgs, hipStream_t s) {
+  auto kern = wsplit_help_kernel<XQ>;
+  static std::atomic<bool> lds_set[kLdsAttrDevices];
+  const hipError_t attr = ensure_lds_limit(reinterpret_cast<const void*>(kern), kMfmaMaxLds, lds_set);
+  if (attr != hipSuccess) return attr;
+  const size_t lds = wsplit_lds_bytes(kHelpRing, XQ, false, 1) + help_lds_bytes(H.M, H.rank);
+  return launch_kernel(kern, dim3(wgs), dim3((kSplitWaves + 1) * kWave), lds, s, L, H);
+}
+
+}  // namespace
+
+hipError_t launch_proj_one(const OneLaunchProj& p, const HelpPlan& plan, hipStream_t s) {
+  const DotProblem& q = p.q;
+  if (q.M < 1 || q.M > kHelpMaxM || plan.wgs != (q.N + 15) / 16) return hipErrorInvalidValue;
+  MfmaLaunch L;
+  L.fb = no_fb_fuse();
+  MfmaArgs& g = L.seg[0].g;
+  g = MfmaArgs{};
+  g.a = q.a;
+  g.lda = q.lda;
+  g.w = q.w;
+  g.ldw = q.ldw;
+  g.ldr = q.ldc;
+  g.out = q.out;
+  g.ldc = q.ldc;
+  g.M = q.M;
+  g.N = q.N;
+  g.K = q.K;
+  g.sps = ksteps_of(q.K);
+  g.tile_rows = 16;
+  L.seg[0].tiles = plan.wgs;
+  L.seg[0].wg_begin = 0;
+  L.seg[0].wg_end = plan.wgs;
+  L.seg[1] = L.seg[0];
+  L.seg[1].wg_begin = L.seg[1].wg_end = 0;
+
+  HelpArgs H;
+  H.x = q.a;
+  H.lda = q.lda;
+  H.w_ab = p.w_ab;
+  H.ldw = q.K;
+  H.pairs = p.pairs;
+  H.sync = p.sync;
+  H.w_b = p.w_b;
+  H.beta = p.beta;
+  H.g1 = p.g1;
+  H.M = q.M;
+  H.K = q.K;
+  H.n_ab = p.n_ab;
+  H.rank = p.rank;
+  H.n_b = p.n_b;
+  H.groups = plan.groups;
+  H.S = plan.S;
+  H.per = plan.per;
+  H.units = plan.units;
+  H.h_begin = plan.units;
+  H.h_end = plan.units + plan.hosts;
+  H.host_rows = plan.host_rows;
+  switch ((q.M + 3) / 4) {
+    case 1: return launch_help_inst<1>(L, H, plan.wgs, s);
+    case 2: return launch_help_inst<2>(L, H, plan.wgs, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace sg

@@ -119,6 +119,58 @@ hipError_t launch_gemv_fused(const DotProblem* segs, const sg_config_t* cfgs, in
                              const FusedFb& fb, int fb_after, hipStream_t s);
 hipError_t launch_mfma_fused(const DotProblem* segs, const sg_config_t* cfgs, int nseg,
                              const FusedFb& fb, int fb_after, hipStream_t s);
+// Geometry of the one-launch KDA projection's helper wave (sg_help.h): W_ab
+// rows per producer unit, 512-k steps per unit at most, K-ranges at most (so
+// K <= 8192), the largest M, g1 rows per F_B host at most, and the largest
+// rank (k-steps of 32 for the MFMA F_B).
+constexpr int kHelpRows = 4;
+constexpr int kHelpSteps = 4;
+constexpr int kHelpMaxS = 4;
+constexpr int kHelpMaxM = 8;
+constexpr int kHelpHostRows = 64;
+constexpr int kHelpMaxRank = 128;
+// K-ranges of the F_A/beta partials: one unit covers at most kHelpSteps
+// steps of 512 k.
+inline int help_ranges(int K) {
+  const int wsteps = (K / 8 + 63) / 64;
+  return (wsteps + kHelpSteps - 1) / kHelpSteps;
+}
+// LDS of the helper behind the four rings: a unit's activation rows
+// (kHelpSteps KiB per row, 4 * XQ rows), or a host's W_b rows (room for
+// kHelpHostRows rows of kHelpMaxRank) and f_a [M][rank], all bf16.
+inline size_t help_lds_bytes(int M, int rank) {
+  const size_t xq = static_cast<size_t>((M + 3) / 4);
+  const size_t unit = static_cast<size_t>(kHelpSteps) * 4 * xq * 1024;
+  const size_t host = static_cast<size_t>(kHelpHostRows) * kHelpMaxRank * 2 +
+                      ((static_cast<size_t>(M) * rank * 2 + 15) & ~static_cast<size_t>(15));
+  return unit > host ? unit : host;
+}
+
+// The one-launch KDA projection: the Q/K/V/G rows of `q` (bf16 out, 16 rows
+// per wave-split workgroup over all of K, M <= 16), each workgroup with a
+// helper wave that runs the F_A/beta -> F_B chain (sg_help.h).  w_ab [n_ab,K]
+// shares q's K; the tagged partials and the hand-off header `sync`
+// (zero before the first call) live in the workspace.
+struct OneLaunchProj {
+  DotProblem q;
+  const uint16_t* w_ab;
+  int n_ab, rank, n_b;
+  const uint16_t* w_b;
+  uint16_t* beta;
+  uint16_t* g1;
+  uint32_t* pairs;   // [S][M][n_ab] (fp32 bits, generation)
+  unsigned* sync;
+};
+// The helper geometry: `groups` units of 4 W_ab rows per K-range, S
+// K-ranges of `per` 512-k steps (units = groups * S producer workgroups),
+// then `hosts` F_B hosts of host_rows g1 rows, all within the wgs Q/K/V/G
+// workgroups.  False when the shapes do not fit it.
+struct HelpPlan {
+  int wgs, groups, S, per, units, hosts, host_rows;
+};
+bool help_plan(int M, int K, int n_qkvg, int n_ab, int rank, int n_b, HelpPlan* out);
+hipError_t launch_proj_one(const OneLaunchProj& p, const HelpPlan& plan, hipStream_t s);
+
 // Bytes at the start of a kda_fab_fb_proj(_fused) workspace that hold the
 // hand-off header (4096 producer flags and 512 consumer cursors, uint32);
 // the fp32 partials follow.

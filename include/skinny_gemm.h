@@ -202,7 +202,8 @@ size_t sg_workspace_bytes(int op, int M, int N, int K);
 enum {
     SG_KDA_QKVG = 0,       /* Q/K/V/G rows in kda_projection_overlap */
     SG_KDA_FAB = 1,        /* F_A/beta rows in kda_projection_overlap */
-    SG_KDA_FAB_ALONE = 2   /* F_A/beta rows in kda_fab_fb_proj */
+    SG_KDA_FAB_ALONE = 2,  /* F_A/beta rows in kda_fab_fb_proj */
+    SG_KDA_ONE_LAUNCH = 3  /* kda_projection_fused's workspace (sg_kda_workspace_bytes only) */
 };
 
 /* Host-only, pure: the configurations the KDA projection entry points use,
@@ -235,7 +236,11 @@ int sg_kda_select(int which, int M, int K, int n_qkvg, int n_ab, sg_config_t *ou
  * SG_KDA_QKVG for ws_main (the Q/K/V/G split-K partials, k_split * M *
  * n_qkvg * 4 rounded up to 256, 0 when unsplit), SG_KDA_FAB for ws_aux (the
  * F_A/beta partials, k_split * M * n_ab * 4 rounded up to 256), with the
- * configurations of sg_kda_select().  0 for any other which. */
+ * configurations of sg_kda_select().  SG_KDA_ONE_LAUNCH: the workspace of
+ * kda_projection_fused, SG_FAB_HEADER_BYTES of hand-off header followed by
+ * the larger of its tagged F_A/beta partials (ceil(ceil(K/512)/4) * M *
+ * n_ab * 8, rounded up to 256) and the SG_KDA_QKVG + SG_KDA_FAB workspaces.
+ * 0 for any other which. */
 size_t sg_kda_workspace_bytes(int which, int M, int K, int n_qkvg, int n_ab);
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -337,6 +342,42 @@ int kda_projection_overlap(const sg_bf16 *x, const sg_bf16 *packed_w, const sg_b
                            void *ws_aux, size_t ws_aux_bytes,
                            sg_stream_t main_stream, sg_stream_t aux_stream,
                            sg_event_t fork, sg_event_t join);
+
+/* The KDA projection of kda_projection_overlap as ONE launch on one stream
+ * [P3 low_latency_gemm.py run_kda_projection_overlap, which runs the
+ * F_A/beta -> F_B chain beside the Q/K/V/G GEMM; the chain's two GEMMs are
+ * themselves linked by programmatic dependent launch there]:
+ * same outputs (qkvg, beta, g1; no f_a), same argument conventions.  Where
+ * the shapes fit (2 <= M <= 8, K <= 8192, n_qkvg / 16 wave-split
+ * workgroups of 16 Q/K/V/G rows that outnumber the F_A/beta units and F_B
+ * hosts, n_ab % 4 == 0, M * n_ab <= 1152, rank <= 128), every Q/K/V/G
+ * workgroup carries a fifth wave: in the first ceil(n_ab/4) *
+ * ceil(ceil(K/512)/4) workgroups it computes fp32 partials of 4 F_A/beta
+ * rows over one K-range (at most 2048 k) and stores each with the call's
+ * generation (workspace header) in one 8-byte store; in the next
+ * ceil(n_b/64) workgroups it reads the partials until all carry the
+ * generation (a bounded wait: on a time-out it writes NaN to g1 and beta),
+ * sums them in fixed order into bf16 f_a and beta and computes its share of
+ * g1 (at most 64 rows).  The Q/K/V/G rows are those of the wave-split tile
+ * over all of K.  Elsewhere (M == 1, M > 8, other shapes) the call runs the
+ * one-stream schedule of kda_projection_overlap with its two workspaces
+ * behind the header.
+ * Results: qkvg as the wave-split tile computes it; beta and g1 from the
+ * same products summed in another order than kda_projection_overlap's (both
+ * within the oracle's tolerance, not bitwise equal).
+ * Workspace: sg_kda_workspace_bytes(SG_KDA_ONE_LAUNCH, ...) bytes.  Its
+ * header (the first SG_FAB_HEADER_BYTES) must be zero before the first call
+ * on a workspace; each call keeps it consistent by itself (it is not zero
+ * afterwards and must not be altered), whatever the shapes of later calls.
+ * Calls that share a workspace must not run concurrently. */
+int kda_projection_fused(const sg_bf16 *x, const sg_bf16 *packed_w, const sg_bf16 *w_b,
+                         sg_bf16 *qkvg, sg_bf16 *beta, sg_bf16 *g1,
+                         int M, int K, int n_qkvg, int n_ab, int rank, int n_b,
+                         void *ws, size_t ws_bytes, sg_stream_t stream);
+
+/* Host-only, pure: 1 if kda_projection_fused runs these shapes as one launch
+ * (the conditions above), 0 if it takes the one-stream schedule. */
+int sg_kda_one_launch_fits(int M, int K, int n_qkvg, int n_ab, int rank, int n_b);
 
 /* Latent-MoE tail [P1 latent_moe_runner.py LatentMoERunner: RMS-norm of the
  * latent partial, replicated up-projection, shared-expert add folded into

@@ -406,3 +406,60 @@ def test_fab_fb_fused_validates_like_fab_fb(lib):
                {"w_b": ODD}, {}, {"M": 0}, {"ws": ctypes.c_void_p(0x90000), "ws_bytes": 100}):
         assert fused(**kw) == _fab(lib, **kw), kw
     assert fused() == E.SG_ERR_WORKSPACE
+
+
+def test_one_launch_fits_and_workspace(lib):
+    """kda_projection_fused's geometry query and workspace size, restated from
+    the header's conditions: one launch at 1 <= M <= 8 for the KDA shapes
+    (K <= 8192, n_ab % 4 == 0, rank <= 128, enough Q/K/V/G workgroups for the
+    F_A/beta units and F_B hosts), the one-stream schedule elsewhere; the
+    workspace is the header plus the larger of the tagged partials
+    (ceil(ceil(K/512)/4) K-ranges x M x n_ab x 8 bytes) and the one-stream
+    schedule's two workspaces."""
+    fits = lambda *a: bool(lib.sg_kda_one_launch_fits(*a))  # noqa: E731
+    for M in range(0, 12):
+        assert fits(M, 7168, 4096, 136, 128, 1024) == (1 <= M <= 8), M
+    assert fits(8, 8192, 4096, 136, 128, 1024)
+    assert not fits(8, 8200, 4096, 136, 128, 1024)     # five K-ranges
+    assert not fits(4, 7168, 4096, 138, 128, 1024)     # n_ab % 4
+    assert not fits(4, 7168, 4096, 136, 256, 1024)     # rank > 128
+    assert not fits(4, 7168, 2048, 136, 128, 1024)     # 128 workgroups < 136 units + 16 hosts
+    assert not fits(4, 7164, 4096, 136, 128, 1024)     # K % 8
+    assert fits(2, 1032, 4096, 136, 128, 1024) and fits(3, 4096, 4096, 136, 128, 1024)
+    for M in (1, 2, 5, 8, 9, 16, 40):
+        for K in (1032, 4096, 7168):
+            ranges = -(-(-(-K // 512)) // 4)
+            one = -(-ranges * M * 136 * 8 // 256) * 256
+            two = lib.sg_kda_workspace_bytes(0, M, K, 4096, 136) + lib.sg_kda_workspace_bytes(1, M, K, 4096, 136)
+            assert lib.sg_kda_workspace_bytes(_lib.SG_KDA_ONE_LAUNCH, M, K, 4096, 136) == \
+                _lib.SG_FAB_HEADER_BYTES + max(one, two), (M, K)
+
+
+def test_projection_fused_validation(lib):
+    """kda_projection_fused checks its arguments before anything is enqueued:
+    the same statuses as kda_projection_overlap for bad shapes and operands,
+    and a workspace of sg_kda_workspace_bytes(SG_KDA_ONE_LAUNCH, ...) bytes."""
+    E = _lib
+    need = lib.sg_kda_workspace_bytes(E.SG_KDA_ONE_LAUNCH, 4, 7168, 4096, 136)
+
+    def fp(**kw):
+        args = dict(x=A16, packed=B16, w_b=C16, qkvg=ctypes.c_void_p(0x80000),
+                    beta=ctypes.c_void_p(0x60000), g1=ctypes.c_void_p(0x70000), M=4, K=7168,
+                    n_qkvg=4096, n_ab=136, rank=128, n_b=1024, ws=ctypes.c_void_p(0x90000),
+                    ws_bytes=need)
+        args.update(kw)
+        return lib.kda_projection_fused(*args.values(), None)
+
+    assert fp(M=-1) == E.SG_ERR_INVALID_ARG
+    assert fp(rank=0) == E.SG_ERR_INVALID_ARG
+    assert fp(rank=100) == E.SG_ERR_UNSUPPORTED
+    assert fp(x=NUL) == E.SG_ERR_INVALID_ARG
+    assert fp(packed=ODD) == E.SG_ERR_MISALIGNED
+    assert fp(g1=NUL) == E.SG_ERR_INVALID_ARG
+    assert fp(ws=NUL) == E.SG_ERR_WORKSPACE
+    assert fp(ws_bytes=need - 1) == E.SG_ERR_WORKSPACE
+    assert fp(ws=ctypes.c_void_p(0x90008)) == E.SG_ERR_MISALIGNED
+    assert fp(M=0) == E.SG_OK
+    # Shapes the one launch does not fit take the one-stream schedule and its checks.
+    assert fp(M=20, ws_bytes=100) == E.SG_ERR_WORKSPACE
+    assert fp(M=20, qkvg=NUL) == E.SG_ERR_INVALID_ARG
