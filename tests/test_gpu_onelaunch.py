@@ -3,8 +3,9 @@
 The F_A/beta -> F_B chain that "Overlap low-M TP8 KDA projections" runs on an
 auxiliary stream beside the Q/K/V/G GEMM rides inside the Q/K/V/G launch: a
 fifth wave of every wave-split workgroup computes a slice of P = x W_ab^T
-(fp32 partials, a flag per slice) and the fifth waves of the last workgroups
-wait for every flag, sum the partials in fixed order and compute g1.  qkvg,
+(fp32 partials, each stored with the call's generation) and the fifth waves of
+the next workgroups read them until all carry it, sum them in fixed order and
+compute g1.  qkvg,
 beta and g1 are checked against the oracle; on integer-lattice inputs every
 partial sum is exact, so all three must equal the oracle bit for bit.  One
 workspace, zero-filled once, serves calls of changing shapes (the header keeps
