@@ -1084,12 +1084,14 @@ bool help_plan(int M, int K, int n_qkvg, int n_ab, int rank, int n_b, HelpPlan* 
   p.per = (wsteps + p.S - 1) / p.S;
   p.groups = (n_ab + kHelpRows - 1) / kHelpRows;
   p.units = p.groups * p.S;
-  // As few hosts as the rows allow: every host reads all the partials.
-  p.hosts = (n_b + kHelpHostRows - 1) / kHelpHostRows;
-  p.host_rows = ((n_b + p.hosts - 1) / p.hosts + 3) / 4 * 4;
+  // As few hosts as the rows allow (every host reads all the partials of its
+  // activation rows), for each group of kHelpHostM activation rows.
+  p.row_hosts = (n_b + kHelpHostRows - 1) / kHelpHostRows;
+  p.host_rows = ((n_b + p.row_hosts - 1) / p.row_hosts + 3) / 4 * 4;
+  p.hosts = p.row_hosts * ((M + kHelpHostM - 1) / kHelpHostM);
   if (p.units > kFbMaxProducers || p.hosts > kFbMaxConsumers || p.units + p.hosts > p.wgs) return false;
   // Each lane of a host polls at most kHelpPollItems 16-byte loads per K-range.
-  if (M * (n_ab / 2) > kHelpPollItems * kWave) return false;
+  if ((M < kHelpHostM ? M : kHelpHostM) * (n_ab / 2) > kHelpPollItems * kWave) return false;
   const int XQ = (M + 3) / 4;
   if (wsplit_lds_bytes(kHelpRing, XQ, false, 1) + help_lds_bytes(M, rank) > kMfmaMaxLds) return false;
   *out = p;
@@ -1156,6 +1158,7 @@ hipError_t launch_proj_one(const OneLaunchProj& p, const HelpPlan& plan, hipStre
   H.units = plan.units;
   H.h_begin = plan.units;
   H.h_end = plan.units + plan.hosts;
+  H.row_hosts = plan.row_hosts;
   H.host_rows = plan.host_rows;
   switch ((q.M + 3) / 4) {
     case 1: return launch_help_inst<1>(L, H, plan.wgs, s);

@@ -62,7 +62,8 @@ struct HelpArgs {
   int S;                   // K-ranges of P, each `per` 512-k steps
   int per;
   int units;               // groups * S: workgroup u < units runs unit (u % groups, u / groups)
-  int h_begin, h_end;      // F_B hosts
+  int h_begin, h_end;      // F_B hosts: row_hosts per group of kHelpHostM activation rows
+  int row_hosts;
   int host_rows;           // g1 rows per host, a multiple of 4, <= kHelpHostRows
 };
 
@@ -161,14 +162,20 @@ __device__ __forceinline__ void help_unit(const HelpArgs& h, int b, void* lds) {
   for (int q = h.units + b + h.units * lane; q < kFbMaxProducers; q += h.units * kWave) store_flag(h.sync + q, gen);
 }
 
-// F_B host `hid`: g1 rows [hid * host_rows, +host_rows) as four 16-row MFMA
-// tiles.  lds: the helper's LDS, W_b rows [kHelpHostRows][kHelpMaxRank]
-// (swizzled) then f_a [M][rank], both bf16.
+// F_B host `hid`: g1 rows [rg * host_rows, +host_rows) of the activation
+// rows [mg * kHelpHostM, +kHelpHostM) (hid = mg * row_hosts + rg) as four
+// 16-row MFMA tiles.  lds: the helper's LDS, W_b rows [kHelpHostRows]
+// [kHelpMaxRank] (swizzled) then the group's f_a [kHelpHostM][rank], both
+// bf16.
 __device__ __forceinline__ void help_host(const HelpArgs& h, int hid, void* lds_raw) {
   const int lane = lane_id();
   uint16_t* wb_lds = static_cast<uint16_t*>(lds_raw);
   uint16_t* fa_lds = wb_lds + kHelpHostRows * kHelpMaxRank;
-  const int row_base = hid * h.host_rows;
+  const int mg = hid / h.row_hosts;
+  const int rg = hid - mg * h.row_hosts;
+  const int m0 = mg * kHelpHostM;
+  const int mc = min(kHelpHostM, h.M - m0);
+  const int row_base = rg * h.host_rows;
   const int nrows = max(0, min(h.host_rows, h.n_b - row_base));
   const int K8b = h.rank >> 3;
   const int rl = lane & 15;
@@ -190,13 +197,13 @@ __device__ __forceinline__ void help_host(const HelpArgs& h, int hid, void* lds_
   unsigned* cursors = h.sync + kFbMaxProducers;
   const unsigned target = load_flag(cursors + hid) + 1u;
 
-  // The partials this host needs: the rank f_a columns of every row m (all
-  // n_ab in host 0, which also stores beta), two columns per 16-byte load,
-  // of every K-range.  A poll loads them all and succeeds when every one
-  // carries generation `target`.
-  const int cols = hid == 0 ? h.n_ab : h.rank;
+  // The partials this host needs: the rank f_a columns of its activation
+  // rows (all n_ab in the group's first host, which also stores their
+  // beta), two columns per 16-byte load, of every K-range.  A poll loads
+  // them all and succeeds when every one carries generation `target`.
+  const int cols = rg == 0 ? h.n_ab : h.rank;
   const int q2 = cols >> 1;
-  const int count = h.M * q2;
+  const int count = mc * q2;
   const uint32_t plane = static_cast<uint32_t>(h.M * h.n_ab * 8);
   const rsrc_t pres = make_rsrc(h.pairs, static_cast<uint32_t>(h.S) * plane);
   uint32_t off[kHelpPollItems];
@@ -206,7 +213,7 @@ __device__ __forceinline__ void help_host(const HelpArgs& h, int hid, void* lds_
     const int idx = e * kWave + lane;
     im[e] = idx / q2;
     ic[e] = 2 * (idx - im[e] * q2);
-    off[e] = idx < count ? static_cast<uint32_t>((im[e] * h.n_ab + ic[e]) * 8) : 0u;
+    off[e] = idx < count ? static_cast<uint32_t>(((m0 + im[e]) * h.n_ab + ic[e]) * 8) : 0u;
   }
   u32x4 pv[kHelpPollItems][kHelpMaxS];
   bool ok = false;
@@ -233,8 +240,8 @@ __device__ __forceinline__ void help_host(const HelpArgs& h, int hid, void* lds_
   // W_b copies issued before them): the wait below costs nothing, and no
   // later wait for the copies has to wait for the beta stores.
   wait_vmcnt<0>();
-  // P in the order s = 0..S-1, rounded to bf16: f_a to LDS, beta (host 0)
-  // to memory; NaN after a time-out.
+  // P in the order s = 0..S-1, rounded to bf16: f_a to LDS (row m - m0),
+  // beta (the group's first host) to memory; NaN after a time-out.
 #pragma unroll
   for (int e = 0; e < kHelpPollItems; ++e) {
     if (e * kWave + lane >= count) continue;
@@ -253,7 +260,7 @@ __device__ __forceinline__ void help_host(const HelpArgs& h, int hid, void* lds_
       *reinterpret_cast<uint32_t*>(fa_lds + m * h.rank + c) =
           ok ? pack_bf16x2(a0, a1) : (static_cast<uint32_t>(kBf16NaN) * 0x10001u);
     } else {
-      uint16_t* bp = h.beta + static_cast<int64_t>(m) * (h.n_ab - h.rank) + (c - h.rank);
+      uint16_t* bp = h.beta + static_cast<int64_t>(m0 + m) * (h.n_ab - h.rank) + (c - h.rank);
       bp[0] = ok ? f32_to_bf16(a0) : kBf16NaN;
       bp[1] = ok ? f32_to_bf16(a1) : kBf16NaN;
     }
@@ -264,15 +271,15 @@ __device__ __forceinline__ void help_host(const HelpArgs& h, int hid, void* lds_
 
   // g1[m, row] = bf16(sum_r f_a[m, r] * w_b[row, r]) on the matrix cores:
   // A = W_b (lane l: row l % 16 of the tile, k group l / 16, zero past rank),
-  // B = f_a (lane l: row m = l % 16, zero past M), the k-steps in order; lane
-  // l ends with rows 4 (l / 16) .. +3 of each tile for m = l % 16 (NaN f_a
-  // after a time-out makes g1 NaN too).
+  // B = f_a (lane l: row m0 + l % 16, zero past the group's rows), the
+  // k-steps in order; lane l ends with rows 4 (l / 16) .. +3 of each tile for
+  // m = m0 + l % 16 (NaN f_a after a time-out makes g1 NaN too).
   u32x4 fb[kHelpMaxRank / 32];
 #pragma unroll
   for (int s = 0; s < kHelpMaxRank / 32; ++s) {
     const int kc = 4 * s + kg;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(fa_lds + min(rl, h.M - 1) * h.rank + min(kc, K8b - 1) * 8);
-    fb[s] = (rl < h.M && kc < K8b) ? v : zero4();
+    const u32x4 v = *reinterpret_cast<const u32x4*>(fa_lds + min(rl, mc - 1) * h.rank + min(kc, K8b - 1) * 8);
+    fb[s] = (rl < mc && kc < K8b) ? v : zero4();
   }
   const bool vec = ((reinterpret_cast<uintptr_t>(h.g1) | (static_cast<uintptr_t>(h.n_b) * 2)) & 7u) == 0;
 #pragma unroll
@@ -287,8 +294,8 @@ __device__ __forceinline__ void help_host(const HelpArgs& h, int hid, void* lds_
                                                    __builtin_bit_cast(bf16x8, fb[s]), acc, 0, 0, 0);
     }
     const int r0 = 16 * tt + 4 * kg;
-    if (rl >= h.M || r0 >= nrows) continue;
-    uint16_t* dst = h.g1 + static_cast<int64_t>(rl) * h.n_b + row_base + r0;
+    if (rl >= mc || r0 >= nrows) continue;
+    uint16_t* dst = h.g1 + static_cast<int64_t>(m0 + rl) * h.n_b + row_base + r0;
     if (vec && r0 + 3 < nrows) {
       uint2 packed;
       packed.x = pack_bf16x2(acc[0], acc[1]);

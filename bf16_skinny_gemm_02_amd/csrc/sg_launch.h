@@ -121,12 +121,13 @@ hipError_t launch_mfma_fused(const DotProblem* segs, const sg_config_t* cfgs, in
                              const FusedFb& fb, int fb_after, hipStream_t s);
 // Geometry of the one-launch KDA projection's helper wave (sg_help.h): W_ab
 // rows per producer unit, 512-k steps per unit at most, K-ranges at most (so
-// K <= 8192), the largest M, g1 rows per F_B host at most, and the largest
-// rank (k-steps of 32 for the MFMA F_B).
+// K <= 8192), the largest M, activation rows and g1 rows per F_B host at
+// most, and the largest rank (k-steps of 32 for the MFMA F_B).
 constexpr int kHelpRows = 4;
 constexpr int kHelpSteps = 4;
 constexpr int kHelpMaxS = 4;
-constexpr int kHelpMaxM = 8;
+constexpr int kHelpMaxM = 8;   // measured: at 9..16 the two launches are faster
+constexpr int kHelpHostM = 8;
 constexpr int kHelpHostRows = 64;
 constexpr int kHelpMaxRank = 128;
 // K-ranges of the F_A/beta partials: one unit covers at most kHelpSteps
@@ -137,12 +138,14 @@ inline int help_ranges(int K) {
 }
 // LDS of the helper behind the four rings: a unit's activation rows
 // (kHelpSteps KiB per row, 4 * XQ rows), or a host's W_b rows (room for
-// kHelpHostRows rows of kHelpMaxRank) and f_a [M][rank], all bf16.
+// kHelpHostRows rows of kHelpMaxRank) and its f_a [<= kHelpHostM][rank], all
+// bf16.
 inline size_t help_lds_bytes(int M, int rank) {
   const size_t xq = static_cast<size_t>((M + 3) / 4);
   const size_t unit = static_cast<size_t>(kHelpSteps) * 4 * xq * 1024;
+  const size_t hm = static_cast<size_t>(M < kHelpHostM ? M : kHelpHostM);
   const size_t host = static_cast<size_t>(kHelpHostRows) * kHelpMaxRank * 2 +
-                      ((static_cast<size_t>(M) * rank * 2 + 15) & ~static_cast<size_t>(15));
+                      ((hm * rank * 2 + 15) & ~static_cast<size_t>(15));
   return unit > host ? unit : host;
 }
 
@@ -163,10 +166,11 @@ struct OneLaunchProj {
 };
 // The helper geometry: `groups` units of 4 W_ab rows per K-range, S
 // K-ranges of `per` 512-k steps (units = groups * S producer workgroups),
-// then `hosts` F_B hosts of host_rows g1 rows, all within the wgs Q/K/V/G
-// workgroups.  False when the shapes do not fit it.
+// then `hosts` F_B hosts, row_hosts of host_rows g1 rows for each group of
+// kHelpHostM activation rows, all within the wgs Q/K/V/G workgroups.  False
+// when the shapes do not fit it.
 struct HelpPlan {
-  int wgs, groups, S, per, units, hosts, host_rows;
+  int wgs, groups, S, per, units, hosts, row_hosts, host_rows;
 };
 bool help_plan(int M, int K, int n_qkvg, int n_ab, int rank, int n_b, HelpPlan* out);
 hipError_t launch_proj_one(const OneLaunchProj& p, const HelpPlan& plan, hipStream_t s);

@@ -39,7 +39,7 @@ def _ws(M, K=synth.HIDDEN, n_qkvg=4096, n_ab=136, device=None):
                        dtype=torch.uint8, device=device)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 12, 16, 17])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 12, 15, 16, 17, 24])
 def test_one_launch_matches_oracle(device, M):
     _say(f"kda_projection_fused M={M}")
     x, packed, w_b = synth.overlap_inputs(M, seed=3000 + M)
@@ -58,13 +58,14 @@ def test_one_launch_matches_oracle(device, M):
         assert _eq(q, q_s) and _eq(g1, g1_s) and _eq(beta, b_s)
 
 
-@pytest.mark.parametrize("M,K", [(2, 7168), (8, 7168), (5, 7168), (3, 4096), (7, 1032)])
+@pytest.mark.parametrize("M,K", [(2, 7168), (8, 7168), (5, 7168), (12, 7168), (16, 7168), (3, 4096),
+                                 (7, 1032), (13, 1032)])
 def test_one_launch_lattice_bitwise(device, M, K):
     """Integer-lattice inputs: every partial sum is exact in fp32, so qkvg,
     beta and g1 must equal the oracle bit for bit whatever the K-ranges,
     the order of the sums or the host that formed f_a.  K = 4096 and 1032
     give other producer counts (fewer K-ranges; one K-range that ends
-    inside a 512-k step)."""
+    inside a 512-k step); M = 12, 13, 16 take the one-stream schedule."""
     _say(f"kda_projection_fused lattice M={M} K={K}")
     x = synth.lattice_activation((M, K), seed=3100 + M)
     packed = synth.lattice_weight((4096 + 136, K), seed=3200 + M)
@@ -80,10 +81,10 @@ def test_one_launch_lattice_bitwise(device, M, K):
 
 def test_one_launch_one_workspace_across_shapes(device):
     """One workspace, zero-filled once, for a sequence of calls of changing M
-    (one launch at 1..8, the one-stream schedule at 9, 16 and 40): every call
+    (one launch at 1..8, the one-stream schedule at 9, 13, 16, 17 and 40): every call
     must equal a call on a fresh workspace, so the flags never fall out of
     step."""
-    seq = [2, 8, 16, 1, 4, 40, 3, 9, 2, 16]
+    seq = [2, 8, 16, 1, 4, 40, 3, 9, 17, 2, 13]
     ws = torch.zeros(max(_ws(M).numel() for M in seq), dtype=torch.uint8, device=device)
     for i, M in enumerate(seq):
         _say(f"shared workspace call {i}: M={M}")
@@ -96,7 +97,7 @@ def test_one_launch_one_workspace_across_shapes(device):
             assert _eq(u, v), (M, n)
 
 
-@pytest.mark.parametrize("M", [2, 8, 12])
+@pytest.mark.parametrize("M", [2, 8, 12, 16])
 def test_one_launch_graph_replay(device, M):
     """Capture the one-launch projection in a graph, replay it several times
     with eager work in between (outputs reset to NaN before each replay), and
@@ -127,7 +128,7 @@ def test_one_launch_graph_replay(device, M):
         del junk
 
 
-@pytest.mark.parametrize("M", [2, 7])
+@pytest.mark.parametrize("M", [2, 7, 13])
 def test_one_launch_writes_only_its_outputs(device, M):
     from tests.test_gpu_guards import Guarded, GuardedWs
     x, packed, w_b = synth.overlap_inputs(M, seed=3600 + M)

@@ -417,13 +417,15 @@ def test_one_launch_fits_and_workspace(lib):
     (ceil(ceil(K/512)/4) K-ranges x M x n_ab x 8 bytes) and the one-stream
     schedule's two workspaces."""
     fits = lambda *a: bool(lib.sg_kda_one_launch_fits(*a))  # noqa: E731
-    for M in range(0, 12):
+    for M in range(0, 20):
         assert fits(M, 7168, 4096, 136, 128, 1024) == (1 <= M <= 8), M
     assert fits(8, 8192, 4096, 136, 128, 1024)
     assert not fits(8, 8200, 4096, 136, 128, 1024)     # five K-ranges
     assert not fits(4, 7168, 4096, 138, 128, 1024)     # n_ab % 4
     assert not fits(4, 7168, 4096, 136, 256, 1024)     # rank > 128
     assert not fits(4, 7168, 2048, 136, 128, 1024)     # 128 workgroups < 136 units + 16 hosts
+    assert fits(8, 7168, 2432, 136, 128, 1024)          # 152 workgroups = 136 units + 16 hosts
+    assert not fits(8, 7168, 2416, 136, 128, 1024)
     assert not fits(4, 7164, 4096, 136, 128, 1024)     # K % 8
     assert fits(2, 1032, 4096, 136, 128, 1024) and fits(3, 4096, 4096, 136, 128, 1024)
     for M in (1, 2, 5, 8, 9, 16, 40):
