@@ -5,7 +5,9 @@
 One step is one pass of the whole hot path over the decode batch sizes
 M in {1, 2, 3, 4, 8, 16, 17, 32, 64}: for every M, the KDA projection (Q/K/V/G
 and F_A/beta -> F_B) through kda_projection_fused, and the latent-MoE tail
-(RMSNorm -> up-projection -> shared add).  At 2 <= M <= 8 the projection is one
+(RMSNorm -> up-projection -> shared add) through latent_moe_tail_fused (at
+17 <= M <= 64 its up-projection sums its two K splits inside the launch).  At
+1 <= M <= 8 the projection is one
 launch (the wave-split Q/K/V/G tile with a helper wave per workgroup that runs
 the F_A/beta -> F_B chain); elsewhere it is the one-stream schedule of
 kda_projection_overlap (the overlap gate is closed, its measured setting on
@@ -156,12 +158,13 @@ class TailCase:
         self.w_up = [w0] + [w0.clone() for _ in range(self.R - 1)]
         self.S = bf16_dev(S, device)
         self.out = torch.empty((M, D_HID), dtype=torch.bfloat16, device=device)
-        self.ws = torch.empty(max(sg.sg_workspace_bytes(sg.SG_OP_LATENT_TAIL, M, D_HID, D_LAT), 256),
+        # latent_moe_tail_fused's workspace: zero-filled once (its header), then reused.
+        self.ws = torch.zeros(sg.sg_workspace_bytes(sg.SG_OP_LATENT_TAIL_FUSED, M, D_HID, D_LAT),
                               dtype=torch.uint8, device=device)
 
     def call(self, r):
-        sg.latent_moe_tail(self.L, self.gamma, self.w_up[r], self.S, eps=1e-6, out=self.out,
-                           workspace=self.ws)
+        sg.latent_moe_tail_fused(self.L, self.gamma, self.w_up[r], self.S, eps=1e-6, out=self.out,
+                                 workspace=self.ws)
 
 
 def capture(fn, R, stream):

@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import (SG_KIND_MFMA_BLOCK, SG_KIND_GEMV_ROW, SG_KIND_GEMV_SMALLK, SG_KIND_GEMV_SPLITK,  # noqa: F401
                    SG_KIND_MFMA_TILE, SG_KIND_MFMA_WAVESPLIT, SG_KIND_NONE,
                    SG_KDA_FAB, SG_KDA_FAB_ALONE, SG_KDA_ONE_LAUNCH, SG_KDA_QKVG, SG_OP_FAB_FB, SG_OP_GEMM,
-                   SG_OP_LATENT_TAIL, SgConfig, SgTableEntry)
+                   SG_OP_LATENT_TAIL, SG_OP_LATENT_TAIL_FUSED, SgConfig, SgTableEntry)
 
 __all__ = [
     "sg_select", "sg_overlap_gate", "sg_overlap_max_tokens", "sg_workspace_bytes",
@@ -32,7 +32,7 @@ __all__ = [
     "sg_config_workspace_bytes", "sg_tuned_table", "sg_set_table_override",
     "skinny_gemm", "kda_qkvg_proj", "kda_fab_fb_proj", "kda_projection_overlap",
     "latent_moe_tail", "kda_projection_noalloc", "kda_fab_fb_proj_fused", "kda_projection_fused",
-    "HipEvent",
+    "latent_moe_tail_fused", "HipEvent",
     "library_path",
 ]
 
@@ -401,10 +401,18 @@ def kda_projection_noalloc(x: torch.Tensor, packed_w: torch.Tensor, w_b: torch.T
     return qkvg, g1, beta
 
 
+def latent_moe_tail_fused(*args, **kwargs):
+    """latent_moe_tail with the GEMM's K-split sum inside its launch: same
+    arguments and results.  A workspace given by the caller must have been
+    zero-filled once before its first use by this call and not altered
+    since."""
+    return latent_moe_tail(*args, _entry="latent_moe_tail_fused", **kwargs)
+
+
 def latent_moe_tail(latent: torch.Tensor, gamma: torch.Tensor, w_up: torch.Tensor,
                     shared: torch.Tensor | None = None, eps: float = 1e-6, *,
                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                    stream=None) -> torch.Tensor:
+                    stream=None, _entry: str = "latent_moe_tail") -> torch.Tensor:
     """out = bf16(shared + RMSNorm(latent; gamma, eps) @ w_up^T)."""
     _check_tensor(latent, "latent", 2)
     _check_tensor(w_up, "w_up", 2)
@@ -423,10 +431,10 @@ def latent_moe_tail(latent: torch.Tensor, gamma: torch.Tensor, w_up: torch.Tenso
             raise ValueError("shared must be a contiguous [M, d_hidden] tensor")
     _same_device(latent, gamma, w_up, shared)
     out = _out(out, (M, D), latent, "out")
-    ws, ws_bytes = _workspace(workspace, sg_workspace_bytes(SG_OP_LATENT_TAIL, M, D, d),
-                              latent.device)
-    st = _lib.load().latent_moe_tail(_ptr(latent), _ptr(gamma), ctypes.c_float(eps), _ptr(w_up),
-                                     _ptr(shared), _ptr(out), M, d, D, _ptr(ws), ws_bytes,
-                                     _stream(stream, latent.device))
-    _lib.check(st, "latent_moe_tail")
+    op = SG_OP_LATENT_TAIL_FUSED if _entry == "latent_moe_tail_fused" else SG_OP_LATENT_TAIL
+    ws, ws_bytes = _workspace(workspace, sg_workspace_bytes(op, M, D, d), latent.device)
+    st = getattr(_lib.load(), _entry)(_ptr(latent), _ptr(gamma), ctypes.c_float(eps), _ptr(w_up),
+                                      _ptr(shared), _ptr(out), M, d, D, _ptr(ws), ws_bytes,
+                                      _stream(stream, latent.device))
+    _lib.check(st, _entry)
     return out

@@ -29,6 +29,7 @@ SG_KIND_MFMA_BLOCK = 6
 SG_OP_GEMM = 0
 SG_OP_FAB_FB = 1
 SG_OP_LATENT_TAIL = 2
+SG_OP_LATENT_TAIL_FUSED = 3
 
 SG_KDA_QKVG = 0
 SG_KDA_FAB = 1
@@ -41,7 +42,7 @@ EXPORTED_SYMBOLS = (
     "sg_kda_select", "sg_kda_workspace_bytes",
     "sg_strerror", "sg_version", "skinny_gemm", "kda_qkvg_proj", "kda_fab_fb_proj",
     "kda_projection_overlap", "latent_moe_tail", "kda_projection_noalloc", "kda_fab_fb_proj_fused",
-    "kda_projection_fused", "sg_kda_one_launch_fits",
+    "kda_projection_fused", "sg_kda_one_launch_fits", "latent_moe_tail_fused",
     "sg_config_supported", "sg_config_workspace_bytes", "sg_tuned_table", "sg_set_table_override",
 )
 
@@ -94,6 +95,8 @@ _PROTOS = {
     "kda_projection_fused": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _vp, _sz, _vp]),
     "sg_kda_one_launch_fits": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "latent_moe_tail_fused": (_i32, [_vp, _vp, ctypes.c_float, _vp, _vp, _vp, _i32, _i32, _i32,
+                                     _vp, _sz, _vp]),
     "sg_config_supported": (_i32, [ctypes.POINTER(SgConfig), _i32, _i32, _i32]),
     "sg_config_workspace_bytes": (_sz, [ctypes.POINTER(SgConfig), _i32, _i32]),
     "sg_tuned_table": (_i32, [ctypes.POINTER(ctypes.POINTER(SgTableEntry))]),

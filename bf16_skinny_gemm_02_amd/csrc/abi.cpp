@@ -447,29 +447,49 @@ extern "C" int kda_projection_fused(const sg_bf16* x, const sg_bf16* packed_w, c
   return hip_status(sg::launch_proj_one(p, plan, static_cast<hipStream_t>(stream)));
 }
 
-extern "C" int latent_moe_tail(const sg_bf16* latent, const sg_bf16* gamma, float eps,
-                               const sg_bf16* w_up, const sg_bf16* shared, sg_bf16* out, int M,
-                               int d_latent, int d_hidden, void* ws, size_t ws_bytes,
-                               sg_stream_t stream) {
+namespace {
+
+// Validation shared by the two tail entry points: fills the configuration
+// and its RMSNorm placement; *empty when there is nothing to do.
+int validate_tail(const sg_bf16* latent, const sg_bf16* gamma, float eps, const sg_bf16* w_up,
+                  const sg_bf16* shared, sg_bf16* out, int M, int d_latent, int d_hidden,
+                  sg_config_t* cfg, bool* fold, bool* mfma_fold, bool* empty) {
+  *empty = false;
   if (M < 0 || d_latent < 0 || d_hidden < 0) return SG_ERR_INVALID_ARG;
   if (!isfinite(eps) || !(eps > 0.f)) return SG_ERR_INVALID_ARG;
-  sg_config_t c;
+  sg_config_t& c = *cfg;
   int st = sg_select(M, d_hidden, d_latent, shared != nullptr, &c);
   if (st != SG_OK) return st;
-  if (c.kind == SG_KIND_NONE) return SG_OK;
+  if (c.kind == SG_KIND_NONE) {
+    *empty = true;
+    return SG_OK;
+  }
   if (d_latent == 0) return SG_ERR_INVALID_ARG;  // RMS of an empty row is undefined
   if ((st = check_operand16(latent, d_latent, d_latent)) != SG_OK) return st;
   if ((st = check_operand16(gamma, d_latent, d_latent)) != SG_OK) return st;
   if ((st = check_operand16(w_up, d_latent, d_latent)) != SG_OK) return st;
   if ((st = check_output2(out, d_hidden, d_hidden)) != SG_OK) return st;
   if (shared != nullptr && (st = check_output2(shared, d_hidden, d_hidden)) != SG_OK) return st;
-  const bool fold = (M == 1) && (c.kind == SG_KIND_GEMV_SMALLK ||
-                                 ((c.kind == SG_KIND_GEMV_ROW || c.kind == SG_KIND_GEMV_SPLITK) &&
-                                  c.k_split == 1));
+  *fold = (M == 1) && (c.kind == SG_KIND_GEMV_SMALLK ||
+                       ((c.kind == SG_KIND_GEMV_ROW || c.kind == SG_KIND_GEMV_SPLITK) && c.k_split == 1));
   // 2 <= M <= 16 on the wave-split MFMA tile: the kernel normalises in registers.
-  const bool mfma_fold = sg::tail_folds(c, d_latent);
-  if (!fold && !mfma_fold && d_latent > sg::kNormMaxD) return SG_ERR_UNSUPPORTED;
-  if (!fold && !spans_ok(kMaxTileRows, d_latent, d_latent)) return SG_ERR_UNSUPPORTED;
+  *mfma_fold = sg::tail_folds(c, d_latent);
+  if (!*fold && !*mfma_fold && d_latent > sg::kNormMaxD) return SG_ERR_UNSUPPORTED;
+  if (!*fold && !spans_ok(kMaxTileRows, d_latent, d_latent)) return SG_ERR_UNSUPPORTED;
+  return SG_OK;
+}
+
+}  // namespace
+
+extern "C" int latent_moe_tail(const sg_bf16* latent, const sg_bf16* gamma, float eps,
+                               const sg_bf16* w_up, const sg_bf16* shared, sg_bf16* out, int M,
+                               int d_latent, int d_hidden, void* ws, size_t ws_bytes,
+                               sg_stream_t stream) {
+  sg_config_t c;
+  bool fold = false, mfma_fold = false, empty = false;
+  int st = validate_tail(latent, gamma, eps, w_up, shared, out, M, d_latent, d_hidden, &c, &fold,
+                         &mfma_fold, &empty);
+  if (st != SG_OK || empty) return st;
   const size_t need = sg_workspace_bytes(SG_OP_LATENT_TAIL, M, d_hidden, d_latent);
   if ((st = check_workspace(ws, ws_bytes, need)) != SG_OK) return st;
 
@@ -536,4 +556,43 @@ extern "C" int latent_moe_tail(const sg_bf16* latent, const sg_bf16* gamma, floa
   p.gamma = gamma;
   p.eps = eps;
   return enqueue_dot(p, c, ws, s);
+}
+
+extern "C" int latent_moe_tail_fused(const sg_bf16* latent, const sg_bf16* gamma, float eps,
+                                     const sg_bf16* w_up, const sg_bf16* shared, sg_bf16* out,
+                                     int M, int d_latent, int d_hidden, void* ws, size_t ws_bytes,
+                                     sg_stream_t stream) {
+  sg_config_t c;
+  bool fold = false, mfma_fold = false, empty = false;
+  int st = validate_tail(latent, gamma, eps, w_up, shared, out, M, d_latent, d_hidden, &c, &fold,
+                         &mfma_fold, &empty);
+  if (st != SG_OK || empty) return st;
+  const size_t need = sg_workspace_bytes(SG_OP_LATENT_TAIL_FUSED, M, d_hidden, d_latent);
+  if ((st = check_workspace(ws, ws_bytes, need)) != SG_OK) return st;
+  char* base = static_cast<char*>(ws) + sg::kSyncBytes;
+  if (fold || mfma_fold || !sg::tail_tags(c, d_hidden))
+    return latent_moe_tail(latent, gamma, eps, w_up, shared, out, M, d_latent, d_hidden, base,
+                           ws_bytes - sg::kSyncBytes, stream);
+  // RMSNorm into a bf16 buffer behind the header, then the GEMM whose second
+  // K split sums the first's tagged sums, adds the shared-expert partial and
+  // stores out.
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t tail_bytes = sg_workspace_bytes(SG_OP_LATENT_TAIL, M, d_hidden, d_latent);
+  sg::NormProblem np{latent, gamma, reinterpret_cast<uint16_t*>(base), M, d_latent, eps};
+  if (sg::launch_rmsnorm(np, s) != hipSuccess) return SG_ERR_HIP;
+  DotProblem p{};
+  p.a = reinterpret_cast<const uint16_t*>(base);
+  p.lda = d_latent;
+  p.w = w_up;
+  p.ldw = d_latent;
+  p.res = shared;
+  p.ldr = d_hidden;
+  p.out = out;
+  p.ldc = d_hidden;
+  p.M = M;
+  p.N = d_hidden;
+  p.K = d_latent;
+  p.pairs = reinterpret_cast<uint64_t*>(base + tail_bytes);
+  p.sync = static_cast<unsigned*>(ws);
+  return hip_status(launch_main(p, c, s));
 }

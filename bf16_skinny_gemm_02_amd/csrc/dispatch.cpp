@@ -392,6 +392,18 @@ bool tail_folds(const sg_config_t& c, int K) {
   return K > 0 && K <= 2048 && ceil_div(sps, 4) <= 16;
 }
 
+// Whether latent_moe_tail_fused sums the two K splits of the tail's GEMM in
+// the launch (the tile kernel's tagged hand-off), shared by the entry point
+// and the workspace size: the 4-wave tile with a 3-slot ring, exactly two K
+// splits, an activation tile of 8, 12 or 16 row groups (17 <= M <= 64), N
+// even (16-byte loads of two pairs), and at most 512 tiles per split (one
+// consumer cursor each in the hand-off header).
+bool tail_tags(const sg_config_t& c, int N) {
+  if (c.kind != SG_KIND_MFMA_TILE || c.k_split != 2 || c.waves != 4 || c.k_unroll != 3) return false;
+  if (c.m_tile != 32 && c.m_tile != 48 && c.m_tile != 64) return false;
+  return N > 0 && N % 2 == 0 && c.rows > 0 && ceil_div(N, c.rows) <= 512;
+}
+
 // Workspace regions start on 256-byte boundaries.
 size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 size_t ws_round(size_t b) { return round256(b); }
@@ -427,6 +439,17 @@ extern "C" size_t sg_workspace_bytes(int op, int M, int N, int K) {
       // The wave-split tile normalises in registers: no normalised copy.
       if (sg::tail_folds(c, K)) return part;
       return sg::round256(static_cast<size_t>(M) * static_cast<size_t>(K) * 2) + part;
+    }
+    case SG_OP_LATENT_TAIL_FUSED: {
+      // The hand-off header, latent_moe_tail's own workspace behind it, and
+      // the first K split's tagged sums where the GEMM sums its splits in the
+      // launch: 8 bytes per output of every 64-row tile and 16-row activation
+      // block (256 threads x 4 outputs per block).
+      const size_t base = sg_workspace_bytes(SG_OP_LATENT_TAIL, M, N, K);
+      const size_t pairs = sg::tail_tags(c, N)
+                               ? static_cast<size_t>(ceil_div(N, 64)) * static_cast<size_t>(c.m_tile / 16) * 8192
+                               : 0;
+      return kFabHeaderBytes + base + pairs;
     }
     default:
       return 0;

@@ -69,6 +69,9 @@ struct MfmaArgs {
   unsigned* arrive;  // in-launch hand-off (FB wave-split instances, sg_fused.h): the flag header
   int nslots;        // producer slots of the launch (one per workgroup of the F_A/beta segment)
   int tile_rows;     // wave-split kernel: weight rows per workgroup (16, or 17..32 with NT = 2)
+  uint64_t* pairs;   // tile kernel, TAG instances: the first split's tagged sums (thread order)
+  unsigned* sync;    // and the hand-off header (flag per tile of split 0, cursor per tile of split 1)
+  int ntiles;        // tiles per K split (TAG instances)
 };
 
 // One launch covers one or two segments (independent problems whose
@@ -200,11 +203,27 @@ __device__ __forceinline__ void store4(const MfmaArgs& g, const f32x4& acc, int 
 // MB: 16-row activation blocks (m_tile = 16*MB); NW: waves = 16-row weight
 // blocks per workgroup; C: ring slots; XQ: activation rows copied per chunk,
 // in groups of 4 (XQ*4 >= M).
-template <int MB, int NW, int C, int XQ, bool RES>
+//
+// TAG (two K splits, bf16 out, one segment): the K-split sum happens in the
+// launch.  A workgroup of split 0 (a producer) stores its fp32 sums as
+// 8-byte pairs (value, generation), one atomic store each, in thread order,
+// and advances its
+// tile's flag without waiting; the workgroup of split 1 for the same tile (a
+// consumer, dispatched after every producer) reads the pairs of the outputs
+// it holds until each carries the generation (a bounded wait: NaN after a
+// time-out), adds them to its own sums -- split 0's then split 1's, the order
+// of the reduction launch -- and stores out = bf16(sum + residual).
+// Generations as in sg_fused.h: the producer's is its flag + 1, the
+// consumer waits for its cursor + 1; both advance, and the tiles share out
+// the absent flags and cursors.
+template <int MB, int NW, int C, int XQ, bool RES, bool TAG = false>
 __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaLaunch L) {
   extern __shared__ u32x4 lds[];
   int tile, split;
   const MfmaArgs g = pick_segment(L, tile, split);
+  // TAG: this call's generation, read before anything else is in flight.
+  unsigned gen = 0u;
+  if constexpr (TAG) gen = load_flag(g.sync + (split == 0 ? tile : kFbMaxProducers + tile)) + 1u;
   constexpr int WROWS = 16 * NW;
   constexpr int XROWS = 4 * XQ;
   constexpr int SLOT = (WROWS + XROWS) * kPieces;
@@ -261,11 +280,12 @@ __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaLaunch L) {
   };
 
   // The residual goes out before the ring's first chunks: loads complete in
-  // issue order, so the chunk waits below never wait for it.
+  // issue order, so the chunk waits below never wait for it.  (TAG: only the
+  // consumer stores, so only it loads the residual.)
   const int n0 = tile_row0 + 16 * wave + 4 * kg;
   Res4 res[MB];
 #pragma unroll
-  for (int a = 0; a < MB; ++a) res[a] = load_res4<RES>(g, 16 * a + rl, n0);
+  for (int a = 0; a < MB; ++a) res[a] = load_res4<RES>(g, 16 * a + rl, n0, !TAG || split == 1);
 
 #pragma unroll
   for (int q = 0; q < C - 1; ++q) issue(q);
@@ -300,6 +320,75 @@ __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaLaunch L) {
   }
   wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
 
+  if constexpr (TAG) {
+    // The pairs of one tile in thread order: pair (a, v) of thread t at
+    // ((tile * MB + a) * 4 + v) * 64 NW + t, so that every store and every
+    // load of them is one contiguous 512-byte access per wave.  Producer and
+    // consumer threads hold the same outputs (same tile, same code).
+    const int lane64 = lane_id();
+    const int t = static_cast<int>(threadIdx.x);
+    uint64_t* tp = g.pairs + static_cast<int64_t>(tile) * MB * 4 * (NW * kWave) + t;
+    if (split == 0) {
+      // Producer: the sums of the outputs (m, n0 .. n0 + 3) this thread holds
+      // (every slot written, outputs past M or N included: the consumer
+      // ignores them).
+#pragma unroll
+      for (int a = 0; a < MB; ++a) {
+        const float v4[4] = {acc[a][0], acc[a][1], acc[a][2], acc[a][3]};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint64_t pair = static_cast<uint64_t>(__builtin_bit_cast(uint32_t, v4[v])) |
+                                (static_cast<uint64_t>(gen) << 32);
+          __hip_atomic_store(tp + (a * 4 + v) * (NW * kWave), pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      // The tile's flag (nothing in this launch waits for it: it keeps the
+      // generations for later calls), and this tile's share of the absent
+      // slots, at most one store per lane.
+      if (wave == 0) {
+        if (lane64 == 0) store_flag(g.sync + tile, gen);
+        for (int q = g.ntiles + tile + g.ntiles * lane64; q < kFbMaxProducers; q += g.ntiles * kWave)
+          store_flag(g.sync + q, gen);
+      }
+      return;
+    }
+    // Consumer: read the producer's pairs of this thread's outputs until all
+    // carry the generation, then add them first.
+    uint64_t pv[MB][4];
+    bool ok = false;
+    for (int polls = 0;;) {
+#pragma unroll
+      for (int a = 0; a < MB; ++a)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          pv[a][v] = __hip_atomic_load(tp + (a * 4 + v) * (NW * kWave), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bool mine = true;
+#pragma unroll
+      for (int a = 0; a < MB; ++a)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) mine = mine && static_cast<unsigned>(pv[a][v] >> 32) == gen;
+      ok = __builtin_amdgcn_ballot_w64(!mine) == 0;
+      if (ok || ++polls >= kFbSpinLimit) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+#pragma unroll
+    for (int a = 0; a < MB; ++a) {
+      const f32x4 p0 = f32x4{__builtin_bit_cast(float, static_cast<uint32_t>(pv[a][0])),
+                             __builtin_bit_cast(float, static_cast<uint32_t>(pv[a][1])),
+                             __builtin_bit_cast(float, static_cast<uint32_t>(pv[a][2])),
+                             __builtin_bit_cast(float, static_cast<uint32_t>(pv[a][3]))};
+      acc[a] = ok ? p0 + acc[a] : f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    }
+#pragma unroll
+    for (int a = 0; a < MB; ++a) store4(g, acc[a], 16 * a + rl, n0, split, res[a]);
+    if (wave == 0) {
+      unsigned* cursors = g.sync + kFbMaxProducers;
+      if (lane64 == 0) store_flag(cursors + tile, gen);
+      for (int q = g.ntiles + tile + g.ntiles * lane64; q < kFbMaxConsumers; q += g.ntiles * kWave)
+        store_flag(cursors + q, gen);
+    }
+    return;
+  }
 #pragma unroll
   for (int a = 0; a < MB; ++a) store4(g, acc[a], 16 * a + rl, n0, split, res[a]);
 }
@@ -777,9 +866,9 @@ __global__ __launch_bounds__(kBlkWaves * kWave) void block_kernel(MfmaLaunch L) 
 
 // One attribute call per kernel instance and device (the ring can exceed the default
 // 64 KiB of dynamic LDS).
-template <int MB, int NW, int C, int XQ, bool RES>
+template <int MB, int NW, int C, int XQ, bool RES, bool TAG = false>
 hipError_t launch_tile_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
-  auto kern = tile_kernel<MB, NW, C, XQ, RES>;
+  auto kern = tile_kernel<MB, NW, C, XQ, RES, TAG>;
   static std::atomic<bool> lds_set[kLdsAttrDevices];
   const hipError_t attr = ensure_lds_limit(reinterpret_cast<const void*>(kern), kMfmaMaxLds, lds_set);
   if (attr != hipSuccess) return attr;
@@ -945,12 +1034,15 @@ hipError_t launch_mfma_impl(const DotProblem* segs, const sg_config_t* cfgs, int
     g.arrive = fb != nullptr ? p.arrive : nullptr;
     g.nslots = 0;
     g.tile_rows = c.rows;
+    g.pairs = p.pairs;
+    g.sync = p.sync;
     const int KS = ksteps_of(p.K);
     const int S = c.k_split > 0 ? c.k_split : 1;
     g.sps = (KS + S - 1) / S;
     if (g.sps < 1) g.sps = 1;
     if (g.sps > max_sps) max_sps = g.sps;
     sgm.tiles = tiles_of(c, p.M, p.N);
+    g.ntiles = sgm.tiles;
     sgm.wg_begin = wgs;
     if (sgm.tiles <= 0) return hipErrorInvalidValue;
     wgs += sgm.tiles * S;
@@ -995,6 +1087,19 @@ hipError_t launch_mfma_impl(const DotProblem* segs, const sg_config_t* cfgs, int
         case 3: return res ? launch_tile_inst<1, 2, 4, 3, true>(L, wgs, s) : launch_tile_inst<1, 2, 4, 3, false>(L, wgs, s);
         case 4: return res ? launch_tile_inst<1, 2, 4, 4, true>(L, wgs, s) : launch_tile_inst<1, 2, 4, 4, false>(L, wgs, s);
         default: break;
+      }
+    }
+    // The in-launch K-split sum: one segment, two K splits, bf16 out.
+    if (segs[0].pairs != nullptr) {
+      const int S = cfg.k_split;
+      if (nseg != 1 || NW != 4 || C != 3 || S != 2 || segs[0].partial != nullptr || segs[0].sync == nullptr ||
+          L.seg[0].tiles > kFbMaxConsumers)
+        return hipErrorInvalidValue;
+      switch (XQ) {
+        case 8: return launch_tile_inst<2, 4, 3, 8, true, true>(L, wgs, s);
+        case 12: return launch_tile_inst<3, 4, 3, 12, true, true>(L, wgs, s);
+        case 16: return launch_tile_inst<4, 4, 3, 16, true, true>(L, wgs, s);
+        default: return hipErrorInvalidValue;
       }
     }
     if (NW == 4 && C == 3) {

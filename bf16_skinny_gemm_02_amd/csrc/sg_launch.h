@@ -75,6 +75,15 @@ struct DotProblem {
   // (GEMV) or workgroup (wave-split) then advances its flag, for an F_B role
   // later in the same grid (sg_fused.h).
   unsigned* arrive;
+  // In-launch K-split sum (the 4-wave tile kernel with exactly two K splits,
+  // bf16 out): the first split's workgroups store their fp32 sums with the
+  // call's generation as 8-byte pairs in `pairs` (in thread order, 8 KiB per
+  // 16 activation rows of a 64-row tile), the second split's
+  // workgroups read them, add them to their own and store the output; the
+  // generations live in the hand-off header `sync` (sg_fused.h: zero before
+  // the first call on a workspace).  No split-K partials, no second launch.
+  uint64_t* pairs;
+  unsigned* sync;
 };
 
 // The F_B role of a fused launch (see sg_fused.h): workgroups that wait for
@@ -192,6 +201,8 @@ bool wsplit_fold_fits(int K, int k_split);
 // Whether latent_moe_tail folds the RMSNorm into the GEMM for configuration c
 // (the single decision the entry point and the workspace size both use).
 bool tail_folds(const sg_config_t& c, int K);
+// Whether latent_moe_tail_fused sums the GEMM's two K splits in the launch.
+bool tail_tags(const sg_config_t& c, int N);
 size_t block_lds_bytes(int c);
 
 // out[m,n] = bf16( sum_{s<S} partial[s][m][n] + res[m,n] ).  The sum runs

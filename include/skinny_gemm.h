@@ -125,7 +125,8 @@ typedef struct {
 enum {
     SG_OP_GEMM = 0,         /* skinny_gemm / kda_qkvg_proj:  N = N            */
     SG_OP_FAB_FB = 1,       /* kda_fab_fb_proj:              N = n_ab         */
-    SG_OP_LATENT_TAIL = 2   /* latent_moe_tail:   N = d_hidden, K = d_latent  */
+    SG_OP_LATENT_TAIL = 2,  /* latent_moe_tail:   N = d_hidden, K = d_latent  */
+    SG_OP_LATENT_TAIL_FUSED = 3  /* latent_moe_tail_fused: the same N, K       */
 };
 
 /* Host-only: the configuration the library uses for C[M,N] = A[M,K] *
@@ -400,6 +401,29 @@ int latent_moe_tail(const sg_bf16 *latent, const sg_bf16 *gamma, float eps,
                     const sg_bf16 *w_up, const sg_bf16 *shared, sg_bf16 *out,
                     int M, int d_latent, int d_hidden,
                     void *ws, size_t ws_bytes, sg_stream_t stream);
+
+/* latent_moe_tail with the up-projection's K-split sum inside its launch:
+ * same arguments and results, bit for bit.  Where latent_moe_tail splits
+ * the GEMM's K in two on the 4-wave MFMA tile (17 <= M <= 64 at the Kimi-K3
+ * shapes) and then sums the splits in a second launch, here each workgroup
+ * of the first split stores its fp32 sums with the call's generation
+ * (workspace header) as 8-byte pairs, and the workgroup of the second split
+ * for the same tile reads them until all carry the generation (a bounded
+ * wait: NaN outputs on a time-out), adds them first and stores out =
+ * bf16(sum + S) -- the order of the reduction launch.  Elsewhere it runs
+ * latent_moe_tail with its workspace behind the header.
+ * Workspace: sg_workspace_bytes(SG_OP_LATENT_TAIL_FUSED, M, d_hidden,
+ * d_latent) = SG_FAB_HEADER_BYTES + latent_moe_tail's workspace + (where
+ * the splits are summed in the launch) ceil(d_hidden/64) * ceil(M/16) *
+ * 8192 bytes (the tagged sums of every 64-row tile and 16-row block).
+ * Its header (the first SG_FAB_HEADER_BYTES) must be zero before the first
+ * call on a workspace; each call keeps it consistent by itself (it is not
+ * zero afterwards and must not be altered), whatever the shapes of later
+ * calls.  Calls that share a workspace must not run concurrently. */
+int latent_moe_tail_fused(const sg_bf16 *latent, const sg_bf16 *gamma, float eps,
+                          const sg_bf16 *w_up, const sg_bf16 *shared, sg_bf16 *out,
+                          int M, int d_latent, int d_hidden,
+                          void *ws, size_t ws_bytes, sg_stream_t stream);
 
 /* For callers that cannot allocate device memory (code under hipGraph
  * capture, tight serving loops, harnesses that forbid allocation): the

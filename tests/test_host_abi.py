@@ -465,3 +465,30 @@ def test_projection_fused_validation(lib):
     # Shapes the one launch does not fit take the one-stream schedule and its checks.
     assert fp(M=20, ws_bytes=100) == E.SG_ERR_WORKSPACE
     assert fp(M=20, qkvg=NUL) == E.SG_ERR_INVALID_ARG
+
+
+def test_tail_fused_validation_and_workspace(lib):
+    """latent_moe_tail_fused validates like latent_moe_tail (the same status
+    for every bad argument, before anything is enqueued) and needs the
+    hand-off header plus latent_moe_tail's workspace plus, where the GEMM
+    sums its two K splits in the launch (17 <= M <= 64 at these shapes),
+    8 KiB per 64-row tile and 16-row activation block."""
+    E = _lib
+    for M in (1, 2, 16, 17, 40, 64, 65, 128, 256):
+        base = lib.sg_workspace_bytes(E.SG_OP_LATENT_TAIL, M, 7168, 2048)
+        pairs = 112 * -(-M // 16) * 8192 if 17 <= M <= 64 else 0
+        assert lib.sg_workspace_bytes(E.SG_OP_LATENT_TAIL_FUSED, M, 7168, 2048) == \
+            E.SG_FAB_HEADER_BYTES + base + pairs, M
+
+    def tails(fn, **kw):
+        args = dict(L=A16, g=B16, eps=1e-6, w=C16, S=NUL, out=ctypes.c_void_p(0x70000), M=20,
+                    d=2048, D=7168, ws=NUL, wsb=0)
+        args.update(kw)
+        return fn(args["L"], args["g"], ctypes.c_float(args["eps"]), args["w"], args["S"], args["out"],
+                  args["M"], args["d"], args["D"], args["ws"], args["wsb"], None)
+
+    for kw in ({"M": -1}, {"eps": 0.0}, {"eps": float("nan")}, {"L": NUL}, {"w": ODD}, {"out": NUL},
+               {"d": 0}, {"M": 0}, {}, {"ws": ctypes.c_void_p(0x90008), "wsb": 1 << 24}):
+        assert tails(lib.latent_moe_tail_fused, **kw) == tails(lib.latent_moe_tail, **kw), kw
+    need = lib.sg_workspace_bytes(E.SG_OP_LATENT_TAIL_FUSED, 20, 7168, 2048)
+    assert tails(lib.latent_moe_tail_fused, ws=ctypes.c_void_p(0x90000), wsb=need - 1) == E.SG_ERR_WORKSPACE
