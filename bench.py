@@ -218,7 +218,7 @@ TRAFFIC_SOURCES = ("bf16_skinny_gemm_02_amd/csrc/mfma.hip", "bf16_skinny_gemm_02
                    "bf16_skinny_gemm_02_amd/csrc/sg_help.h", "bf16_skinny_gemm_02_amd/csrc/sg_fused.h",
                    "bf16_skinny_gemm_02_amd/csrc/dispatch.cpp", "bf16_skinny_gemm_02_amd/csrc/abi.cpp",
                    "bf16_skinny_gemm_02_amd/csrc/tuned_table.inc")
-TRAFFIC_PMC = {"sources_sha256": "657c35009b092beba29462def63ae3426972e3cb481e57717280afe072c5a5e8", "bytes_per_call": 63196628}
+TRAFFIC_PMC = {"sources_sha256": "23559b3cdd6cd86fa62f84b8d28ca661323ffa34e052ab4896e5572821e536d0", "bytes_per_call": 63196143}
 
 
 def sources_sha256():
