@@ -131,3 +131,22 @@ def test_fused_writes_only_its_outputs(device, M):
         t.check(f"fused {n}")
     o = oracle.fab_fb(x, w_ab, w_b)
     assert_close(g1.bits(), o["g1_exact"], "guarded fused g1")
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_fused_timeout_gives_nan_and_recovers(device, M):
+    """The F_B workgroups' wait is bounded: with a header whose generations
+    never match, the call still returns with NaN g1 and beta; zero-filling
+    the header again restores the two-launch results."""
+    x, w_ab, w_b = synth.fab_fb_inputs(M, seed=2300 + M)
+    xd, ad, bd = dev(x, device), dev(w_ab, device), dev(w_b, device)
+    ws = _ws(M, 136, device=device)
+    ws[:sg._lib.SG_FAB_HEADER_BYTES].view(torch.int32)[4096:].fill_(1000)
+    g1, beta = sg.kda_fab_fb_proj_fused(xd, ad, bd, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(g1.float()).all() and torch.isnan(beta.float()).all()
+    ws.zero_()
+    g1b, betab = sg.kda_fab_fb_proj_fused(xd, ad, bd, workspace=ws)
+    g1_t, beta_t = sg.kda_fab_fb_proj(xd, ad, bd)
+    torch.cuda.synchronize()
+    assert _eq(g1b, g1_t) and _eq(betab, beta_t)

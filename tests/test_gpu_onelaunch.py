@@ -145,3 +145,33 @@ def test_one_launch_writes_only_its_outputs(device, M):
     assert_close(q.bits(), o["qkvg_exact"], "guarded qkvg")
     assert_close(g1.bits(), o["g1_exact"], "guarded g1")
     assert_close(beta.bits(), o["beta_exact"], "guarded beta")
+
+
+def _desync(ws):
+    """A header whose cursors are far ahead of its flags: every waiter's
+    generation (its cursor + 1) is one no producer of the next call stores
+    (its flag + 1), so each bounded wait runs to its limit."""
+    hdr = ws[:sg._lib.SG_FAB_HEADER_BYTES].view(torch.int32)
+    hdr[:4096].zero_()
+    hdr[4096:].fill_(1000)
+
+
+def test_one_launch_timeout_gives_nan_and_recovers(device):
+    """The hosts' wait is bounded: with a header whose generations never
+    match, the call still returns, qkvg (which does not wait) is right, and
+    g1 and beta are NaN; zero-filling the header again restores the results."""
+    M = 4
+    x, packed, w_b = synth.overlap_inputs(M, seed=3700)
+    xd, pd, wbd = dev(x, device), dev(packed, device), dev(w_b, device)
+    ws = _ws(M, device=device)
+    _desync(ws)
+    q, g1, beta = sg.kda_projection_fused(xd, pd, wbd, workspace=ws)
+    torch.cuda.synchronize()
+    o = oracle.projection_overlap(x, packed, w_b)
+    assert_close(host(q), o["qkvg_exact"], "qkvg after a time-out")
+    assert torch.isnan(g1.float()).all() and torch.isnan(beta.float()).all()
+    ws.zero_()
+    q2, g2, b2 = sg.kda_projection_fused(xd, pd, wbd, workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(host(g2), o["g1_exact"], "g1 after re-zeroing")
+    assert_close(host(b2), o["beta_exact"], "beta after re-zeroing")

@@ -139,3 +139,22 @@ def test_tail_fused_zero_weights_is_shared(device):
                                    workspace=_ws(M, device))
     torch.cuda.synchronize()
     assert np.array_equal(host(out), S)
+
+
+def test_tail_fused_timeout_gives_nan_and_recovers(device):
+    """The second split's wait is bounded: with a header whose generations
+    never match, the call still returns with NaN outputs; zero-filling the
+    header again restores latent_moe_tail's results."""
+    M = 24
+    L, gamma, w_up, S = synth.tail_inputs(M, seed=5600)
+    args = [dev(a, device) for a in (L, gamma, w_up, S)]
+    ws = _ws(M, device)
+    hdr = ws[:sg._lib.SG_FAB_HEADER_BYTES].view(torch.int32)
+    hdr[4096:].fill_(1000)  # consumers wait for 1001; producers tag 1
+    out = sg.latent_moe_tail_fused(*args, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all()
+    ws.zero_()
+    out2 = sg.latent_moe_tail_fused(*args, workspace=ws)
+    torch.cuda.synchronize()
+    assert _eq(out2, sg.latent_moe_tail(*args))
