@@ -53,7 +53,11 @@
  *    no-allocation scratch array (kda_projection_noalloc), and the
  *    configuration override a tuner may install (sg_set_table_override;
  *    empty unless set).  The entry points are thread-safe as long as the
- *    override does not change during calls.
+ *    override does not change during calls.  The one-launch entry points
+ *    (kda_fab_fb_proj_fused, kda_projection_fused, latent_moe_tail_fused)
+ *    keep their hand-off generations in a header at the start of the
+ *    caller's workspace: zero before the first call on it, left consistent
+ *    by every call, and not to be altered between calls.
  */
 #ifndef SKINNY_GEMM_H
 #define SKINNY_GEMM_H
