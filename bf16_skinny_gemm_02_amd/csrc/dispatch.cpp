@@ -381,9 +381,9 @@ namespace sg {
 
 // The one decision on the wave-split tile's RMSNorm fold (latent-MoE tail),
 // shared by the entry point and the workspace size: whole latent rows of at
-// most 2048 (4 16-byte chunks per lane), and at most 16 k-steps per wave so
-// that one wave's gamma range is one 64-piece copy.  The kernel launcher
-// checks the same limits again before it launches.
+// most 2048 (4 16-byte chunks per lane, normalised once into LDS), and at
+// most 16 k-steps per wave.  The kernel launcher checks the same limits
+// again before it launches.
 bool tail_folds(const sg_config_t& c, int K) {
   if (c.kind != SG_KIND_MFMA_WAVESPLIT) return false;
   const int ks = ceil_div(K, 32);

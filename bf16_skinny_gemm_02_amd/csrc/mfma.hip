@@ -398,17 +398,22 @@ __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaLaunch L) {
 constexpr int kSplitWaves = 4;
 constexpr int kHelpRing = 3;  // ring slots of the one-launch projection's tile
 // RMSNorm fold: the latent row is read in at most this many 16-byte chunks
-// per lane (d_latent <= 2048), and one wave's K-range of gamma fits one copy.
+// per lane (d_latent <= 2048).
 constexpr int kFoldChunks = 4;
 constexpr int kFoldMaxK = kFoldChunks * kWave * 8;
+// 16-byte pieces per normalised activation row in LDS (the longest row).
+constexpr int kFoldStride = kFoldChunks * kWave;
 
 // NORM (the latent-MoE tail): the activation rows are the raw latent L.  Each
-// wave first computes r[m] = 1/sqrt(mean(L[m,:]^2) + eps) for the rows it
-// owns (m = wave + 4j), from whole rows read into registers while its ring's
-// first chunks are in flight, and stages its K-range of gamma in LDS; every
-// activation fragment is then normalised in registers, n = bf16((L * r) *
-// gamma), before its MFMA: the rounding of the bf16 normalised latent that a
-// separate RMSNorm kernel would store.
+// wave reads whole rows of it into registers (rows m = wave + 4j), with the
+// whole of gamma, while its ring's first chunks are in flight; it computes
+// r[m] = 1/sqrt(mean(L[m,:]^2) + eps) and writes n = bf16((L * r) * gamma),
+// the rounding of the bf16 normalised latent that a separate RMSNorm kernel
+// would store, into an LDS region behind the rings that holds every
+// activation row over all of K.  One barrier, and the chunk loop reads its
+// activation fragments from there: the rings carry the weight rows only, so
+// no chunk refill waits for normalisation arithmetic and the latent crosses
+// L2 once per workgroup.
 //
 // FB (instances of the one-launch F_A/beta -> F_B branch only): workgroups in
 // L.fb's range run the F_B role, and the segment with `arrive` set hands its
@@ -435,8 +440,8 @@ __device__ __forceinline__ void wsplit_body(const MfmaLaunch& L, u32x4* lds) {
   if constexpr (FB) prev = g.arrive != nullptr ? load_flag(g.arrive + slot) : 0u;
   constexpr int XROWS = 4 * XQ;
   constexpr int WROWS = 16 * NT;
-  constexpr int SLOT = (WROWS + XROWS) * kPieces;
-  constexpr int P = 4 * NT + XQ;
+  constexpr int SLOT = (WROWS + (NORM ? 0 : XROWS)) * kPieces;  // NORM: weight rows only
+  constexpr int P = 4 * NT + (NORM ? 0 : XQ);                  // copies per chunk
   constexpr int kInFlight = (C - 2) * P;
   static_assert(XQ >= 1 && XQ <= 4 && C >= 2 && (NT == 1 || NT == 2), "configuration");
 
@@ -463,15 +468,10 @@ __device__ __forceinline__ void wsplit_body(const MfmaLaunch& L, u32x4* lds) {
   const rsrc_t xres = make_rsrc(g.a, static_cast<uint32_t>(((g.M - 1) * g.lda + g.K) * 2));
   const int dr = lane >> 4;
   const int dp = lane & 15;
-  // Behind the rings (NORM): 64 gamma pieces per wave, then r[16].
-  u32x4* gam = lds + kSplitWaves * C * SLOT + wave * kWave;
-  float* rsc = reinterpret_cast<float*>(lds + kSplitWaves * C * SLOT + kSplitWaves * kWave);
-  if constexpr (NORM) {
-    const rsrc_t gres = make_rsrc(g.gamma, static_cast<uint32_t>(g.K * 2));
-    const uint32_t off =
-        (lane < npieces && c0 + lane < K8) ? static_cast<uint32_t>((c0 + lane) * 16) : kOob;
-    copy16_to_lds(gres, gam, off);
-  }
+  // Behind the rings (NORM): the normalised activation, XROWS rows of
+  // kFoldStride 16-byte pieces, piece p of row m at (p & ~15) | ((p ^ m) & 15)
+  // so that the 16 rows of a fragment read fall in distinct banks.
+  u32x4* xs = lds + kSplitWaves * C * SLOT;
   auto issue = [&](int q) {
     u32x4* slot = ring + (q % C) * SLOT;
 #pragma unroll
@@ -483,25 +483,34 @@ __device__ __forceinline__ void wsplit_body(const MfmaLaunch& L, u32x4* lds) {
                                : kOob;
       copy16_to_lds_nt(wres, slot + 4 * i * kPieces, off);
     }
+    if constexpr (!NORM) {
 #pragma unroll
-    for (int j = 0; j < XQ; ++j) {
-      const int m = 4 * j + dr;
-      const int pc = kPieces * q + (dp ^ m);
-      const uint32_t off = (m < g.M && pc < npieces && c0 + pc < K8)
-                               ? static_cast<uint32_t>((m * g.lda + (c0 + pc) * 8) * 2)
-                               : kOob;
-      copy16_to_lds(xres, slot + (WROWS + 4 * j) * kPieces, off);
+      for (int j = 0; j < XQ; ++j) {
+        const int m = 4 * j + dr;
+        const int pc = kPieces * q + (dp ^ m);
+        const uint32_t off = (m < g.M && pc < npieces && c0 + pc < K8)
+                                 ? static_cast<uint32_t>((m * g.lda + (c0 + pc) * 8) * 2)
+                                 : kOob;
+        copy16_to_lds(xres, slot + (WROWS + 4 * j) * kPieces, off);
+      }
     }
   };
 
-  // The residual and (NORM) the whole latent rows go out before the ring's
-  // first chunks: loads complete in issue order, so neither the RMSNorm
-  // below nor the chunk waits of the loop wait for the other's loads.
+  // The residual and (NORM) gamma and the whole latent rows go out before the
+  // ring's first chunks: loads complete in issue order, so neither the
+  // RMSNorm below nor the chunk waits of the loop wait for the other's loads.
   Res4 res[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) res[nt] = load_res4<RES>(g, rl, row0 + 16 * nt + 4 * kg, wave == 0);
+  u32x4 gv[NORM ? kFoldChunks : 1];
   u32x4 lv[NORM ? XQ : 1][kFoldChunks];
   if constexpr (NORM) {
+    const rsrc_t gres = make_rsrc(g.gamma, static_cast<uint32_t>(g.K * 2));
+#pragma unroll
+    for (int i = 0; i < kFoldChunks; ++i) {
+      const int c = lane + kWave * i;
+      gv[i] = buf_load(gres, c < K8 ? static_cast<uint32_t>(c * 16) : kOob);
+    }
 #pragma unroll
     for (int j = 0; j < XQ; ++j) {
       const int m = wave + 4 * j;
@@ -518,7 +527,6 @@ __device__ __forceinline__ void wsplit_body(const MfmaLaunch& L, u32x4* lds) {
 #pragma unroll
   for (int q = 0; q < C - 1; ++q) issue(q);
 
-  float rn = 0.f;  // NORM: r of this lane's activation row (0 past the rows)
   if constexpr (NORM) {
 #pragma unroll
     for (int j = 0; j < XQ; ++j) {
@@ -533,15 +541,23 @@ __device__ __forceinline__ void wsplit_body(const MfmaLaunch& L, u32x4* lds) {
         }
       ss = wave_allreduce(ss);
       const int m = wave + 4 * j;
-      if (lane == 0)
-        rsc[m] = m < g.M ? __frsqrt_rn(ss / static_cast<float>(g.K) + g.eps) : 0.f;
+      const float r = m < g.M ? __frsqrt_rn(ss / static_cast<float>(g.K) + g.eps) : 0.f;
+#pragma unroll
+      for (int i = 0; i < kFoldChunks; ++i) {
+        const int c = lane + kWave * i;
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = pack_bf16x2(bf16_lo(lv[j][i][e]) * r * bf16_lo(gv[i][e]),
+                             bf16_hi(lv[j][i][e]) * r * bf16_hi(gv[i][e]));
+        xs[m * kFoldStride + ((c & ~15) | ((c ^ m) & 15))] = o;
+      }
     }
-    // r of every row is in LDS.  A plain barrier after the LDS writes: a
-    // __syncthreads would also wait for the ring's chunks in flight (the
+    // Every activation row is in LDS.  A plain barrier after the LDS writes:
+    // a __syncthreads would also wait for the ring's chunks in flight (the
     // global->LDS copies count as memory loads), which no other wave reads.
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
-    rn = rl < XROWS ? rsc[rl] : 0.f;
   }
 
   f32x4 acc[NT];
@@ -556,18 +572,13 @@ __device__ __forceinline__ void wsplit_body(const MfmaLaunch& L, u32x4* lds) {
     for (int t = 0; t < kChunkSteps; ++t) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) wf[t][nt] = slot[(16 * nt + rl) * kPieces + ((4 * t + kg) ^ rl)];
-      xf[t] = slot[(WROWS + xr) * kPieces + ((4 * t + kg) ^ xr)];
-    }
-    if constexpr (NORM) {
-#pragma unroll
-      for (int t = 0; t < kChunkSteps; ++t) {
-        const u32x4 gv = gam[kPieces * q + 4 * t + kg];
-        u32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          o[e] = pack_bf16x2(bf16_lo(xf[t][e]) * rn * bf16_lo(gv[e]),
-                             bf16_hi(xf[t][e]) * rn * bf16_hi(gv[e]));
-        xf[t] = o;
+      if constexpr (NORM) {
+        // Pieces past the wave's K-range meet zero weights; the clamp keeps
+        // the read inside the row.
+        const int p = min(c0 + kPieces * q + 4 * t + kg, kFoldStride - 1);
+        xf[t] = xs[xr * kFoldStride + ((p & ~15) | ((p ^ xr) & 15))];
+      } else {
+        xf[t] = slot[(WROWS + xr) * kPieces + ((4 * t + kg) ^ xr)];
       }
     }
     wait_lgkmcnt0();  // the slot is in registers before the copy below refills the ring
@@ -965,13 +976,14 @@ size_t block_lds_bytes(int c) {
 }
 
 size_t wsplit_lds_bytes(int c, int xq, bool norm, int nt) {
-  const size_t rings = static_cast<size_t>(kSplitWaves) * c * (16 * nt + 4 * xq) * kPieces * 16;
-  return rings + (norm ? kSplitWaves * kWave * 16 + 16 * sizeof(float) : 0);
+  // NORM: weight rows only in the rings, then the normalised activation rows.
+  const size_t rings = static_cast<size_t>(kSplitWaves) * c * (16 * nt + (norm ? 0 : 4 * xq)) * kPieces * 16;
+  return rings + (norm ? static_cast<size_t>(4 * xq) * kFoldStride * 16 : 0);
 }
 
 bool wsplit_fold_fits(int K, int k_split) {
-  // Whole latent rows in kFoldChunks chunks per lane; each wave's K-range of
-  // gamma in one 64-piece copy (at most 16 k-steps per wave).
+  // Whole latent rows in kFoldChunks chunks per lane, and at most 16 k-steps
+  // per wave.
   const int ks = ksteps_of(K);
   const int S = k_split > 0 ? k_split : 1;
   const int sps = (ks + S - 1) / S;
