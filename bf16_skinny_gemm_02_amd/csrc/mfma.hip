@@ -1280,6 +1280,7 @@ hipError_t launch_proj_one(const OneLaunchProj& p, const HelpPlan& plan, hipStre
   switch ((q.M + 3) / 4) {
     case 1: return launch_help_inst<1>(L, H, plan.wgs, s);
     case 2: return launch_help_inst<2>(L, H, plan.wgs, s);
+    case 3: return launch_help_inst<3>(L, H, plan.wgs, s);
     default: return hipErrorInvalidValue;
   }
 }

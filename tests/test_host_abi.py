@@ -410,7 +410,7 @@ def test_fab_fb_fused_validates_like_fab_fb(lib):
 
 def test_one_launch_fits_and_workspace(lib):
     """kda_projection_fused's geometry query and workspace size, restated from
-    the header's conditions: one launch at 1 <= M <= 8 for the KDA shapes
+    the header's conditions: one launch at 1 <= M <= 12 for the KDA shapes
     (K <= 8192, n_ab % 4 == 0, rank <= 128, enough Q/K/V/G workgroups for the
     F_A/beta units and F_B hosts), the one-stream schedule elsewhere; the
     workspace is the header plus the larger of the tagged partials
@@ -418,7 +418,7 @@ def test_one_launch_fits_and_workspace(lib):
     schedule's two workspaces."""
     fits = lambda *a: bool(lib.sg_kda_one_launch_fits(*a))  # noqa: E731
     for M in range(0, 20):
-        assert fits(M, 7168, 4096, 136, 128, 1024) == (1 <= M <= 8), M
+        assert fits(M, 7168, 4096, 136, 128, 1024) == (1 <= M <= 12), M
     assert fits(8, 8192, 4096, 136, 128, 1024)
     assert not fits(8, 8200, 4096, 136, 128, 1024)     # five K-ranges
     assert not fits(4, 7168, 4096, 138, 128, 1024)     # n_ab % 4
@@ -426,6 +426,10 @@ def test_one_launch_fits_and_workspace(lib):
     assert not fits(4, 7168, 2048, 136, 128, 1024)     # 128 workgroups < 136 units + 16 hosts
     assert fits(8, 7168, 2432, 136, 128, 1024)          # 152 workgroups = 136 units + 16 hosts
     assert not fits(8, 7168, 2416, 136, 128, 1024)
+    assert fits(12, 7168, 2688, 136, 128, 1024)         # 168 workgroups = 136 units + 32 hosts
+    assert not fits(12, 7168, 2672, 136, 128, 1024)
+    assert fits(12, 7168, 4096, 144, 128, 1024)          # a host polls 8 x 144 / 2 = 576 pieces
+    assert not fits(12, 7168, 4096, 148, 128, 1024)
     assert not fits(4, 7164, 4096, 136, 128, 1024)     # K % 8
     assert fits(2, 1032, 4096, 136, 128, 1024) and fits(3, 4096, 4096, 136, 128, 1024)
     for M in (1, 2, 5, 8, 9, 16, 40):
