@@ -358,7 +358,8 @@ extern "C" int kda_projection_overlap(const sg_bf16* x, const sg_bf16* packed_w,
     const DotProblem segs[2] = {q, f};
     const sg_config_t cfgs[2] = {cq, cf};
     hipError_t e = hipSuccess;
-    if (have_q && is_mfma(cq.kind) && is_mfma(cf.kind) && sg::mfma_same_instance(cq, cf)) {
+    if (have_q && is_mfma(cq.kind) && is_mfma(cf.kind) && cq.kind != SG_KIND_MFMA_WAVESPLIT &&
+        sg::mfma_same_instance(cq, cf)) {
       e = sg::launch_mfma(segs, cfgs, 2, sm);
     } else if (have_q && !is_mfma(cq.kind) && cq.kind != SG_KIND_GEMV_SMALLK &&
                !is_mfma(cf.kind) && sg::gemv_same_instance(cq, cf)) {

@@ -63,12 +63,12 @@ struct MfmaArgs {
   int64_t ldc2;
   int n_split;
   int M, N, K;
-  int sps;  // k-steps (32 k) per split
+  int sps;        // k-steps (32 k) per split
+  int tile_rows;  // wave-split kernel: weight rows per workgroup (16, or 17..32 with NT = 2)
   const uint16_t* gamma;  // RMSNorm fold (wave-split kernel): gamma[K], else unused
   float eps;
   unsigned* arrive;  // in-launch hand-off (FB wave-split instances, sg_fused.h): the flag header
   int nslots;        // producer slots of the launch (one per workgroup of the F_A/beta segment)
-  int tile_rows;     // wave-split kernel: weight rows per workgroup (16, or 17..32 with NT = 2)
   uint64_t* pairs;   // tile kernel, TAG instances: the first split's tagged sums (thread order)
   unsigned* sync;    // and the hand-off header (flag per tile of split 0, cursor per tile of split 1)
   int ntiles;        // tiles per K split (TAG instances)
@@ -81,6 +81,7 @@ struct MfmaArgs {
 struct MfmaSeg {
   MfmaArgs g;
   int tiles;
+  unsigned tiles_magic;  // floor(2^32 / tiles) (2^32 - 1 for one tile): local / tiles by multiply-high
   int wg_begin, wg_end;  // the segment's workgroups (empty range: unused)
 };
 struct MfmaLaunch {
@@ -89,19 +90,28 @@ struct MfmaLaunch {
 };
 
 // The segment's arguments are copied into registers once (uniform values in
-// SGPRs), so nothing re-reads the kernel arguments inside the loops.
+// SGPRs), so nothing re-reads the kernel arguments inside the loops.  ONE
+// (instances only ever launched with one segment): no selection, so the
+// kernel arguments come in one round of scalar loads and the first copies
+// go out sooner (measured: 0.1-0.5 us per launch).  The K-range index is a
+// multiply-high by the host's floor(2^32 / tiles), which is the quotient or
+// one less (local < 2^32), and one branch-free correction: no division, and
+// no branch for the compiler to schedule the argument loads around.
+template <bool ONE = false>
 __device__ __forceinline__ MfmaArgs pick_segment(const MfmaLaunch& L, int& tile, int& split,
                                                  int& local) {
   const int b = static_cast<int>(blockIdx.x);
-  const MfmaSeg sg = (b >= L.seg[1].wg_begin && b < L.seg[1].wg_end) ? L.seg[1] : L.seg[0];
+  const MfmaSeg sg = (ONE || !(b >= L.seg[1].wg_begin && b < L.seg[1].wg_end)) ? L.seg[0] : L.seg[1];
   local = b - sg.wg_begin;
-  split = local / sg.tiles;
+  const unsigned q = __umulhi(static_cast<unsigned>(local), sg.tiles_magic);
+  split = static_cast<int>((q + 1u) * static_cast<unsigned>(sg.tiles) <= static_cast<unsigned>(local) ? q + 1u : q);
   tile = local - split * sg.tiles;
   return sg.g;
 }
+template <bool ONE = false>
 __device__ __forceinline__ MfmaArgs pick_segment(const MfmaLaunch& L, int& tile, int& split) {
   int local;
-  return pick_segment(L, tile, split, local);
+  return pick_segment<ONE>(L, tile, split, local);
 }
 
 constexpr int kKStep = 32;       // k per MFMA
@@ -220,7 +230,7 @@ template <int MB, int NW, int C, int XQ, bool RES, bool TAG = false>
 __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaLaunch L) {
   extern __shared__ u32x4 lds[];
   int tile, split;
-  const MfmaArgs g = pick_segment(L, tile, split);
+  const MfmaArgs g = pick_segment<TAG>(L, tile, split);
   // TAG: this call's generation, read before anything else is in flight.
   unsigned gen = 0u;
   if constexpr (TAG) gen = load_flag(g.sync + (split == 0 ? tile : kFbMaxProducers + tile)) + 1u;
@@ -422,7 +432,7 @@ constexpr int kFoldStride = kFoldChunks * kWave;
 // NT: 16-row weight fragments per workgroup (1, or 2 for a workgroup of
 // 17..32 rows: the second fragment's rows past g.tile_rows read zeros and are
 // not stored), so that e.g. 7168 rows make exactly 256 workgroups of 28.
-template <int XQ, int C, bool NORM, bool RES, bool FB, int NT>
+template <int XQ, int C, bool NORM, bool RES, bool FB, int NT, bool ONE = true>
 __device__ __forceinline__ void wsplit_body(const MfmaLaunch& L, u32x4* lds) {
   if constexpr (FB) {
     static_assert(kSplitWaves * kWave == kFbThreads && !NORM && !RES, "F_B role instances");
@@ -433,7 +443,13 @@ __device__ __forceinline__ void wsplit_body(const MfmaLaunch& L, u32x4* lds) {
     }
   }
   int tile, split, slot;
-  const MfmaArgs g = pick_segment(L, tile, split, slot);
+  const MfmaArgs g = pick_segment<ONE>(L, tile, split, slot);
+  // Every argument the ring's first copies need, requested in one round of
+  // scalar loads (left to itself the compiler issues a second round behind
+  // a wait for the first, which holds back the copies).
+  if constexpr (ONE)
+    asm volatile("" ::"s"(g.w), "s"(g.ldw), "s"(g.a), "s"(g.lda), "s"(g.M), "s"(g.N), "s"(g.K), "s"(g.sps),
+                 "s"(g.tile_rows), "s"(g.res), "s"(g.ldr), "s"(g.out), "s"(g.ldc), "s"(g.gamma));
   // Hand-off: this workgroup's producer flag (slot = its index in the
   // segment), read before anything else is in flight.
   unsigned prev = 0u;
@@ -526,6 +542,9 @@ __device__ __forceinline__ void wsplit_body(const MfmaLaunch& L, u32x4* lds) {
 
 #pragma unroll
   for (int q = 0; q < C - 1; ++q) issue(q);
+  // Nothing below moves above the ring's first copies (the RMSNorm's waits
+  // for the latent rows would otherwise hold them back).
+  __builtin_amdgcn_sched_barrier(0);
 
   if constexpr (NORM) {
 #pragma unroll
@@ -644,7 +663,11 @@ __global__ __launch_bounds__((kSplitWaves + 1) * kWave) void wsplit_help_kernel(
     __syncthreads();
     return;
   }
-  wsplit_body<XQ, kHelpRing, false, false, false, 1>(L, lds);
+  // The main waves' quicker start (one segment, one round of argument
+  // loads) measured even at M <= 4, 0.5 us faster at M = 9..12 and 0.4 us
+  // slower at M = 5..8 (with every host sleep tried there), where the units'
+  // loads then queue behind more ring copies.
+  wsplit_body<XQ, kHelpRing, false, false, false, 1, XQ != 2>(L, lds);
 }
 
 // ---- two-dimensional LDS block tile (M > 64) ----------------------------------------
@@ -956,6 +979,14 @@ hipError_t launch_block_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
 
 int ksteps_of(int K) { return (K + kKStep - 1) / kKStep; }
 
+// floor(2^32 / tiles) for pick_segment's multiply-high (2^32 - 1 for one
+// tile): local * floor(2^32/t) / 2^32 falls short of local / t by less than
+// local / 2^32 < 1, so the estimate is the quotient or one less.
+unsigned tiles_magic_of(int tiles) {
+  if (tiles <= 1) return 0xFFFFFFFFu;
+  return static_cast<unsigned>(0x100000000ull / static_cast<unsigned>(tiles));
+}
+
 // Workgroup tiles of one K-range: c.rows weight rows each (16 * NW for
 // TILE, 16 or 17..32 for WAVESPLIT), or (BLOCK) 64 weight rows x 128
 // activation rows.
@@ -1054,6 +1085,7 @@ hipError_t launch_mfma_impl(const DotProblem* segs, const sg_config_t* cfgs, int
     if (g.sps < 1) g.sps = 1;
     if (g.sps > max_sps) max_sps = g.sps;
     sgm.tiles = tiles_of(c, p.M, p.N);
+    sgm.tiles_magic = tiles_magic_of(sgm.tiles);
     g.ntiles = sgm.tiles;
     sgm.wg_begin = wgs;
     if (sgm.tiles <= 0) return hipErrorInvalidValue;
@@ -1137,6 +1169,8 @@ hipError_t launch_mfma_impl(const DotProblem* segs, const sg_config_t* cfgs, int
     return hipErrorInvalidValue;
   }
   if (cfg.kind == SG_KIND_MFMA_WAVESPLIT) {
+    // One segment: the instances read only the first (pick_segment<true>).
+    if (nseg != 1) return hipErrorInvalidValue;
     const int C = cfg.k_unroll, XQ = cfg.m_tile / 4;
     // 16 rows per workgroup (one fragment), or 17..32 in steps of 4 (two).
     const int NT = cfg.rows == 16 ? 1 : 2;
@@ -1249,6 +1283,7 @@ hipError_t launch_proj_one(const OneLaunchProj& p, const HelpPlan& plan, hipStre
   g.sps = ksteps_of(q.K);
   g.tile_rows = 16;
   L.seg[0].tiles = plan.wgs;
+  L.seg[0].tiles_magic = tiles_magic_of(plan.wgs);
   L.seg[0].wg_begin = 0;
   L.seg[0].wg_end = plan.wgs;
   L.seg[1] = L.seg[0];
