@@ -74,6 +74,7 @@ struct GemvArgs {
 struct GemvSeg {
   GemvArgs g;
   int groups;
+  unsigned groups_magic;  // quotient_magic(groups)
   int wg_begin, wg_end;  // the segment's workgroups (empty range: unused)
 };
 struct GemvLaunch {
@@ -98,10 +99,19 @@ __global__ __launch_bounds__(NW * kWave) void gemv_kernel(GemvLaunch L) {
       return;
     }
   }
-  const GemvSeg sgm = (b >= L.seg[1].wg_begin && b < L.seg[1].wg_end) ? L.seg[1] : L.seg[0];
+  // FOLD instances take one segment: no selection, and every argument the
+  // first copies need requested in one round of scalar loads (left to itself
+  // the compiler issues a second round behind a wait for the first).
+  if constexpr (FOLD) {
+    const GemvSeg& s0 = L.seg[0];
+    asm volatile("" ::"s"(s0.g.a), "s"(s0.g.lda), "s"(s0.g.w), "s"(s0.g.ldw), "s"(s0.g.res), "s"(s0.g.ldr),
+                 "s"(s0.g.gamma), "s"(s0.g.N), "s"(s0.g.K), "s"(s0.g.sps), "s"(s0.groups), "s"(s0.groups_magic),
+                 "s"(s0.wg_begin));
+  }
+  const GemvSeg sgm = (FOLD || !(b >= L.seg[1].wg_begin && b < L.seg[1].wg_end)) ? L.seg[0] : L.seg[1];
   const GemvArgs g = sgm.g;
   const int local = b - sgm.wg_begin;
-  const int split = local / sgm.groups;
+  const int split = quotient_by(local, sgm.groups, sgm.groups_magic);
   const int group = local - split * sgm.groups;
   constexpr int kThreads = NW * kWave;
   const int tid = static_cast<int>(threadIdx.x);
@@ -359,8 +369,9 @@ namespace {
 hipError_t launch_gemv_impl(const DotProblem* segs, const sg_config_t* cfgs, int nseg,
                             const FusedFb* fb, int fb_after, hipStream_t s) {
   if (nseg < 1 || nseg > 2) return hipErrorInvalidValue;
+  // The fold instances read one segment only.
   if (nseg == 2 && (!gemv_same_instance(cfgs[0], cfgs[1]) || segs[0].M != segs[1].M ||
-                    (segs[0].gamma == nullptr) != (segs[1].gamma == nullptr)))
+                    segs[0].gamma != nullptr || segs[1].gamma != nullptr))
     return hipErrorInvalidValue;
   if (fb != nullptr && (fb_after < 0 || fb_after > nseg || cfgs[0].waves * kWave != kFbThreads ||
                         segs[0].gamma != nullptr))
@@ -413,6 +424,7 @@ hipError_t launch_gemv_impl(const DotProblem* segs, const sg_config_t* cfgs, int
     const int rows_per_wg = cfg.waves * cfg.rows;
     sgm.groups = (p.N + rows_per_wg - 1) / rows_per_wg;
     if (sgm.groups <= 0) return hipErrorInvalidValue;
+    sgm.groups_magic = quotient_magic(sgm.groups);
     sgm.wg_begin = wgs;
     wgs += sgm.groups * S;
     sgm.wg_end = wgs;

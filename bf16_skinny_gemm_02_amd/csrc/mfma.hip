@@ -81,7 +81,7 @@ struct MfmaArgs {
 struct MfmaSeg {
   MfmaArgs g;
   int tiles;
-  unsigned tiles_magic;  // floor(2^32 / tiles) (2^32 - 1 for one tile): local / tiles by multiply-high
+  unsigned tiles_magic;  // quotient_magic(tiles)
   int wg_begin, wg_end;  // the segment's workgroups (empty range: unused)
 };
 struct MfmaLaunch {
@@ -93,18 +93,16 @@ struct MfmaLaunch {
 // SGPRs), so nothing re-reads the kernel arguments inside the loops.  ONE
 // (instances only ever launched with one segment): no selection, so the
 // kernel arguments come in one round of scalar loads and the first copies
-// go out sooner (measured: 0.1-0.5 us per launch).  The K-range index is a
-// multiply-high by the host's floor(2^32 / tiles), which is the quotient or
-// one less (local < 2^32), and one branch-free correction: no division, and
-// no branch for the compiler to schedule the argument loads around.
+// go out sooner (measured: 0.1-0.5 us per launch).  The K-range index is
+// quotient_by(): no division, and no branch for the compiler to schedule
+// the argument loads around.
 template <bool ONE = false>
 __device__ __forceinline__ MfmaArgs pick_segment(const MfmaLaunch& L, int& tile, int& split,
                                                  int& local) {
   const int b = static_cast<int>(blockIdx.x);
   const MfmaSeg sg = (ONE || !(b >= L.seg[1].wg_begin && b < L.seg[1].wg_end)) ? L.seg[0] : L.seg[1];
   local = b - sg.wg_begin;
-  const unsigned q = __umulhi(static_cast<unsigned>(local), sg.tiles_magic);
-  split = static_cast<int>((q + 1u) * static_cast<unsigned>(sg.tiles) <= static_cast<unsigned>(local) ? q + 1u : q);
+  split = quotient_by(local, sg.tiles, sg.tiles_magic);
   tile = local - split * sg.tiles;
   return sg.g;
 }
@@ -979,14 +977,6 @@ hipError_t launch_block_inst(const MfmaLaunch& L, int wgs, hipStream_t s) {
 
 int ksteps_of(int K) { return (K + kKStep - 1) / kKStep; }
 
-// floor(2^32 / tiles) for pick_segment's multiply-high (2^32 - 1 for one
-// tile): local * floor(2^32/t) / 2^32 falls short of local / t by less than
-// local / 2^32 < 1, so the estimate is the quotient or one less.
-unsigned tiles_magic_of(int tiles) {
-  if (tiles <= 1) return 0xFFFFFFFFu;
-  return static_cast<unsigned>(0x100000000ull / static_cast<unsigned>(tiles));
-}
-
 // Workgroup tiles of one K-range: c.rows weight rows each (16 * NW for
 // TILE, 16 or 17..32 for WAVESPLIT), or (BLOCK) 64 weight rows x 128
 // activation rows.
@@ -1085,7 +1075,7 @@ hipError_t launch_mfma_impl(const DotProblem* segs, const sg_config_t* cfgs, int
     if (g.sps < 1) g.sps = 1;
     if (g.sps > max_sps) max_sps = g.sps;
     sgm.tiles = tiles_of(c, p.M, p.N);
-    sgm.tiles_magic = tiles_magic_of(sgm.tiles);
+    sgm.tiles_magic = quotient_magic(sgm.tiles);
     g.ntiles = sgm.tiles;
     sgm.wg_begin = wgs;
     if (sgm.tiles <= 0) return hipErrorInvalidValue;
@@ -1283,7 +1273,7 @@ hipError_t launch_proj_one(const OneLaunchProj& p, const HelpPlan& plan, hipStre
   g.sps = ksteps_of(q.K);
   g.tile_rows = 16;
   L.seg[0].tiles = plan.wgs;
-  L.seg[0].tiles_magic = tiles_magic_of(plan.wgs);
+  L.seg[0].tiles_magic = quotient_magic(plan.wgs);
   L.seg[0].wg_begin = 0;
   L.seg[0].wg_end = plan.wgs;
   L.seg[1] = L.seg[0];

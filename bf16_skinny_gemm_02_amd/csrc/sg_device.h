@@ -170,6 +170,13 @@ __device__ __forceinline__ float row16_allreduce(float v) {
   return v;
 }
 
+// n / d for 0 <= n, d with n + d < 2^32, given magic = quotient_magic(d)
+// (the host's): a multiply-high and one branch-free correction, no division.
+__device__ __forceinline__ int quotient_by(int n, int d, unsigned magic) {
+  const unsigned q = __umulhi(static_cast<unsigned>(n), magic);
+  return static_cast<int>((q + 1u) * static_cast<unsigned>(d) <= static_cast<unsigned>(n) ? q + 1u : q);
+}
+
 // Sum over all 64 lanes; every lane gets it.  After the 16-lane sums,
 // v_permlane16_swap exchanges odd and even rows and v_permlane32_swap the two
 // 32-lane halves.

@@ -105,6 +105,15 @@ size_t ws_round(size_t bytes);
 // Workspace layout for split-K partials of a [M,N] problem with S splits.
 inline size_t partial_floats(int S, int M, int N) { return (size_t)S * M * N; }
 
+// floor(2^32 / d) for the kernels' workgroup-index quotient (2^32 - 1 for
+// d = 1): n * floor(2^32/d) / 2^32 falls short of n / d by less than
+// n / 2^32 < 1, so its integer part is the quotient or one less, and
+// quotient_by() corrects it.
+inline unsigned quotient_magic(int d) {
+  if (d <= 1) return 0xFFFFFFFFu;
+  return static_cast<unsigned>(0x100000000ull / static_cast<unsigned>(d));
+}
+
 hipError_t launch_gemv(const DotProblem& p, const sg_config_t& cfg, hipStream_t s);
 hipError_t launch_smallk(const DotProblem& p, const sg_config_t& cfg, hipStream_t s);
 hipError_t launch_mfma(const DotProblem& p, const sg_config_t& cfg, hipStream_t s);
