@@ -701,7 +701,9 @@ template <int C, int RES>
 __global__ __launch_bounds__(kBlkWaves * kWave) void block_kernel(MfmaLaunch L) {
   extern __shared__ u32x4 lds[];
   int tile, split;
-  const MfmaArgs g = pick_segment(L, tile, split);
+  // RES == 2 (one segment with row-aligned residual and output) takes the
+  // single-segment selection.
+  const MfmaArgs g = pick_segment<RES == 2>(L, tile, split);
   constexpr int SLOT = (kBlkRows + kBlkM) * kPieces;
   constexpr int WC = kBlkRows / 4 / kBlkWaves;  // weight copies per wave per chunk
   constexpr int XC = kBlkM / 4 / kBlkWaves;     // activation copies per wave per chunk
