@@ -1236,7 +1236,7 @@ bool help_plan(int M, int K, int n_qkvg, int n_ab, int rank, int n_b, HelpPlan* 
   // Each lane of a host polls at most kHelpPollItems 16-byte loads per K-range.
   if ((M < kHelpHostM ? M : kHelpHostM) * (n_ab / 2) > kHelpPollItems * kWave) return false;
   const int XQ = (M + 3) / 4;
-  if (wsplit_lds_bytes(kHelpRing, XQ, false, 1) + help_lds_bytes(M, rank) > kMfmaMaxLds) return false;
+  if (wsplit_lds_bytes(kHelpRing, XQ, false, 1) + help_lds_bytes(M, rank, n_ab) > kMfmaMaxLds) return false;
   *out = p;
   return true;
 }
@@ -1249,7 +1249,7 @@ hipError_t launch_help_inst(const MfmaLaunch& L, const HelpArgs& H, int wgs, hip
   static std::atomic<bool> lds_set[kLdsAttrDevices];
   const hipError_t attr = ensure_lds_limit(reinterpret_cast<const void*>(kern), kMfmaMaxLds, lds_set);
   if (attr != hipSuccess) return attr;
-  const size_t lds = wsplit_lds_bytes(kHelpRing, XQ, false, 1) + help_lds_bytes(H.M, H.rank);
+  const size_t lds = wsplit_lds_bytes(kHelpRing, XQ, false, 1) + help_lds_bytes(H.M, H.rank, H.n_ab);
   return launch_kernel(kern, dim3(wgs), dim3((kSplitWaves + 1) * kWave), lds, s, L, H);
 }
 

@@ -166,13 +166,14 @@ __device__ __forceinline__ void help_unit(const HelpArgs& h, int b, void* lds) {
 // [rg * host_rows, +host_rows) of the activation
 // rows [mg * kHelpHostM, +kHelpHostM) (hid = mg * row_hosts + rg) as four
 // 16-row MFMA tiles.  lds: the helper's LDS, W_b rows [kHelpHostRows]
-// [kHelpMaxRank] (swizzled) then the group's f_a [kHelpHostM][rank], both
-// bf16.
+// [kHelpMaxRank] (swizzled) then the group's P [kHelpHostM][help_p_stride
+// (n_ab)] (f_a then beta columns), both bf16.
 template <int XQ>
 __device__ __forceinline__ void help_host(const HelpArgs& h, int hid, void* lds_raw) {
   const int lane = lane_id();
   uint16_t* wb_lds = static_cast<uint16_t*>(lds_raw);
-  uint16_t* fa_lds = wb_lds + kHelpHostRows * kHelpMaxRank;
+  uint16_t* p_lds = wb_lds + kHelpHostRows * kHelpMaxRank;
+  const int pst = help_p_stride(h.n_ab);
   const int mg = hid / h.row_hosts;
   const int rg = hid - mg * h.row_hosts;
   const int m0 = mg * kHelpHostM;
@@ -209,13 +210,14 @@ __device__ __forceinline__ void help_host(const HelpArgs& h, int hid, void* lds_
   const uint32_t plane = static_cast<uint32_t>(h.M * h.n_ab * 8);
   const rsrc_t pres = make_rsrc(h.pairs, static_cast<uint32_t>(h.S) * plane);
   uint32_t off[kHelpPollItems];
-  int im[kHelpPollItems], ic[kHelpPollItems];  // row m and first column of each load
+  int lo[kHelpPollItems];  // each load's two columns in p_lds (bf16 units)
 #pragma unroll
   for (int e = 0; e < kHelpPollItems; ++e) {
     const int idx = e * kWave + lane;
-    im[e] = idx / q2;
-    ic[e] = 2 * (idx - im[e] * q2);
-    off[e] = idx < count ? static_cast<uint32_t>(((m0 + im[e]) * h.n_ab + ic[e]) * 8) : 0u;
+    const int m = idx / q2;
+    const int c = 2 * (idx - m * q2);
+    off[e] = idx < count ? static_cast<uint32_t>(((m0 + m) * h.n_ab + c) * 8) : 0u;
+    lo[e] = m * pst + c;
   }
   u32x4 pv[kHelpPollItems][kHelpMaxS];
   bool ok = false;
@@ -252,34 +254,34 @@ __device__ __forceinline__ void help_host(const HelpArgs& h, int hid, void* lds_
   // W_b copies issued before them): the wait below costs nothing, and no
   // later wait for the copies has to wait for the beta stores.
   wait_vmcnt<0>();
-  // P in the order s = 0..S-1, rounded to bf16: f_a to LDS (row m - m0),
-  // beta (the group's first host) to memory; NaN after a time-out.
+  // P in the order s = 0..S-1, rounded to bf16, into LDS (row m - m0; the
+  // beta columns only in the group's first host); NaN after a time-out.
+  // One LDS store per load, no branch on the column: the per-item work is
+  // the sum, the rounding and the store.
+  const uint32_t nan2 = static_cast<uint32_t>(kBf16NaN) * 0x10001u;
 #pragma unroll
   for (int e = 0; e < kHelpPollItems; ++e) {
-    if (e * kWave + lane >= count) continue;
-    const int m = im[e];
-    const int c = ic[e];
+    if (e * kWave + lane >= count) break;
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int s = 0; s < kHelpMaxS; ++s) {
       const f32x4 f = __builtin_bit_cast(f32x4, pv[e][s]);
-      if (s < h.S) {
-        a0 += f[0];
-        a1 += f[2];
-      }
+      a0 += s < h.S ? f[0] : 0.f;
+      a1 += s < h.S ? f[2] : 0.f;
     }
-    if (c < h.rank) {  // rank is even: both columns are f_a
-      *reinterpret_cast<uint32_t*>(fa_lds + m * h.rank + c) =
-          ok ? pack_bf16x2(a0, a1) : (static_cast<uint32_t>(kBf16NaN) * 0x10001u);
-    } else {
-      uint16_t* bp = h.beta + static_cast<int64_t>(m0 + m) * (h.n_ab - h.rank) + (c - h.rank);
-      bp[0] = ok ? f32_to_bf16(a0) : kBf16NaN;
-      bp[1] = ok ? f32_to_bf16(a1) : kBf16NaN;
-    }
+    *reinterpret_cast<uint32_t*>(p_lds + lo[e]) = ok ? pack_bf16x2(a0, a1) : nan2;
   }
-  // f_a was written to LDS by this wave (in order for the LDS unit); keep the
+  // P was written to LDS by this wave (in order for the LDS unit); keep the
   // compiler from moving the reads below above those writes.
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (rg == 0) {  // the group's beta columns, from LDS to memory
+    const int nbeta = h.n_ab - h.rank;
+    for (int i = lane; i < mc * nbeta; i += kWave) {
+      const int m = i / nbeta;
+      const int j = i - m * nbeta;
+      h.beta[static_cast<int64_t>(m0 + m) * nbeta + j] = p_lds[m * pst + h.rank + j];
+    }
+  }
 
   // g1[m, row] = bf16(sum_r f_a[m, r] * w_b[row, r]) on the matrix cores:
   // A = W_b (lane l: row l % 16 of the tile, k group l / 16, zero past rank),
@@ -290,7 +292,7 @@ __device__ __forceinline__ void help_host(const HelpArgs& h, int hid, void* lds_
 #pragma unroll
   for (int s = 0; s < kHelpMaxRank / 32; ++s) {
     const int kc = 4 * s + kg;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(fa_lds + min(rl, mc - 1) * h.rank + min(kc, K8b - 1) * 8);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p_lds + min(rl, mc - 1) * pst + min(kc, K8b - 1) * 8);
     fb[s] = (rl < mc && kc < K8b) ? v : zero4();
   }
   const bool vec = ((reinterpret_cast<uintptr_t>(h.g1) | (static_cast<uintptr_t>(h.n_b) * 2)) & 7u) == 0;
@@ -328,7 +330,7 @@ __device__ __forceinline__ void help_host(const HelpArgs& h, int hid, void* lds_
   for (int q = nhosts + hid + nhosts * lane; q < kFbMaxConsumers; q += nhosts * kWave) store_flag(cursors + q, target);
 }
 
-// The helper wave of workgroup b.  lds: help_lds_bytes(M, rank) of dynamic
+// The helper wave of workgroup b.  lds: help_lds_bytes(M, rank, n_ab) of dynamic
 // LDS no other wave uses.
 template <int XQ>
 __device__ __forceinline__ void help_wave(const HelpArgs& h, int b, void* lds) {

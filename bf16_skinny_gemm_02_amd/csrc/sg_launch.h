@@ -154,16 +154,20 @@ inline int help_ranges(int K) {
   const int wsteps = (K / 8 + 63) / 64;
   return (wsteps + kHelpSteps - 1) / kHelpSteps;
 }
+// A host's P rows in LDS: n_ab columns padded to whole 16-byte pieces, so
+// that every row's f_a starts 16-byte aligned for the MFMA operand reads.
+__host__ __device__ inline int help_p_stride(int n_ab) { return (n_ab + 7) / 8 * 8; }
 // LDS of the helper behind the four rings: a unit's activation rows
 // (kHelpSteps KiB per row, 4 * XQ rows), or a host's W_b rows (room for
-// kHelpHostRows rows of kHelpMaxRank) and its f_a [<= kHelpHostM][rank], all
-// bf16.
-inline size_t help_lds_bytes(int M, int rank) {
+// kHelpHostRows rows of kHelpMaxRank) and its P [<= kHelpHostM]
+// [help_p_stride(n_ab)], all bf16.
+inline size_t help_lds_bytes(int M, int rank, int n_ab) {
+  (void)rank;
   const size_t xq = static_cast<size_t>((M + 3) / 4);
   const size_t unit = static_cast<size_t>(kHelpSteps) * 4 * xq * 1024;
   const size_t hm = static_cast<size_t>(M < kHelpHostM ? M : kHelpHostM);
   const size_t host = static_cast<size_t>(kHelpHostRows) * kHelpMaxRank * 2 +
-                      ((hm * rank * 2 + 15) & ~static_cast<size_t>(15));
+                      hm * static_cast<size_t>(help_p_stride(n_ab)) * 2;
   return unit > host ? unit : host;
 }
 
