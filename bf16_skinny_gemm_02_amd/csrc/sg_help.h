@@ -18,8 +18,9 @@
 //  * in workgroups [h_begin, h_end) (none of them a producer) acts as an F_B
 //    host: loads its rows of W_b, then reads every partial it needs until all
 //    carry this call's generation (a bounded spin), sums them in the fixed
-//    order s = 0..S-1 into bf16 f_a (in LDS) and, in the first host, beta,
-//    and computes its rows of g1 on the matrix cores.
+//    order s = 0..S-1 into a bf16 P tile in LDS (f_a, and in the group's
+//    first host beta, which it then stores), and computes its rows of g1 on
+//    the matrix cores.
 //
 // A partial tagged with the generation needs no separate flag: its producer
 // never waits for its store to complete, and the host's wait is the load of
