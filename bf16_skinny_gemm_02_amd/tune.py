@@ -192,6 +192,7 @@ def render_md(table: dict) -> str:
 
 def emit(table: dict, out_dir: Path | None = None) -> None:
     pkg = out_dir or PKG
+    pkg.mkdir(parents=True, exist_ok=True)
     (pkg / "tuned_table.json").write_text(json.dumps(table, indent=1) + "\n")
     (pkg / "csrc").mkdir(parents=True, exist_ok=True)
     (pkg / "csrc" / "tuned_table.inc").write_text(render_inc(table))
