@@ -170,7 +170,8 @@ bool supported(const sg_config_t& c, int M, int N, int K) {
       break;
     case SG_KIND_MFMA_TILE:
       if (!((c.waves == 2 && c.rows == 32 && c.k_unroll == kWideRing && M <= 16) ||
-            (c.waves == 4 && c.rows == 64 && c.k_unroll == kTileRing && M >= 17 && M <= 64)))
+            (c.waves == 4 && c.rows == 64 && c.k_unroll == kTileRing && M >= 17 && M <= 64) ||
+            (c.waves == kPairWaves && c.rows == kPairRows && c.k_unroll == kPairRing && M >= 17 && M <= 64)))
         return false;
       break;
     case SG_KIND_MFMA_BLOCK:

@@ -1146,7 +1146,15 @@ hipError_t launch_mfma_impl(const DotProblem* segs, const sg_config_t* cfgs, int
         default: break;
       }
     }
-    if (NW == 8 && C == 3 && !res) {  // the packed KDA projection, 2 <= M <= 64
+    if (NW == 8 && C == 3 && res) {  // table entries at 17 <= M <= 64
+      switch (XQ) {
+        case 8: return launch_tile_inst<2, 8, 3, 8, true>(L, wgs, s);
+        case 12: return launch_tile_inst<3, 8, 3, 12, true>(L, wgs, s);
+        case 16: return launch_tile_inst<4, 8, 3, 16, true>(L, wgs, s);
+        default: break;
+      }
+    }
+    if (NW == 8 && C == 3 && !res) {  // the packed KDA projection, 2 <= M <= 64, and table entries
       switch (XQ) {
         case 1: return launch_tile_inst<1, 8, 3, 1, false>(L, wgs, s);
         case 2: return launch_tile_inst<1, 8, 3, 2, false>(L, wgs, s);

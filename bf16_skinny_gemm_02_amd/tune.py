@@ -105,6 +105,8 @@ def candidates(N: int, K: int, lo: int, hi: int) -> list:
     if lo >= 17 and hi <= 64:
         for s in (1, 2, 3, 4, 7, 8, 14):
             add(MFMA_TILE, 64, 4, 3, _eff(ks, s))
+        for s in (1, 2, 4, 7, 8, 14):  # 8 waves, 128 rows: the packed projection's tile
+            add(MFMA_TILE, 128, 8, 3, _eff(ks, s))
     if lo >= 17:
         for s in (1, 2, 4, 7, 8):
             add(MFMA_BLOCK, 64, 4, 3, _eff(ks, s))

@@ -192,9 +192,10 @@ def test_kda_select_pairs_the_projection_tiles():
         assert (q["rows"], q["waves"], q["k_split"], q["grid"]) == (128, 8, 7, 224)
         assert (f["rows"], f["waves"], f["k_split"], f["grid"]) == (128, 8, 7, 14)
         assert q["m_tile"] == (4 * -(-M // 4) if M <= 16 else 16 * -(-M // 16))
-        # the standalone calls keep the table's own kernels
-        assert selection.select(M, 4096, 7168)[1]["rows"] in (16, 64)
-        assert selection.kda_select(2, M, 7168, 4096, 136)[1]["rows"] in (16, 64)
+        # the standalone calls keep the table's own kernels (the 128-row
+        # tile too where the measured table picked it)
+        assert selection.select(M, 4096, 7168)[1]["rows"] in (16, 64, 128)
+        assert selection.kda_select(2, M, 7168, 4096, 136)[1]["rows"] in (16, 64, 128)
     for M in (1, 65, 256):
         assert selection.kda_select(0, M, 7168, 4096, 136)[1] == selection.select(M, 4096, 7168)[1]
 
@@ -210,10 +211,13 @@ def test_overlap_gate_matches_oracle(lib):
 
 def test_workspace_bytes(lib):
     # QKVG for M <= 16 needs no workspace (one launch, no K split); the
-    # 64-row tile for M > 16 splits K four ways; F_A/beta always keeps partials.
+    # tiles for M > 16 split K (the 64-row tile four ways at M = 32, the
+    # measured table's 128-row tile eight ways at M = 64); F_A/beta always
+    # keeps partials.
     assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, 1, 4096, 7168) == 0
     assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, 8, 4096, 7168) == 0
-    assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, 64, 4096, 7168) == 4 * 64 * 4096 * 4
+    assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, 32, 4096, 7168) == 4 * 32 * 4096 * 4
+    assert lib.sg_workspace_bytes(_lib.SG_OP_GEMM, 64, 4096, 7168) == 8 * 64 * 4096 * 4
     # The standalone F_A/beta -> F_B call sizes its partials for the F_A/beta
     # configuration it runs alone, at most 8 K-ranges at the projection shape.
     for M in (1, 2, 4, 8, 16, 32, 64, 65, 200):
