@@ -7,7 +7,7 @@ M in {1, 2, 3, 4, 8, 16, 17, 32, 64}: for every M, the KDA projection (Q/K/V/G
 and F_A/beta -> F_B) through kda_projection_fused, and the latent-MoE tail
 (RMSNorm -> up-projection -> shared add) through latent_moe_tail_fused (at
 17 <= M <= 64 its up-projection sums its two K splits inside the launch).  At
-1 <= M <= 12 the projection is one
+1 <= M <= 16 the projection is one
 launch (the wave-split Q/K/V/G tile with a helper wave per workgroup that runs
 the F_A/beta -> F_B chain); elsewhere it is the one-stream schedule of
 kda_projection_overlap (the overlap gate is closed, its measured setting on
@@ -206,7 +206,7 @@ def time_graph(g, stream, reps, warm=3):
 BREAKDOWN_REPS = 20
 BREAKDOWN_REPEATS = 5   # per-M breakdown: median, and the lowest / highest repeat (p10 / p90 of 5)
 
-ROOFLINE_M = 8   # the projection call the roofline leg times (one launch at 1 <= M <= 12)
+ROOFLINE_M = 8   # the projection call the roofline leg times (one launch at 1 <= M <= 16)
 
 # HBM traffic of one projection call at M = ROOFLINE_M (its one launch) from two rocprofv3
 # --pmc runs of `bench.py --counters` (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 KiB per dispatch;
@@ -692,7 +692,7 @@ def main():
         "config": {
             "workload": "kda_decode_projection_sweep",
             "description": "KDA projection per M through kda_projection_fused (one launch at "
-                           "1 <= M <= 12, else the one-stream schedule the closed overlap gate picks; QKVG "
+                           "1 <= M <= 16, else the one-stream schedule the closed overlap gate picks; QKVG "
                            "[4096,7168] and F_A/beta [136,7168] -> F_B [1024,128], hipGraph), "
                            "plus the latent-MoE tail (RMSNorm 2048 -> up-proj [7168,2048] + "
                            "shared add) per M; value = mean us per projection call over the "

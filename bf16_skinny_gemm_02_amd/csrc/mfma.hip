@@ -662,7 +662,7 @@ __global__ __launch_bounds__((kSplitWaves + 1) * kWave) void wsplit_help_kernel(
     return;
   }
   // The main waves' quicker start (one segment, one round of argument
-  // loads) measured even at M <= 4, 0.5 us faster at M = 9..12 and 0.4 us
+  // loads) measured even at M <= 4, 0.5 us faster at M = 9..16 and 0.4 us
   // slower at M = 5..8 (with every host sleep tried there), where the units'
   // loads then queue behind more ring copies.
   wsplit_body<XQ, kHelpRing, false, false, false, 1, XQ != 2>(L, lds);
@@ -1316,6 +1316,7 @@ hipError_t launch_proj_one(const OneLaunchProj& p, const HelpPlan& plan, hipStre
     case 1: return launch_help_inst<1>(L, H, plan.wgs, s);
     case 2: return launch_help_inst<2>(L, H, plan.wgs, s);
     case 3: return launch_help_inst<3>(L, H, plan.wgs, s);
+    case 4: return launch_help_inst<4>(L, H, plan.wgs, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -226,12 +226,15 @@ __device__ __forceinline__ void help_host(const HelpArgs& h, int hid, void* lds_
   // before then only adds coherent loads to this workgroup's own stream.
   // The first poll therefore waits about that long (s_sleep counts 64
   // clocks per unit): measured best among none / 1.8 / 2.8 / 3.9 / 4.8 /
-  // 5.8 / 7.7 us of sleep, 0.4-0.9 us per call faster than polling at once;
-  // with 9..12 activation rows (larger units) 127 + 100 units measured best
-  // among +30 / +60 / +100 / +127 / +180 / +254 (0.6-1 us faster than +30).
+  // 5.8 / 7.7 us of sleep, 0.4-0.9 us per call faster than polling at once.
+  // Larger units land later: beyond 127 units, 30 more at M = 5..8, 100 at
+  // 9..12 (best among 30 / 60 / 100 / 127 / 180 / 254, 0.6-1 us faster than
+  // 30) and 16 (M - 4) at 13..16 (against 12 (M - 4) and 14 (M - 4)).
   __builtin_amdgcn_s_sleep(127);
   if constexpr (XQ == 2) __builtin_amdgcn_s_sleep(30);
-  if constexpr (XQ >= 3) __builtin_amdgcn_s_sleep(100);
+  if constexpr (XQ == 3) __builtin_amdgcn_s_sleep(100);
+  if constexpr (XQ == 4)
+    for (int z = 0; z < 16 * (h.M - 4); z += 16) __builtin_amdgcn_s_sleep(16);
   {
     int polls = 0;
     for (;;) {

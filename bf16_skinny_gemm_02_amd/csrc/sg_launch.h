@@ -144,7 +144,7 @@ hipError_t launch_mfma_fused(const DotProblem* segs, const sg_config_t* cfgs, in
 constexpr int kHelpRows = 4;
 constexpr int kHelpSteps = 4;
 constexpr int kHelpMaxS = 4;
-constexpr int kHelpMaxM = 12;  // measured: at 13..16 the two launches are faster
+constexpr int kHelpMaxM = 16;
 constexpr int kHelpHostM = 8;
 constexpr int kHelpHostRows = 64;
 constexpr int kHelpMaxRank = 128;

@@ -353,7 +353,7 @@ int kda_projection_overlap(const sg_bf16 *x, const sg_bf16 *packed_w, const sg_b
  * F_A/beta -> F_B chain beside the Q/K/V/G GEMM; the chain's two GEMMs are
  * themselves linked by programmatic dependent launch there]:
  * same outputs (qkvg, beta, g1; no f_a), same argument conventions.  Where
- * the shapes fit (1 <= M <= 12, K <= 8192, n_qkvg / 16 wave-split
+ * the shapes fit (1 <= M <= 16, K <= 8192, n_qkvg / 16 wave-split
  * workgroups of 16 Q/K/V/G rows that outnumber the F_A/beta units and F_B
  * hosts, n_ab % 4 == 0, min(M, 8) * n_ab <= 1152, rank <= 128), every Q/K/V/G
  * workgroup carries a fifth wave: in the first ceil(n_ab/4) *
@@ -365,7 +365,7 @@ int kda_projection_overlap(const sg_bf16 *x, const sg_bf16 *packed_w, const sg_b
  * generation (a bounded wait: on a time-out it writes NaN to g1 and beta),
  * sums them in fixed order into bf16 f_a and beta and computes its share of
  * g1 (at most 64 rows).  The Q/K/V/G rows are those of the wave-split tile
- * over all of K.  Elsewhere (M > 12, other shapes) the call runs the
+ * over all of K.  Elsewhere (M > 16, other shapes) the call runs the
  * one-stream schedule of kda_projection_overlap with its two workspaces
  * behind the header.
  * Results: qkvg as the wave-split tile computes it; beta and g1 from the

@@ -65,8 +65,8 @@ def test_one_launch_lattice_bitwise(device, M, K):
     beta and g1 must equal the oracle bit for bit whatever the K-ranges,
     the order of the sums or the host that formed f_a.  K = 4096 and 1032
     give other producer counts (fewer K-ranges; one K-range that ends
-    inside a 512-k step); M = 12 has two groups of activation rows, M = 13
-    and 16 take the one-stream schedule."""
+    inside a 512-k step); M = 12, 13 and 16 have two groups of activation
+    rows."""
     _say(f"kda_projection_fused lattice M={M} K={K}")
     x = synth.lattice_activation((M, K), seed=3100 + M)
     packed = synth.lattice_weight((4096 + 136, K), seed=3200 + M)
@@ -82,7 +82,7 @@ def test_one_launch_lattice_bitwise(device, M, K):
 
 def test_one_launch_one_workspace_across_shapes(device):
     """One workspace, zero-filled once, for a sequence of calls of changing M
-    (one launch at 1..12, the one-stream schedule at 13, 16, 17 and 40): every call
+    (one launch at 1..16, the one-stream schedule at 17 and 40): every call
     must equal a call on a fresh workspace, so the flags never fall out of
     step."""
     seq = [2, 8, 16, 1, 4, 40, 3, 9, 17, 2, 13]
