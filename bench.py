@@ -218,7 +218,7 @@ TRAFFIC_SOURCES = ("bf16_skinny_gemm_02_amd/csrc/mfma.hip", "bf16_skinny_gemm_02
                    "bf16_skinny_gemm_02_amd/csrc/sg_help.h", "bf16_skinny_gemm_02_amd/csrc/sg_fused.h",
                    "bf16_skinny_gemm_02_amd/csrc/dispatch.cpp", "bf16_skinny_gemm_02_amd/csrc/abi.cpp",
                    "bf16_skinny_gemm_02_amd/csrc/tuned_table.inc")
-TRAFFIC_PMC = {"sources_sha256": "a53219bbb4131229b9ebf9507b783d23ea9ee1a9960babdf367bf9b27414128b", "bytes_per_call": 62747112}
+TRAFFIC_PMC = {"sources_sha256": "a146d448ff33d3585672dbbf50558aadfb4e0c9c5be02b24c777ca0428d8de37", "bytes_per_call": 62781234}
 
 
 def sources_sha256():
