@@ -9,6 +9,8 @@
 // table can be tested on any host.
 #include <stddef.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -197,19 +199,126 @@ bool lookup(const sg_table_entry_t* t, int n, int M, int N, int K, sg_config_t* 
   return false;
 }
 
-}  // namespace
+// Checks the entries as sg_set_table_override documents and, if all pass,
+// makes them the override table.
+int install_override(const sg_table_entry_t* entries, int n) {
+  if (n < 0 || n > kMaxOverride || (n > 0 && entries == nullptr)) return SG_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i) {
+    const sg_table_entry_t& e = entries[i];
+    if (e.N < 1 || e.K < 8 || e.K % 8 != 0 || e.m_lo < 1 || e.m_hi < e.m_lo || e.m_hi > 256)
+      return SG_ERR_INVALID_ARG;
+    for (int M = e.m_lo; M <= e.m_hi; ++M)
+      if (!supported(from_entry(e, M, e.N), M, e.N, e.K)) return SG_ERR_UNSUPPORTED;
+  }
+  g_override_n.store(0, std::memory_order_release);
+  for (int i = 0; i < n; ++i) g_override[i] = entries[i];
+  g_override_n.store(n, std::memory_order_release);
+  return SG_OK;
+}
 
-extern "C" int sg_select(int M, int N, int K, int has_residual, sg_config_t* out) {
-  (void)has_residual;
-  if (out == nullptr) return SG_ERR_INVALID_ARG;
+// Parses "N,K,m_lo,m_hi,kind,rows,waves,k_unroll,k_split" entries separated
+// by ';' (blanks allowed around the numbers, an empty entry skipped).
+// Returns the number of entries, or -1 if the text is malformed or holds
+// more than kMaxOverride entries.
+int parse_table(const char* text, sg_table_entry_t* out) {
+  int n = 0;
+  const char* p = text;
+  while (*p != '\0') {
+    while (*p == ' ' || *p == ';') ++p;
+    if (*p == '\0') break;
+    if (n == kMaxOverride) return -1;
+    int32_t v[9];
+    for (int f = 0; f < 9; ++f) {
+      char* end = nullptr;
+      const long x = strtol(p, &end, 10);
+      if (end == p || x < INT32_MIN || x > INT32_MAX) return -1;
+      v[f] = static_cast<int32_t>(x);
+      p = end;
+      while (*p == ' ') ++p;
+      if (f < 8) {
+        if (*p != ',') return -1;
+        ++p;
+      }
+    }
+    if (*p != ';' && *p != '\0') return -1;
+    out[n++] = sg_table_entry_t{v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7], v[8]};
+  }
+  return n;
+}
+
+// The environment, read once, by the first configuration call of the
+// process:
+//   SKINNY_GEMM_LOG      non-empty and not "0": every sg_select and
+//                        sg_kda_select prints its choice on stderr.
+//   SKINNY_GEMM_TABLE    override entries (parse_table's format), installed
+//                        as sg_set_table_override would; a malformed or
+//                        unsupported value is reported on stderr and ignored.
+// Later sg_set_table_override calls replace what the environment installed.
+struct EnvState {
+  bool log;
+};
+
+const EnvState& env() {
+  static const EnvState state = [] {
+    EnvState s{false};
+    const char* log = getenv("SKINNY_GEMM_LOG");
+    s.log = log != nullptr && log[0] != '\0' && strcmp(log, "0") != 0;
+    const char* table = getenv("SKINNY_GEMM_TABLE");
+    if (table != nullptr && table[0] != '\0') {
+      sg_table_entry_t entries[kMaxOverride];
+      const int n = parse_table(table, entries);
+      const int st = n < 0 ? SG_ERR_INVALID_ARG : install_override(entries, n);
+      if (st != SG_OK)
+        fprintf(stderr, "skinny_gemm: SKINNY_GEMM_TABLE ignored (%s)\n",
+                n < 0 ? "malformed" : (st == SG_ERR_UNSUPPORTED ? "unsupported entry" : "invalid entry"));
+      else if (s.log)
+        fprintf(stderr, "skinny_gemm: SKINNY_GEMM_TABLE installed %d entries\n", n);
+    }
+    return s;
+  }();
+  return state;
+}
+
+const char* kind_name(int kind) {
+  static const char* const names[] = {"none", "gemv_row", "gemv_splitk", "gemv_smallk",
+                                      "mfma_tile", "mfma_wavesplit", "mfma_block"};
+  return (kind >= 0 && kind < 7) ? names[kind] : "?";
+}
+
+void log_choice(const char* what, int M, int N, int K, const sg_config_t& c, const char* source) {
+  fprintf(stderr,
+          "skinny_gemm: %s M=%d N=%d K=%d -> %s m_tile=%d rows=%d waves=%d k_unroll=%d "
+          "k_split=%d grid=%d (%s)\n",
+          what, M, N, K, kind_name(c.kind), c.m_tile, c.rows, c.waves, c.k_unroll, c.k_split,
+          c.grid, source);
+}
+
+// sg_select without the log line; *source names where the choice came from.
+int select_impl(int M, int N, int K, sg_config_t* out, const char** source) {
+  *source = "rule";
   const int st = rule_select(M, N, K, out);
   if (st != SG_OK || out->kind == SG_KIND_NONE) return st;
   // The override, then the measured table, replace the rule's choice where
   // they cover the shape.
   const int n_over = g_override_n.load(std::memory_order_acquire);
-  if (n_over > 0 && lookup(g_override, n_over, M, N, K, out)) return SG_OK;
-  lookup(kTunedTable, kTunedCount, M, N, K, out);
+  if (n_over > 0 && lookup(g_override, n_over, M, N, K, out)) {
+    *source = "override";
+    return SG_OK;
+  }
+  if (lookup(kTunedTable, kTunedCount, M, N, K, out)) *source = "measured table";
   return SG_OK;
+}
+
+}  // namespace
+
+extern "C" int sg_select(int M, int N, int K, int has_residual, sg_config_t* out) {
+  (void)has_residual;
+  if (out == nullptr) return SG_ERR_INVALID_ARG;
+  const bool log = env().log;
+  const char* source;
+  const int st = select_impl(M, N, K, out, &source);
+  if (log && st == SG_OK) log_choice("select", M, N, K, *out, source);
+  return st;
 }
 
 extern "C" int sg_config_supported(const sg_config_t* cfg, int M, int N, int K) {
@@ -233,18 +342,8 @@ extern "C" int sg_tuned_table(const sg_table_entry_t** entries) {
 }
 
 extern "C" int sg_set_table_override(const sg_table_entry_t* entries, int n) {
-  if (n < 0 || n > kMaxOverride || (n > 0 && entries == nullptr)) return SG_ERR_INVALID_ARG;
-  for (int i = 0; i < n; ++i) {
-    const sg_table_entry_t& e = entries[i];
-    if (e.N < 1 || e.K < 8 || e.K % 8 != 0 || e.m_lo < 1 || e.m_hi < e.m_lo || e.m_hi > 256)
-      return SG_ERR_INVALID_ARG;
-    for (int M = e.m_lo; M <= e.m_hi; ++M)
-      if (!supported(from_entry(e, M, e.N), M, e.N, e.K)) return SG_ERR_UNSUPPORTED;
-  }
-  g_override_n.store(0, std::memory_order_release);
-  for (int i = 0; i < n; ++i) g_override[i] = entries[i];
-  g_override_n.store(n, std::memory_order_release);
-  return SG_OK;
+  env();  // the environment's entries, if any, are in place before these replace them
+  return install_override(entries, n);
 }
 
 namespace {
@@ -474,10 +573,12 @@ extern "C" const char* sg_version(void) { return "0.1.0"; }
 extern "C" int sg_kda_select(int which, int M, int K, int n_qkvg, int n_ab, sg_config_t* out) {
   if (out == nullptr || which < SG_KDA_QKVG || which > SG_KDA_FAB_ALONE) return SG_ERR_INVALID_ARG;
   if (M < 0 || K < 0 || n_qkvg < 0 || n_ab < 0) return SG_ERR_INVALID_ARG;
+  const bool log = env().log;
   sg_config_t q, f;
-  int st = sg_select(M, n_qkvg, K, 0, &q);
+  const char *src_q, *src_f;
+  int st = select_impl(M, n_qkvg, K, &q, &src_q);
   if (st != SG_OK) return st;
-  if ((st = sg_select(M, n_ab, K, 0, &f)) != SG_OK) return st;
+  if ((st = select_impl(M, n_ab, K, &f, &src_f)) != SG_OK) return st;
   // The F_A/beta rows always leave fp32 partials for the F_B stage to sum, so
   // the small-K kind (which has no partial output) is replaced by the kind
   // the table uses for these M at larger K, over one K-range.
@@ -498,6 +599,7 @@ extern "C" int sg_kda_select(int which, int M, int K, int n_qkvg, int n_ab, sg_c
       f.grid = ceil_div(n_ab, 16);
     }
     f.k_split = 1;
+    src_f = "small-K replaced";
   }
   if (f.k_split < 1) f.k_split = 1;
   // At most one batch of partials for the F_B stage (kFabMaxSplit, one memory
@@ -513,6 +615,7 @@ extern "C" int sg_kda_select(int which, int M, int K, int n_qkvg, int n_ab, sg_c
   }
   if (which == SG_KDA_FAB_ALONE) {
     *out = f;
+    if (log) log_choice("kda F_A/beta alone", M, n_ab, K, f, src_f);
     return SG_OK;
   }
   // M = 1 with the Q/K/V/G rows on the whole-row GEMV: the F_A/beta rows join
@@ -525,6 +628,7 @@ extern "C" int sg_kda_select(int which, int M, int K, int n_qkvg, int n_ab, sg_c
     f.kind = SG_KIND_GEMV_SPLITK;
     f.k_split = effective_split(ceil_div(K / 8, 64), kFabGemvSplit);
     f.grid = ceil_div(n_ab, q.waves * q.rows) * f.k_split;
+    src_f = "second GEMV segment";
   }
   // 2 <= M <= 64: the table's wave-split and 64-row tiles give the Q/K/V/G
   // rows alone 256 workgroups, one per CU, so the F_A/beta segment would start
@@ -551,8 +655,13 @@ extern "C" int sg_kda_select(int which, int M, int K, int n_qkvg, int n_ab, sg_c
       both[i]->k_split = S;
       both[i]->grid = tiles[i] * S;
     }
+    src_q = src_f = "one-round 128-row pairing";
   }
   *out = (which == SG_KDA_QKVG) ? q : f;
+  if (log)
+    log_choice(which == SG_KDA_QKVG ? "kda Q/K/V/G" : "kda F_A/beta", M,
+               which == SG_KDA_QKVG ? n_qkvg : n_ab, K, *out,
+               which == SG_KDA_QKVG ? src_q : src_f);
   return SG_OK;
 }
 

@@ -53,7 +53,17 @@
  *    no-allocation scratch array (kda_projection_noalloc), and the
  *    configuration override a tuner may install (sg_set_table_override;
  *    empty unless set).  The entry points are thread-safe as long as the
- *    override does not change during calls.  The one-launch entry points
+ *    override does not change during calls.
+ *  - Environment, read once by the first configuration call of the process
+ *    (sg_select, sg_kda_select, sg_set_table_override or any entry point):
+ *    SKINNY_GEMM_LOG (set, not "0") prints every configuration choice on
+ *    stderr with its source (rule, measured table, override, KDA pairing);
+ *    SKINNY_GEMM_TABLE installs override entries, each nine integers
+ *    "N,K,m_lo,m_hi,kind,rows,waves,k_unroll,k_split" (the fields of
+ *    sg_table_entry_t), entries separated by ';', checked as
+ *    sg_set_table_override checks them; a malformed or unsupported value is
+ *    reported on stderr and ignored.  sg_set_table_override replaces what
+ *    the environment installed.  The one-launch entry points
  *    (kda_fab_fb_proj_fused, kda_projection_fused, latent_moe_tail_fused)
  *    keep their hand-off generations in a header at the start of the
  *    caller's workspace: zero before the first call on it, left consistent

@@ -137,3 +137,24 @@ def test_oracle_rounding_under_sanitizers(oracle_driver):
     got = _run_oracle(oracle_driver, text)
     want = oracle.round_bf16(np.array(vals, dtype=np.float64))
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("text,installed", [
+    ("4096,7168,2,4,5,32,4,3,2", True),
+    (" ; 4096 , 7168 , 2 , 4 , 5 , 32 , 4 , 3 , 2 ;;", True),
+    ("4096,7168,2,4,5,32,4,3", False),
+    ("99999999999999999999,7168,2,4,5,32,4,3,2", False),
+    ("-4096,7168,2,4,5,32,4,3,2", False),
+    (",,,,,,,,", False),
+    ("4096,7168,2,4,5,32,4,3,2;" * 70, False),
+    ("x" * 5000, False),
+])
+def test_environment_table_parser_under_sanitizers(select_driver, text, installed):
+    # The environment is read by the first configuration call; whatever the
+    # text, it is installed or reported, and nothing reads out of bounds.
+    env = dict(ENV, SKINNY_GEMM_TABLE=text, SKINNY_GEMM_LOG="1")
+    res = subprocess.run([str(select_driver)], capture_output=True, text=True, env=env, timeout=300)
+    assert res.returncode == 0, res.stderr[-4000:]
+    head = [ln for ln in res.stderr.splitlines() if "SKINNY_GEMM_TABLE" in ln]
+    assert len(head) == 1
+    assert ("installed 1 entries" in head[0]) == installed, head
