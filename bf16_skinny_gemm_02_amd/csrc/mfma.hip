@@ -290,10 +290,27 @@ __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaLaunch L) {
   // The residual goes out before the ring's first chunks: loads complete in
   // issue order, so the chunk waits below never wait for it.  (TAG: only the
   // consumer stores, so only it loads the residual.)
+  // Eight waves over 128 weight rows x 64 activation rows (QUAD): wave w
+  // reads weight rows 32 (w & 3) .. +31 and activation rows 32 (w >> 2) ..
+  // +31, four fragments per k-step instead of one weight and four activation
+  // fragments, 20% fewer LDS reads for the same MFMAs (each output keeps its
+  // k order).  The copies are the same.  acc[2 f + a]: weight fragment f,
+  // activation fragment a.
+  constexpr bool QUAD = NW == 8 && MB == 4 && !TAG;
+  const int wq = wave & 3;
+  const int wm = wave >> 2;
   const int n0 = tile_row0 + 16 * wave + 4 * kg;
   Res4 res[MB];
+  if constexpr (QUAD) {
 #pragma unroll
-  for (int a = 0; a < MB; ++a) res[a] = load_res4<RES>(g, 16 * a + rl, n0, !TAG || split == 1);
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        res[2 * f + a] = load_res4<RES>(g, 32 * wm + 16 * a + rl, tile_row0 + 32 * wq + 16 * f + 4 * kg);
+  } else {
+#pragma unroll
+    for (int a = 0; a < MB; ++a) res[a] = load_res4<RES>(g, 16 * a + rl, n0, !TAG || split == 1);
+  }
 
 #pragma unroll
   for (int q = 0; q < C - 1; ++q) issue(q);
@@ -310,21 +327,42 @@ __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaLaunch L) {
     __builtin_amdgcn_s_barrier();
     issue(q + C - 1);
     const u32x4* slot = lds + (q % C) * SLOT;
-    u32x4 wf[kChunkSteps], xf[kChunkSteps][MB];
+    if constexpr (QUAD) {
+      u32x4 wf[kChunkSteps][2], xf[kChunkSteps][2];
 #pragma unroll
-    for (int t = 0; t < kChunkSteps; ++t) {
-      wf[t] = slot[wrow + ((4 * t + kg) ^ rl)];
+      for (int t = 0; t < kChunkSteps; ++t) {
 #pragma unroll
-      for (int a = 0; a < MB; ++a) {
-        // Rows past the copied ones only feed outputs that are not stored.
-        const int xr = (16 * a + rl < XROWS) ? 16 * a + rl : XROWS - 1;
-        xf[t][a] = slot[(WROWS + xr) * kPieces + ((4 * t + kg) ^ (xr & 15))];
+        for (int f = 0; f < 2; ++f) wf[t][f] = slot[(32 * wq + 16 * f + rl) * kPieces + ((4 * t + kg) ^ rl)];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const int x0 = 32 * wm + 16 * a + rl;
+          const int xr = x0 < XROWS ? x0 : XROWS - 1;
+          xf[t][a] = slot[(WROWS + xr) * kPieces + ((4 * t + kg) ^ (xr & 15))];
+        }
       }
+#pragma unroll
+      for (int t = 0; t < kChunkSteps; ++t)
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int a = 0; a < 2; ++a) acc[2 * f + a] = mfma16(wf[t][f], xf[t][a], acc[2 * f + a]);
+    } else {
+      u32x4 wf[kChunkSteps], xf[kChunkSteps][MB];
+#pragma unroll
+      for (int t = 0; t < kChunkSteps; ++t) {
+        wf[t] = slot[wrow + ((4 * t + kg) ^ rl)];
+#pragma unroll
+        for (int a = 0; a < MB; ++a) {
+          // Rows past the copied ones only feed outputs that are not stored.
+          const int xr = (16 * a + rl < XROWS) ? 16 * a + rl : XROWS - 1;
+          xf[t][a] = slot[(WROWS + xr) * kPieces + ((4 * t + kg) ^ (xr & 15))];
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kChunkSteps; ++t)
+#pragma unroll
+        for (int a = 0; a < MB; ++a) acc[a] = mfma16(wf[t], xf[t][a], acc[a]);
     }
-#pragma unroll
-    for (int t = 0; t < kChunkSteps; ++t)
-#pragma unroll
-      for (int a = 0; a < MB; ++a) acc[a] = mfma16(wf[t], xf[t][a], acc[a]);
   }
   wait_vmcnt<0>();  // no copy may land after the workgroup's LDS is released
 
@@ -397,8 +435,17 @@ __global__ __launch_bounds__(NW * kWave) void tile_kernel(MfmaLaunch L) {
     }
     return;
   }
+  if constexpr (QUAD) {
 #pragma unroll
-  for (int a = 0; a < MB; ++a) store4(g, acc[a], 16 * a + rl, n0, split, res[a]);
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        store4(g, acc[2 * f + a], 32 * wm + 16 * a + rl, tile_row0 + 32 * wq + 16 * f + 4 * kg, split,
+               res[2 * f + a]);
+  } else {
+#pragma unroll
+    for (int a = 0; a < MB; ++a) store4(g, acc[a], 16 * a + rl, n0, split, res[a]);
+  }
 }
 
 // ---- wave-split LDS tile (M <= 16) ------------------------------------------------
