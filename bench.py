@@ -218,7 +218,7 @@ TRAFFIC_SOURCES = ("bf16_skinny_gemm_02_amd/csrc/mfma.hip", "bf16_skinny_gemm_02
                    "bf16_skinny_gemm_02_amd/csrc/sg_help.h", "bf16_skinny_gemm_02_amd/csrc/sg_fused.h",
                    "bf16_skinny_gemm_02_amd/csrc/dispatch.cpp", "bf16_skinny_gemm_02_amd/csrc/abi.cpp",
                    "bf16_skinny_gemm_02_amd/csrc/tuned_table.inc")
-TRAFFIC_PMC = {"sources_sha256": "a146d448ff33d3585672dbbf50558aadfb4e0c9c5be02b24c777ca0428d8de37", "bytes_per_call": 62781234}
+TRAFFIC_PMC = {"sources_sha256": "14b6eeb13f43906ceaae7fc958a3535114d1d1a171670fbc73ebf36a1024df21", "bytes_per_call": 62781725}
 
 
 def sources_sha256():
